@@ -1,0 +1,359 @@
+"""Plain, slow, float64 CPU oracle for the alias-free BigVGAN decoder.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import this
+module: only the tests, the smoke check and the benchmark's CPU-baseline
+leg use it.  It shares no code with the HIP library (different language,
+different filter designer, different loops) and imports nothing from the
+package next to it.
+
+Every function takes float arrays (normally float32 values promoted to
+float64) and computes in float64 throughout, with no intermediate float32
+rounding, by the plain definition the pages give.  Library primitives serve
+as single steps (a matrix product per convolution tap); there is no tiling,
+fusion or reordering beyond the definitions.
+
+Sources (cited by page and item, never by line):
+  [H3]  docs.rs source page of ``cortiq_engine/audiovae.rs`` (cortiq-engine
+        0.5.74) -- MiniMax-H3 audio VAE decoder, the authority.
+  [LTX] docs.rs source page of ``cortiq_engine/ltxaudio.rs`` (cortiq-engine
+        0.6.3) -- LTX-2.5 BigVGAN v2 vocoder, second source.
+
+Readings taken where the pages are silent or disagree are listed in the
+function docstrings (and in the design notes of the repository).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+FILTER_LEN = 12  # [H3] constant FILTER_LEN: both resampling filters have 12 taps
+
+
+# --------------------------------------------------------------------------
+# Filter design  ([H3] bessel_i0, sinc, kaiser_sinc)
+# --------------------------------------------------------------------------
+
+def bessel_i0(x: float) -> float:
+    """Modified Bessel function I0 by its power series ([H3] ``bessel_i0``).
+
+    term_k = term_{k-1} * (x / 2k)^2, summed from 1; at most 39 terms,
+    stopping once a term falls below 1e-18 of the running sum.
+    """
+    s = 1.0
+    term = 1.0
+    for k in range(1, 40):
+        term *= (x / (2.0 * k)) ** 2
+        s += term
+        if term < 1e-18 * s:
+            break
+    return s
+
+
+def sinc(x: float) -> float:
+    """Normalised sinc sin(pi x)/(pi x), 1 at 0 ([H3] ``sinc``)."""
+    if x == 0.0:
+        return 1.0
+    return math.sin(math.pi * x) / (math.pi * x)
+
+
+def kaiser_params(half_width: float, k: int) -> Tuple[float, float]:
+    """Attenuation A and Kaiser beta of the design ([H3] ``kaiser_sinc``).
+
+    A = 2.285 (k/2 - 1) pi (4 half_width) + 7.95; beta by Kaiser's piecewise
+    rule (A > 50, A >= 21, else 0).
+    """
+    half = k // 2
+    delta_f = 4.0 * half_width
+    a = 2.285 * (half - 1.0) * math.pi * delta_f + 7.95
+    if a > 50.0:
+        beta = 0.1102 * (a - 8.7)
+    elif a >= 21.0:
+        beta = 0.5842 * (a - 21.0) ** 0.4 + 0.07886 * (a - 21.0)
+    else:
+        beta = 0.0
+    return a, beta
+
+
+def kaiser_sinc_f64(cutoff: float, half_width: float, k: int) -> np.ndarray:
+    """Kaiser-windowed sinc lowpass, unit sum, unrounded float64 ([H3] ``kaiser_sinc``).
+
+    Tap i sits at the half-integer t = i - k/2 + 0.5 (even length); its
+    window is I0(beta sqrt(1 - r^2)) / I0(beta) with r = 2i/(k-1) - 1; its
+    value is 2 cutoff * window * sinc(2 cutoff t).  The taps are then divided
+    by their sum.
+    """
+    half = k // 2
+    _, beta = kaiser_params(half_width, k)
+    denom = bessel_i0(beta)
+    n = k - 1.0
+    taps = []
+    for i in range(k):
+        r = 2.0 * i / n - 1.0
+        win = bessel_i0(beta * math.sqrt(max(1.0 - r * r, 0.0))) / denom
+        t = -half + i + 0.5
+        taps.append(2.0 * cutoff * win * sinc(2.0 * cutoff * t))
+    f = np.array(taps, dtype=np.float64)
+    return f / f.sum()
+
+
+def kaiser_sinc(cutoff: float = 0.25, half_width: float = 0.3, k: int = FILTER_LEN) -> np.ndarray:
+    """The designed taps as the model stores them: float64 design rounded to
+    float32 ([H3] ``kaiser_sinc`` ends with a cast to f32).  Returned as float64
+    holding float32 values."""
+    return kaiser_sinc_f64(cutoff, half_width, k).astype(np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# Activation1d  ([H3] Activation1d::apply, fir_pad, SnakeBeta;
+#                [LTX] Aliasing::upsample / downsample, SnakeBeta::forward)
+# --------------------------------------------------------------------------
+
+def _clamp_index(n_out: int, shift: int, n: int) -> np.ndarray:
+    return np.clip(np.arange(n_out) - shift, 0, n - 1)
+
+
+def upsample2(x: np.ndarray, up: np.ndarray, ratio: int = 2) -> np.ndarray:
+    """Anti-aliased x2 upsample over the last axis ([LTX] ``Aliasing::upsample``,
+    [H3] first half of ``Activation1d::apply``).
+
+    pad = K/ratio - 1 replicate samples each side; transposed convolution with
+    the filter at stride ``ratio`` and gain ``ratio``:
+    u[ratio*i + j] += ratio * xp[i] * up[j]; then trim
+    pad*ratio + (K-ratio)//2 on the left and pad*ratio + ceil((K-ratio)/2) on
+    the right, leaving ratio*T samples.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    up = np.asarray(up, dtype=np.float64)
+    k = up.shape[0]
+    n = x.shape[-1]
+    pad = k // ratio - 1
+    pad_l = pad * ratio + (k - ratio) // 2
+    pad_r = pad * ratio + (k - ratio + 1) // 2
+    tp = n + 2 * pad
+    xp = x[..., _clamp_index(tp, pad, n)]
+    full = (tp - 1) * ratio + k
+    u = np.zeros(x.shape[:-1] + (full,), dtype=np.float64)
+    for j in range(k):
+        # positions ratio*i + j for i in [0, tp)
+        u[..., j: j + ratio * (tp - 1) + 1: ratio] += ratio * xp * up[j]
+    return u[..., pad_l: full - pad_r]
+
+
+def snake_beta(v: np.ndarray, log_alpha: np.ndarray, log_beta: np.ndarray) -> np.ndarray:
+    """SnakeBeta with log-scale parameters ([H3] ``SnakeBeta``, [LTX] ``SnakeBeta::forward``):
+    v + sin(exp(a_c) v)^2 / (exp(b_c) + 1e-9), channel c on axis -2."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.exp(np.asarray(log_alpha, dtype=np.float64))[:, None]
+    b = np.exp(np.asarray(log_beta, dtype=np.float64))[:, None]
+    s = np.sin(a * v)
+    return v + s * s / (b + 1e-9)
+
+
+def downsample2(m: np.ndarray, down: np.ndarray, ratio: int = 2) -> np.ndarray:
+    """Lowpass x2 downsample over the last axis ([H3] ``fir_pad`` as called by
+    ``Activation1d::apply``, [LTX] ``Aliasing::downsample``).
+
+    Replicate-pad K/2 - 1 on the left (even K) and K/2 on the right, then the
+    FIR at stride ``ratio``: y[t] = sum_j down[j] * buf[ratio*t + j], with
+    (n + pad_l + pad_r - K)/ratio + 1 outputs.
+    """
+    m = np.asarray(m, dtype=np.float64)
+    down = np.asarray(down, dtype=np.float64)
+    k = down.shape[0]
+    n = m.shape[-1]
+    pad_l = k // 2 - (1 if k % 2 == 0 else 0)
+    pad_r = k // 2
+    padded = n + pad_l + pad_r
+    buf = m[..., _clamp_index(padded, pad_l, n)]
+    out_n = (padded - k) // ratio + 1
+    y = np.zeros(m.shape[:-1] + (out_n,), dtype=np.float64)
+    for j in range(k):
+        y += down[j] * buf[..., j: j + ratio * (out_n - 1) + 1: ratio]
+    return y
+
+
+def act1d(x: np.ndarray, log_alpha, log_beta, up=None, down=None) -> np.ndarray:
+    """Alias-free activation, ``[..., C, T] -> [..., C, T]`` ([H3] ``Activation1d::apply``):
+    upsample x2, SnakeBeta at the doubled rate, lowpass-downsample x2.
+    ``up``/``down`` default to the designed taps ([H3] ``Activation1d::load``
+    falls back to ``kaiser_sinc(0.25, 0.3, 12)`` for both)."""
+    if up is None:
+        up = kaiser_sinc()
+    if down is None:
+        down = kaiser_sinc()
+    mid = upsample2(x, up)
+    mid = snake_beta(mid, log_alpha, log_beta)
+    return downsample2(mid, down)
+
+
+# --------------------------------------------------------------------------
+# Convolutions  ([H3] Conv1d::apply, ConvT1d::apply; [LTX] Conv1d, ConvT1d)
+# --------------------------------------------------------------------------
+
+def conv1d(x: np.ndarray, w: np.ndarray, b: Optional[np.ndarray] = None, dilation: int = 1,
+           pad: Optional[int] = None, residual: Optional[np.ndarray] = None) -> np.ndarray:
+    """Dilated correlation with zero padding ([H3] ``Conv1d::apply``).
+
+    x ``[B, Cin, n]``, w ``[Cout, Cin, k]``; out length n + 2 pad - d (k - 1);
+    y[o, t] = b[o] + sum_i sum_j w[o, i, j] x[i, t + j d - pad] (zero outside).
+    ``pad`` defaults to the "same" padding (k d - d) / 2 ([H3] ``get_padding``).
+    ``residual`` (same shape as y) is added afterwards: the AMP residual
+    ``cur += xt`` of [H3] ``AmpBlock::apply``.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    cout, cin, k = w.shape
+    assert x.shape[-2] == cin
+    n = x.shape[-1]
+    if pad is None:
+        pad = (k * dilation - dilation) // 2
+    out_n = n + 2 * pad - dilation * (k - 1)
+    assert out_n >= 0
+    xp = np.zeros(x.shape[:-1] + (n + 2 * pad,), dtype=np.float64)
+    xp[..., pad: pad + n] = x
+    y = np.zeros(x.shape[:-2] + (cout, out_n), dtype=np.float64)
+    for j in range(k):
+        # tap j reads x[i, t + j d - pad] = xp[i, t + j d]
+        y += np.matmul(w[:, :, j], xp[..., j * dilation: j * dilation + out_n])
+    if b is not None:
+        y += np.asarray(b, dtype=np.float64)[:, None]
+    if residual is not None:
+        y += np.asarray(residual, dtype=np.float64)
+    return y
+
+
+def convtr1d(x: np.ndarray, w: np.ndarray, b: Optional[np.ndarray], stride: int,
+             pad: Optional[int] = None) -> np.ndarray:
+    """Transposed convolution by scatter and crop ([H3] ``ConvT1d::apply``).
+
+    x ``[B, Cin, n]``, w ``[Cin, Cout, k]``; pad defaults to (k - stride) // 2
+    ([H3] ``ConvT1d::load``); out length (n - 1) stride + k - 2 pad;
+    out[o, t stride + j - pad] += x[i, t] w[i, o, j], plus b[o].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    cin, cout, k = w.shape
+    assert x.shape[-2] == cin
+    n = x.shape[-1]
+    if pad is None:
+        pad = (k - stride) // 2
+    full = (n - 1) * stride + k
+    out_n = full - 2 * pad
+    buf = np.zeros(x.shape[:-2] + (cout, full), dtype=np.float64)
+    for j in range(k):
+        # input t lands at t*stride + j
+        buf[..., j: j + stride * (n - 1) + 1: stride] += np.matmul(w[:, :, j].T, x)
+    y = buf[..., pad: pad + out_n].copy()
+    if b is not None:
+        y += np.asarray(b, dtype=np.float64)[:, None]
+    return y
+
+
+# --------------------------------------------------------------------------
+# AMP block, MRF, decoder  ([H3] AmpBlock::apply, AudioVae::decode;
+#                           [LTX] AmpBlock::forward, Vocoder::forward)
+# --------------------------------------------------------------------------
+
+@dataclass
+class AmpParams:
+    """One AMP residual block with kernel size k and dilations ``dil``.
+    w1[q], b1[q]: convs1 (dilation dil[q]); w2[q], b2[q]: convs2 (dilation 1);
+    la[q], lb[q] for q < 2 len(dil): activation q's log alpha / log beta."""
+    k: int
+    dil: Sequence[int]
+    w1: List[np.ndarray]
+    b1: List[Optional[np.ndarray]]
+    w2: List[np.ndarray]
+    b2: List[Optional[np.ndarray]]
+    la: List[np.ndarray]
+    lb: List[np.ndarray]
+
+
+def amp_block(x: np.ndarray, p: AmpParams, up=None, down=None) -> np.ndarray:
+    """[H3] ``AmpBlock::apply``: for each dilation q,
+    cur += conv2_q(act_{2q+1}(conv1_q(act_{2q}(cur))))."""
+    cur = np.asarray(x, dtype=np.float64)
+    for q, d in enumerate(p.dil):
+        xt = act1d(cur, p.la[2 * q], p.lb[2 * q], up, down)
+        xt = conv1d(xt, p.w1[q], p.b1[q], dilation=d, pad=(p.k * d - d) // 2)
+        xt = act1d(xt, p.la[2 * q + 1], p.lb[2 * q + 1], up, down)
+        cur = conv1d(xt, p.w2[q], p.b2[q], dilation=1, pad=(p.k - 1) // 2, residual=cur)
+    return cur
+
+
+def mrf(x: np.ndarray, blocks: Sequence[AmpParams], up=None, down=None) -> np.ndarray:
+    """Multi-receptive-field fusion ([H3] ``AudioVae::decode`` stage loop):
+    the AMP blocks of a stage all read the same input and their outputs are
+    summed, then divided by the number of blocks."""
+    acc = None
+    for p in blocks:
+        r = amp_block(x, p, up, down)
+        acc = r if acc is None else acc + r
+    return acc / len(blocks)
+
+
+@dataclass
+class DecoderParams:
+    """Weights of a BigVGAN decoder.  ``final`` is 'none', 'tanh' or 'clamp'."""
+    conv_pre_w: np.ndarray                 # [C0, Cin, k_pre]
+    conv_pre_b: Optional[np.ndarray]
+    up_w: List[np.ndarray]                 # stage i: [C_i, C_{i+1}, k_i]
+    up_b: List[Optional[np.ndarray]]
+    rates: Sequence[int]
+    blocks: List[List[AmpParams]]          # [stage][kernel]
+    post_la: np.ndarray
+    post_lb: np.ndarray
+    conv_post_w: np.ndarray                # [1, C_last, k_post]
+    conv_post_b: Optional[np.ndarray]
+    final: str = "tanh"
+    latent_mean: Optional[np.ndarray] = None
+    latent_std: Optional[np.ndarray] = None
+    dec_in_w: Optional[np.ndarray] = None  # [Cin', Cin, 1]
+    dec_in_b: Optional[np.ndarray] = None
+    stages: List[np.ndarray] = field(default_factory=list)  # filled by decode(record=True)
+
+
+def decode(latent: np.ndarray, p: DecoderParams, up=None, down=None,
+           record: bool = False) -> np.ndarray:
+    """One BigVGAN decode ([H3] ``AudioVae::decode``, [LTX] ``Vocoder::forward``).
+
+    latent ``[B, Cin, F]``; each of the B rows is an independent mono pass
+    (the stereo channels of [H3] are two such passes).  Steps: optional
+    latent affine z*std + mean and optional 1x1 ``dec_in`` conv; ``conv_pre``
+    ("same" padding); per stage a transposed conv at the stage's rate
+    followed by the MRF average; ``act_post``; ``conv_post``; the final
+    nonlinearity (tanh, clamp to [-1, 1], or none).
+    With ``record`` the per-stage outputs and the pre-final conv_post output
+    are kept in ``p.stages`` for stage-by-stage comparison.
+    """
+    x = np.asarray(latent, dtype=np.float64)
+    if p.latent_std is not None:
+        x = x * np.asarray(p.latent_std, np.float64)[:, None]
+    if p.latent_mean is not None:
+        x = x + np.asarray(p.latent_mean, np.float64)[:, None]
+    if p.dec_in_w is not None:
+        x = conv1d(x, p.dec_in_w, p.dec_in_b, dilation=1, pad=0)
+    kp = p.conv_pre_w.shape[2]
+    x = conv1d(x, p.conv_pre_w, p.conv_pre_b, dilation=1, pad=(kp - 1) // 2)
+    if record:
+        p.stages = [x]
+    for i, r in enumerate(p.rates):
+        x = convtr1d(x, p.up_w[i], p.up_b[i], stride=r)
+        x = mrf(x, p.blocks[i], up, down)
+        if record:
+            p.stages.append(x)
+    x = act1d(x, p.post_la, p.post_lb, up, down)
+    kq = p.conv_post_w.shape[2]
+    y = conv1d(x, p.conv_post_w, p.conv_post_b, dilation=1, pad=(kq - 1) // 2)
+    if record:
+        p.stages.append(y)
+    if p.final == "tanh":
+        y = np.tanh(y)
+    elif p.final == "clamp":
+        y = np.clip(y, -1.0, 1.0)
+    elif p.final != "none":
+        raise ValueError(p.final)
+    return y[..., 0, :]

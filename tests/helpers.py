@@ -1,0 +1,58 @@
+"""Test glue: turns the seeded tensors of a workload into the oracle's
+parameter objects, and the error metric every parity test uses."""
+from __future__ import annotations
+
+from typing import Dict, Sequence
+
+import numpy as np
+
+from oracle import avae_oracle as O
+
+
+def f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+def amp_params(t: Dict[str, np.ndarray], prefix: str, k: int, dil: Sequence[int]) -> O.AmpParams:
+    n = len(dil)
+    return O.AmpParams(
+        k=k, dil=list(dil),
+        w1=[f64(t[f"{prefix}.convs1.{q}.weight"]) for q in range(n)],
+        b1=[f64(t[f"{prefix}.convs1.{q}.bias"]) for q in range(n)],
+        w2=[f64(t[f"{prefix}.convs2.{q}.weight"]) for q in range(n)],
+        b2=[f64(t[f"{prefix}.convs2.{q}.bias"]) for q in range(n)],
+        la=[f64(t[f"{prefix}.activations.{q}.act.alpha"]) for q in range(2 * n)],
+        lb=[f64(t[f"{prefix}.activations.{q}.act.beta"]) for q in range(2 * n)],
+    )
+
+
+def decoder_params(spec, t: Dict[str, np.ndarray]) -> O.DecoderParams:
+    nk = len(spec.rb_k)
+    blocks = []
+    for i in range(len(spec.rates)):
+        blocks.append([amp_params(t, f"resblocks.{i * nk + j}", spec.rb_k[j], spec.rb_d[j])
+                       for j in range(nk)])
+    return O.DecoderParams(
+        conv_pre_w=f64(t["conv_pre.weight"]), conv_pre_b=f64(t["conv_pre.bias"]),
+        up_w=[f64(t[f"ups.{i}.weight"]) for i in range(len(spec.rates))],
+        up_b=[f64(t[f"ups.{i}.bias"]) for i in range(len(spec.rates))],
+        rates=list(spec.rates), blocks=blocks,
+        post_la=f64(t["activation_post.act.alpha"]), post_lb=f64(t["activation_post.act.beta"]),
+        conv_post_w=f64(t["conv_post.weight"]), conv_post_b=f64(t["conv_post.bias"]),
+        final=spec.final,
+        latent_mean=f64(t["latents_mean"]) if "latents_mean" in t else None,
+        latent_std=f64(t["latents_std"]) if "latents_std" in t else None,
+        dec_in_w=f64(t["dec_in.weight"]) if "dec_in.weight" in t else None,
+        dec_in_b=f64(t["dec_in.bias"]) if "dec_in.bias" in t else None,
+    )
+
+
+def rel_err(got, ref) -> float:
+    """max|got - ref| / RMS(ref): the parity metric, in float64."""
+    got = f64(got)
+    ref = f64(ref)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    if rms == 0.0:
+        return float(np.max(np.abs(got - ref))) if got.size else 0.0
+    return float(np.max(np.abs(got - ref))) / rms if got.size else 0.0
