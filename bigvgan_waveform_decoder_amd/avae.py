@@ -1,0 +1,363 @@
+"""Thin ctypes binding over libavae.so (see include/avae.h).
+
+Argument marshalling only: every step of the decoder runs in the library's
+HIP kernels.  PyTorch provides device memory (``tensor.data_ptr()``) and the
+stream (``torch.cuda.current_stream().cuda_stream``).  There is no fallback:
+if the library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libavae.so")
+
+AVAE_FILTER_LEN = 12
+AVAE_MAX_STAGES = 8
+AVAE_MAX_KERNELS = 4
+AVAE_MAX_DIL = 4
+FINAL = {"none": 0, "tanh": 1, "clamp": 2}
+
+c_int, c_float, c_double, c_size_t, c_void_p = (ctypes.c_int, ctypes.c_float, ctypes.c_double,
+                                                ctypes.c_size_t, ctypes.c_void_p)
+P = c_void_p
+
+
+class AvaeError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libavae error {code}: {msg}")
+        self.code = code
+
+
+class avae_config(ctypes.Structure):
+    _fields_ = [
+        ("c_in", c_int), ("dec_in_ch", c_int), ("has_latent_affine", c_int),
+        ("k_pre", c_int), ("k_post", c_int), ("n_stages", c_int),
+        ("ch", c_int * (AVAE_MAX_STAGES + 1)),
+        ("rates", c_int * AVAE_MAX_STAGES), ("up_k", c_int * AVAE_MAX_STAGES),
+        ("n_kernels", c_int), ("rb_k", c_int * AVAE_MAX_KERNELS), ("n_dil", c_int),
+        ("rb_d", (c_int * AVAE_MAX_DIL) * AVAE_MAX_KERNELS), ("final_act", c_int),
+    ]
+
+
+_W3 = ((P * AVAE_MAX_DIL) * AVAE_MAX_KERNELS) * AVAE_MAX_STAGES
+_A3 = ((P * (2 * AVAE_MAX_DIL)) * AVAE_MAX_KERNELS) * AVAE_MAX_STAGES
+
+
+class avae_weights(ctypes.Structure):
+    _fields_ = [
+        ("latent_mean", P), ("latent_std", P), ("dec_in_w", P), ("dec_in_b", P),
+        ("conv_pre_w", P), ("conv_pre_b", P),
+        ("up_w", P * AVAE_MAX_STAGES), ("up_b", P * AVAE_MAX_STAGES),
+        ("w1", _W3), ("b1", _W3), ("w2", _W3), ("b2", _W3),
+        ("act_la", _A3), ("act_lb", _A3),
+        ("post_la", P), ("post_lb", P), ("conv_post_w", P), ("conv_post_b", P),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                           "(python -m bigvgan_waveform_decoder_amd.build)")
+    L = ctypes.CDLL(LIB_PATH)
+    L.avae_last_error.restype = ctypes.c_char_p
+    L.avae_last_error.argtypes = []
+    L.avae_version.restype = c_int
+    L.avae_kaiser_sinc.restype = c_int
+    L.avae_kaiser_sinc.argtypes = [c_double, c_double, c_int, P]
+    L.avae_act1d.restype = c_int
+    L.avae_act1d.argtypes = [P, P, c_int, c_int, c_int, P, P, P, P, P]
+    L.avae_conv1d.restype = c_int
+    L.avae_conv1d.argtypes = [P, P, c_int, c_int, c_int, c_int, P, P, c_int, c_int, c_int, P, P]
+    L.avae_convtr1d.restype = c_int
+    L.avae_convtr1d.argtypes = [P, P, c_int, c_int, c_int, c_int, P, P, c_int, c_int, c_int, P]
+    L.avae_amp_block_workspace_bytes.restype = c_size_t
+    L.avae_amp_block_workspace_bytes.argtypes = [c_int, c_int, c_int]
+    L.avae_amp_block.restype = c_int
+    L.avae_amp_block.argtypes = [P, P, c_int, c_int, c_int, c_int, c_int, P, P, P, P, P, P, P,
+                                 c_float, c_int, P, c_size_t, P]
+    L.avae_decoder_create.restype = c_int
+    L.avae_decoder_create.argtypes = [ctypes.POINTER(avae_config), ctypes.POINTER(avae_weights),
+                                      ctypes.POINTER(P)]
+    L.avae_decoder_destroy.restype = None
+    L.avae_decoder_destroy.argtypes = [P]
+    L.avae_decoder_output_length.restype = c_int
+    L.avae_decoder_output_length.argtypes = [P, c_int, ctypes.POINTER(c_int)]
+    L.avae_decoder_workspace_bytes.restype = c_size_t
+    L.avae_decoder_workspace_bytes.argtypes = [P, c_int, c_int]
+    L.avae_bigvgan_decode.restype = c_int
+    L.avae_bigvgan_decode.argtypes = [P, P, c_int, c_int, P, P, c_size_t, P]
+    L.avae_bigvgan_decode_traced.restype = c_int
+    L.avae_bigvgan_decode_traced.argtypes = [P, P, c_int, c_int, P, P, c_size_t, P, P]
+    _lib = L
+    return L
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise AvaeError(rc, lib().avae_last_error().decode())
+
+
+# ------------------------------------------------------------------ helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev(t, name: str, shape: Optional[Sequence[int]] = None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if t.dtype != torch.float32:
+        raise ValueError(f"{name}: must be float32, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def _opt(t, name, shape=None):
+    return None if t is None else _dev(t, name, shape)
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _host_taps(taps):
+    if taps is None:
+        return None, None
+    a = np.ascontiguousarray(np.asarray(taps, dtype=np.float32))
+    if a.shape != (AVAE_FILTER_LEN,):
+        raise ValueError(f"taps must have {AVAE_FILTER_LEN} entries")
+    return a, a.ctypes.data
+
+
+# ------------------------------------------------------------------ entry points
+
+def version() -> int:
+    return lib().avae_version()
+
+
+def kaiser_sinc(cutoff: float = 0.25, half_width: float = 0.3, taps: int = 12) -> np.ndarray:
+    out = np.zeros(max(int(taps), 1), dtype=np.float32)
+    _check(lib().avae_kaiser_sinc(cutoff, half_width, int(taps), out.ctypes.data))
+    return out
+
+
+def act1d(x, log_alpha, log_beta, up_taps=None, down_taps=None, out=None, stream=None):
+    """avae_act1d: [B, C, T] -> [B, C, T]."""
+    torch = _torch()
+    B, C, T = x.shape
+    px = _dev(x, "x")
+    if out is None:
+        out = torch.empty_like(x)
+    py = _dev(out, "out", (B, C, T))
+    ua, up = _host_taps(up_taps)
+    da, dp = _host_taps(down_taps)
+    _check(lib().avae_act1d(px, py, B, C, T, _dev(log_alpha, "log_alpha", (C,)),
+                            _dev(log_beta, "log_beta", (C,)), up, dp, _stream(stream)))
+    return out
+
+
+def conv1d(x, w, bias=None, dilation: int = 1, pad: Optional[int] = None, residual=None,
+           out=None, stream=None):
+    """avae_conv1d; pad defaults to the 'same' padding (K*d - d)/2."""
+    torch = _torch()
+    B, Cin, T = x.shape
+    Cout, Cin_w, K = w.shape
+    if Cin_w != Cin:
+        raise ValueError(f"weight has {Cin_w} input channels, x has {Cin}")
+    if pad is None:
+        pad = (K * dilation - dilation) // 2
+    Tout = T + 2 * pad - dilation * (K - 1)
+    if out is None:
+        out = torch.empty((B, Cout, max(Tout, 0)), device=x.device, dtype=torch.float32)
+    _check(lib().avae_conv1d(_dev(x, "x"), _dev(out, "out", (B, Cout, Tout)), B, Cin, Cout, T,
+                             _dev(w, "w"), _opt(bias, "bias", (Cout,)), K, dilation, pad,
+                             _opt(residual, "residual", (B, Cout, Tout)), _stream(stream)))
+    return out
+
+
+def convtr1d(x, w, bias=None, stride: int = 1, pad: int = -1, out=None, stream=None):
+    """avae_convtr1d; pad < 0 selects (K - stride)/2."""
+    torch = _torch()
+    B, Cin, Tin = x.shape
+    Cin_w, Cout, K = w.shape
+    if Cin_w != Cin:
+        raise ValueError(f"weight has {Cin_w} input channels, x has {Cin}")
+    p = (K - stride) // 2 if pad < 0 else pad
+    Tout = (Tin - 1) * stride + K - 2 * p
+    if out is None:
+        out = torch.empty((B, Cout, max(Tout, 0)), device=x.device, dtype=torch.float32)
+    _check(lib().avae_convtr1d(_dev(x, "x"), _dev(out, "out", (B, Cout, Tout)), B, Cin, Cout, Tin,
+                               _dev(w, "w"), _opt(bias, "bias", (Cout,)), K, stride, pad,
+                               _stream(stream)))
+    return out
+
+
+def amp_block_workspace_bytes(B: int, C: int, T: int) -> int:
+    return int(lib().avae_amp_block_workspace_bytes(B, C, T))
+
+
+def amp_block(x, K: int, dil: Sequence[int], w1: List, b1: List, w2: List, b2: List,
+              log_alpha: List, log_beta: List, out_scale: float = 1.0, accumulate: bool = False,
+              out=None, workspace=None, stream=None):
+    """avae_amp_block: out = [out +] out_scale * AMP(x)."""
+    torch = _torch()
+    B, C, T = x.shape
+    n = len(dil)
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs an existing out tensor")
+        out = torch.empty_like(x)
+    if workspace is None:
+        workspace = torch.empty(amp_block_workspace_bytes(B, C, T), dtype=torch.uint8,
+                                device=x.device)
+    dil_a = (c_int * n)(*[int(d) for d in dil])
+    arr = lambda ts, nm, shape: (P * len(ts))(*[_opt(t, nm, shape) for t in ts])
+    w1a = arr(w1, "w1", (C, C, K))
+    b1a = arr(b1, "b1", (C,))
+    w2a = arr(w2, "w2", (C, C, K))
+    b2a = arr(b2, "b2", (C,))
+    laa = arr(log_alpha, "log_alpha", (C,))
+    lba = arr(log_beta, "log_beta", (C,))
+    if len(w1) != n or len(w2) != n or len(log_alpha) != 2 * n or len(log_beta) != 2 * n:
+        raise ValueError("amp_block: per-dilation lists have the wrong length")
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda:
+        raise ValueError("workspace must be a uint8 device tensor")
+    _check(lib().avae_amp_block(
+        _dev(x, "x"), _dev(out, "out", (B, C, T)), B, C, T, K, n, ctypes.addressof(dil_a),
+        ctypes.addressof(w1a), ctypes.addressof(b1a), ctypes.addressof(w2a),
+        ctypes.addressof(b2a), ctypes.addressof(laa), ctypes.addressof(lba), float(out_scale),
+        1 if accumulate else 0, workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return out
+
+
+class Decoder:
+    """avae_decoder_create / avae_bigvgan_decode over device weight tensors
+    named as on the H3 page (``conv_pre.weight``, ``ups.{i}.weight``,
+    ``resblocks.{i*nk+j}.convs1.{q}.weight``,
+    ``resblocks.{..}.activations.{q}.act.alpha`` ...)."""
+
+    def __init__(self, spec, tensors: Dict[str, "object"]):
+        cfg = avae_config()
+        cfg.c_in = spec.c_in
+        cfg.dec_in_ch = int(spec.dec_in)
+        cfg.has_latent_affine = 1 if spec.latent_affine else 0
+        cfg.k_pre, cfg.k_post = spec.k_pre, spec.k_post
+        ns = len(spec.rates)
+        if ns > AVAE_MAX_STAGES:
+            raise ValueError("too many stages")
+        cfg.n_stages = ns
+        for i, c in enumerate(spec.widths()):
+            cfg.ch[i] = c
+        for i, (r, k) in enumerate(zip(spec.rates, spec.up_k)):
+            cfg.rates[i], cfg.up_k[i] = r, k
+        nk = len(spec.rb_k)
+        cfg.n_kernels = nk
+        nd = len(spec.rb_d[0])
+        cfg.n_dil = nd
+        for j in range(nk):
+            cfg.rb_k[j] = spec.rb_k[j]
+            if len(spec.rb_d[j]) != nd:
+                raise ValueError("every AMP block needs the same number of dilations")
+            for q in range(nd):
+                cfg.rb_d[j][q] = spec.rb_d[j][q]
+        cfg.final_act = FINAL[spec.final]
+        self.spec = spec
+        self.cfg = cfg
+        t = tensors
+        g = lambda name: _dev(t[name], name) if name in t else None
+        w = avae_weights()
+        w.latent_mean, w.latent_std = g("latents_mean"), g("latents_std")
+        w.dec_in_w, w.dec_in_b = g("dec_in.weight"), g("dec_in.bias")
+        w.conv_pre_w, w.conv_pre_b = g("conv_pre.weight"), g("conv_pre.bias")
+        for i in range(ns):
+            w.up_w[i], w.up_b[i] = g(f"ups.{i}.weight"), g(f"ups.{i}.bias")
+            for j in range(nk):
+                p = f"resblocks.{i * nk + j}"
+                for q in range(nd):
+                    w.w1[i][j][q] = g(f"{p}.convs1.{q}.weight")
+                    w.b1[i][j][q] = g(f"{p}.convs1.{q}.bias")
+                    w.w2[i][j][q] = g(f"{p}.convs2.{q}.weight")
+                    w.b2[i][j][q] = g(f"{p}.convs2.{q}.bias")
+                for q in range(2 * nd):
+                    w.act_la[i][j][q] = g(f"{p}.activations.{q}.act.alpha")
+                    w.act_lb[i][j][q] = g(f"{p}.activations.{q}.act.beta")
+        w.post_la, w.post_lb = g("activation_post.act.alpha"), g("activation_post.act.beta")
+        w.conv_post_w, w.conv_post_b = g("conv_post.weight"), g("conv_post.bias")
+        h = P()
+        _check(lib().avae_decoder_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(h)))
+        self._h = h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h and _lib is not None:
+            _lib.avae_decoder_destroy(h)
+            self._h = None
+
+    def output_length(self, frames: int) -> int:
+        n = c_int()
+        _check(lib().avae_decoder_output_length(self._h, frames, ctypes.byref(n)))
+        return n.value
+
+    def workspace_bytes(self, B: int, frames: int) -> int:
+        return int(lib().avae_decoder_workspace_bytes(self._h, B, frames))
+
+    def stage_shapes(self, B: int, frames: int):
+        """Shapes of the traced intermediates (conv_pre, each stage, pre-final)."""
+        w = self.spec.widths()
+        shapes = [(B, w[0], frames)]
+        T = frames
+        for i, (r, k) in enumerate(zip(self.spec.rates, self.spec.up_k)):
+            T = (T - 1) * r + k - 2 * ((k - r) // 2)
+            shapes.append((B, w[i + 1], T))
+        shapes.append((B, self.output_length(frames)))
+        return shapes
+
+    def decode(self, latent, out=None, workspace=None, stream=None, trace: bool = False):
+        """latent [B, c_in, F] -> wave [B, L]; with trace=True also returns
+        the list of intermediates."""
+        torch = _torch()
+        B, C, F = latent.shape
+        if C != self.spec.c_in:
+            raise ValueError(f"latent has {C} channels, decoder expects {self.spec.c_in}")
+        L = self.output_length(F)
+        if out is None:
+            out = torch.empty((B, L), device=latent.device, dtype=torch.float32)
+        if workspace is None:
+            workspace = torch.empty(self.workspace_bytes(B, F), dtype=torch.uint8,
+                                    device=latent.device)
+        if workspace.dtype != torch.uint8 or not workspace.is_cuda:
+            raise ValueError("workspace must be a uint8 device tensor")
+        if not trace:
+            _check(lib().avae_bigvgan_decode(self._h, _dev(latent, "latent"), B, F,
+                                             _dev(out, "out", (B, L)), workspace.data_ptr(),
+                                             workspace.numel(), _stream(stream)))
+            return out
+        stages = [torch.empty(s, device=latent.device, dtype=torch.float32)
+                  for s in self.stage_shapes(B, F)]
+        arr = (P * len(stages))(*[s.data_ptr() for s in stages])
+        _check(lib().avae_bigvgan_decode_traced(self._h, _dev(latent, "latent"), B, F,
+                                                _dev(out, "out", (B, L)), workspace.data_ptr(),
+                                                workspace.numel(), ctypes.addressof(arr),
+                                                _stream(stream)))
+        return out, stages

@@ -1,0 +1,527 @@
+// C-ABI of libavae.so: argument checking, error reporting, the AMP block
+// sequence and the decoder plan.  Every check runs before the first launch;
+// the compute calls never allocate or synchronise.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/avae.h"
+#include "avae_internal.h"
+
+using avae::ActTaps;
+using avae::ConvEpilogue;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(AVAE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define AVAE_TRY(expr, what)                                   \
+    do {                                                       \
+        hipError_t e_ = (expr);                                \
+        if (e_ != hipSuccess) return hip_fail(e_, what);       \
+    } while (0)
+
+// The designed taps avae_kaiser_sinc(0.25, 0.3, 12), computed once.
+const float* designed_taps() {
+    static float taps[avae::kFilterLen];
+    static std::once_flag once;
+    std::call_once(once, [] {
+        double d[avae::kFilterLen];
+        avae::design_kaiser_sinc(0.25, 0.3, avae::kFilterLen, d);
+        for (int i = 0; i < avae::kFilterLen; ++i) taps[i] = (float)d[i];
+    });
+    return taps;
+}
+
+ActTaps make_taps(const float* up, const float* down) {
+    ActTaps t;
+    const float* u = up ? up : designed_taps();
+    const float* d = down ? down : designed_taps();
+    for (int i = 0; i < avae::kFilterLen; ++i) {
+        t.up2[i] = 2.0f * u[i];
+        t.down[i] = d[i];
+    }
+    return t;
+}
+
+size_t round_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
+
+int conv_out_len(int T, int K, int dil, int pad) { return T + 2 * pad - dil * (K - 1); }
+
+// One AMP block into y (y = scale*AMP(x) [+ y]); cur, t1, t2 are [B,C,T]
+// scratch buffers.  Activations use `taps`.
+int run_amp(const float* x, float* y, int B, int C, int T, int K, int n_dil, const int* dil,
+            const float* const* w1, const float* const* b1, const float* const* w2,
+            const float* const* b2, const float* const* la, const float* const* lb,
+            float out_scale, int accumulate, float* cur, float* t1, float* t2,
+            const ActTaps& taps, hipStream_t s) {
+    for (int q = 0; q < n_dil; ++q) {
+        const float* src = (q == 0) ? x : cur;
+        const int d = dil[q];
+        AVAE_TRY(avae::launch_act1d(src, t1, B, C, T, la[2 * q], lb[2 * q], taps, s), "act1d");
+        ConvEpilogue e1{b1[q], nullptr, 1.0f, 0};
+        AVAE_TRY(avae::launch_conv1d(t1, t2, w1[q], B, C, C, T, T, K, d, (K * d - d) / 2, e1, s),
+                 "conv1d (convs1)");
+        AVAE_TRY(avae::launch_act1d(t2, t1, B, C, T, la[2 * q + 1], lb[2 * q + 1], taps, s),
+                 "act1d");
+        const bool last = (q == n_dil - 1);
+        ConvEpilogue e2{b2[q], src, last ? out_scale : 1.0f, last ? accumulate : 0};
+        AVAE_TRY(avae::launch_conv1d(t1, last ? y : cur, w2[q], B, C, C, T, T, K, 1, (K - 1) / 2,
+                                     e2, s),
+                 "conv1d (convs2)");
+    }
+    return AVAE_OK;
+}
+
+}  // namespace
+
+// =========================================================================
+// Small entry points
+// =========================================================================
+
+extern "C" const char* avae_last_error(void) { return g_err.c_str(); }
+
+extern "C" int avae_version(void) { return 100; }
+
+extern "C" int avae_kaiser_sinc(double cutoff, double half_width, int taps, float* out_host) {
+    if (!out_host) return fail(AVAE_EINVAL, "avae_kaiser_sinc: out_host is null");
+    if (taps < 2 || taps % 2 != 0 || taps > 1024)
+        return fail(AVAE_EINVAL, "avae_kaiser_sinc: taps must be even in [2, 1024], got %d", taps);
+    if (!(cutoff > 0.0 && cutoff <= 0.5) || !(half_width > 0.0 && half_width <= 0.5))
+        return fail(AVAE_EINVAL, "avae_kaiser_sinc: cutoff and half_width must be in (0, 0.5]");
+    std::vector<double> d(taps);
+    avae::design_kaiser_sinc(cutoff, half_width, taps, d.data());
+    for (int i = 0; i < taps; ++i) out_host[i] = (float)d[i];
+    return AVAE_OK;
+}
+
+extern "C" int avae_act1d(const float* x, float* y, int B, int C, int T, const float* log_alpha,
+                          const float* log_beta, const float* up_taps, const float* down_taps,
+                          void* stream) {
+    if (!x || !y || !log_alpha || !log_beta)
+        return fail(AVAE_EINVAL, "avae_act1d: null tensor pointer");
+    if (B < 1 || C < 1 || T < 1)
+        return fail(AVAE_EINVAL, "avae_act1d: B, C, T must be >= 1 (got %d, %d, %d)", B, C, T);
+    if (x == y) return fail(AVAE_EINVAL, "avae_act1d: x and y must not overlap");
+    const ActTaps taps = make_taps(up_taps, down_taps);
+    AVAE_TRY(avae::launch_act1d(x, y, B, C, T, log_alpha, log_beta, taps, (hipStream_t)stream),
+             "avae_act1d launch");
+    return AVAE_OK;
+}
+
+extern "C" int avae_conv1d(const float* x, float* y, int B, int Cin, int Cout, int T,
+                           const float* w, const float* bias, int K, int dilation, int pad,
+                           const float* residual, void* stream) {
+    if (!x || !y || !w) return fail(AVAE_EINVAL, "avae_conv1d: null tensor pointer");
+    if (B < 1 || Cin < 1 || Cout < 1 || T < 1 || K < 1 || dilation < 1 || pad < 0)
+        return fail(AVAE_EINVAL, "avae_conv1d: bad size (B=%d Cin=%d Cout=%d T=%d K=%d d=%d pad=%d)",
+                    B, Cin, Cout, T, K, dilation, pad);
+    if (K > AVAE_MAX_TAPS) return fail(AVAE_ESHAPE, "avae_conv1d: K=%d > %d", K, AVAE_MAX_TAPS);
+    if ((long long)(K - 1) * dilation > 4096)
+        return fail(AVAE_ESHAPE, "avae_conv1d: receptive field (K-1)*d too large");
+    const int Tout = conv_out_len(T, K, dilation, pad);
+    if (Tout < 1) return fail(AVAE_ESHAPE, "avae_conv1d: output length %d < 1", Tout);
+    if (x == y) return fail(AVAE_EINVAL, "avae_conv1d: x and y must not overlap");
+    ConvEpilogue ep{bias, residual, 1.0f, 0};
+    hipError_t e = avae::launch_conv1d(x, y, w, B, Cin, Cout, T, Tout, K, dilation, pad, ep,
+                                       (hipStream_t)stream);
+    if (e == hipErrorInvalidValue)
+        return fail(AVAE_ESHAPE, "avae_conv1d: shape exceeds the kernel's LDS or grid limits");
+    if (e != hipSuccess) return hip_fail(e, "avae_conv1d launch");
+    return AVAE_OK;
+}
+
+extern "C" int avae_convtr1d(const float* x, float* y, int B, int Cin, int Cout, int Tin,
+                             const float* w, const float* bias, int K, int stride, int pad,
+                             void* stream) {
+    if (!x || !y || !w) return fail(AVAE_EINVAL, "avae_convtr1d: null tensor pointer");
+    if (B < 1 || Cin < 1 || Cout < 1 || Tin < 1 || K < 1 || stride < 1)
+        return fail(AVAE_EINVAL, "avae_convtr1d: bad size (B=%d Cin=%d Cout=%d Tin=%d K=%d s=%d)",
+                    B, Cin, Cout, Tin, K, stride);
+    if (K > AVAE_MAX_TAPS) return fail(AVAE_ESHAPE, "avae_convtr1d: K=%d > %d", K, AVAE_MAX_TAPS);
+    if (pad < 0) {
+        if (K < stride) return fail(AVAE_ESHAPE, "avae_convtr1d: default pad needs K >= stride");
+        pad = (K - stride) / 2;
+    }
+    const long long Tout = (long long)(Tin - 1) * stride + K - 2LL * pad;
+    if (Tout < 1 || Tout > 0x7fffffffLL)
+        return fail(AVAE_ESHAPE, "avae_convtr1d: output length %lld out of range", Tout);
+    if (x == y) return fail(AVAE_EINVAL, "avae_convtr1d: x and y must not overlap");
+    hipError_t e = avae::launch_convtr1d(x, y, w, bias, B, Cin, Cout, Tin, (int)Tout, K, stride,
+                                         pad, (hipStream_t)stream);
+    if (e == hipErrorInvalidValue)
+        return fail(AVAE_ESHAPE, "avae_convtr1d: shape exceeds the kernel's LDS or grid limits");
+    if (e != hipSuccess) return hip_fail(e, "avae_convtr1d launch");
+    return AVAE_OK;
+}
+
+extern "C" size_t avae_amp_block_workspace_bytes(int B, int C, int T) {
+    if (B < 1 || C < 1 || T < 1) return 0;
+    return 3 * round_up((size_t)B * C * T * sizeof(float), 256);
+}
+
+extern "C" int avae_amp_block(const float* x, float* y, int B, int C, int T, int K, int n_dil,
+                              const int* dil, const float* const* w1, const float* const* b1,
+                              const float* const* w2, const float* const* b2,
+                              const float* const* log_alpha, const float* const* log_beta,
+                              float out_scale, int accumulate, void* workspace, size_t ws_bytes,
+                              void* stream) {
+    if (!x || !y || !dil || !w1 || !w2 || !log_alpha || !log_beta)
+        return fail(AVAE_EINVAL, "avae_amp_block: null pointer");
+    if (B < 1 || C < 1 || T < 1 || n_dil < 1)
+        return fail(AVAE_EINVAL, "avae_amp_block: bad size");
+    if (n_dil > AVAE_MAX_DIL) return fail(AVAE_ESHAPE, "avae_amp_block: n_dil > %d", AVAE_MAX_DIL);
+    if (K < 1 || K % 2 == 0 || K > AVAE_MAX_TAPS)
+        return fail(AVAE_ESHAPE, "avae_amp_block: K must be odd and <= %d", AVAE_MAX_TAPS);
+    if (x == y) return fail(AVAE_EINVAL, "avae_amp_block: x and y must not overlap");
+    static const float* const kNull[AVAE_MAX_DIL] = {nullptr, nullptr, nullptr, nullptr};
+    for (int q = 0; q < n_dil; ++q) {
+        if (dil[q] < 1) return fail(AVAE_EINVAL, "avae_amp_block: dilation < 1");
+        if ((long long)(K - 1) * dil[q] > 4096)
+            return fail(AVAE_ESHAPE, "avae_amp_block: receptive field too large");
+        if (!w1[q] || !w2[q]) return fail(AVAE_EINVAL, "avae_amp_block: null weight");
+        if (!log_alpha[2 * q] || !log_alpha[2 * q + 1] || !log_beta[2 * q] || !log_beta[2 * q + 1])
+            return fail(AVAE_EINVAL, "avae_amp_block: null activation parameter");
+    }
+    const size_t need = avae_amp_block_workspace_bytes(B, C, T);
+    if (!workspace || ws_bytes < need)
+        return fail(AVAE_EWORKSPACE, "avae_amp_block: workspace %zu bytes < %zu needed", ws_bytes,
+                    need);
+    const size_t slot = need / 3;
+    char* ws = (char*)workspace;
+    float* cur = (float*)ws;
+    float* t1 = (float*)(ws + slot);
+    float* t2 = (float*)(ws + 2 * slot);
+    return run_amp(x, y, B, C, T, K, n_dil, dil, w1, b1 ? b1 : kNull, w2, b2 ? b2 : kNull,
+                   log_alpha, log_beta, out_scale, accumulate, cur, t1, t2,
+                   make_taps(nullptr, nullptr), (hipStream_t)stream);
+}
+
+// =========================================================================
+// Decoder
+// =========================================================================
+
+struct avae_decoder {
+    avae_config cfg;
+    avae_weights w;  // pointers into `blob`
+    void* blob = nullptr;
+    size_t blob_bytes = 0;
+    int device = 0;
+    ActTaps taps;
+};
+
+namespace {
+
+int check_config(const avae_config* c) {
+    if (c->c_in < 1) return fail(AVAE_EINVAL, "config: c_in < 1");
+    if (c->dec_in_ch < 0) return fail(AVAE_EINVAL, "config: dec_in_ch < 0");
+    if (c->k_pre < 1 || c->k_pre % 2 == 0 || c->k_pre > AVAE_MAX_TAPS ||
+        c->k_post < 1 || c->k_post % 2 == 0 || c->k_post > AVAE_MAX_TAPS)
+        return fail(AVAE_ESHAPE, "config: k_pre/k_post must be odd and <= %d", AVAE_MAX_TAPS);
+    if (c->n_stages < 1 || c->n_stages > AVAE_MAX_STAGES)
+        return fail(AVAE_ESHAPE, "config: n_stages must be in [1, %d]", AVAE_MAX_STAGES);
+    if (c->n_kernels < 1 || c->n_kernels > AVAE_MAX_KERNELS)
+        return fail(AVAE_ESHAPE, "config: n_kernels must be in [1, %d]", AVAE_MAX_KERNELS);
+    if (c->n_dil < 1 || c->n_dil > AVAE_MAX_DIL)
+        return fail(AVAE_ESHAPE, "config: n_dil must be in [1, %d]", AVAE_MAX_DIL);
+    for (int i = 0; i <= c->n_stages; ++i)
+        if (c->ch[i] < 1) return fail(AVAE_EINVAL, "config: ch[%d] < 1", i);
+    if (c->ch[c->n_stages] > 1024)
+        return fail(AVAE_ESHAPE, "config: last width %d too wide for conv_post", c->ch[c->n_stages]);
+    for (int i = 0; i < c->n_stages; ++i) {
+        if (c->rates[i] < 1 || c->up_k[i] < c->rates[i] || c->up_k[i] > AVAE_MAX_TAPS)
+            return fail(AVAE_ESHAPE, "config: stage %d needs 1 <= rate <= up_k <= %d", i,
+                        AVAE_MAX_TAPS);
+    }
+    for (int j = 0; j < c->n_kernels; ++j) {
+        if (c->rb_k[j] < 1 || c->rb_k[j] % 2 == 0 || c->rb_k[j] > AVAE_MAX_TAPS)
+            return fail(AVAE_ESHAPE, "config: rb_k[%d] must be odd and <= %d", j, AVAE_MAX_TAPS);
+        for (int q = 0; q < c->n_dil; ++q)
+            if (c->rb_d[j][q] < 1 || (c->rb_k[j] - 1) * c->rb_d[j][q] > 4096)
+                return fail(AVAE_ESHAPE, "config: bad dilation rb_d[%d][%d]", j, q);
+    }
+    if (c->final_act < AVAE_FINAL_NONE || c->final_act > AVAE_FINAL_CLAMP)
+        return fail(AVAE_EINVAL, "config: bad final_act");
+    return AVAE_OK;
+}
+
+// Per-stage lengths for `frames` frames: T[0] = frames, T[i+1] after stage i.
+int stage_lengths(const avae_config& c, int frames, long long* T) {
+    T[0] = frames;
+    for (int i = 0; i < c.n_stages; ++i) {
+        const int p = (c.up_k[i] - c.rates[i]) / 2;
+        T[i + 1] = (T[i] - 1) * c.rates[i] + c.up_k[i] - 2LL * p;
+        if (T[i + 1] < 1 || T[i + 1] > 0x7fffffffLL) return -1;
+    }
+    return 0;
+}
+
+// Bytes of each of the five decode buffers (largest activation).
+size_t decode_slot_bytes(const avae_config& c, int B, const long long* T) {
+    size_t m = 0;
+    auto upd = [&](long long ch, long long t) {
+        size_t v = (size_t)B * (size_t)ch * (size_t)t * sizeof(float);
+        if (v > m) m = v;
+    };
+    upd(c.c_in, T[0]);
+    if (c.dec_in_ch) upd(c.dec_in_ch, T[0]);
+    upd(c.ch[0], T[0]);
+    for (int i = 0; i < c.n_stages; ++i) upd(c.ch[i + 1], T[i + 1]);
+    return round_up(m, 256);
+}
+
+struct BlobPlan {
+    std::vector<std::pair<const float**, std::pair<const float*, size_t>>> items;
+    size_t total = 0;
+    // dst: where the blob pointer goes; src: caller pointer; n: floats
+    void add(const float** dst, const float* src, size_t n) {
+        if (!src) {
+            *dst = nullptr;
+            return;
+        }
+        items.push_back({dst, {src, n}});
+        total += round_up(n * sizeof(float), 256);
+    }
+};
+
+}  // namespace
+
+extern "C" int avae_decoder_create(const avae_config* cfg, const avae_weights* w,
+                                   avae_decoder** out) {
+    if (!cfg || !w || !out) return fail(AVAE_EINVAL, "avae_decoder_create: null argument");
+    *out = nullptr;
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    const avae_config& c = *cfg;
+    // required tensors
+    if (!w->conv_pre_w || !w->conv_post_w || !w->post_la || !w->post_lb)
+        return fail(AVAE_EINVAL, "avae_decoder_create: missing conv_pre/conv_post/act_post weights");
+    if (c.has_latent_affine && (!w->latent_mean || !w->latent_std))
+        return fail(AVAE_EINVAL, "avae_decoder_create: latent affine needs mean and std");
+    if (c.dec_in_ch && !w->dec_in_w) return fail(AVAE_EINVAL, "avae_decoder_create: missing dec_in_w");
+    for (int i = 0; i < c.n_stages; ++i) {
+        if (!w->up_w[i]) return fail(AVAE_EINVAL, "avae_decoder_create: missing up_w[%d]", i);
+        for (int j = 0; j < c.n_kernels; ++j) {
+            for (int q = 0; q < c.n_dil; ++q)
+                if (!w->w1[i][j][q] || !w->w2[i][j][q])
+                    return fail(AVAE_EINVAL, "avae_decoder_create: missing conv weight [%d][%d][%d]",
+                                i, j, q);
+            for (int q = 0; q < 2 * c.n_dil; ++q)
+                if (!w->act_la[i][j][q] || !w->act_lb[i][j][q])
+                    return fail(AVAE_EINVAL, "avae_decoder_create: missing activation [%d][%d][%d]",
+                                i, j, q);
+        }
+    }
+
+    avae_decoder* d = new (std::nothrow) avae_decoder();
+    if (!d) return fail(AVAE_ENOMEM, "avae_decoder_create: host allocation failed");
+    d->cfg = c;
+    d->taps = make_taps(nullptr, nullptr);
+    std::memset(&d->w, 0, sizeof(d->w));
+
+    BlobPlan plan;
+    const int cin2 = c.dec_in_ch ? c.dec_in_ch : c.c_in;
+    if (c.has_latent_affine) {
+        plan.add(&d->w.latent_mean, w->latent_mean, c.c_in);
+        plan.add(&d->w.latent_std, w->latent_std, c.c_in);
+    }
+    if (c.dec_in_ch) {
+        plan.add(&d->w.dec_in_w, w->dec_in_w, (size_t)c.dec_in_ch * c.c_in);
+        plan.add(&d->w.dec_in_b, w->dec_in_b, c.dec_in_ch);
+    }
+    plan.add(&d->w.conv_pre_w, w->conv_pre_w, (size_t)c.ch[0] * cin2 * c.k_pre);
+    plan.add(&d->w.conv_pre_b, w->conv_pre_b, c.ch[0]);
+    for (int i = 0; i < c.n_stages; ++i) {
+        const size_t ci = c.ch[i], co = c.ch[i + 1];
+        plan.add(&d->w.up_w[i], w->up_w[i], ci * co * c.up_k[i]);
+        plan.add(&d->w.up_b[i], w->up_b[i], co);
+        for (int j = 0; j < c.n_kernels; ++j) {
+            for (int q = 0; q < c.n_dil; ++q) {
+                plan.add(&d->w.w1[i][j][q], w->w1[i][j][q], co * co * c.rb_k[j]);
+                plan.add(&d->w.b1[i][j][q], w->b1[i][j][q], co);
+                plan.add(&d->w.w2[i][j][q], w->w2[i][j][q], co * co * c.rb_k[j]);
+                plan.add(&d->w.b2[i][j][q], w->b2[i][j][q], co);
+            }
+            for (int q = 0; q < 2 * c.n_dil; ++q) {
+                plan.add(&d->w.act_la[i][j][q], w->act_la[i][j][q], co);
+                plan.add(&d->w.act_lb[i][j][q], w->act_lb[i][j][q], co);
+            }
+        }
+    }
+    const size_t cl = c.ch[c.n_stages];
+    plan.add(&d->w.post_la, w->post_la, cl);
+    plan.add(&d->w.post_lb, w->post_lb, cl);
+    plan.add(&d->w.conv_post_w, w->conv_post_w, cl * c.k_post);
+    plan.add(&d->w.conv_post_b, w->conv_post_b, 1);
+
+    hipError_t e = hipGetDevice(&d->device);
+    if (e != hipSuccess) {
+        delete d;
+        return hip_fail(e, "avae_decoder_create: hipGetDevice");
+    }
+    e = hipMalloc(&d->blob, plan.total);
+    if (e != hipSuccess) {
+        delete d;
+        return fail(AVAE_ENOMEM, "avae_decoder_create: hipMalloc(%zu): %s", plan.total,
+                    hipGetErrorString(e));
+    }
+    d->blob_bytes = plan.total;
+    char* p = (char*)d->blob;
+    for (auto& it : plan.items) {
+        const size_t n = it.second.second;
+        e = hipMemcpy(p, it.second.first, n * sizeof(float), hipMemcpyDefault);
+        if (e != hipSuccess) {
+            (void)hipFree(d->blob);
+            delete d;
+            return hip_fail(e, "avae_decoder_create: weight copy");
+        }
+        *it.first = (const float*)p;
+        p += round_up(n * sizeof(float), 256);
+    }
+    *out = d;
+    return AVAE_OK;
+}
+
+extern "C" void avae_decoder_destroy(avae_decoder* dec) {
+    if (!dec) return;
+    if (dec->blob) {
+        int cur = 0;
+        (void)hipGetDevice(&cur);
+        (void)hipSetDevice(dec->device);
+        (void)hipFree(dec->blob);
+        (void)hipSetDevice(cur);
+    }
+    delete dec;
+}
+
+extern "C" int avae_decoder_output_length(const avae_decoder* dec, int frames, int* out_len) {
+    if (!dec || !out_len) return fail(AVAE_EINVAL, "avae_decoder_output_length: null argument");
+    if (frames < 1) return fail(AVAE_EINVAL, "avae_decoder_output_length: frames < 1");
+    long long T[AVAE_MAX_STAGES + 1];
+    if (stage_lengths(dec->cfg, frames, T))
+        return fail(AVAE_ESHAPE, "avae_decoder_output_length: length overflow");
+    *out_len = (int)T[dec->cfg.n_stages];
+    return AVAE_OK;
+}
+
+extern "C" size_t avae_decoder_workspace_bytes(const avae_decoder* dec, int B, int frames) {
+    if (!dec || B < 1 || frames < 1) return 0;
+    long long T[AVAE_MAX_STAGES + 1];
+    if (stage_lengths(dec->cfg, frames, T)) return 0;
+    return 5 * decode_slot_bytes(dec->cfg, B, T);
+}
+
+namespace {
+
+int decode_impl(const avae_decoder* dec, const float* latent, int B, int frames, float* wave,
+                void* workspace, size_t ws_bytes, float* const* stage_out, hipStream_t s) {
+    if (!dec || !latent || !wave) return fail(AVAE_EINVAL, "avae_bigvgan_decode: null argument");
+    if (B < 1 || frames < 1) return fail(AVAE_EINVAL, "avae_bigvgan_decode: B, frames must be >= 1");
+    const avae_config& c = dec->cfg;
+    const avae_weights& w = dec->w;
+    long long T[AVAE_MAX_STAGES + 1];
+    if (stage_lengths(c, frames, T))
+        return fail(AVAE_ESHAPE, "avae_bigvgan_decode: length overflow");
+    const size_t slot = decode_slot_bytes(c, B, T);
+    if (!workspace || ws_bytes < 5 * slot)
+        return fail(AVAE_EWORKSPACE, "avae_bigvgan_decode: workspace %zu bytes < %zu needed",
+                    ws_bytes, 5 * slot);
+    char* ws = (char*)workspace;
+    float* M = (float*)(ws + 0 * slot);   // stage input/output (MRF accumulator)
+    float* X = (float*)(ws + 1 * slot);   // ConvT output: every AMP block's input
+    float* cur = (float*)(ws + 2 * slot);
+    float* t1 = (float*)(ws + 3 * slot);
+    float* t2 = (float*)(ws + 4 * slot);
+
+    const int F = frames;
+    const float* h = latent;
+    int cin = c.c_in;
+    if (c.has_latent_affine) {
+        AVAE_TRY(avae::launch_channel_affine(h, X, w.latent_std, w.latent_mean, B, c.c_in, F, s),
+                 "latent affine");
+        h = X;
+    }
+    if (c.dec_in_ch) {
+        ConvEpilogue e{w.dec_in_b, nullptr, 1.0f, 0};
+        AVAE_TRY(avae::launch_conv1d(h, cur, w.dec_in_w, B, cin, c.dec_in_ch, F, F, 1, 1, 0, e, s),
+                 "dec_in");
+        h = cur;
+        cin = c.dec_in_ch;
+    }
+    {
+        ConvEpilogue e{w.conv_pre_b, nullptr, 1.0f, 0};
+        AVAE_TRY(avae::launch_conv1d(h, M, w.conv_pre_w, B, cin, c.ch[0], F, F, c.k_pre, 1,
+                                     (c.k_pre - 1) / 2, e, s),
+                 "conv_pre");
+    }
+    if (stage_out && stage_out[0])
+        AVAE_TRY(hipMemcpyAsync(stage_out[0], M, (size_t)B * c.ch[0] * F * sizeof(float),
+                                hipMemcpyDeviceToDevice, s),
+                 "trace copy");
+    const float inv_nk = 1.0f / (float)c.n_kernels;
+    for (int i = 0; i < c.n_stages; ++i) {
+        const int ci = c.ch[i], co = c.ch[i + 1];
+        const int Ti = (int)T[i], To = (int)T[i + 1];
+        const int pad = (c.up_k[i] - c.rates[i]) / 2;
+        AVAE_TRY(avae::launch_convtr1d(M, X, w.up_w[i], w.up_b[i], B, ci, co, Ti, To, c.up_k[i],
+                                       c.rates[i], pad, s),
+                 "ConvTranspose1d");
+        for (int j = 0; j < c.n_kernels; ++j) {
+            int rc = run_amp(X, M, B, co, To, c.rb_k[j], c.n_dil, c.rb_d[j], w.w1[i][j],
+                             w.b1[i][j], w.w2[i][j], w.b2[i][j], w.act_la[i][j], w.act_lb[i][j],
+                             inv_nk, j > 0 ? 1 : 0, cur, t1, t2, dec->taps, s);
+            if (rc) return rc;
+        }
+        if (stage_out && stage_out[1 + i])
+            AVAE_TRY(hipMemcpyAsync(stage_out[1 + i], M, (size_t)B * co * To * sizeof(float),
+                                    hipMemcpyDeviceToDevice, s),
+                     "trace copy");
+    }
+    const int cl = c.ch[c.n_stages];
+    const int TL = (int)T[c.n_stages];
+    AVAE_TRY(avae::launch_act1d(M, t1, B, cl, TL, w.post_la, w.post_lb, dec->taps, s),
+             "act_post");
+    float* pre = (stage_out && stage_out[c.n_stages + 1]) ? stage_out[c.n_stages + 1] : nullptr;
+    AVAE_TRY(avae::launch_conv_out1(t1, wave, pre, w.conv_post_w, w.conv_post_b, B, cl, TL,
+                                    c.k_post, c.final_act, s),
+             "conv_post");
+    return AVAE_OK;
+}
+
+}  // namespace
+
+extern "C" int avae_bigvgan_decode(const avae_decoder* dec, const float* latent, int B,
+                                   int frames, float* wave, void* workspace, size_t ws_bytes,
+                                   void* stream) {
+    return decode_impl(dec, latent, B, frames, wave, workspace, ws_bytes, nullptr,
+                       (hipStream_t)stream);
+}
+
+extern "C" int avae_bigvgan_decode_traced(const avae_decoder* dec, const float* latent, int B,
+                                          int frames, float* wave, void* workspace,
+                                          size_t ws_bytes, float* const* stage_out,
+                                          void* stream) {
+    return decode_impl(dec, latent, B, frames, wave, workspace, ws_bytes, stage_out,
+                       (hipStream_t)stream);
+}

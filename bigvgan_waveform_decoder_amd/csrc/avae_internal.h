@@ -1,0 +1,60 @@
+// Internal launch interface between the C-ABI layer and the HIP kernels.
+// Not installed; include/avae.h is the public boundary.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace avae {
+
+constexpr int kFilterLen = 12;
+
+// Resampling taps passed by value to the activation kernel (they land in
+// scalar registers).  up2 holds the upsampling taps already multiplied by
+// the x2 gain of the transposed convolution (exact: a power of two).
+struct ActTaps {
+    float up2[kFilterLen];
+    float down[kFilterLen];
+};
+
+// Epilogue of the Conv1d kernel:
+//   v   = conv + bias[o] (+ residual[idx])
+//   out = v * out_scale (+ out[idx] if accumulate)
+// residual may alias out (same element read then written by one lane).
+struct ConvEpilogue {
+    const float* bias;      // [Cout] or null
+    const float* residual;  // [B, Cout, Tout] or null
+    float out_scale;
+    int accumulate;
+};
+
+// Host-side float64 Kaiser-sinc design (filter_design.cpp).
+void design_kaiser_sinc(double cutoff, double half_width, int taps, double* out);
+
+hipError_t launch_act1d(const float* x, float* y, int B, int C, int T,
+                        const float* log_alpha, const float* log_beta,
+                        const ActTaps& taps, hipStream_t stream);
+
+// Returns hipErrorInvalidValue if the shape needs more LDS than a block has.
+hipError_t launch_conv1d(const float* x, float* y, const float* w, int B, int Cin, int Cout,
+                         int T, int Tout, int K, int dilation, int pad,
+                         const ConvEpilogue& ep, hipStream_t stream);
+
+hipError_t launch_convtr1d(const float* x, float* y, const float* w, const float* bias,
+                           int B, int Cin, int Cout, int Tin, int Tout, int K, int stride,
+                           int pad, hipStream_t stream);
+
+// Conv1d to a single output channel ("same" padding, odd K) followed by the
+// final nonlinearity (0 none, 1 tanh, 2 clamp to [-1,1]).  pre_final, if not
+// null, also receives the value before the nonlinearity.
+hipError_t launch_conv_out1(const float* x, float* y, float* pre_final, const float* w,
+                            const float* bias, int B, int Cin, int T, int K, int final_act,
+                            hipStream_t stream);
+
+// y[b,c,t] = x[b,c,t] * scale[c] + shift[c]
+hipError_t launch_channel_affine(const float* x, float* y, const float* scale,
+                                 const float* shift, int B, int C, int T, hipStream_t stream);
+
+}  // namespace avae

@@ -1,0 +1,437 @@
+// Conv1d and ConvTranspose1d as implicit GEMMs on the gfx950 FP32 matrix
+// cores (v_mfma_f32_16x16x4_f32), plus the one-output-channel conv_post.
+//
+// Operations ([H3] = docs.rs page of cortiq_engine/audiovae.rs):
+//   Conv1d::apply:  y[o,t] = b[o] + sum_i sum_j w[o,i,j] x[i, t + j d - pad]
+//                   (zero padding).  The page notes that w is already the
+//                   [Cout x Cin*K] GEMM operand of an im2col formulation.
+//   ConvT1d::apply: y[o, t s + j - pad] += x[i,t] w[i,o,j], plus b[o].
+//
+// Conv1d: GEMM with M = Cout, N = time, K = Cin * taps.  There is no im2col
+// buffer: a block stages kKC input channels of its time window plus the
+// (K-1)*d halo in LDS once, and every tap j reads the same LDS rows shifted
+// by j*d.  The weight slice [BM rows x kKC*K] is staged in LDS in the
+// caller's [Cout, Cin, K] order (rows contiguous in global memory, so loads
+// coalesce; odd row stride so LDS writes and fragment reads spread over the
+// banks).
+//
+// ConvTranspose1d: polyphase gather.  Output t' = q*s + r - pad (phase r)
+// receives sum_i sum_m w[i,o,r+s*m] * x[i, q-m], m < ceil((K-r)/s): one
+// small GEMM per phase, no zero-stuffing and no atomics; each block owns
+// one (Cout tile, phase, q tile).
+//
+// MFMA 16x16x4 f32 operand layout (wave64): lane l supplies A[l%16][l/16]
+// and B[l/16][l%16]; the 4 accumulator registers of lane l hold
+// D[4*(l/16) + r][l%16], r = 0..3.  Rows map to output channels and columns
+// to time, so consecutive lanes store consecutive samples.
+#include "avae_internal.h"
+
+namespace avae {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kKC = 8;  // input channels per K chunk: two MFMA k-steps of 4
+
+// Workgroups are dispatched round-robin over the 8 XCDs; remap so that each
+// XCD works through a contiguous range of logical tiles (neighbouring output
+// channel tiles of one time window share the staged input in that XCD's L2).
+__device__ __forceinline__ int xcd_remap(int bid, int nblk) {
+    const int q = nblk >> 3, r = nblk & 7;
+    const int xcd = bid & 7, idx = bid >> 3;
+    return (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+}
+
+__device__ __forceinline__ int floor_div(int a, int b) {
+    int q = a / b;
+    if ((a % b != 0) && ((a < 0) != (b < 0))) --q;
+    return q;
+}
+
+// ------------------------------------------------------------------ Conv1d
+
+template <int BM, int BN, int WM, int WN, int KT>
+__global__ __launch_bounds__(WM * WN * 64) void conv1d_mfma_kernel(
+    const float* __restrict__ x, float* y, const float* __restrict__ w, int Cin, int Cout,
+    int T, int Tout, int Kr, int dil, int pad, int m_tiles, int n_tiles, int nblk,
+    int ws_stride, int xs_stride, ConvEpilogue ep) {
+    constexpr int NT = WM * WN * 64;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int MT = WTM / 16, NTL = WTN / 16;
+    static_assert(MT >= 1 && NTL >= 1, "wave tile must hold at least one 16x16 MFMA tile");
+    const int K = KT > 0 ? KT : Kr;
+
+    extern __shared__ float lds[];
+    float* Ws = lds;                     // [BM][ws_stride]: col i*K + j
+    float* Xs = lds + BM * ws_stride;    // [kKC][xs_stride]: col u <-> t0 - pad + u
+
+    const int lid = xcd_remap(blockIdx.x, nblk);
+    const int mt_i = lid % m_tiles;
+    const int rest = lid / m_tiles;
+    const int nt_i = rest % n_tiles;
+    const int b = rest / n_tiles;
+    const int o0 = mt_i * BM, t0 = nt_i * BN;
+
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int wm0 = (wid / WN) * WTM, wn0 = (wid % WN) * WTN;
+    const int l16 = lane & 15, g = lane >> 4;
+
+    f32x4 acc[MT][NTL];
+#pragma unroll
+    for (int a = 0; a < MT; ++a)
+#pragma unroll
+        for (int c = 0; c < NTL; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int xw = BN + (K - 1) * dil;
+    const int wrow = kKC * K;
+    const float* xb = x + (size_t)b * Cin * T;
+
+    for (int ic0 = 0; ic0 < Cin; ic0 += kKC) {
+        for (int e = tid; e < BM * wrow; e += NT) {
+            const int ol = e / wrow;
+            const int f = e - ol * wrow;
+            const int i = f / K;
+            const int o = o0 + ol;
+            float v = 0.f;
+            if (o < Cout && ic0 + i < Cin) v = w[((size_t)o * Cin + ic0) * K + f];
+            Ws[ol * ws_stride + f] = v;
+        }
+        for (int e = tid; e < kKC * xw; e += NT) {
+            const int i = e / xw;
+            const int u = e - i * xw;
+            const int t = t0 - pad + u;
+            float v = 0.f;
+            if (ic0 + i < Cin && t >= 0 && t < T) v = xb[(size_t)(ic0 + i) * T + t];
+            Xs[i * xs_stride + u] = v;
+        }
+        __syncthreads();
+
+        for (int j = 0; j < K; ++j) {
+#pragma unroll
+            for (int kk = 0; kk < kKC / 4; ++kk) {
+                float av[MT], bv[NTL];
+#pragma unroll
+                for (int a = 0; a < MT; ++a)
+                    av[a] = Ws[(wm0 + a * 16 + l16) * ws_stride + (kk * 4 + g) * K + j];
+#pragma unroll
+                for (int c = 0; c < NTL; ++c)
+                    bv[c] = Xs[(kk * 4 + g) * xs_stride + wn0 + c * 16 + l16 + j * dil];
+#pragma unroll
+                for (int a = 0; a < MT; ++a)
+#pragma unroll
+                    for (int c = 0; c < NTL; ++c)
+                        acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a], bv[c], acc[a][c],
+                                                                         0, 0, 0);
+            }
+        }
+        __syncthreads();
+    }
+
+    float* yb = y + (size_t)b * Cout * Tout;
+    const float* rb = ep.residual ? ep.residual + (size_t)b * Cout * Tout : nullptr;
+#pragma unroll
+    for (int a = 0; a < MT; ++a) {
+#pragma unroll
+        for (int c = 0; c < NTL; ++c) {
+            const int t = t0 + wn0 + c * 16 + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int o = o0 + wm0 + a * 16 + g * 4 + r;
+                if (o < Cout && t < Tout) {
+                    const size_t idx = (size_t)o * Tout + t;
+                    float v = acc[a][c][r];
+                    if (ep.bias) v += ep.bias[o];
+                    if (rb) v += rb[idx];
+                    v *= ep.out_scale;
+                    if (ep.accumulate) v += yb[idx];
+                    yb[idx] = v;
+                }
+            }
+        }
+    }
+}
+
+struct ConvTile {
+    int bm, bn;
+};
+
+// LDS row strides: the weight rows get an odd stride; the input rows a
+// stride = 16 (mod 64) so the four 16-lane groups of a fragment read fall in
+// disjoint bank ranges.
+inline int xs_stride_for(int xw) {
+    int s = (xw + 63) / 64 * 64 + 16;
+    if (s - 64 >= xw) s -= 64;
+    return s;
+}
+
+template <int BM, int BN, int WM, int WN, int KT>
+hipError_t run_conv1d(const float* x, float* y, const float* w, int B, int Cin, int Cout, int T,
+                      int Tout, int K, int dil, int pad, const ConvEpilogue& ep,
+                      hipStream_t stream) {
+    const int m_tiles = (Cout + BM - 1) / BM;
+    const int n_tiles = (Tout + BN - 1) / BN;
+    const long long nblk = (long long)m_tiles * n_tiles * B;
+    if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
+    const int ws_stride = kKC * K + 1;
+    const int xs_stride = xs_stride_for(BN + (K - 1) * dil);
+    const size_t lds = (size_t)(BM * ws_stride + kKC * xs_stride) * sizeof(float);
+    if (lds > 160 * 1024) return hipErrorInvalidValue;
+    auto kern = conv1d_mfma_kernel<BM, BN, WM, WN, KT>;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(WM * WN * 64), lds, stream, x, y, w, Cin,
+                       Cout, T, Tout, K, dil, pad, m_tiles, n_tiles, (int)nblk, ws_stride,
+                       xs_stride, ep);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN>
+hipError_t dispatch_k(const float* x, float* y, const float* w, int B, int Cin, int Cout, int T,
+                      int Tout, int K, int dil, int pad, const ConvEpilogue& ep,
+                      hipStream_t stream) {
+    switch (K) {
+        case 1: return run_conv1d<BM, BN, WM, WN, 1>(x, y, w, B, Cin, Cout, T, Tout, K, dil, pad, ep, stream);
+        case 3: return run_conv1d<BM, BN, WM, WN, 3>(x, y, w, B, Cin, Cout, T, Tout, K, dil, pad, ep, stream);
+        case 7: return run_conv1d<BM, BN, WM, WN, 7>(x, y, w, B, Cin, Cout, T, Tout, K, dil, pad, ep, stream);
+        case 11: return run_conv1d<BM, BN, WM, WN, 11>(x, y, w, B, Cin, Cout, T, Tout, K, dil, pad, ep, stream);
+        default: return run_conv1d<BM, BN, WM, WN, 0>(x, y, w, B, Cin, Cout, T, Tout, K, dil, pad, ep, stream);
+    }
+}
+
+// ------------------------------------------------------------------ ConvTranspose1d
+
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) void convtr1d_mfma_kernel(
+    const float* __restrict__ x, float* __restrict__ y, const float* __restrict__ w,
+    const float* __restrict__ bias, int Cin, int Cout, int Tin, int Tout, int K, int s, int pad,
+    int ntap_max, int m_tiles, int q_tiles, int nblk, int ws_stride, int xs_stride) {
+    constexpr int NT = WM * WN * 64;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int MT = WTM / 16, NTL = WTN / 16;
+
+    extern __shared__ float lds[];
+    float* Ws = lds;                   // [BM][ws_stride]: col i*ntap_max + m
+    float* Xs = lds + BM * ws_stride;  // [kKC][xs_stride]: col u <-> x[q0-(ntap_max-1)+u]
+
+    const int lid = xcd_remap(blockIdx.x, nblk);
+    const int mt_i = lid % m_tiles;
+    int rest = lid / m_tiles;
+    const int r = rest % s;
+    rest /= s;
+    const int qt = rest % q_tiles;
+    const int b = rest / q_tiles;
+
+    const int ntap = (r < K) ? (K - r + s - 1) / s : 0;
+    const int qmin = -floor_div(r - pad, s);             // ceil((pad - r)/s)
+    const int qmax = floor_div(Tout - 1 + pad - r, s);
+    const int q0 = qmin + qt * BN;
+    if (q0 > qmax) return;  // uniform over the block, before any barrier
+    const int o0 = mt_i * BM;
+
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int wm0 = (wid / WN) * WTM, wn0 = (wid % WN) * WTN;
+    const int l16 = lane & 15, g = lane >> 4;
+
+    f32x4 acc[MT][NTL];
+#pragma unroll
+    for (int a = 0; a < MT; ++a)
+#pragma unroll
+        for (int c = 0; c < NTL; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int xw = BN + ntap_max - 1;
+    const int wrow = kKC * ntap_max;
+    const float* xb = x + (size_t)b * Cin * Tin;
+    const int xbase = q0 - (ntap_max - 1);
+
+    for (int ic0 = 0; ic0 < Cin; ic0 += kKC) {
+        for (int e = tid; e < BM * wrow; e += NT) {
+            const int ol = e / wrow;
+            const int f = e - ol * wrow;
+            const int i = f / ntap_max;
+            const int m = f - i * ntap_max;
+            const int o = o0 + ol, ic = ic0 + i;
+            float v = 0.f;
+            if (o < Cout && ic < Cin && m < ntap) v = w[((size_t)ic * Cout + o) * K + r + s * m];
+            Ws[ol * ws_stride + f] = v;
+        }
+        for (int e = tid; e < kKC * xw; e += NT) {
+            const int i = e / xw;
+            const int u = e - i * xw;
+            const int t = xbase + u;
+            float v = 0.f;
+            if (ic0 + i < Cin && t >= 0 && t < Tin) v = xb[(size_t)(ic0 + i) * Tin + t];
+            Xs[i * xs_stride + u] = v;
+        }
+        __syncthreads();
+        for (int m = 0; m < ntap; ++m) {
+#pragma unroll
+            for (int kk = 0; kk < kKC / 4; ++kk) {
+                float av[MT], bv[NTL];
+#pragma unroll
+                for (int a = 0; a < MT; ++a)
+                    av[a] = Ws[(wm0 + a * 16 + l16) * ws_stride + (kk * 4 + g) * ntap_max + m];
+#pragma unroll
+                for (int c = 0; c < NTL; ++c)
+                    bv[c] = Xs[(kk * 4 + g) * xs_stride + wn0 + c * 16 + l16 + (ntap_max - 1 - m)];
+#pragma unroll
+                for (int a = 0; a < MT; ++a)
+#pragma unroll
+                    for (int c = 0; c < NTL; ++c)
+                        acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a], bv[c], acc[a][c],
+                                                                         0, 0, 0);
+            }
+        }
+        __syncthreads();
+    }
+
+    float* yb = y + (size_t)b * Cout * Tout;
+#pragma unroll
+    for (int a = 0; a < MT; ++a) {
+#pragma unroll
+        for (int c = 0; c < NTL; ++c) {
+            const int q = q0 + wn0 + c * 16 + l16;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int o = o0 + wm0 + a * 16 + g * 4 + rr;
+                if (o < Cout && q <= qmax) {
+                    float v = acc[a][c][rr];
+                    if (bias) v += bias[o];
+                    yb[(size_t)o * Tout + (q * s + r - pad)] = v;
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ conv_post (Cout = 1)
+
+constexpr int kOutThreads = 256;
+constexpr int kOutChunk = 16;
+
+__global__ __launch_bounds__(kOutThreads) void conv_out1_kernel(
+    const float* __restrict__ x, float* __restrict__ y, float* __restrict__ pre,
+    const float* __restrict__ w, const float* __restrict__ bias, int Cin, int T, int K,
+    int final_act, int tiles) {
+    extern __shared__ float sm[];
+    const int xw = kOutThreads + K - 1;
+    float* ws = sm;                 // [Cin*K]
+    float* xs = sm + Cin * K;       // [kOutChunk][xw]
+    const int b = blockIdx.x / tiles;
+    const int t0 = (blockIdx.x - b * tiles) * kOutThreads;
+    const int tid = threadIdx.x;
+    const int pad = (K - 1) / 2;
+    for (int e = tid; e < Cin * K; e += kOutThreads) ws[e] = w[e];
+    float acc = 0.f;
+    const float* xb = x + (size_t)b * Cin * T;
+    for (int ic0 = 0; ic0 < Cin; ic0 += kOutChunk) {
+        __syncthreads();
+        for (int e = tid; e < kOutChunk * xw; e += kOutThreads) {
+            const int i = e / xw;
+            const int u = e - i * xw;
+            const int t = t0 - pad + u;
+            float v = 0.f;
+            if (ic0 + i < Cin && t >= 0 && t < T) v = xb[(size_t)(ic0 + i) * T + t];
+            xs[i * xw + u] = v;
+        }
+        __syncthreads();
+        const int nc = min(kOutChunk, Cin - ic0);
+        for (int i = 0; i < nc; ++i)
+            for (int j = 0; j < K; ++j) acc = fmaf(ws[(ic0 + i) * K + j], xs[i * xw + tid + j], acc);
+    }
+    const int t = t0 + tid;
+    if (t < T) {
+        if (bias) acc += bias[0];
+        if (pre) pre[(size_t)b * T + t] = acc;
+        float v = acc;
+        if (final_act == 1) v = tanhf(v);
+        else if (final_act == 2) v = fminf(fmaxf(v, -1.f), 1.f);
+        y[(size_t)b * T + t] = v;
+    }
+}
+
+__global__ void channel_affine_kernel(const float* __restrict__ x, float* __restrict__ y,
+                                      const float* __restrict__ scale,
+                                      const float* __restrict__ shift, int C, int T, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (size_t)gridDim.x * blockDim.x) {
+        const int c = (int)((i / (size_t)T) % (size_t)C);
+        y[i] = fmaf(x[i], scale[c], shift[c]);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_conv1d(const float* x, float* y, const float* w, int B, int Cin, int Cout,
+                         int T, int Tout, int K, int dilation, int pad, const ConvEpilogue& ep,
+                         hipStream_t stream) {
+    // Tile choice: the largest Cout tile that wastes little of the matrix
+    // cores, shrunk while the grid would leave the 256 CUs under-filled.
+    auto blocks = [&](int bm, int bn) {
+        return (long long)((Cout + bm - 1) / bm) * ((Tout + bn - 1) / bn) * B;
+    };
+    int bm;
+    if (Cout >= 256 && Cout % 128 == 0) bm = 128;
+    else if (Cout >= 64) bm = 64;
+    else if (Cout > 16) bm = 32;
+    else bm = 16;
+    if (bm == 128 && blocks(128, 128) < 512) bm = 64;
+    if (bm == 64 && blocks(64, 128) < 256) bm = 32;
+    switch (bm) {
+        case 128: return dispatch_k<128, 128, 2, 2>(x, y, w, B, Cin, Cout, T, Tout, K, dilation, pad, ep, stream);
+        case 64: return dispatch_k<64, 128, 2, 2>(x, y, w, B, Cin, Cout, T, Tout, K, dilation, pad, ep, stream);
+        case 32: return dispatch_k<32, 256, 1, 4>(x, y, w, B, Cin, Cout, T, Tout, K, dilation, pad, ep, stream);
+        default: return dispatch_k<16, 256, 1, 4>(x, y, w, B, Cin, Cout, T, Tout, K, dilation, pad, ep, stream);
+    }
+}
+
+hipError_t launch_convtr1d(const float* x, float* y, const float* w, const float* bias, int B,
+                           int Cin, int Cout, int Tin, int Tout, int K, int stride, int pad,
+                           hipStream_t stream) {
+    constexpr int BM = 64, BN = 64, WM = 2, WN = 2;
+    const int ntap_max = (K + stride - 1) / stride;
+    auto fdiv = [](int a, int b) { int q = a / b; if ((a % b != 0) && ((a < 0) != (b < 0))) --q; return q; };
+    int nq = 0;
+    for (int r = 0; r < stride; ++r) {
+        const int qmin = -fdiv(r - pad, stride);
+        const int qmax = fdiv(Tout - 1 + pad - r, stride);
+        nq = qmax - qmin + 1 > nq ? qmax - qmin + 1 : nq;
+    }
+    const int m_tiles = (Cout + BM - 1) / BM;
+    const int q_tiles = (nq + BN - 1) / BN;
+    const long long nblk = (long long)m_tiles * stride * q_tiles * B;
+    if (nblk > 0x7fffffffLL || nq < 1) return hipErrorInvalidValue;
+    const int ws_stride = kKC * ntap_max + 1;
+    const int xs_stride = xs_stride_for(BN + ntap_max - 1);
+    const size_t lds = (size_t)(BM * ws_stride + kKC * xs_stride) * sizeof(float);
+    if (lds > 64 * 1024) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((convtr1d_mfma_kernel<BM, BN, WM, WN>), dim3((unsigned)nblk),
+                       dim3(WM * WN * 64), lds, stream, x, y, w, bias, Cin, Cout, Tin, Tout, K,
+                       stride, pad, ntap_max, m_tiles, q_tiles, (int)nblk, ws_stride, xs_stride);
+    return hipGetLastError();
+}
+
+hipError_t launch_conv_out1(const float* x, float* y, float* pre_final, const float* w,
+                            const float* bias, int B, int Cin, int T, int K, int final_act,
+                            hipStream_t stream) {
+    const int tiles = (T + kOutThreads - 1) / kOutThreads;
+    const long long nblk = (long long)tiles * B;
+    const size_t lds = (size_t)(Cin * K + kOutChunk * (kOutThreads + K - 1)) * sizeof(float);
+    if (nblk > 0x7fffffffLL || lds > 64 * 1024) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(conv_out1_kernel, dim3((unsigned)nblk), dim3(kOutThreads), lds, stream, x,
+                       y, pre_final, w, bias, Cin, T, K, final_act, tiles);
+    return hipGetLastError();
+}
+
+hipError_t launch_channel_affine(const float* x, float* y, const float* scale, const float* shift,
+                                 int B, int C, int T, hipStream_t stream) {
+    const size_t n = (size_t)B * C * T;
+    const unsigned blocks = (unsigned)((n + 255) / 256 > 65536 ? 65536 : (n + 255) / 256);
+    hipLaunchKernelGGL(channel_affine_kernel, dim3(blocks), dim3(256), 0, stream, x, y, scale,
+                       shift, C, T, n);
+    return hipGetLastError();
+}
+
+}  // namespace avae

@@ -1,0 +1,238 @@
+/*
+ * avae.h -- C-ABI of libavae.so: the alias-free BigVGAN waveform decoder on
+ * one MI355X (gfx950).
+ *
+ * Sources of the operations (cited by page and item):
+ *   [H3]  docs.rs source page of cortiq_engine/audiovae.rs (cortiq-engine
+ *         0.5.74): the MiniMax-H3 audio VAE decoder.
+ *   [LTX] docs.rs source page of cortiq_engine/ltxaudio.rs (cortiq-engine
+ *         0.6.3): the LTX-2.5 BigVGAN v2 vocoder.
+ *
+ * Conventions for every entry point
+ *   - Tensors are float32, contiguous, row-major, in DEVICE memory unless a
+ *     parameter says "host".  Activations are [B, C, T]: B independent mono
+ *     passes (stereo = B 2), C channels, T samples, time fastest.
+ *   - The caller owns every buffer it passes; the library never frees or
+ *     keeps a caller pointer beyond the call, except that a decoder keeps
+ *     its own copy of the weights (avae_decoder_create).
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every compute
+ *     call is asynchronous on that stream, allocates nothing and never
+ *     synchronises.
+ *   - Return value: AVAE_OK (0) on success, or a negative AVAE_E* code.
+ *     All argument and shape checks happen before anything is launched, so
+ *     a failed call has no effect on the device.  avae_last_error() gives a
+ *     message for the last failure on the calling thread.
+ *   - Input and output buffers must not overlap unless a parameter says so.
+ */
+#ifndef AVAE_H
+#define AVAE_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AVAE_OK          0
+#define AVAE_EINVAL     -1 /* null pointer, non-positive size, bad enum      */
+#define AVAE_ESHAPE     -2 /* shapes that do not fit together or exceed a cap */
+#define AVAE_EWORKSPACE -3 /* workspace missing or too small                 */
+#define AVAE_EHIP       -4 /* the HIP runtime reported an error               */
+#define AVAE_ENOMEM     -5 /* device allocation failed (create only)          */
+
+#define AVAE_FILTER_LEN   12 /* [H3] FILTER_LEN: both resampling filters       */
+#define AVAE_MAX_STAGES    8
+#define AVAE_MAX_KERNELS   4
+#define AVAE_MAX_DIL       4
+#define AVAE_MAX_TAPS     31 /* largest Conv1d / ConvTranspose1d kernel size  */
+
+enum avae_final { AVAE_FINAL_NONE = 0, AVAE_FINAL_TANH = 1, AVAE_FINAL_CLAMP = 2 };
+
+/* Message for the last non-zero return on this thread ("" if none). */
+const char* avae_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int avae_version(void);
+
+/*
+ * Kaiser-windowed sinc lowpass taps, designed in float64 on the host and
+ * rounded to float32, normalised to unit sum ([H3] kaiser_sinc, bessel_i0,
+ * sinc).  Tap i sits at t = i - taps/2 + 0.5; window I0(beta*sqrt(1-r^2))/I0(beta)
+ * with r = 2i/(taps-1) - 1 and Kaiser's beta for the attenuation
+ * 2.285*(taps/2 - 1)*pi*(4*half_width) + 7.95.  The decoder's filters are
+ * avae_kaiser_sinc(0.25, 0.3, 12, out).
+ *   out_host: host array of `taps` floats (written).
+ * Errors: EINVAL for taps < 2, taps odd, cutoff or half_width not in (0, 0.5].
+ * Touches no device.
+ */
+int avae_kaiser_sinc(double cutoff, double half_width, int taps, float* out_host);
+
+/*
+ * Alias-free activation, [B, C, T] -> [B, C, T] ([H3] Activation1d::apply,
+ * SnakeBeta, fir_pad; [LTX] Aliasing::upsample/downsample, SnakeBeta::forward):
+ *   mid = x2 upsample: replicate-pad 5 each side, transposed FIR (stride 2,
+ *         gain 2) with up_taps, trim 15 each side  -> 2T samples;
+ *   mid = mid + sin^2(exp(log_alpha[c]) * mid) / (exp(log_beta[c]) + 1e-9);
+ *   y   = replicate-pad mid 5 left / 6 right, FIR with down_taps, stride 2.
+ *   x, y:                 [B, C, T] device; must not overlap.
+ *   log_alpha, log_beta:  [C] device, log-scale SnakeBeta parameters.
+ *   up_taps, down_taps:   HOST arrays of AVAE_FILTER_LEN floats, or NULL for
+ *                         the designed avae_kaiser_sinc(0.25, 0.3, 12) taps.
+ * Errors: EINVAL (null tensor, B, C or T < 1).
+ */
+int avae_act1d(const float* x, float* y, int B, int C, int T,
+               const float* log_alpha, const float* log_beta,
+               const float* up_taps, const float* down_taps, void* stream);
+
+/*
+ * Dilated Conv1d with zero padding ([H3] Conv1d::apply, get_padding):
+ *   y[b,o,t] = bias[o] + sum_i sum_j w[o,i,j] * x[b,i, t + j*dilation - pad]
+ *              (+ residual[b,o,t] if residual != NULL)
+ *   Tout = T + 2*pad - dilation*(K-1)  (the "same" length for pad = (K*d-d)/2).
+ *   x: [B, Cin, T]; y: [B, Cout, Tout]; w: [Cout, Cin, K] (PyTorch layout);
+ *   bias: [Cout] or NULL; residual: [B, Cout, Tout] or NULL, and it MAY be
+ *   the same buffer as y (in-place residual add, as in [H3] AmpBlock::apply).
+ *   Arithmetic: float32 products accumulated in float32 on the FP32 matrix
+ *   cores.
+ * Errors: EINVAL (null x/y/w, sizes < 1, dilation < 1, pad < 0);
+ *         ESHAPE (Tout < 1, K > AVAE_MAX_TAPS).
+ */
+int avae_conv1d(const float* x, float* y, int B, int Cin, int Cout, int T,
+                const float* w, const float* bias, int K, int dilation, int pad,
+                const float* residual, void* stream);
+
+/*
+ * ConvTranspose1d ([H3] ConvT1d::apply/load; [LTX] ConvT1d):
+ *   y[b, o, t*stride + j - pad] += x[b,i,t] * w[i,o,j], plus bias[o];
+ *   Tout = (Tin - 1)*stride + K - 2*pad.
+ *   Computed as `stride` polyphase gathers (no atomics, no zero-stuffing).
+ *   x: [B, Cin, Tin]; y: [B, Cout, Tout]; w: [Cin, Cout, K] (PyTorch layout);
+ *   bias: [Cout] or NULL; pad < 0 selects (K - stride)/2 (integer division,
+ *   the pages' choice; needs K >= stride).
+ * Errors: EINVAL (null x/y/w, sizes < 1, stride < 1);
+ *         ESHAPE (Tout < 1, K > AVAE_MAX_TAPS, pad < 0 with K < stride).
+ */
+int avae_convtr1d(const float* x, float* y, int B, int Cin, int Cout, int Tin,
+                  const float* w, const float* bias, int K, int stride, int pad,
+                  void* stream);
+
+/*
+ * One AMP residual block ([H3] AmpBlock::apply, [LTX] AmpBlock::forward):
+ *   cur = x; for q < n_dil:
+ *     cur += conv2_q(act_{2q+1}(conv1_q(act_{2q}(cur))))
+ *   with conv1_q of kernel K, dilation dil[q], "same" padding, and conv2_q of
+ *   kernel K, dilation 1.  Then
+ *     y = out_scale * cur            (accumulate == 0)
+ *     y = y + out_scale * cur        (accumulate != 0)
+ *   which gives the MRF average of [H3] AudioVae::decode with
+ *   out_scale = 1/n_kernels over n_kernels calls into one y.
+ *   x, y: [B, C, T] device, must not overlap.
+ *   dil: HOST array [n_dil].  w1, b1, w2, b2: HOST arrays [n_dil] of device
+ *   pointers (w: [C, C, K]; b: [C] or NULL).  log_alpha, log_beta: HOST
+ *   arrays [2*n_dil] of device pointers to [C] (activation q's parameters).
+ *   Activations use the designed taps.
+ *   workspace: device, at least avae_amp_block_workspace_bytes(B, C, T).
+ * Errors: EINVAL, ESHAPE (n_dil > AVAE_MAX_DIL, K even or > AVAE_MAX_TAPS),
+ *         EWORKSPACE.
+ */
+size_t avae_amp_block_workspace_bytes(int B, int C, int T);
+int avae_amp_block(const float* x, float* y, int B, int C, int T, int K,
+                   int n_dil, const int* dil,
+                   const float* const* w1, const float* const* b1,
+                   const float* const* w2, const float* const* b2,
+                   const float* const* log_alpha, const float* const* log_beta,
+                   float out_scale, int accumulate,
+                   void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Whole decoder ([H3] AudioVae::from_cmf/decode; [LTX] Vocoder::forward):
+ *   [optional z*std + mean] -> [optional 1x1 dec_in conv] -> conv_pre
+ *   (k_pre, "same") -> per stage i: ConvTranspose1d (rate rates[i], kernel
+ *   up_k[i], pad (up_k[i]-rates[i])/2) then the MRF average of n_kernels AMP
+ *   blocks -> act_post -> conv_post (k_post, "same", 1 channel) -> final
+ *   (none / tanh / clamp to [-1, 1]).
+ *   Channel widths: ch[0] = conv_pre output, ch[i+1] = stage i output.
+ */
+typedef struct avae_config {
+    int c_in;                       /* latent channels                          */
+    int dec_in_ch;                  /* >0: 1x1 dec_in conv c_in -> dec_in_ch     */
+    int has_latent_affine;          /* !=0: z*latent_std + latent_mean first     */
+    int k_pre, k_post;              /* conv_pre / conv_post kernel sizes (odd)   */
+    int n_stages;
+    int ch[AVAE_MAX_STAGES + 1];
+    int rates[AVAE_MAX_STAGES];
+    int up_k[AVAE_MAX_STAGES];
+    int n_kernels;                  /* AMP blocks per stage                      */
+    int rb_k[AVAE_MAX_KERNELS];     /* their kernel sizes (odd)                  */
+    int n_dil;                      /* dilations per AMP block                   */
+    int rb_d[AVAE_MAX_KERNELS][AVAE_MAX_DIL];
+    int final_act;                  /* enum avae_final                           */
+} avae_config;
+
+/* Device pointers to the caller's weights (PyTorch layouts).  Biases may be
+ * NULL (treated as zero).  Unused entries are ignored. */
+typedef struct avae_weights {
+    const float* latent_mean;       /* [c_in]                                   */
+    const float* latent_std;        /* [c_in]                                   */
+    const float* dec_in_w;          /* [dec_in_ch, c_in, 1]                     */
+    const float* dec_in_b;
+    const float* conv_pre_w;        /* [ch0, c_in or dec_in_ch, k_pre]          */
+    const float* conv_pre_b;
+    const float* up_w[AVAE_MAX_STAGES];   /* [ch[i], ch[i+1], up_k[i]]          */
+    const float* up_b[AVAE_MAX_STAGES];
+    const float* w1[AVAE_MAX_STAGES][AVAE_MAX_KERNELS][AVAE_MAX_DIL]; /* [C,C,k] */
+    const float* b1[AVAE_MAX_STAGES][AVAE_MAX_KERNELS][AVAE_MAX_DIL];
+    const float* w2[AVAE_MAX_STAGES][AVAE_MAX_KERNELS][AVAE_MAX_DIL];
+    const float* b2[AVAE_MAX_STAGES][AVAE_MAX_KERNELS][AVAE_MAX_DIL];
+    const float* act_la[AVAE_MAX_STAGES][AVAE_MAX_KERNELS][2 * AVAE_MAX_DIL];
+    const float* act_lb[AVAE_MAX_STAGES][AVAE_MAX_KERNELS][2 * AVAE_MAX_DIL];
+    const float* post_la;           /* [ch[n_stages]]                           */
+    const float* post_lb;
+    const float* conv_post_w;       /* [1, ch[n_stages], k_post]                */
+    const float* conv_post_b;       /* [1]                                      */
+} avae_weights;
+
+typedef struct avae_decoder avae_decoder;
+
+/* Validates the config and copies every weight into one library-owned
+ * device allocation on the current device (synchronous; the only call that
+ * allocates).  *out receives the decoder.  Errors: EINVAL, ESHAPE, ENOMEM,
+ * EHIP. */
+int avae_decoder_create(const avae_config* cfg, const avae_weights* w, avae_decoder** out);
+void avae_decoder_destroy(avae_decoder* dec);
+
+/* Output samples per pass for `frames` latent frames (frames*hop for the
+ * pages' kernel/rate pairs).  Errors: EINVAL, ESHAPE. */
+int avae_decoder_output_length(const avae_decoder* dec, int frames, int* out_len);
+
+/* Workspace bytes avae_bigvgan_decode needs for B passes of `frames` frames
+ * (0 on invalid arguments). */
+size_t avae_decoder_workspace_bytes(const avae_decoder* dec, int B, int frames);
+
+/*
+ * Decode: latent [B, c_in, frames] -> wave [B, L] float32, L from
+ * avae_decoder_output_length; each row is an independent mono pass.
+ * Concurrent calls on different streams are safe with separate workspaces
+ * (the decoder is read-only here).
+ * Errors: EINVAL, ESHAPE, EWORKSPACE, EHIP.
+ */
+int avae_bigvgan_decode(const avae_decoder* dec, const float* latent, int B, int frames,
+                        float* wave, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Decode and also copy intermediate results out, for stage-by-stage
+ * comparison ([H3] AudioVae::decode prints them under CMF_AVAE_PROF).
+ * stage_out: HOST array of n_stages + 2 device pointers (any may be NULL):
+ *   [0]            conv_pre output     [B, ch[0], frames]
+ *   [1 + i]        stage i output      [B, ch[i+1], T_{i+1}]
+ *   [n_stages + 1] conv_post output before the final nonlinearity [B, L]
+ */
+int avae_bigvgan_decode_traced(const avae_decoder* dec, const float* latent, int B, int frames,
+                               float* wave, void* workspace, size_t ws_bytes,
+                               float* const* stage_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AVAE_H */

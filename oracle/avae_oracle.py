@@ -217,7 +217,10 @@ def conv1d(x: np.ndarray, w: np.ndarray, b: Optional[np.ndarray] = None, dilatio
     y = np.zeros(x.shape[:-2] + (cout, out_n), dtype=np.float64)
     for j in range(k):
         # tap j reads x[i, t + j d - pad] = xp[i, t + j d]
-        y += np.matmul(w[:, :, j], xp[..., j * dilation: j * dilation + out_n])
+        # (contiguous operands keep numpy's matmul on BLAS)
+        wj = np.ascontiguousarray(w[:, :, j])
+        xj = np.ascontiguousarray(xp[..., j * dilation: j * dilation + out_n])
+        y += np.matmul(wj, xj)
     if b is not None:
         y += np.asarray(b, dtype=np.float64)[:, None]
     if residual is not None:
@@ -245,7 +248,8 @@ def convtr1d(x: np.ndarray, w: np.ndarray, b: Optional[np.ndarray], stride: int,
     buf = np.zeros(x.shape[:-2] + (cout, full), dtype=np.float64)
     for j in range(k):
         # input t lands at t*stride + j
-        buf[..., j: j + stride * (n - 1) + 1: stride] += np.matmul(w[:, :, j].T, x)
+        buf[..., j: j + stride * (n - 1) + 1: stride] += np.matmul(
+            np.ascontiguousarray(w[:, :, j].T), np.ascontiguousarray(x))
     y = buf[..., pad: pad + out_n].copy()
     if b is not None:
         y += np.asarray(b, dtype=np.float64)[:, None]

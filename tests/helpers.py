@@ -56,3 +56,28 @@ def rel_err(got, ref) -> float:
     if rms == 0.0:
         return float(np.max(np.abs(got - ref))) if got.size else 0.0
     return float(np.max(np.abs(got - ref))) / rms if got.size else 0.0
+
+
+def decoder_reach_frames(spec) -> int:
+    """Upper bound, in latent frames, on how far an output sample's
+    dependence reaches into the latent on either side.  Per layer, in that
+    layer's input samples: Activation1d reads x[t-5 .. t+5]; a "same" Conv1d
+    (k, d) reaches (k-1)d/2; a ConvTranspose1d output reads inputs within
+    ceil(k/s) + 1.  Each reach is divided by the upsampling factor already
+    applied, and the sum is rounded up (plus one frame of slack)."""
+    import math
+    reach = (spec.k_pre - 1) / 2.0
+    rate = 1
+    for r, k in zip(spec.rates, spec.up_k):
+        reach += (math.ceil(k / r) + 1) / rate
+        rate *= r
+        mrf = max(sum(5 + (kj - 1) * d / 2.0 + 5 + (kj - 1) / 2.0 for d in dj)
+                  for kj, dj in zip(spec.rb_k, spec.rb_d))
+        reach += mrf / rate
+    reach += (5 + (spec.k_post - 1) / 2.0) / rate
+    return int(math.ceil(reach)) + 1
+
+
+def amp_reach(k, dil) -> int:
+    """Samples an AMP block's output reaches on either side (same rule)."""
+    return int(sum(5 + (k - 1) * d // 2 + 5 + (k - 1) // 2 for d in dil))

@@ -1,0 +1,92 @@
+"""CPU-side checks of the C-ABI library: it loads, it exports every entry
+point the header declares, its host-only filter designer agrees with the
+oracle, and argument errors are reported before anything touches a device."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from bigvgan_waveform_decoder_amd import avae
+from oracle import avae_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "avae.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(avae_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = avae.lib()
+    names = _declared_functions()
+    assert len(names) >= 14, names
+    for n in names:
+        assert hasattr(L, n), f"libavae.so does not export {n}"
+
+
+def test_version():
+    assert avae.version() >= 100
+
+
+def test_kaiser_sinc_matches_oracle():
+    """The library's float64 designer (its own C++) rounds to the same float32
+    taps as the oracle's design, for the decoder's filter and a few others."""
+    for cutoff, hw, k in [(0.25, 0.3, 12), (0.25, 0.3, 16), (0.2, 0.25, 24), (0.4, 0.1, 8)]:
+        got = avae.kaiser_sinc(cutoff, hw, k).astype(np.float64)
+        ref = O.kaiser_sinc(cutoff, hw, k)
+        ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+        assert np.all(np.abs(got - ref) <= ulp), (cutoff, hw, k, got - ref)
+
+
+def test_kaiser_sinc_rejects_bad_arguments():
+    L = avae.lib()
+    out = np.zeros(16, np.float32)
+    assert L.avae_kaiser_sinc(0.25, 0.3, 11, out.ctypes.data) == -1
+    assert L.avae_kaiser_sinc(0.0, 0.3, 12, out.ctypes.data) == -1
+    assert L.avae_kaiser_sinc(0.25, 0.3, 12, None) == -1
+    assert b"taps" in L.avae_last_error() or b"null" in L.avae_last_error()
+
+
+def test_argument_errors_before_any_launch():
+    """Null pointers and impossible shapes fail with a code and a message,
+    without any device call (this runs where there is no GPU)."""
+    L = avae.lib()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: checks fail first
+    assert L.avae_act1d(None, fake, 1, 1, 1, fake, fake, None, None, None) == -1
+    assert L.avae_act1d(fake, fake, 0, 1, 1, fake, fake, None, None, None) == -1
+    assert L.avae_conv1d(fake, fake, 1, 1, 1, 4, None, None, 3, 1, 1, None, None) == -1
+    # Tout = 4 + 0 - 5*(3-1) < 1
+    assert L.avae_conv1d(fake, ctypes.c_void_p(0x2000), 1, 1, 1, 4, fake, None, 3, 5, 0,
+                         None, None) == -2
+    assert L.avae_conv1d(fake, ctypes.c_void_p(0x2000), 1, 1, 1, 4, fake, None, 33, 1, 16,
+                         None, None) == -2
+    assert L.avae_convtr1d(fake, ctypes.c_void_p(0x2000), 1, 1, 1, 4, fake, None, 2, 5, -1,
+                           None) == -2
+    assert L.avae_convtr1d(fake, ctypes.c_void_p(0x2000), 1, 1, 1, 4, fake, None, 4, 0, -1,
+                           None) == -1
+    assert len(L.avae_last_error()) > 0
+    # workspace too small
+    dil = (ctypes.c_int * 1)(1)
+    ptrs = (ctypes.c_void_p * 2)(0x1000, 0x1000)
+    rc = L.avae_amp_block(fake, ctypes.c_void_p(0x2000), 1, 4, 8, 3, 1, ctypes.addressof(dil),
+                          ctypes.addressof(ptrs), None, ctypes.addressof(ptrs), None,
+                          ctypes.addressof(ptrs), ctypes.addressof(ptrs), 1.0, 0, fake, 16, None)
+    assert rc == -3
+    assert L.avae_amp_block_workspace_bytes(2, 4, 8) >= 3 * 2 * 4 * 8 * 4
+    assert L.avae_amp_block_workspace_bytes(0, 4, 8) == 0
+
+
+def test_decoder_create_rejects_bad_config():
+    L = avae.lib()
+    cfg = avae.avae_config()
+    w = avae.avae_weights()
+    h = ctypes.c_void_p()
+    assert L.avae_decoder_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(h)) in (-1, -2)
+    assert not h.value
+    assert L.avae_decoder_create(None, ctypes.byref(w), ctypes.byref(h)) == -1
+    assert L.avae_decoder_workspace_bytes(None, 1, 1) == 0

@@ -1,0 +1,120 @@
+"""Parity of the AMP block and the MRF average (avae_amp_block, alone and
+accumulated) and of one full upsample stage, with the float64 oracle.
+
+Composite bar: an AMP block is 12 kernel calls in sequence (6 activations,
+6 convolutions), a stage 37; each call's float32 rounding adds to the
+output, so these are held to max|err| / RMS(ref) <= 1e-4 (ten per-kernel
+bars), the decode to 1e-3."""
+import numpy as np
+import pytest
+import torch
+
+from bigvgan_waveform_decoder_amd import avae
+from bigvgan_waveform_decoder_amd import workloads as W
+from oracle import avae_oracle as O
+from tests.gpu_util import announce, cuda, cuda_dict, host
+from tests.helpers import amp_params, amp_reach, rel_err
+
+pytestmark = pytest.mark.gpu
+TOL_BLOCK = 1e-4
+
+
+def _amp_call(x_dev, td, prefix, K, dil, out=None, scale=1.0, accumulate=False, ws=None):
+    n = len(dil)
+    return avae.amp_block(
+        x_dev, K, dil,
+        [td[f"{prefix}.convs1.{q}.weight"] for q in range(n)],
+        [td[f"{prefix}.convs1.{q}.bias"] for q in range(n)],
+        [td[f"{prefix}.convs2.{q}.weight"] for q in range(n)],
+        [td[f"{prefix}.convs2.{q}.bias"] for q in range(n)],
+        [td[f"{prefix}.activations.{q}.act.alpha"] for q in range(2 * n)],
+        [td[f"{prefix}.activations.{q}.act.beta"] for q in range(2 * n)],
+        out_scale=scale, accumulate=accumulate, out=out, workspace=ws)
+
+
+def test_amp_block_workload1_full():
+    """Workload 1: one AMP block, [1, 32, 4096], k=3, d=(1,3,5), whole output."""
+    announce("amp workload1")
+    x, t = W.workload1()
+    y = host(_amp_call(cuda(x), cuda_dict(t), "block", 3, (1, 3, 5)))
+    ref = O.amp_block(x, amp_params(t, "block", 3, (1, 3, 5)))
+    assert rel_err(y, ref) <= TOL_BLOCK
+
+
+@pytest.mark.parametrize("C,T,K", [(12, 2500, 11), (48, 1031, 7), (130, 700, 3)])
+def test_amp_block_odd_shapes(C, T, K):
+    announce(f"amp C={C} T={T} K={K}")
+    x = W.normal(0, f"amp/{C}/{T}/x", [2, C, T])
+    t = W.amp_tensors(0, f"amp{C}", C, K, (1, 3, 5), weight_var=2.0 / (C * K))
+    y = host(_amp_call(cuda(x), cuda_dict(t), f"amp{C}", K, (1, 3, 5)))
+    ref = O.amp_block(x, amp_params(t, f"amp{C}", K, (1, 3, 5)))
+    assert rel_err(y, ref) <= TOL_BLOCK
+
+
+def test_mrf_accumulate_matches_oracle():
+    """Three blocks accumulated into one output with scale 1/3 = the MRF."""
+    announce("mrf accumulate")
+    C, T = 24, 1500
+    x = W.normal(0, "mrf/x", [2, C, T])
+    ts, blocks = [], []
+    for j, k in enumerate((3, 7, 11)):
+        t = W.amp_tensors(0, f"resblocks.{j}", C, k, (1, 3, 5), weight_var=2.0 / (C * k))
+        ts.append(t)
+        blocks.append(amp_params(t, f"resblocks.{j}", k, (1, 3, 5)))
+    xd = cuda(x)
+    out = cuda(np.zeros((2, C, T), np.float32))
+    for j, k in enumerate((3, 7, 11)):
+        _amp_call(xd, cuda_dict(ts[j]), f"resblocks.{j}", k, (1, 3, 5), out=out,
+                  scale=1.0 / 3.0, accumulate=j > 0)
+    ref = O.mrf(x, blocks)
+    assert rel_err(host(out), ref) <= TOL_BLOCK
+
+
+def _crop(x, a, e, m):
+    """x[..., a-m : e+m] clipped to the signal; returns the crop and the
+    offset of a inside it."""
+    lo, hi = max(a - m, 0), min(e + m, x.shape[-1])
+    return x[..., lo:hi], a - lo
+
+
+def test_amp_block_workload2_full_size_sampled_windows():
+    """Workload 2's AMP block at full size, [2, 512, 65536]: outputs on
+    windows at both ends and inside, each recomputed by the oracle from a
+    crop whose margin exceeds the block's reach (42 samples for k=3,
+    d=(1,3,5)), so the crop edges cannot touch the window."""
+    announce("amp workload2 full size")
+    x, _, _, t = W.workload2()
+    y = host(_amp_call(cuda(x), cuda_dict(t), "block", 3, (1, 3, 5)))
+    p = amp_params(t, "block", 3, (1, 3, 5))
+    m = amp_reach(3, (1, 3, 5)) + 8
+    T = x.shape[-1]
+    for a in (0, 30000, T - 256):
+        xc, off = _crop(x, a, a + 256, m)
+        ref = O.amp_block(xc, p)[..., off:off + 256]
+        assert rel_err(y[..., a:a + 256], ref) <= TOL_BLOCK, a
+
+
+def test_upsample_stage_workload3_full_size_sampled_windows():
+    """Workload 3 at full size: ConvTranspose1d 1024 -> 512 (k=10, s=5) on
+    [2, 1024, 8000], then the MRF of blocks k=(3,7,11) x d=(1,3,5).  The
+    oracle's upsampler output is exact in full; the MRF is recomputed on
+    windows with a margin beyond the widest block's reach (90 samples)."""
+    announce("stage workload3 full size")
+    x, t = W.workload3()
+    td = cuda_dict(t)
+    up = avae.convtr1d(cuda(x), td["ups.0.weight"], td["ups.0.bias"], stride=5)
+    out = torch.empty_like(up)
+    ws = None
+    for j, k in enumerate((3, 7, 11)):
+        _amp_call(up, td, f"resblocks.{j}", k, (1, 3, 5), out=out, scale=1.0 / 3.0,
+                  accumulate=j > 0, ws=ws)
+    y = host(out)
+    assert y.shape == (2, 512, 40001)
+    xo = O.convtr1d(x, t["ups.0.weight"], t["ups.0.bias"], stride=5)
+    blocks = [amp_params(t, f"resblocks.{j}", k, (1, 3, 5)) for j, k in enumerate((3, 7, 11))]
+    m = max(amp_reach(k, (1, 3, 5)) for k in (3, 7, 11)) + 8
+    T = xo.shape[-1]
+    for a in (0, 20000, T - 200):
+        xc, off = _crop(xo, a, a + 200, m)
+        ref = O.mrf(xc, blocks)[..., off:off + 200]
+        assert rel_err(y[..., a:a + 200], ref) <= TOL_BLOCK, a

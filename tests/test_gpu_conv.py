@@ -1,0 +1,127 @@
+"""Parity of the FP32-MFMA Conv1d and polyphase ConvTranspose1d kernels
+(avae_conv1d, avae_convtr1d) with the float64 oracle:
+max|err| / RMS(ref) <= 1e-5 per kernel call."""
+import numpy as np
+import pytest
+
+from bigvgan_waveform_decoder_amd import avae
+from bigvgan_waveform_decoder_amd import workloads as W
+from oracle import avae_oracle as O
+from tests.gpu_util import announce, cuda, host
+from tests.helpers import rel_err
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+
+
+def _conv_inputs(tag, B, Cin, Cout, T, K):
+    x = W.normal(0, f"conv/{tag}/x", [B, Cin, T])
+    w = W.normal(0, f"conv/{tag}/w", [Cout, Cin, K], 0.0, 1.0 / (Cin * K))
+    b = W.normal(0, f"conv/{tag}/b", [Cout], 0.0, 0.01)
+    return x, w, b
+
+
+CONV_CASES = [
+    # B, Cin, Cout, T, K, d, pad (None = same), residual
+    (1, 8, 16, 100, 3, 1, None, False),
+    (2, 13, 21, 257, 3, 3, None, True),
+    (1, 32, 12, 1000, 7, 5, None, False),
+    (2, 24, 130, 300, 11, 5, None, True),
+    (1, 12, 1, 64, 7, 1, None, False),
+    (1, 5, 7, 50, 5, 2, None, False),      # K outside the specialised set
+    (1, 9, 9, 40, 3, 1, 0, False),          # "valid" padding: Tout = T - 2
+    (1, 9, 9, 40, 3, 2, 5, False),          # more padding than "same"
+    (1, 256, 256, 513, 3, 1, None, True),   # 128-row tiles
+    (2, 512, 512, 700, 11, 3, None, False),
+    (1, 768, 768, 260, 11, 5, None, True),  # H3 stage-1 width, long K
+    (2, 1, 3, 33, 1, 1, None, False),
+]
+
+
+@pytest.mark.parametrize("B,Cin,Cout,T,K,d,pad,res", CONV_CASES)
+def test_conv1d_matches_oracle(B, Cin, Cout, T, K, d, pad, res):
+    announce(f"conv1d B={B} Cin={Cin} Cout={Cout} T={T} K={K} d={d} pad={pad} res={res}")
+    x, w, b = _conv_inputs(f"{B}-{Cin}-{Cout}-{T}-{K}-{d}-{pad}", B, Cin, Cout, T, K)
+    p = (K * d - d) // 2 if pad is None else pad
+    Tout = T + 2 * p - d * (K - 1)
+    r = W.normal(0, f"conv/{Cin}-{Cout}-{T}/res", [B, Cout, Tout]) if res else None
+    y = host(avae.conv1d(cuda(x), cuda(w), cuda(b), dilation=d, pad=p,
+                         residual=cuda(r) if res else None))
+    ref = O.conv1d(x, w, b, dilation=d, pad=p, residual=r)
+    assert y.shape == ref.shape
+    assert rel_err(y, ref) <= TOL
+
+
+def test_conv1d_inplace_residual():
+    """residual may be the output buffer itself (cur += conv(...))."""
+    announce("conv1d in-place residual")
+    x, w, b = _conv_inputs("inplace", 2, 64, 64, 777, 3)
+    cur = W.normal(0, "conv/inplace/cur", [2, 64, 777])
+    out = cuda(cur)
+    avae.conv1d(cuda(x), cuda(w), cuda(b), dilation=3, residual=out, out=out)
+    ref = O.conv1d(x, w, b, dilation=3, residual=cur)
+    assert rel_err(host(out), ref) <= TOL
+
+
+def _window_conv(x, w, b, d, a, e):
+    """Oracle outputs y[..., a:e] of a 'same' conv, from the inputs it reads
+    (zero beyond the signal)."""
+    K = w.shape[2]
+    p = (K * d - d) // 2
+    T = x.shape[-1]
+    lo, hi = a - p, e - p + (K - 1) * d
+    xw = np.zeros(x.shape[:-1] + (hi - lo,), np.float64)
+    s0, s1 = max(lo, 0), min(hi, T)
+    xw[..., s0 - lo:s1 - lo] = x[..., s0:s1]
+    return O.conv1d(xw, w, b, dilation=d, pad=0)
+
+
+@pytest.mark.parametrize("d", [1, 5])
+def test_conv1d_full_size_workload2_sampled_windows(d):
+    """Workload 2's AMP conv at full size ([2, 512, 65536], 512 -> 512, k=3)
+    on windows at both ends and inside, every output channel."""
+    announce(f"conv1d workload2 full size d={d}")
+    x, _, _, t = W.workload2()
+    w = t["block.convs1.0.weight"]
+    b = t["block.convs1.0.bias"]
+    y = host(avae.conv1d(cuda(x), cuda(w), cuda(b), dilation=d))
+    T = x.shape[-1]
+    for a in (0, 12345, 40000, T - 300):
+        ref = _window_conv(x, w, b, d, a, a + 300)
+        assert rel_err(y[..., a:a + 300], ref) <= TOL, a
+
+
+CONVT_CASES = [
+    # B, Cin, Cout, Tin, K, s, pad (-1 = (K-s)/2)
+    (1, 8, 16, 10, 10, 5, -1),
+    (2, 24, 12, 33, 11, 5, -1),
+    (1, 16, 8, 40, 4, 2, -1),
+    (1, 70, 130, 17, 4, 2, -1),
+    (2, 6, 5, 9, 3, 1, -1),
+    (1, 4, 4, 6, 4, 2, 0),
+    (1, 12, 6, 300, 11, 5, 4),
+    (2, 96, 48, 1000, 4, 2, -1),
+]
+
+
+@pytest.mark.parametrize("B,Cin,Cout,Tin,K,s,pad", CONVT_CASES)
+def test_convtr1d_matches_oracle(B, Cin, Cout, Tin, K, s, pad):
+    announce(f"convtr1d B={B} Cin={Cin} Cout={Cout} Tin={Tin} K={K} s={s} pad={pad}")
+    x = W.normal(0, f"convt/{Cin}-{Cout}-{Tin}/x", [B, Cin, Tin])
+    w = W.normal(0, f"convt/{Cin}-{Cout}-{Tin}/w", [Cin, Cout, K], 0.0, 2.0 / (Cin * K))
+    b = W.normal(0, f"convt/{Cin}-{Cout}-{Tin}/b", [Cout], 0.0, 0.01)
+    y = host(avae.convtr1d(cuda(x), cuda(w), cuda(b), stride=s, pad=pad))
+    p = (K - s) // 2 if pad < 0 else pad
+    ref = O.convtr1d(x, w, b, stride=s, pad=p)
+    assert y.shape == ref.shape
+    assert rel_err(y, ref) <= TOL
+
+
+def test_convtr1d_full_size_workload3():
+    """Workload 3's upsampler at full size: [2, 1024, 8000] -> [2, 512, 40001]."""
+    announce("convtr1d workload3 full size")
+    x, t = W.workload3()
+    y = host(avae.convtr1d(cuda(x), cuda(t["ups.0.weight"]), cuda(t["ups.0.bias"]), stride=5))
+    ref = O.convtr1d(x, t["ups.0.weight"], t["ups.0.bias"], stride=5)
+    assert y.shape == (2, 512, 40001)
+    assert rel_err(y, ref) <= TOL

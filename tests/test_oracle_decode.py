@@ -106,3 +106,25 @@ def test_decode_optional_affine_and_dec_in():
     p2.latent_mean = p2.latent_std = p2.dec_in_w = p2.dec_in_b = None
     y2 = O.decode(lat, p2)
     assert rel_err(y, y2) < 1e-10  # only f64 summation order differs
+
+
+@pytest.mark.parametrize("spec", [W.scaled_spec(W.H3, 128, final="none"),
+                                  W.scaled_spec(W.LTX, 64, final="none")])
+def test_receptive_field_bound_holds(spec):
+    """The crop margin used by the full-size parity tests is a true bound:
+    perturbing one latent frame changes no output sample more than
+    decoder_reach_frames(spec) frames away."""
+    from tests.helpers import decoder_reach_frames
+    R = decoder_reach_frames(spec)
+    frames = 2 * R + 5
+    z = W.normal(4, "latent", [1, spec.c_in, frames])
+    p = decoder_params(spec, W.decoder_tensors(spec, 4))
+    y0 = O.decode(z, p)[0]
+    f = R + 2
+    z2 = z.copy()
+    z2[0, :, f] += 1.0
+    d = np.abs(O.decode(z2, p)[0] - y0)
+    hop = spec.hop
+    assert d[f * hop:(f + 1) * hop].max() > 0
+    assert d[:max(0, (f - R) * hop)].max(initial=0.0) == 0.0
+    assert d[(f + R + 1) * hop:].max(initial=0.0) == 0.0
