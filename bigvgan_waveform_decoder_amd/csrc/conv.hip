@@ -54,7 +54,7 @@ template <int BM, int BN, int WM, int WN, int KT>
 __global__ __launch_bounds__(WM * WN * 64) void conv1d_mfma_kernel(
     const float* __restrict__ x, float* y, const float* __restrict__ w, int Cin, int Cout,
     int T, int Tout, int Kr, int dil, int pad, int m_tiles, int n_tiles, int nblk,
-    int ws_stride, int xs_stride, ConvEpilogue ep) {
+    int ws_stride, int xs_stride, int flush, ConvEpilogue ep) {
     constexpr int NT = WM * WN * 64;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int MT = WTM / 16, NTL = WTN / 16;
@@ -76,17 +76,25 @@ __global__ __launch_bounds__(WM * WN * 64) void conv1d_mfma_kernel(
     const int wm0 = (wid / WN) * WTM, wn0 = (wid % WN) * WTN;
     const int l16 = lane & 15, g = lane >> 4;
 
-    f32x4 acc[MT][NTL];
+    // Blocked accumulation: the matrix cores accumulate `flush` K chunks into
+    // `part`, which is then added into `acc`.  This keeps every float32
+    // running sum short (a few dozen MFMA steps plus Cin/(8*flush) block
+    // additions instead of Cin*K/4 sequential MFMA steps).
+    f32x4 acc[MT][NTL], part[MT][NTL];
 #pragma unroll
     for (int a = 0; a < MT; ++a)
 #pragma unroll
-        for (int c = 0; c < NTL; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < NTL; ++c) {
+            acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+            part[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 
     const int xw = BN + (K - 1) * dil;
     const int wrow = kKC * K;
     const float* xb = x + (size_t)b * Cin * T;
 
-    for (int ic0 = 0; ic0 < Cin; ic0 += kKC) {
+    int chunk = 0;
+    for (int ic0 = 0; ic0 < Cin; ic0 += kKC, ++chunk) {
         for (int e = tid; e < BM * wrow; e += NT) {
             const int ol = e / wrow;
             const int f = e - ol * wrow;
@@ -120,9 +128,18 @@ __global__ __launch_bounds__(WM * WN * 64) void conv1d_mfma_kernel(
                 for (int a = 0; a < MT; ++a)
 #pragma unroll
                     for (int c = 0; c < NTL; ++c)
-                        acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a], bv[c], acc[a][c],
-                                                                         0, 0, 0);
+                        part[a][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a], bv[c],
+                                                                          part[a][c], 0, 0, 0);
             }
+        }
+        if ((chunk + 1) % flush == 0 || ic0 + kKC >= Cin) {
+#pragma unroll
+            for (int a = 0; a < MT; ++a)
+#pragma unroll
+                for (int c = 0; c < NTL; ++c) {
+                    acc[a][c] += part[a][c];
+                    part[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
         }
         __syncthreads();
     }
@@ -182,9 +199,11 @@ hipError_t run_conv1d(const float* x, float* y, const float* w, int B, int Cin, 
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
+    // about two dozen MFMA k-steps (2*K per chunk) between block additions
+    const int flush = K >= 12 ? 1 : (24 / (2 * K) > 0 ? 24 / (2 * K) : 1);
     hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(WM * WN * 64), lds, stream, x, y, w, Cin,
                        Cout, T, Tout, K, dil, pad, m_tiles, n_tiles, (int)nblk, ws_stride,
-                       xs_stride, ep);
+                       xs_stride, flush, ep);
     return hipGetLastError();
 }
 
@@ -207,7 +226,8 @@ template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(WM * WN * 64) void convtr1d_mfma_kernel(
     const float* __restrict__ x, float* __restrict__ y, const float* __restrict__ w,
     const float* __restrict__ bias, int Cin, int Cout, int Tin, int Tout, int K, int s, int pad,
-    int ntap_max, int m_tiles, int q_tiles, int nblk, int ws_stride, int xs_stride) {
+    int ntap_max, int m_tiles, int q_tiles, int nblk, int ws_stride, int xs_stride,
+    int flush) {
     constexpr int NT = WM * WN * 64;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int MT = WTM / 16, NTL = WTN / 16;
@@ -235,18 +255,22 @@ __global__ __launch_bounds__(WM * WN * 64) void convtr1d_mfma_kernel(
     const int wm0 = (wid / WN) * WTM, wn0 = (wid % WN) * WTN;
     const int l16 = lane & 15, g = lane >> 4;
 
-    f32x4 acc[MT][NTL];
+    f32x4 acc[MT][NTL], part[MT][NTL];  // blocked accumulation, as in Conv1d
 #pragma unroll
     for (int a = 0; a < MT; ++a)
 #pragma unroll
-        for (int c = 0; c < NTL; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < NTL; ++c) {
+            acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+            part[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 
     const int xw = BN + ntap_max - 1;
     const int wrow = kKC * ntap_max;
     const float* xb = x + (size_t)b * Cin * Tin;
     const int xbase = q0 - (ntap_max - 1);
 
-    for (int ic0 = 0; ic0 < Cin; ic0 += kKC) {
+    int chunk = 0;
+    for (int ic0 = 0; ic0 < Cin; ic0 += kKC, ++chunk) {
         for (int e = tid; e < BM * wrow; e += NT) {
             const int ol = e / wrow;
             const int f = e - ol * wrow;
@@ -280,9 +304,18 @@ __global__ __launch_bounds__(WM * WN * 64) void convtr1d_mfma_kernel(
                 for (int a = 0; a < MT; ++a)
 #pragma unroll
                     for (int c = 0; c < NTL; ++c)
-                        acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a], bv[c], acc[a][c],
-                                                                         0, 0, 0);
+                        part[a][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a], bv[c],
+                                                                          part[a][c], 0, 0, 0);
             }
+        }
+        if ((chunk + 1) % flush == 0 || ic0 + kKC >= Cin) {
+#pragma unroll
+            for (int a = 0; a < MT; ++a)
+#pragma unroll
+                for (int c = 0; c < NTL; ++c) {
+                    acc[a][c] += part[a][c];
+                    part[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
         }
         __syncthreads();
     }
@@ -407,9 +440,11 @@ hipError_t launch_convtr1d(const float* x, float* y, const float* w, const float
     const int xs_stride = xs_stride_for(BN + ntap_max - 1);
     const size_t lds = (size_t)(BM * ws_stride + kKC * xs_stride) * sizeof(float);
     if (lds > 64 * 1024) return hipErrorInvalidValue;
+    const int flush = 24 / (2 * ntap_max) > 0 ? 24 / (2 * ntap_max) : 1;
     hipLaunchKernelGGL((convtr1d_mfma_kernel<BM, BN, WM, WN>), dim3((unsigned)nblk),
                        dim3(WM * WN * 64), lds, stream, x, y, w, bias, Cin, Cout, Tin, Tout, K,
-                       stride, pad, ntap_max, m_tiles, q_tiles, (int)nblk, ws_stride, xs_stride);
+                       stride, pad, ntap_max, m_tiles, q_tiles, (int)nblk, ws_stride, xs_stride,
+                       flush);
     return hipGetLastError();
 }
 
