@@ -59,6 +59,70 @@ def cpu_baseline(spec, z, t, frames):
                       f"({samples} output samples) in {dt:.1f} s"}
 
 
+def roofline(kernels, steps):
+    """Roofline entry for the kernel with the largest share of decode time:
+    achieved = algorithmic flops (matrix kernels) or bytes (Activation1d)
+    per launch / average launch duration, against MI355X's published peak."""
+    name, k = max(kernels.items(), key=lambda kv: kv[1]["total_ms"])
+    avg_s = k["total_ms"] / 1e3 / k["launches"]
+    if name.startswith("act1d") or name.startswith("channel_affine"):
+        achieved = k["bytes"] / k["launches"] / avg_s / 1e9
+        peak, unit, bound = HBM_PEAK_GBPS, "GB/s", "hbm"
+    else:
+        achieved = k["flops"] / k["launches"] / avg_s / 1e12
+        peak, unit, bound = FP32_MFMA_PEAK_TFLOPS, "TFLOP/s", "mfma"
+    return {"kernel": name, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+            "frac": achieved / peak, "traffic": traffic_for(name),
+            "launches_per_step": k["launches"] / steps, "avg_launch_us": avg_s * 1e6,
+            "algorithmic_per_launch": (k["bytes"] if bound == "hbm" else k["flops"]) / k["launches"]}
+
+
+def traffic_for(name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        import hashlib
+        d = json.load(open(path))
+        e = d.get("kernels", {}).get(name)
+        if not e:
+            return None
+        src = os.path.join(ROOT, e["source"])
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if sha != e["source_sha256"]:
+            return None
+        return e["hbm_bytes_per_launch"]
+    except Exception:
+        return None
+
+
+def act1d_standalone(torch, avae, W, steps):
+    """avae_act1d alone on workload 2's shape [2, 512, 65536]: HBM GB/s."""
+    dev = torch.device("cuda:0")
+    x, la, lb, _ = W.workload2()
+    xd = torch.from_numpy(x).to(dev)
+    lad = torch.from_numpy(la).to(dev)
+    lbd = torch.from_numpy(lb).to(dev)
+    yd = torch.empty_like(xd)
+    for _ in range(3):
+        avae.act1d(xd, lad, lbd, out=yd)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    n = max(steps, 10)
+    e0.record(s)
+    for _ in range(n):
+        avae.act1d(xd, lad, lbd, out=yd)
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    gbps = 8.0 * x.size / (ms / 1e3) / 1e9
+    return {"shape": list(x.shape), "ms": ms, "GBps": gbps, "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -120,6 +184,25 @@ def main():
                                f"wave [{B},{L}] at {spec.sample_rate} Hz",
                    "global_batch": B, "frames": F, "parallelism": "none (1 GPU)"},
     }
+    # Profiled pass over the same number of steps: per-kernel event timing
+    # inside the library (the clean timed region above carries no events).
+    avae.profile_begin(args.steps * 400 + 64)
+    for _ in range(args.steps):
+        dec.decode(zd, out=out, workspace=ws)
+    kernels, phases = avae.profile_end()
+    res["profiled_ms_per_step"] = sum(k["total_ms"] for k in kernels.values()) / args.steps
+    res["phases_ms_per_step"] = {k: v / args.steps for k, v in phases.items()}
+    res["roofline"] = roofline(kernels, args.steps)
+    acts = [v for k, v in kernels.items() if k.startswith("act1d")]
+    if acts:
+        ab = sum(v["bytes"] for v in acts)
+        at = sum(v["total_ms"] for v in acts)
+        res["act1d_in_decode_GBps"] = ab / (at / 1e3) / 1e9
+    res["act1d_workload2"] = act1d_standalone(torch, avae, W, args.steps)
+    res["kernels"] = {k: {"launches_per_step": v["launches"] / args.steps,
+                          "ms_per_step": v["total_ms"] / args.steps,
+                          "avg_us": 1e3 * v["total_ms"] / max(v["launches"], 1)}
+                      for k, v in sorted(kernels.items(), key=lambda kv: -kv[1]["total_ms"])}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(spec, z, t, args.cpu_frames)
     print(json.dumps(res), flush=True)

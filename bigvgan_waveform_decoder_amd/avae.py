@@ -100,6 +100,19 @@ def lib() -> ctypes.CDLL:
     L.avae_bigvgan_decode.argtypes = [P, P, c_int, c_int, P, P, c_size_t, P]
     L.avae_bigvgan_decode_traced.restype = c_int
     L.avae_bigvgan_decode_traced.argtypes = [P, P, c_int, c_int, P, P, c_size_t, P, P]
+    L.avae_profile_begin.restype = c_int
+    L.avae_profile_begin.argtypes = [c_int]
+    L.avae_profile_end.restype = c_int
+    L.avae_profile_end.argtypes = []
+    L.avae_profile_count.restype = c_int
+    L.avae_profile_count.argtypes = []
+    L.avae_profile_entry.restype = c_int
+    L.avae_profile_entry.argtypes = [c_int, ctypes.c_char_p, c_int,
+                                     ctypes.POINTER(ctypes.c_longlong),
+                                     ctypes.POINTER(c_double), ctypes.POINTER(c_double),
+                                     ctypes.POINTER(c_double)]
+    L.avae_profile_phases.restype = c_int
+    L.avae_profile_phases.argtypes = [ctypes.POINTER(c_double)]
     _lib = L
     return L
 
@@ -154,6 +167,33 @@ def _host_taps(taps):
 
 def version() -> int:
     return lib().avae_version()
+
+
+PHASES = ("dec_in", "conv_pre", "upsamples", "resblocks", "act_post", "conv_post")
+
+
+def profile_begin(max_launches: int):
+    """Open a profiled region (avae_profile_begin)."""
+    _check(lib().avae_profile_begin(int(max_launches)))
+
+
+def profile_end():
+    """Close the region; returns (per-kernel dict, per-phase ms dict).
+    Per kernel: launches, total_ms, flops, bytes (algorithmic, summed)."""
+    L = lib()
+    _check(L.avae_profile_end())
+    out = {}
+    for i in range(L.avae_profile_count()):
+        name = ctypes.create_string_buffer(256)
+        n = ctypes.c_longlong()
+        ms, fl, by = c_double(), c_double(), c_double()
+        _check(L.avae_profile_entry(i, name, 256, ctypes.byref(n), ctypes.byref(ms),
+                                    ctypes.byref(fl), ctypes.byref(by)))
+        out[name.value.decode()] = {"launches": n.value, "total_ms": ms.value,
+                                    "flops": fl.value, "bytes": by.value}
+    ph = (c_double * 6)()
+    _check(L.avae_profile_phases(ph))
+    return out, dict(zip(PHASES, list(ph)))
 
 
 def kaiser_sinc(cutoff: float = 0.25, half_width: float = 0.3, taps: int = 12) -> np.ndarray:

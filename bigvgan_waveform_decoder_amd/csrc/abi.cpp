@@ -125,6 +125,7 @@ extern "C" int avae_act1d(const float* x, float* y, int B, int C, int T, const f
         return fail(AVAE_EINVAL, "avae_act1d: B, C, T must be >= 1 (got %d, %d, %d)", B, C, T);
     if (x == y) return fail(AVAE_EINVAL, "avae_act1d: x and y must not overlap");
     const ActTaps taps = make_taps(up_taps, down_taps);
+    avae::prof_set_phase(avae::kPhaseNone);
     AVAE_TRY(avae::launch_act1d(x, y, B, C, T, log_alpha, log_beta, taps, (hipStream_t)stream),
              "avae_act1d launch");
     return AVAE_OK;
@@ -144,6 +145,7 @@ extern "C" int avae_conv1d(const float* x, float* y, int B, int Cin, int Cout, i
     if (Tout < 1) return fail(AVAE_ESHAPE, "avae_conv1d: output length %d < 1", Tout);
     if (x == y) return fail(AVAE_EINVAL, "avae_conv1d: x and y must not overlap");
     ConvEpilogue ep{bias, residual, 1.0f, 0};
+    avae::prof_set_phase(avae::kPhaseNone);
     hipError_t e = avae::launch_conv1d(x, y, w, B, Cin, Cout, T, Tout, K, dilation, pad, ep,
                                        (hipStream_t)stream);
     if (e == hipErrorInvalidValue)
@@ -168,6 +170,7 @@ extern "C" int avae_convtr1d(const float* x, float* y, int B, int Cin, int Cout,
     if (Tout < 1 || Tout > 0x7fffffffLL)
         return fail(AVAE_ESHAPE, "avae_convtr1d: output length %lld out of range", Tout);
     if (x == y) return fail(AVAE_EINVAL, "avae_convtr1d: x and y must not overlap");
+    avae::prof_set_phase(avae::kPhaseNone);
     hipError_t e = avae::launch_convtr1d(x, y, w, bias, B, Cin, Cout, Tin, (int)Tout, K, stride,
                                          pad, (hipStream_t)stream);
     if (e == hipErrorInvalidValue)
@@ -213,6 +216,7 @@ extern "C" int avae_amp_block(const float* x, float* y, int B, int C, int T, int
     float* cur = (float*)ws;
     float* t1 = (float*)(ws + slot);
     float* t2 = (float*)(ws + 2 * slot);
+    avae::prof_set_phase(avae::kPhaseNone);
     return run_amp(x, y, B, C, T, K, n_dil, dil, w1, b1 ? b1 : kNull, w2, b2 ? b2 : kNull,
                    log_alpha, log_beta, out_scale, accumulate, cur, t1, t2,
                    make_taps(nullptr, nullptr), (hipStream_t)stream);
@@ -457,6 +461,7 @@ int decode_impl(const avae_decoder* dec, const float* latent, int B, int frames,
     const int F = frames;
     const float* h = latent;
     int cin = c.c_in;
+    avae::prof_set_phase(avae::kPhaseDecIn);
     if (c.has_latent_affine) {
         AVAE_TRY(avae::launch_channel_affine(h, X, w.latent_std, w.latent_mean, B, c.c_in, F, s),
                  "latent affine");
@@ -469,6 +474,7 @@ int decode_impl(const avae_decoder* dec, const float* latent, int B, int frames,
         h = cur;
         cin = c.dec_in_ch;
     }
+    avae::prof_set_phase(avae::kPhaseConvPre);
     {
         ConvEpilogue e{w.conv_pre_b, nullptr, 1.0f, 0};
         AVAE_TRY(avae::launch_conv1d(h, M, w.conv_pre_w, B, cin, c.ch[0], F, F, c.k_pre, 1,
@@ -484,9 +490,11 @@ int decode_impl(const avae_decoder* dec, const float* latent, int B, int frames,
         const int ci = c.ch[i], co = c.ch[i + 1];
         const int Ti = (int)T[i], To = (int)T[i + 1];
         const int pad = (c.up_k[i] - c.rates[i]) / 2;
+        avae::prof_set_phase(avae::kPhaseUpsamples);
         AVAE_TRY(avae::launch_convtr1d(M, X, w.up_w[i], w.up_b[i], B, ci, co, Ti, To, c.up_k[i],
                                        c.rates[i], pad, s),
                  "ConvTranspose1d");
+        avae::prof_set_phase(avae::kPhaseResblocks);
         for (int j = 0; j < c.n_kernels; ++j) {
             int rc = run_amp(X, M, B, co, To, c.rb_k[j], c.n_dil, c.rb_d[j], w.w1[i][j],
                              w.b1[i][j], w.w2[i][j], w.b2[i][j], w.act_la[i][j], w.act_lb[i][j],
@@ -500,12 +508,15 @@ int decode_impl(const avae_decoder* dec, const float* latent, int B, int frames,
     }
     const int cl = c.ch[c.n_stages];
     const int TL = (int)T[c.n_stages];
+    avae::prof_set_phase(avae::kPhaseActPost);
     AVAE_TRY(avae::launch_act1d(M, t1, B, cl, TL, w.post_la, w.post_lb, dec->taps, s),
              "act_post");
+    avae::prof_set_phase(avae::kPhaseConvPost);
     float* pre = (stage_out && stage_out[c.n_stages + 1]) ? stage_out[c.n_stages + 1] : nullptr;
     AVAE_TRY(avae::launch_conv_out1(t1, wave, pre, w.conv_post_w, w.conv_post_b, B, cl, TL,
                                     c.k_post, c.final_act, s),
              "conv_post");
+    avae::prof_set_phase(avae::kPhaseNone);
     return AVAE_OK;
 }
 

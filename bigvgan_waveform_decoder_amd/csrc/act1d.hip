@@ -21,18 +21,28 @@
 // rate sample and its SnakeBeta exactly once into two LDS phase arrays,
 // then runs the stride-2 FIR from LDS and writes the outputs once.  HBM
 // traffic is one read and one write of the row (8 bytes per element).
+// kTile = 8*256 - 6 so that the kTile + 6 phase positions fill every lane
+// of eight passes.
+//
+// SnakeBeta's sine: sin(alpha v) = sin(2 pi r) with r = v * (alpha / 2 pi);
+// r is reduced to [0, 1) by v_fract_f32 (exact) and v_sin_f32 evaluates
+// sin(2 pi r) directly in revolutions.  Against the reduced argument the
+// hardware sine is within ~1.3e-7 (measured on MI355X over [0, 1)); the only
+// other error is the float32 rounding of r itself, relative ~1e-7 of the
+// phase, the same order as rounding alpha*v before any float32 sine.
 #include "avae_internal.h"
 
 namespace avae {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTile = 1024;        // outputs per block
-constexpr int kQ = kTile + 6;      // phase positions q in [t0-3, t0+kTile+3)
+constexpr int kQ = 8 * kThreads;   // phase positions q in [t0-3, t0+kTile+3)
+constexpr int kTile = kQ - 6;      // outputs per block
 constexpr int kX = kTile + 12;     // input window [t0-6, t0+kTile+6)
 
-__device__ __forceinline__ float snake_beta(float v, float alpha, float inv_beta) {
-    const float s = sinf(alpha * v);
+__device__ __forceinline__ float snake_beta(float v, float alpha_rev, float inv_beta) {
+    const float r = v * alpha_rev;
+    const float s = __builtin_amdgcn_sinf(__builtin_amdgcn_fractf(r));
     return fmaf(s * s, inv_beta, v);
 }
 
@@ -48,16 +58,28 @@ __global__ __launch_bounds__(kThreads) void act1d_kernel(
     const int c = row % C;
     const int t0 = tile * kTile;
     const size_t base = (size_t)row * (size_t)T;
-    const float alpha = expf(log_alpha[c]);
+    const float alpha_rev = expf(log_alpha[c]) * 0.15915494309189535f;  // alpha / (2 pi)
     const float inv_beta = 1.0f / (expf(log_beta[c]) + 1e-9f);
 
     // Stage x[clamp(t0-6+i)]: the clamp is the upsampler's replicate padding.
-    for (int i = threadIdx.x; i < kX; i += kThreads) {
+    // All of a thread's loads are issued before the first LDS write, so they
+    // are in flight together.
+    constexpr int kLoads = (kX + kThreads - 1) / kThreads;
+    float xv[kLoads];
+#pragma unroll
+    for (int r = 0; r < kLoads; ++r) {
+        const int i = threadIdx.x + r * kThreads;
         const int t = min(max(t0 - 6 + i, 0), T - 1);
-        xs[i] = x[base + t];
+        xv[r] = (i < kX) ? x[base + t] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < kLoads; ++r) {
+        const int i = threadIdx.x + r * kThreads;
+        if (i < kX) xs[i] = xv[r];
     }
     __syncthreads();
 
+#pragma unroll
     for (int i = threadIdx.x; i < kQ; i += kThreads) {
         const int q = t0 - 3 + i;
         const int qc = min(max(q, 0), T - 1);
@@ -72,11 +94,12 @@ __global__ __launch_bounds__(kThreads) void act1d_kernel(
         // past 2T-1 replicate s[2T-1] (odd phase at q = T-1).
         if (q < 0) o = e;
         if (q > T - 1) e = o;
-        se[i] = snake_beta(e, alpha, inv_beta);
-        so[i] = snake_beta(o, alpha, inv_beta);
+        se[i] = snake_beta(e, alpha_rev, inv_beta);
+        so[i] = snake_beta(o, alpha_rev, inv_beta);
     }
     __syncthreads();
 
+#pragma unroll
     for (int i = threadIdx.x; i < kTile; i += kThreads) {
         const int t = t0 + i;
         if (t >= T) break;
@@ -98,9 +121,14 @@ hipError_t launch_act1d(const float* x, float* y, int B, int C, int T,
     const int tiles = (T + kTile - 1) / kTile;
     const long long blocks = (long long)B * C * tiles;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    prof_pre(stream);
     hipLaunchKernelGGL(act1d_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, x, y, C,
                        T, tiles, log_alpha, log_beta, taps);
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    // algorithmic: 24 FMA + 2 SnakeBeta (mul, fma) per output; one read, one write
+    const double n = (double)B * C * T;
+    prof_post(stream, "act1d_kernel", 52.0 * n, 8.0 * n);
+    return e;
 }
 
 }  // namespace avae

@@ -30,6 +30,15 @@ struct ConvEpilogue {
     int accumulate;
 };
 
+// Launch profiler (profile.cpp).  prof_pre/prof_post bracket one launch;
+// they do nothing unless a profiled region is open.  Phases: 0 dec_in,
+// 1 conv_pre, 2 upsamples, 3 resblocks, 4 act_post, 5 conv_post, -1 none.
+enum Phase { kPhaseNone = -1, kPhaseDecIn = 0, kPhaseConvPre = 1, kPhaseUpsamples = 2,
+             kPhaseResblocks = 3, kPhaseActPost = 4, kPhaseConvPost = 5 };
+void prof_set_phase(int phase);
+void prof_pre(hipStream_t s);
+void prof_post(hipStream_t s, const char* name, double flops, double bytes);
+
 // Host-side float64 Kaiser-sinc design (filter_design.cpp).
 void design_kaiser_sinc(double cutoff, double half_width, int taps, double* out);
 

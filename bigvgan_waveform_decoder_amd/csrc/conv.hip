@@ -24,6 +24,8 @@
 // and B[l/16][l%16]; the 4 accumulator registers of lane l hold
 // D[4*(l/16) + r][l%16], r = 0..3.  Rows map to output channels and columns
 // to time, so consecutive lanes store consecutive samples.
+#include <string>
+
 #include "avae_internal.h"
 
 namespace avae {
@@ -168,6 +170,190 @@ __global__ __launch_bounds__(WM * WN * 64) void conv1d_mfma_kernel(
     }
 }
 
+// Pipelined Conv1d for the decoder's shapes (K in {1,3,7,11}, dilation <= 5,
+// Cin a multiple of 4, 16-byte aligned weights).  Same GEMM and blocked
+// accumulation as conv1d_mfma_kernel, plus:
+//  - the next K chunk's weights (float4 loads) and input window are loaded
+//    into registers while the matrix cores work on the current chunk from
+//    LDS, so global latency hides behind the MFMA work of the same block;
+//  - the input window is staged row by row (32 lanes per channel row), no
+//    integer division per element;
+//  - `n_fastest` walks time tiles fastest within each XCD's range, so the
+//    blocks resident on an XCD share one weight slice in its L2.
+constexpr int kDilMax = 5;
+constexpr int kXLanes = 32;  // lanes per staged input row (8 rows x 32 = 256)
+
+constexpr int xs_stride_const(int xw) {
+    return ((xw + 63) / 64 * 64 + 16) - 64 >= xw ? ((xw + 63) / 64 * 64 + 16) - 64
+                                                   : (xw + 63) / 64 * 64 + 16;
+}
+
+template <int BM, int BN, int WM, int WN, int KT>
+__global__ __launch_bounds__(WM * WN * 64) void conv1d_pipe_kernel(
+    const float* __restrict__ x, float* y, const float* __restrict__ w, int Cin, int Cout,
+    int T, int Tout, int dil, int pad, int m_tiles, int n_tiles, int nblk, int flush,
+    int n_fastest, ConvEpilogue ep) {
+    constexpr int NT = WM * WN * 64;
+    static_assert(NT == 256, "256 threads: 8 staged rows x 32 lanes");
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int MT = WTM / 16, NTL = WTN / 16;
+    constexpr int WROW = kKC * KT;      // weight floats per row per chunk
+    constexpr int WS = WROW + 1;        // odd LDS row stride
+    constexpr int WV = WROW / 4;        // float4 per row per chunk
+    constexpr int WV_PT = (BM * WV + NT - 1) / NT;
+    constexpr int XW_MAX = BN + (KT - 1) * kDilMax;
+    constexpr int XS = xs_stride_const(XW_MAX);
+    constexpr int X_PT = (XW_MAX + kXLanes - 1) / kXLanes;
+    static_assert(WROW % 4 == 0, "float4 weight rows");
+
+    __shared__ float Ws[BM * WS];
+    __shared__ float Xs[kKC * XS];
+
+    const int lid = xcd_remap(blockIdx.x, nblk);
+    int mt_i, nt_i, b;
+    if (n_fastest) {
+        nt_i = lid % n_tiles;
+        const int rest = lid / n_tiles;
+        mt_i = rest % m_tiles;
+        b = rest / m_tiles;
+    } else {
+        mt_i = lid % m_tiles;
+        const int rest = lid / m_tiles;
+        nt_i = rest % n_tiles;
+        b = rest / n_tiles;
+    }
+    const int o0 = mt_i * BM, t0 = nt_i * BN;
+
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int wm0 = (wid / WN) * WTM, wn0 = (wid % WN) * WTN;
+    const int l16 = lane & 15, g = lane >> 4;
+    const int xrow = tid / kXLanes, xcol = tid % kXLanes;
+
+    f32x4 acc[MT][NTL], part[MT][NTL];
+#pragma unroll
+    for (int a = 0; a < MT; ++a)
+#pragma unroll
+        for (int c = 0; c < NTL; ++c) {
+            acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+            part[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+
+    const int xw = BN + (KT - 1) * dil;
+    const float* xb = x + (size_t)b * Cin * T;
+    const int nch = (Cin + kKC - 1) / kKC;
+
+    float4 wr[WV_PT];
+    float xr[X_PT];
+
+    auto gload = [&](int ic0) {
+        const int valid_f = (Cin - ic0 < kKC ? Cin - ic0 : kKC) * KT;  // multiple of 4
+#pragma unroll
+        for (int r = 0; r < WV_PT; ++r) {
+            const int e4 = tid + r * NT;
+            const int ol = e4 / WV;
+            const int f4 = e4 - ol * WV;
+            const int o = o0 + ol;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (e4 < BM * WV && o < Cout && 4 * f4 < valid_f)
+                v = *reinterpret_cast<const float4*>(w + ((size_t)o * Cin + ic0) * KT + 4 * f4);
+            wr[r] = v;
+        }
+        const int ic = ic0 + xrow;
+        const float* xrowp = xb + (size_t)ic * T;
+#pragma unroll
+        for (int r = 0; r < X_PT; ++r) {
+            const int u = xcol + r * kXLanes;
+            const int t = t0 - pad + u;
+            float v = 0.f;
+            if (u < xw && ic < Cin && t >= 0 && t < T) v = xrowp[t];
+            xr[r] = v;
+        }
+    };
+    auto lstore = [&]() {
+#pragma unroll
+        for (int r = 0; r < WV_PT; ++r) {
+            const int e4 = tid + r * NT;
+            if (e4 < BM * WV) {
+                const int ol = e4 / WV;
+                const int f4 = e4 - ol * WV;
+                float* d = Ws + ol * WS + 4 * f4;
+                d[0] = wr[r].x;
+                d[1] = wr[r].y;
+                d[2] = wr[r].z;
+                d[3] = wr[r].w;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < X_PT; ++r) {
+            const int u = xcol + r * kXLanes;
+            if (u < xw) Xs[xrow * XS + u] = xr[r];
+        }
+    };
+
+    gload(0);
+    lstore();
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+        if (c + 1 < nch) gload((c + 1) * kKC);
+#pragma unroll 1
+        for (int j = 0; j < KT; ++j) {
+#pragma unroll
+            for (int kk = 0; kk < kKC / 4; ++kk) {
+                float av[MT], bv[NTL];
+#pragma unroll
+                for (int a = 0; a < MT; ++a)
+                    av[a] = Ws[(wm0 + a * 16 + l16) * WS + (kk * 4 + g) * KT + j];
+#pragma unroll
+                for (int cc = 0; cc < NTL; ++cc)
+                    bv[cc] = Xs[(kk * 4 + g) * XS + wn0 + cc * 16 + l16 + j * dil];
+#pragma unroll
+                for (int a = 0; a < MT; ++a)
+#pragma unroll
+                    for (int cc = 0; cc < NTL; ++cc)
+                        part[a][cc] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a], bv[cc],
+                                                                           part[a][cc], 0, 0, 0);
+            }
+        }
+        if ((c + 1) % flush == 0 || c + 1 == nch) {
+#pragma unroll
+            for (int a = 0; a < MT; ++a)
+#pragma unroll
+                for (int cc = 0; cc < NTL; ++cc) {
+                    acc[a][cc] += part[a][cc];
+                    part[a][cc] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+        }
+        __syncthreads();
+        if (c + 1 < nch) {
+            lstore();
+            __syncthreads();
+        }
+    }
+
+    float* yb = y + (size_t)b * Cout * Tout;
+    const float* rb = ep.residual ? ep.residual + (size_t)b * Cout * Tout : nullptr;
+#pragma unroll
+    for (int a = 0; a < MT; ++a) {
+#pragma unroll
+        for (int cc = 0; cc < NTL; ++cc) {
+            const int t = t0 + wn0 + cc * 16 + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int o = o0 + wm0 + a * 16 + g * 4 + r;
+                if (o < Cout && t < Tout) {
+                    const size_t idx = (size_t)o * Tout + t;
+                    float v = acc[a][cc][r];
+                    if (ep.bias) v += ep.bias[o];
+                    if (rb) v += rb[idx];
+                    v *= ep.out_scale;
+                    if (ep.accumulate) v += yb[idx];
+                    yb[idx] = v;
+                }
+            }
+        }
+    }
+}
+
 struct ConvTile {
     int bm, bn;
 };
@@ -201,10 +387,56 @@ hipError_t run_conv1d(const float* x, float* y, const float* w, int B, int Cin, 
     }
     // about two dozen MFMA k-steps (2*K per chunk) between block additions
     const int flush = K >= 12 ? 1 : (24 / (2 * K) > 0 ? 24 / (2 * K) : 1);
+    static const std::string name = "conv1d_mfma_kernel<" + std::to_string(BM) + "," +
+                                    std::to_string(BN) + "," + std::to_string(WM) + "," +
+                                    std::to_string(WN) + "," + std::to_string(KT) + ">";
+    prof_pre(stream);
     hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(WM * WN * 64), lds, stream, x, y, w, Cin,
                        Cout, T, Tout, K, dil, pad, m_tiles, n_tiles, (int)nblk, ws_stride,
                        xs_stride, flush, ep);
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    const double out_n = (double)B * Cout * Tout;
+    prof_post(stream, name.c_str(), 2.0 * out_n * Cin * K,
+              4.0 * ((double)B * Cin * T + out_n * (1 + (ep.residual ? 1 : 0) + ep.accumulate) +
+                     (double)Cout * Cin * K));
+    return e;
+}
+
+template <int BM, int BN, int WM, int WN, int KT>
+hipError_t run_conv1d_pipe(const float* x, float* y, const float* w, int B, int Cin, int Cout,
+                           int T, int Tout, int dil, int pad, const ConvEpilogue& ep,
+                           hipStream_t stream) {
+    const int m_tiles = (Cout + BM - 1) / BM;
+    const int n_tiles = (Tout + BN - 1) / BN;
+    const long long nblk = (long long)m_tiles * n_tiles * B;
+    if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
+    const int flush = KT >= 12 ? 1 : (24 / (2 * KT) > 0 ? 24 / (2 * KT) : 1);
+    const int n_fastest = 1;
+    static const std::string name = "conv1d_pipe_kernel<" + std::to_string(BM) + "," +
+                                    std::to_string(BN) + "," + std::to_string(WM) + "," +
+                                    std::to_string(WN) + "," + std::to_string(KT) + ">";
+    prof_pre(stream);
+    hipLaunchKernelGGL((conv1d_pipe_kernel<BM, BN, WM, WN, KT>), dim3((unsigned)nblk),
+                       dim3(WM * WN * 64), 0, stream, x, y, w, Cin, Cout, T, Tout, dil, pad,
+                       m_tiles, n_tiles, (int)nblk, flush, n_fastest, ep);
+    const hipError_t e = hipGetLastError();
+    const double out_n = (double)B * Cout * Tout;
+    prof_post(stream, name.c_str(), 2.0 * out_n * Cin * KT,
+              4.0 * ((double)B * Cin * T + out_n * (1 + (ep.residual ? 1 : 0) + ep.accumulate) +
+                     (double)Cout * Cin * KT));
+    return e;
+}
+
+template <int BM, int BN, int WM, int WN>
+hipError_t dispatch_pipe(const float* x, float* y, const float* w, int B, int Cin, int Cout,
+                         int T, int Tout, int K, int dil, int pad, const ConvEpilogue& ep,
+                         hipStream_t stream) {
+    switch (K) {
+        case 1: return run_conv1d_pipe<BM, BN, WM, WN, 1>(x, y, w, B, Cin, Cout, T, Tout, dil, pad, ep, stream);
+        case 3: return run_conv1d_pipe<BM, BN, WM, WN, 3>(x, y, w, B, Cin, Cout, T, Tout, dil, pad, ep, stream);
+        case 7: return run_conv1d_pipe<BM, BN, WM, WN, 7>(x, y, w, B, Cin, Cout, T, Tout, dil, pad, ep, stream);
+        default: return run_conv1d_pipe<BM, BN, WM, WN, 11>(x, y, w, B, Cin, Cout, T, Tout, dil, pad, ep, stream);
+    }
 }
 
 template <int BM, int BN, int WM, int WN>
@@ -339,6 +571,194 @@ __global__ __launch_bounds__(WM * WN * 64) void convtr1d_mfma_kernel(
     }
 }
 
+// All-phase polyphase ConvTranspose1d for the decoder's (K, stride) pairs.
+// One block owns BMo = 16*WM output channels x NQ consecutive q (input-rate
+// positions) and computes every phase r of them: output t' = q*S + r - pad.
+// Each wave owns 16 channels and all S phases (one 16-row MFMA tile per
+// phase), so a phase with fewer taps (r + S*m >= K) simply issues fewer
+// MFMAs.  The input window x[q0-NTAP+1 .. q0+NQ) and the weight slice
+// w[ic][o0 .. o0+BMo)[0 .. K) (contiguous in the caller's [Cin, Cout, K]
+// layout) are staged once per K chunk for all phases, with the next chunk
+// prefetched into registers during the MFMA work, as in conv1d_pipe_kernel.
+constexpr int kKCT = 16;  // input channels per ConvT K chunk
+
+template <int WM, int WN, int NTL, int KT, int S>
+__global__ __launch_bounds__(WM * WN * 64) void convtr1d_poly_kernel(
+    const float* __restrict__ x, float* __restrict__ y, const float* __restrict__ w,
+    const float* __restrict__ bias, int Cin, int Cout, int Tin, int Tout, int pad, int qlo,
+    int m_tiles, int q_tiles, int nblk, int flush) {
+    constexpr int NT = WM * WN * 64;
+    static_assert(NT == 256, "256 threads");
+    constexpr int BMO = 16 * WM;              // output channels per block
+    constexpr int NQ = 16 * NTL * WN;         // q positions per block
+    constexpr int NTAP = (KT + S - 1) / S;    // taps of the longest phase
+    constexpr int WROW = BMO * KT;            // weight floats per input channel
+    constexpr int RS = (WROW % 32 <= 16) ? WROW - WROW % 32 + 16 : WROW - WROW % 32 + 48;
+    static_assert(WROW % 4 == 0, "float4 weight slices");
+    constexpr int WV = WROW / 4;              // float4 per input channel
+    constexpr int W_PT = (kKCT * WV + NT - 1) / NT;
+    constexpr int XW = NQ + NTAP - 1;
+    constexpr int XS = xs_stride_const(XW);
+    constexpr int XR = NT / kKCT;             // lanes per staged input row
+    constexpr int X_PT = (XW + XR - 1) / XR;
+
+    __shared__ float Ws[kKCT * RS];
+    __shared__ float Xs[kKCT * XS];
+
+    const int lid = xcd_remap(blockIdx.x, nblk);
+    const int qt = lid % q_tiles;
+    const int rest = lid / q_tiles;
+    const int mt_i = rest % m_tiles;
+    const int b = rest / m_tiles;
+    const int o0 = mt_i * BMO;
+    const int q0 = qlo + qt * NQ;
+
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int wm = wid / WN, wn0 = (wid % WN) * (16 * NTL);
+    const int l16 = lane & 15, g = lane >> 4;
+    const int xrow = tid / XR, xcol = tid % XR;
+
+    f32x4 acc[S][NTL], part[S][NTL];
+#pragma unroll
+    for (int r = 0; r < S; ++r)
+#pragma unroll
+        for (int c = 0; c < NTL; ++c) {
+            acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+            part[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+
+    const float* xb = x + (size_t)b * Cin * Tin;
+    const int xbase = q0 - (NTAP - 1);
+    const int nch = (Cin + kKCT - 1) / kKCT;
+    float4 wr[W_PT];
+    float xr[X_PT];
+
+    auto gload = [&](int ic0) {
+#pragma unroll
+        for (int k = 0; k < W_PT; ++k) {
+            const int e = tid + k * NT;
+            const int i = e / WV;
+            const int f = 4 * (e - i * WV);  // (o - o0) * KT + j, multiple of 4
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (e < kKCT * WV && ic0 + i < Cin && o0 * KT + f < Cout * KT)
+                v = *reinterpret_cast<const float4*>(w + ((size_t)(ic0 + i) * Cout + o0) * KT + f);
+            wr[k] = v;
+        }
+        const int ic = ic0 + xrow;
+#pragma unroll
+        for (int k = 0; k < X_PT; ++k) {
+            const int u = xcol + k * XR;
+            const int t = xbase + u;
+            float v = 0.f;
+            if (u < XW && ic < Cin && t >= 0 && t < Tin) v = xb[(size_t)ic * Tin + t];
+            xr[k] = v;
+        }
+    };
+    auto lstore = [&]() {
+#pragma unroll
+        for (int k = 0; k < W_PT; ++k) {
+            const int e = tid + k * NT;
+            if (e < kKCT * WV) {
+                const int i = e / WV;
+                *reinterpret_cast<float4*>(Ws + i * RS + 4 * (e - i * WV)) = wr[k];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < X_PT; ++k) {
+            const int u = xcol + k * XR;
+            if (u < XW) Xs[xrow * XS + u] = xr[k];
+        }
+    };
+
+    gload(0);
+    lstore();
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+        if (c + 1 < nch) gload((c + 1) * kKCT);
+#pragma unroll
+        for (int m = 0; m < NTAP; ++m) {
+#pragma unroll 1
+            for (int kk = 0; kk < kKCT / 4; ++kk) {
+                float bv[NTL];
+#pragma unroll
+                for (int cc = 0; cc < NTL; ++cc)
+                    bv[cc] = Xs[(kk * 4 + g) * XS + wn0 + cc * 16 + l16 + (NTAP - 1 - m)];
+#pragma unroll
+                for (int r = 0; r < S; ++r) {
+                    if (r + S * m < KT) {
+                        const float av =
+                            Ws[(kk * 4 + g) * RS + (wm * 16 + l16) * KT + r + S * m];
+#pragma unroll
+                        for (int cc = 0; cc < NTL; ++cc)
+                            part[r][cc] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                av, bv[cc], part[r][cc], 0, 0, 0);
+                    }
+                }
+            }
+        }
+        if ((c + 1) % flush == 0 || c + 1 == nch) {
+#pragma unroll
+            for (int r = 0; r < S; ++r)
+#pragma unroll
+                for (int cc = 0; cc < NTL; ++cc) {
+                    acc[r][cc] += part[r][cc];
+                    part[r][cc] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+        }
+        __syncthreads();
+        if (c + 1 < nch) {
+            lstore();
+            __syncthreads();
+        }
+    }
+
+    float* yb = y + (size_t)b * Cout * Tout;
+#pragma unroll
+    for (int r = 0; r < S; ++r) {
+#pragma unroll
+        for (int cc = 0; cc < NTL; ++cc) {
+            const int q = q0 + wn0 + cc * 16 + l16;
+            const int t = q * S + r - pad;
+#pragma unroll
+            for (int ri = 0; ri < 4; ++ri) {
+                const int o = o0 + wm * 16 + g * 4 + ri;
+                if (o < Cout && t >= 0 && t < Tout) {
+                    float v = acc[r][cc][ri];
+                    if (bias) v += bias[o];
+                    yb[(size_t)o * Tout + t] = v;
+                }
+            }
+        }
+    }
+}
+
+template <int WM, int WN, int NTL, int KT, int S>
+hipError_t run_convtr1d_poly(const float* x, float* y, const float* w, const float* bias, int B,
+                             int Cin, int Cout, int Tin, int Tout, int pad, hipStream_t stream) {
+    constexpr int BMO = 16 * WM;
+    constexpr int NQ = 16 * NTL * WN;
+    // q = floor((t' + pad) / S) over all outputs t' in [0, Tout)
+    const int qlo = pad / S;
+    const int qhi = (Tout - 1 + pad) / S;
+    const int m_tiles = (Cout + BMO - 1) / BMO;
+    const int q_tiles = (qhi - qlo + 1 + NQ - 1) / NQ;
+    const long long nblk = (long long)m_tiles * q_tiles * B;
+    if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
+    constexpr int NTAP = (KT + S - 1) / S;
+    const int flush = 24 / (NTAP * (kKCT / 4)) > 0 ? 24 / (NTAP * (kKCT / 4)) : 1;
+    static const std::string name = "convtr1d_poly_kernel<" + std::to_string(WM) + "," +
+                                    std::to_string(WN) + "," + std::to_string(NTL) + "," +
+                                    std::to_string(KT) + "," + std::to_string(S) + ">";
+    prof_pre(stream);
+    hipLaunchKernelGGL((convtr1d_poly_kernel<WM, WN, NTL, KT, S>), dim3((unsigned)nblk),
+                       dim3(WM * WN * 64), 0, stream, x, y, w, bias, Cin, Cout, Tin, Tout, pad,
+                       qlo, m_tiles, q_tiles, (int)nblk, flush);
+    const hipError_t e = hipGetLastError();
+    prof_post(stream, name.c_str(), 2.0 * B * Cin * Cout * (double)KT * Tin,
+              4.0 * ((double)B * Cin * Tin + (double)B * Cout * Tout + (double)Cin * Cout * KT));
+    return e;
+}
+
 // ------------------------------------------------------------------ conv_post (Cout = 1)
 
 constexpr int kOutThreads = 256;
@@ -400,6 +820,23 @@ __global__ void channel_affine_kernel(const float* __restrict__ x, float* __rest
 hipError_t launch_conv1d(const float* x, float* y, const float* w, int B, int Cin, int Cout,
                          int T, int Tout, int K, int dilation, int pad, const ConvEpilogue& ep,
                          hipStream_t stream) {
+    const bool pipe_ok = (K == 1 || K == 3 || K == 7 || K == 11) && dilation <= kDilMax &&
+                         Cin % 4 == 0 && ((uintptr_t)w & 15) == 0;
+    if (pipe_ok) {
+        auto blocks = [&](int bm, int bn) {
+            return (long long)((Cout + bm - 1) / bm) * ((Tout + bn - 1) / bn) * B;
+        };
+        if (Cout > 32) {
+            // 64 x 128 tiles; 64 x 64 when that would leave fewer than ~2.5
+            // blocks per CU on 256 CUs.
+            if (blocks(64, 128) >= 640)
+                return dispatch_pipe<64, 128, 2, 2>(x, y, w, B, Cin, Cout, T, Tout, K, dilation, pad, ep, stream);
+            return dispatch_pipe<64, 64, 2, 2>(x, y, w, B, Cin, Cout, T, Tout, K, dilation, pad, ep, stream);
+        }
+        if (Cout > 16)
+            return dispatch_pipe<32, 256, 1, 4>(x, y, w, B, Cin, Cout, T, Tout, K, dilation, pad, ep, stream);
+        return dispatch_pipe<16, 256, 1, 4>(x, y, w, B, Cin, Cout, T, Tout, K, dilation, pad, ep, stream);
+    }
     // Tile choice: the largest Cout tile that wastes little of the matrix
     // cores, shrunk while the grid would leave the 256 CUs under-filled.
     auto blocks = [&](int bm, int bn) {
@@ -423,6 +860,14 @@ hipError_t launch_conv1d(const float* x, float* y, const float* w, int B, int Ci
 hipError_t launch_convtr1d(const float* x, float* y, const float* w, const float* bias, int B,
                            int Cin, int Cout, int Tin, int Tout, int K, int stride, int pad,
                            hipStream_t stream) {
+    // float4 weight slices need Cout*K % 4 == 0 and a 16-byte aligned base
+    const bool vec = ((long long)Cout * K) % 4 == 0 && ((uintptr_t)w & 15) == 0;
+    if (vec && stride == 5 && K == 11)
+        return run_convtr1d_poly<2, 2, 2, 11, 5>(x, y, w, bias, B, Cin, Cout, Tin, Tout, pad, stream);
+    if (vec && stride == 5 && K == 10)
+        return run_convtr1d_poly<2, 2, 2, 10, 5>(x, y, w, bias, B, Cin, Cout, Tin, Tout, pad, stream);
+    if (vec && stride == 2 && K == 4)
+        return run_convtr1d_poly<4, 1, 4, 4, 2>(x, y, w, bias, B, Cin, Cout, Tin, Tout, pad, stream);
     constexpr int BM = 64, BN = 64, WM = 2, WN = 2;
     const int ntap_max = (K + stride - 1) / stride;
     auto fdiv = [](int a, int b) { int q = a / b; if ((a % b != 0) && ((a < 0) != (b < 0))) --q; return q; };
@@ -441,11 +886,15 @@ hipError_t launch_convtr1d(const float* x, float* y, const float* w, const float
     const size_t lds = (size_t)(BM * ws_stride + kKC * xs_stride) * sizeof(float);
     if (lds > 64 * 1024) return hipErrorInvalidValue;
     const int flush = 24 / (2 * ntap_max) > 0 ? 24 / (2 * ntap_max) : 1;
+    prof_pre(stream);
     hipLaunchKernelGGL((convtr1d_mfma_kernel<BM, BN, WM, WN>), dim3((unsigned)nblk),
                        dim3(WM * WN * 64), lds, stream, x, y, w, bias, Cin, Cout, Tin, Tout, K,
                        stride, pad, ntap_max, m_tiles, q_tiles, (int)nblk, ws_stride, xs_stride,
                        flush);
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    prof_post(stream, "convtr1d_mfma_kernel<64,64,2,2>", 2.0 * B * Cin * Cout * (double)K * Tin,
+              4.0 * ((double)B * Cin * Tin + (double)B * Cout * Tout + (double)Cin * Cout * K));
+    return e;
 }
 
 hipError_t launch_conv_out1(const float* x, float* y, float* pre_final, const float* w,
@@ -455,18 +904,25 @@ hipError_t launch_conv_out1(const float* x, float* y, float* pre_final, const fl
     const long long nblk = (long long)tiles * B;
     const size_t lds = (size_t)(Cin * K + kOutChunk * (kOutThreads + K - 1)) * sizeof(float);
     if (nblk > 0x7fffffffLL || lds > 64 * 1024) return hipErrorInvalidValue;
+    prof_pre(stream);
     hipLaunchKernelGGL(conv_out1_kernel, dim3((unsigned)nblk), dim3(kOutThreads), lds, stream, x,
                        y, pre_final, w, bias, Cin, T, K, final_act, tiles);
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    prof_post(stream, "conv_out1_kernel", 2.0 * B * Cin * (double)K * T,
+              4.0 * ((double)B * Cin * T + (double)B * T * (pre_final ? 2 : 1) + (double)Cin * K));
+    return e;
 }
 
 hipError_t launch_channel_affine(const float* x, float* y, const float* scale, const float* shift,
                                  int B, int C, int T, hipStream_t stream) {
     const size_t n = (size_t)B * C * T;
     const unsigned blocks = (unsigned)((n + 255) / 256 > 65536 ? 65536 : (n + 255) / 256);
+    prof_pre(stream);
     hipLaunchKernelGGL(channel_affine_kernel, dim3(blocks), dim3(256), 0, stream, x, y, scale,
                        shift, C, T, n);
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    prof_post(stream, "channel_affine_kernel", 2.0 * n, 8.0 * n);
+    return e;
 }
 
 }  // namespace avae

@@ -231,6 +231,32 @@ int avae_bigvgan_decode_traced(const avae_decoder* dec, const float* latent, int
                                float* wave, void* workspace, size_t ws_bytes,
                                float* const* stage_out, void* stream);
 
+/*
+ * Launch profiler, the device-side counterpart of the audio decoder's own
+ * phase report ([H3] AVAE_TIME / avae_time_report, phases dec_in, conv_pre,
+ * upsamples, resblocks, act_post, conv_post).  Between avae_profile_begin and
+ * avae_profile_end every kernel launched by this library (any entry point,
+ * any stream) is bracketed by two hipEvents and tagged with its kernel name,
+ * its decode phase and its algorithmic flops and bytes.  The events are
+ * created by avae_profile_begin (room for max_launches launches), so compute
+ * calls inside the region still allocate nothing.  Process-wide: one region
+ * at a time, driven from one host thread.
+ *   avae_profile_begin: EINVAL (max_launches < 1), EHIP.
+ *   avae_profile_end:   synchronises on the last event and aggregates per
+ *                       kernel name; ESHAPE if launches were dropped because
+ *                       the region overflowed max_launches.
+ *   avae_profile_entry: entry i < avae_profile_count(): name (copied into
+ *                       `name`, NUL-terminated), launches, summed event time
+ *                       in ms, summed algorithmic flops and bytes.
+ *   avae_profile_phases: host array of 6 doubles, ms per decode phase.
+ */
+int avae_profile_begin(int max_launches);
+int avae_profile_end(void);
+int avae_profile_count(void);
+int avae_profile_entry(int i, char* name, int name_len, long long* launches, double* total_ms,
+                       double* flops, double* bytes);
+int avae_profile_phases(double* ms6);
+
 #ifdef __cplusplus
 }
 #endif
