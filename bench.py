@@ -32,8 +32,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=4, choices=(4, 5))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-frames", type=int, default=24,
+    ap.add_argument("--cpu-frames", type=int, default=120,
                     help="latent frames of the oracle's bounded CPU sample (one pass)")
+    ap.add_argument("--pmc-calibration", action="store_true",
+                    help="also run one plain 256 MiB device-to-device copy, whose "
+                         "FETCH_SIZE / WRITE_SIZE counters calibrate the traffic figures")
     return ap.parse_args()
 
 
@@ -203,6 +206,12 @@ def main():
                           "ms_per_step": v["total_ms"] / args.steps,
                           "avg_us": 1e3 * v["total_ms"] / max(v["launches"], 1)}
                       for k, v in sorted(kernels.items(), key=lambda kv: -kv[1]["total_ms"])}
+    if args.pmc_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["pmc_calibration_copy_bytes"] = src.numel() * 4
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(spec, z, t, args.cpu_frames)
     print(json.dumps(res), flush=True)
