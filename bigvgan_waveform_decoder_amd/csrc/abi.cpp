@@ -12,7 +12,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/avae.h"
+#include "avae.h"
 #include "avae_internal.h"
 
 using avae::ActTaps;

@@ -16,13 +16,11 @@
 // signal, not on an extended upsample).  Each output therefore reads
 // x[t-5 .. t+5].
 //
-// One block owns one (b, c) row segment of kTile outputs: it stages the
-// input window in LDS (coalesced loads along time), computes each doubled-
-// rate sample and its SnakeBeta exactly once into two LDS phase arrays,
+// One block owns one (b, c) row segment of kTile = 2048 outputs: it stages
+// the input window in LDS, computes each doubled-rate sample and its
+// SnakeBeta exactly once into two LDS phase arrays (even and odd positions),
 // then runs the stride-2 FIR from LDS and writes the outputs once.  HBM
 // traffic is one read and one write of the row (8 bytes per element).
-// kTile = 8*256 - 6 so that the kTile + 6 phase positions fill every lane
-// of eight passes.
 //
 // SnakeBeta's sine: sin(alpha v) = sin(2 pi r) with r = v * (alpha / 2 pi);
 // r is reduced to [0, 1) by v_fract_f32 (exact) and v_sin_f32 evaluates
@@ -36,9 +34,9 @@ namespace avae {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kQ = 8 * kThreads;   // phase positions q in [t0-3, t0+kTile+3)
-constexpr int kTile = kQ - 6;      // outputs per block
-constexpr int kX = kTile + 12;     // input window [t0-6, t0+kTile+6)
+constexpr int kTile = 8 * kThreads;        // outputs per block
+constexpr int kX = kTile + 16;             // staged input: x[t0-8 .. t0+kTile+8)
+constexpr int kQ = kTile + 16;             // phase arrays: index j <-> q = t0 - 8 + j
 
 __device__ __forceinline__ float snake_beta(float v, float alpha_rev, float inv_beta) {
     const float r = v * alpha_rev;
@@ -46,12 +44,164 @@ __device__ __forceinline__ float snake_beta(float v, float alpha_rev, float inv_
     return fmaf(s * s, inv_beta, v);
 }
 
+// The doubled-rate pair (2q, 2q+1) from x[q-3 .. q+3], xq pointing at x[q].
+__device__ __forceinline__ void up_pair(const float* xq, const ActTaps& taps, float& e, float& o) {
+    e = 0.f;
+    o = 0.f;
+#pragma unroll
+    for (int k = 0; k < 6; ++k) {
+        e = fmaf(taps.up2[2 * k + 1], xq[2 - k], e);
+        o = fmaf(taps.up2[2 * k], xq[3 - k], o);
+    }
+}
+
+// Interior tile: x[t0-8 .. t0+kTile+8) lies inside the row, every output
+// exists, the row start is 16-byte aligned (T % 4 == 0).  Each thread owns
+// two runs of 4 consecutive outputs, t0 + 4*tid + 1024*r + (0..3), so every
+// global and LDS access is a float4 and the 64 lanes of a wave touch 1 KiB
+// contiguously (no LDS bank conflicts).  A 12-value register window of x
+// feeds a run's 4 polyphase pairs; two 12-value windows of the phase
+// arrays feed its 4 stride-2 FIR outputs.
+__device__ __forceinline__ void load12(const float* p, float* w) {
+    const float4* v = reinterpret_cast<const float4*>(p);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const float4 f = v[i];
+        w[4 * i] = f.x;
+        w[4 * i + 1] = f.y;
+        w[4 * i + 2] = f.z;
+        w[4 * i + 3] = f.w;
+    }
+}
+
+__device__ __forceinline__ void act1d_tile_interior(const float* __restrict__ xrow,
+                                                    float* __restrict__ yrow, int t0,
+                                                    float alpha_rev, float inv_beta,
+                                                    const ActTaps& taps, float* xs, float* se,
+                                                    float* so) {
+    constexpr int kHalf = kTile / 2;
+    const int tid = threadIdx.x;
+    {
+        const float4* src = reinterpret_cast<const float4*>(xrow + t0 - 8);
+        float4* dst = reinterpret_cast<float4*>(xs);
+        const float4 a = src[tid];
+        const float4 b = src[tid + kThreads];
+        float4 c = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (tid < 4) c = src[tid + 2 * kThreads];
+        dst[tid] = a;
+        dst[tid + kThreads] = b;
+        if (tid < 4) dst[tid + 2 * kThreads] = c;
+    }
+    __syncthreads();
+
+    // Phase 1: q = t0 + 4 tid + kHalf r + k  <->  j = 8 + 4 tid + kHalf r + k.
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int j0 = 8 + 4 * tid + kHalf * r;
+        float xw[12];  // xw[u] = xs[j0 - 4 + u] = x[q0 - 4 + u]
+        load12(xs + j0 - 4, xw);
+        float ev[4], ov[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            float e, o;
+            up_pair(xw + k + 4, taps, e, o);
+            ev[k] = snake_beta(e, alpha_rev, inv_beta);
+            ov[k] = snake_beta(o, alpha_rev, inv_beta);
+        }
+        *reinterpret_cast<float4*>(se + j0) = make_float4(ev[0], ev[1], ev[2], ev[3]);
+        *reinterpret_cast<float4*>(so + j0) = make_float4(ov[0], ov[1], ov[2], ov[3]);
+    }
+    // halo: q = t0-3 .. t0-1 (j = 5, 6, 7) and q = t0+kTile .. +2 (j = kTile+8 .. +10)
+    if (tid < 6) {
+        const int j = tid < 3 ? 5 + tid : kTile + 5 + tid;
+        float e, o;
+        up_pair(xs + j, taps, e, o);
+        se[j] = snake_beta(e, alpha_rev, inv_beta);
+        so[j] = snake_beta(o, alpha_rev, inv_beta);
+    }
+    __syncthreads();
+
+    // Phase 2: y[t] = sum_m down[2m] so[t+m-3] + down[2m+1] se[t+m-2] for
+    // t = t0 + 4 tid + kHalf r + k; so index = j0 + k + m - 3, se index + 1.
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int j0 = 8 + 4 * tid + kHalf * r;
+        float sw[12], ew[12];  // sw[u] = so[j0 - 4 + u], ew[u] = se[j0 - 4 + u]
+        load12(so + j0 - 4, sw);
+        load12(se + j0 - 4, ew);
+        float out[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            float acc = 0.f;
+#pragma unroll
+            for (int m = 0; m < 6; ++m) {
+                acc = fmaf(taps.down[2 * m], sw[k + m + 1], acc);
+                acc = fmaf(taps.down[2 * m + 1], ew[k + m + 2], acc);
+            }
+            out[k] = acc;
+        }
+        *reinterpret_cast<float4*>(yrow + t0 + 4 * tid + kHalf * r) =
+            make_float4(out[0], out[1], out[2], out[3]);
+    }
+}
+
+// Edge tile (first or last tile of a row, a row shorter than a tile, or
+// T % 4 != 0): same arrays and index conventions, scalar and strided over
+// the block, every index clamped to implement the replicate padding.
+__device__ __forceinline__ void act1d_tile_edge(const float* __restrict__ xrow,
+                                                float* __restrict__ yrow, int T, int t0,
+                                                float alpha_rev, float inv_beta,
+                                                const ActTaps& taps, float* xs, float* se,
+                                                float* so) {
+    // All of a thread's loads are issued before its first LDS write.
+    constexpr int kLoads = (kX + kThreads - 1) / kThreads;
+    float xv[kLoads];
+#pragma unroll
+    for (int r = 0; r < kLoads; ++r) {
+        const int i = threadIdx.x + r * kThreads;
+        xv[r] = (i < kX) ? xrow[min(max(t0 - 8 + i, 0), T - 1)] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < kLoads; ++r) {
+        const int i = threadIdx.x + r * kThreads;
+        if (i < kX) xs[i] = xv[r];
+    }
+    __syncthreads();
+    // q = t0 - 8 + j for j in [5, kTile + 11): q in [t0-3, t0+kTile+3)
+#pragma unroll 3
+    for (int j = 5 + threadIdx.x; j < kTile + 11; j += kThreads) {
+        const int q = t0 - 8 + j;
+        const int qc = min(max(q, 0), T - 1);
+        float e, o;
+        up_pair(xs + (qc - (t0 - 8)), taps, e, o);
+        // Positions before 0 replicate s[0] (even phase at q = 0); positions
+        // past 2T-1 replicate s[2T-1] (odd phase at q = T-1).
+        if (q < 0) o = e;
+        if (q > T - 1) e = o;
+        se[j] = snake_beta(e, alpha_rev, inv_beta);
+        so[j] = snake_beta(o, alpha_rev, inv_beta);
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int i = threadIdx.x; i < kTile; i += kThreads) {
+        const int t = t0 + i;
+        if (t >= T) break;
+        float acc = 0.f;
+#pragma unroll
+        for (int m = 0; m < 6; ++m) {
+            acc = fmaf(taps.down[2 * m], so[i + m + 5], acc);
+            acc = fmaf(taps.down[2 * m + 1], se[i + m + 6], acc);
+        }
+        yrow[t] = acc;
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void act1d_kernel(
-    const float* __restrict__ x, float* __restrict__ y, int C, int T, int tiles,
+    const float* __restrict__ x, float* __restrict__ y, int C, int T, int tiles, int vec_ok,
     const float* __restrict__ log_alpha, const float* __restrict__ log_beta, ActTaps taps) {
-    __shared__ float xs[kX];
-    __shared__ float se[kQ];  // s at even doubled-rate positions 2q
-    __shared__ float so[kQ];  // s at odd doubled-rate positions 2q+1
+    __shared__ __align__(16) float xs[kX];
+    __shared__ __align__(16) float se[kQ];  // s at even doubled-rate positions 2q
+    __shared__ __align__(16) float so[kQ];  // s at odd doubled-rate positions 2q+1
 
     const int row = blockIdx.x / tiles;  // b*C + c
     const int tile = blockIdx.x - row * tiles;
@@ -60,57 +210,10 @@ __global__ __launch_bounds__(kThreads) void act1d_kernel(
     const size_t base = (size_t)row * (size_t)T;
     const float alpha_rev = expf(log_alpha[c]) * 0.15915494309189535f;  // alpha / (2 pi)
     const float inv_beta = 1.0f / (expf(log_beta[c]) + 1e-9f);
-
-    // Stage x[clamp(t0-6+i)]: the clamp is the upsampler's replicate padding.
-    // All of a thread's loads are issued before the first LDS write, so they
-    // are in flight together.
-    constexpr int kLoads = (kX + kThreads - 1) / kThreads;
-    float xv[kLoads];
-#pragma unroll
-    for (int r = 0; r < kLoads; ++r) {
-        const int i = threadIdx.x + r * kThreads;
-        const int t = min(max(t0 - 6 + i, 0), T - 1);
-        xv[r] = (i < kX) ? x[base + t] : 0.f;
-    }
-#pragma unroll
-    for (int r = 0; r < kLoads; ++r) {
-        const int i = threadIdx.x + r * kThreads;
-        if (i < kX) xs[i] = xv[r];
-    }
-    __syncthreads();
-
-#pragma unroll
-    for (int i = threadIdx.x; i < kQ; i += kThreads) {
-        const int q = t0 - 3 + i;
-        const int qc = min(max(q, 0), T - 1);
-        const int p = qc - (t0 - 6);  // xs index of x[qc]
-        float e = 0.f, o = 0.f;
-#pragma unroll
-        for (int k = 0; k < 6; ++k) {
-            e = fmaf(taps.up2[2 * k + 1], xs[p + 2 - k], e);
-            o = fmaf(taps.up2[2 * k], xs[p + 3 - k], o);
-        }
-        // Positions before 0 replicate s[0] (even phase at q = 0); positions
-        // past 2T-1 replicate s[2T-1] (odd phase at q = T-1).
-        if (q < 0) o = e;
-        if (q > T - 1) e = o;
-        se[i] = snake_beta(e, alpha_rev, inv_beta);
-        so[i] = snake_beta(o, alpha_rev, inv_beta);
-    }
-    __syncthreads();
-
-#pragma unroll
-    for (int i = threadIdx.x; i < kTile; i += kThreads) {
-        const int t = t0 + i;
-        if (t >= T) break;
-        float acc = 0.f;
-#pragma unroll
-        for (int k = 0; k < 6; ++k) {
-            acc = fmaf(taps.down[2 * k], so[i + k], acc);
-            acc = fmaf(taps.down[2 * k + 1], se[i + k + 1], acc);
-        }
-        y[base + t] = acc;
-    }
+    if (vec_ok && t0 >= 8 && t0 + kTile + 8 <= T)
+        act1d_tile_interior(x + base, y + base, t0, alpha_rev, inv_beta, taps, xs, se, so);
+    else
+        act1d_tile_edge(x + base, y + base, T, t0, alpha_rev, inv_beta, taps, xs, se, so);
 }
 
 }  // namespace
@@ -122,8 +225,10 @@ hipError_t launch_act1d(const float* x, float* y, int B, int C, int T,
     const long long blocks = (long long)B * C * tiles;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     prof_pre(stream);
+    // float4 rows need T % 4 == 0 and 16-byte aligned tensors
+    const int vec_ok = (T % 4 == 0) && (((uintptr_t)x | (uintptr_t)y) & 15) == 0;
     hipLaunchKernelGGL(act1d_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, x, y, C,
-                       T, tiles, log_alpha, log_beta, taps);
+                       T, tiles, vec_ok, log_alpha, log_beta, taps);
     const hipError_t e = hipGetLastError();
     // algorithmic: 24 FMA + 2 SnakeBeta (mul, fma) per output; one read, one write
     const double n = (double)B * C * T;

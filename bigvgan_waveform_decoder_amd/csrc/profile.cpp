@@ -17,7 +17,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/avae.h"
+#include "avae.h"
 #include "avae_internal.h"
 
 namespace avae {
