@@ -12,8 +12,7 @@
 // (K-1)*d halo in LDS once, and every tap j reads the same LDS rows shifted
 // by j*d.  The weight slice [BM rows x kKC*K] is staged in LDS in the
 // caller's [Cout, Cin, K] order (rows contiguous in global memory, so loads
-// coalesce; odd row stride so LDS writes and fragment reads spread over the
-// banks).
+// coalesce).
 //
 // ConvTranspose1d: polyphase gather.  Output t' = q*s + r - pad (phase r)
 // receives sum_i sum_m w[i,o,r+s*m] * x[i, q-m], m < ceil((K-r)/s): one
@@ -178,7 +177,7 @@ __global__ __launch_bounds__(WM * WN * 64) void conv1d_mfma_kernel(
 //    LDS, so global latency hides behind the MFMA work of the same block;
 //  - the input window is staged row by row (256/KC lanes per channel row),
 //    no integer division per element;
-//  - KC = 16 input channels per chunk for K <= 3 (more MFMA work between
+//  - KC = 16 input channels per chunk for small K (more MFMA work between
 //    barriers), 8 otherwise;
 //  - `n_fastest` selects the tile walk within each XCD's range: output
 //    channel tiles fastest (0: neighbouring blocks share the staged input)
@@ -203,7 +202,9 @@ __global__ __launch_bounds__(WM * WN * 64) void conv1d_pipe_kernel(
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int MT = WTM / 16, NTL = WTN / 16;
     constexpr int WROW = KC * KT;      // weight floats per row per chunk
-    constexpr int WS = WROW + 1;        // odd LDS row stride
+    // row stride = 4 (mod 8) floats: each staged float4 is one ds_write_b128
+    // (an odd stride split it into four conflicting scalar writes)
+    constexpr int WS = (WROW % 8 == 0) ? WROW + 4 : WROW + 8;
     constexpr int WV = WROW / 4;        // float4 per row per chunk
     constexpr int WV_PT = (BM * WV + NT - 1) / NT;
     constexpr int XW_MAX = BN + (KT - 1) * kDilMax;
@@ -211,8 +212,8 @@ __global__ __launch_bounds__(WM * WN * 64) void conv1d_pipe_kernel(
     constexpr int X_PT = (XW_MAX + kXLanes - 1) / kXLanes;
     static_assert(WROW % 4 == 0, "float4 weight rows");
 
-    __shared__ float Ws[BM * WS];
-    __shared__ float Xs[KC * XS];
+    __shared__ __align__(16) float Ws[BM * WS];
+    __shared__ __align__(16) float Xs[KC * XS];
 
     const int lid = xcd_remap(blockIdx.x, nblk);
     int mt_i, nt_i, b;
@@ -281,11 +282,7 @@ __global__ __launch_bounds__(WM * WN * 64) void conv1d_pipe_kernel(
             if (e4 < BM * WV) {
                 const int ol = e4 / WV;
                 const int f4 = e4 - ol * WV;
-                float* d = Ws + ol * WS + 4 * f4;
-                d[0] = wr[r].x;
-                d[1] = wr[r].y;
-                d[2] = wr[r].z;
-                d[3] = wr[r].w;
+                *reinterpret_cast<float4*>(Ws + ol * WS + 4 * f4) = wr[r];
             }
         }
 #pragma unroll
@@ -300,10 +297,10 @@ __global__ __launch_bounds__(WM * WN * 64) void conv1d_pipe_kernel(
     __syncthreads();
     for (int c = 0; c < nch; ++c) {
         if (c + 1 < nch) gload((c + 1) * KC);
-        // Two taps per iteration let the next tap's LDS reads overlap the
-        // current tap's MFMAs (measured +5-20% for tiles of 48+ rows); the
-        // small tiles keep one tap per iteration.
-        constexpr int kTapUnroll = BM >= 48 ? 2 : 1;
+        // Several taps per iteration let the next taps' LDS reads overlap
+        // the current tap's MFMAs (measured +5-25% for tiles of 48+ rows);
+        // the small tiles keep one tap per iteration.
+        constexpr int kTapUnroll = BM >= 48 ? 4 : 1;
 #pragma unroll kTapUnroll
         for (int j = 0; j < KT; ++j) {
 #pragma unroll
@@ -419,7 +416,9 @@ hipError_t run_conv1d_pipe(const float* x, float* y, const float* w, int B, int 
     const int n_tiles = (Tout + BN - 1) / BN;
     const long long nblk = (long long)m_tiles * n_tiles * B;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
-    constexpr int KC = KT <= 3 ? 16 : 8;
+    // 16 input channels per chunk for K <= 3, and for K = 7 on the 64x128
+    // tile (measured faster); 8 otherwise (larger chunks cost occupancy).
+    constexpr int KC = (KT <= 3 || (KT == 7 && BM == 64 && BN == 128)) ? 16 : 8;
     // about two dozen MFMA k-steps (KC/4 per tap) between block additions
     const int flush = (24 / ((KC / 4) * KT)) > 0 ? 24 / ((KC / 4) * KT) : 1;
     const int n_fastest = 0;
