@@ -190,8 +190,16 @@ constexpr int xs_stride_const(int xw) {
                                                    : (xw + 63) / 64 * 64 + 16;
 }
 
+// Minimum waves per SIMD requested from the register allocator: 3 for the
+// tiles that measured faster at that occupancy (no or few spills), none for
+// the 64-row tiles whose prefetch and accumulator registers would spill.
+template <int BM, int BN, int KT>
+constexpr int pipe_min_waves() {
+    return (BM == 96 || BM == 48 || BM == 32 || (BM == 64 && BN == 64 && KT <= 3)) ? 3 : 1;
+}
+
 template <int BM, int BN, int WM, int WN, int KT, int KC>
-__global__ __launch_bounds__(WM * WN * 64) void conv1d_pipe_kernel(
+__global__ __launch_bounds__(WM * WN * 64, (pipe_min_waves<BM, BN, KT>())) void conv1d_pipe_kernel(
     const float* __restrict__ x, float* y, const float* __restrict__ w, int Cin, int Cout,
     int T, int Tout, int dil, int pad, int m_tiles, int n_tiles, int nblk, int flush,
     int n_fastest, ConvEpilogue ep) {
