@@ -34,6 +34,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-frames", type=int, default=120,
                     help="latent frames of the oracle's bounded CPU sample (one pass)")
+    ap.add_argument("--stream-tile", type=int, default=100,
+                    help="latent frames per tile of the streaming-decode figure (0: skip it)")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="also run one plain 256 MiB device-to-device copy, whose "
                          "FETCH_SIZE / WRITE_SIZE counters calibrate the traffic figures")
@@ -126,6 +128,33 @@ def act1d_standalone(torch, avae, W, steps):
     return {"shape": list(x.shape), "ms": ms, "GBps": gbps, "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS}
 
 
+def streaming(torch, dec, zd, out, tile, steps):
+    """avae_bigvgan_decode_streaming over the same batch in tiles of `tile`
+    frames with the receptive-field halo: throughput and recompute overhead."""
+    B, _, F = zd.shape
+    ws = torch.empty(dec.streaming_workspace_bytes(B, min(tile, F)), dtype=torch.uint8,
+                     device=zd.device)
+    for _ in range(2):
+        dec.decode_streaming(zd, tile, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    n = max(steps // 2, 3)
+    e0.record(s)
+    for _ in range(n):
+        dec.decode_streaming(zd, tile, out=out, workspace=ws)
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    R = dec.reach_frames()
+    tiles = -(-F // tile)
+    decoded = sum(min(F, (i + 1) * tile + R) - max(0, i * tile - R) for i in range(tiles))
+    return {"tile_frames": tile, "halo_frames": R, "tiles": tiles, "ms": ms,
+            "samples_per_s": out.numel() / (ms / 1e3), "decoded_frames_ratio": decoded / F,
+            "workspace_MB": ws.numel() / 1e6}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -206,6 +235,8 @@ def main():
                           "ms_per_step": v["total_ms"] / args.steps,
                           "avg_us": 1e3 * v["total_ms"] / max(v["launches"], 1)}
                       for k, v in sorted(kernels.items(), key=lambda kv: -kv[1]["total_ms"])}
+    if args.stream_tile > 0:
+        res["streaming"] = streaming(torch, dec, zd, out, args.stream_tile, args.steps)
     if args.pmc_calibration:
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

@@ -100,6 +100,12 @@ def lib() -> ctypes.CDLL:
     L.avae_bigvgan_decode.argtypes = [P, P, c_int, c_int, P, P, c_size_t, P]
     L.avae_bigvgan_decode_traced.restype = c_int
     L.avae_bigvgan_decode_traced.argtypes = [P, P, c_int, c_int, P, P, c_size_t, P, P]
+    L.avae_decoder_reach_frames.restype = c_int
+    L.avae_decoder_reach_frames.argtypes = [P, ctypes.POINTER(c_int)]
+    L.avae_decoder_streaming_workspace_bytes.restype = c_size_t
+    L.avae_decoder_streaming_workspace_bytes.argtypes = [P, c_int, c_int, c_int]
+    L.avae_bigvgan_decode_streaming.restype = c_int
+    L.avae_bigvgan_decode_streaming.argtypes = [P, P, c_int, c_int, P, c_int, c_int, P, c_size_t, P]
     L.avae_profile_begin.restype = c_int
     L.avae_profile_begin.argtypes = [c_int]
     L.avae_profile_end.restype = c_int
@@ -401,3 +407,32 @@ class Decoder:
                                                 workspace.numel(), ctypes.addressof(arr),
                                                 _stream(stream)))
         return out, stages
+
+    def reach_frames(self) -> int:
+        n = c_int()
+        _check(lib().avae_decoder_reach_frames(self._h, ctypes.byref(n)))
+        return n.value
+
+    def streaming_workspace_bytes(self, B: int, tile_frames: int, halo_frames: int = -1) -> int:
+        return int(lib().avae_decoder_streaming_workspace_bytes(self._h, B, tile_frames,
+                                                                  halo_frames))
+
+    def decode_streaming(self, latent, tile_frames: int, halo_frames: int = -1, out=None,
+                         workspace=None, stream=None):
+        """avae_bigvgan_decode_streaming: latent [B, c_in, F] -> wave [B, F*hop] in
+        tiles of tile_frames frames (halo < 0: the decoder's receptive-field reach)."""
+        torch = _torch()
+        B, C, F = latent.shape
+        if C != self.spec.c_in:
+            raise ValueError(f"latent has {C} channels, decoder expects {self.spec.c_in}")
+        L = F * self.spec.hop
+        if out is None:
+            out = torch.empty((B, L), device=latent.device, dtype=torch.float32)
+        if workspace is None:
+            workspace = torch.empty(self.streaming_workspace_bytes(B, min(tile_frames, F),
+                                                                   halo_frames),
+                                    dtype=torch.uint8, device=latent.device)
+        _check(lib().avae_bigvgan_decode_streaming(
+            self._h, _dev(latent, "latent"), B, F, _dev(out, "out", (B, L)), int(tile_frames),
+            int(halo_frames), workspace.data_ptr(), workspace.numel(), _stream(stream)))
+        return out

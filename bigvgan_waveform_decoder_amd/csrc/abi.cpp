@@ -536,3 +536,123 @@ extern "C" int avae_bigvgan_decode_traced(const avae_decoder* dec, const float* 
     return decode_impl(dec, latent, B, frames, wave, workspace, ws_bytes, stage_out,
                        (hipStream_t)stream);
 }
+
+// =========================================================================
+// Streaming decode
+// =========================================================================
+
+namespace {
+
+// Receptive-field reach in latent frames (per layer, in that layer's input
+// samples: Activation1d +-5, a "same" conv (k-1)d/2, a ConvTranspose1d
+// ceil(k/s)+1; each divided by the upsampling already applied), rounded up,
+// plus one frame of slack.
+int reach_frames(const avae_config& c) {
+    double reach = (c.k_pre - 1) / 2.0;
+    double rate = 1.0;
+    for (int i = 0; i < c.n_stages; ++i) {
+        reach += ((c.up_k[i] + c.rates[i] - 1) / c.rates[i] + 1) / rate;
+        rate *= c.rates[i];
+        double mrf = 0.0;
+        for (int j = 0; j < c.n_kernels; ++j) {
+            double r = 0.0;
+            for (int q = 0; q < c.n_dil; ++q)
+                r += 5.0 + (c.rb_k[j] - 1) * c.rb_d[j][q] / 2.0 + 5.0 + (c.rb_k[j] - 1) / 2.0;
+            mrf = r > mrf ? r : mrf;
+        }
+        reach += mrf / rate;
+    }
+    reach += (5.0 + (c.k_post - 1) / 2.0) / rate;
+    return (int)std::ceil(reach) + 1;
+}
+
+long long hop_of(const avae_config& c) {
+    long long h = 1;
+    for (int i = 0; i < c.n_stages; ++i) h *= c.rates[i];
+    return h;
+}
+
+// The streaming workspace: latent crop, tile waveform, decode workspace.
+struct StreamPlan {
+    size_t crop_bytes, wave_bytes, dec_bytes;
+    size_t total() const { return crop_bytes + wave_bytes + dec_bytes; }
+};
+
+bool stream_plan(const avae_decoder* dec, int B, int tile_frames, int halo, StreamPlan* p) {
+    const avae_config& c = dec->cfg;
+    const long long cf = (long long)tile_frames + 2LL * halo;
+    if (cf > 0x3fffffffLL) return false;
+    long long T[AVAE_MAX_STAGES + 1];
+    if (stage_lengths(c, (int)cf, T)) return false;
+    p->crop_bytes = round_up((size_t)B * c.c_in * cf * sizeof(float), 256);
+    p->wave_bytes = round_up((size_t)B * T[c.n_stages] * sizeof(float), 256);
+    p->dec_bytes = 5 * decode_slot_bytes(c, B, T);
+    return true;
+}
+
+}  // namespace
+
+extern "C" int avae_decoder_reach_frames(const avae_decoder* dec, int* out_frames) {
+    if (!dec || !out_frames) return fail(AVAE_EINVAL, "avae_decoder_reach_frames: null argument");
+    *out_frames = reach_frames(dec->cfg);
+    return AVAE_OK;
+}
+
+extern "C" size_t avae_decoder_streaming_workspace_bytes(const avae_decoder* dec, int B,
+                                                         int tile_frames, int halo_frames) {
+    if (!dec || B < 1 || tile_frames < 1) return 0;
+    const int halo = halo_frames < 0 ? reach_frames(dec->cfg) : halo_frames;
+    StreamPlan p;
+    if (!stream_plan(dec, B, tile_frames, halo, &p)) return 0;
+    return p.total();
+}
+
+extern "C" int avae_bigvgan_decode_streaming(const avae_decoder* dec, const float* latent, int B,
+                                             int frames, float* wave, int tile_frames,
+                                             int halo_frames, void* workspace, size_t ws_bytes,
+                                             void* stream) {
+    if (!dec || !latent || !wave)
+        return fail(AVAE_EINVAL, "avae_bigvgan_decode_streaming: null argument");
+    if (B < 1 || frames < 1 || tile_frames < 1)
+        return fail(AVAE_EINVAL, "avae_bigvgan_decode_streaming: B, frames, tile_frames must be >= 1");
+    const avae_config& c = dec->cfg;
+    const long long hop = hop_of(c);
+    long long T[AVAE_MAX_STAGES + 1];
+    if (stage_lengths(c, frames, T) || T[c.n_stages] != frames * hop ||
+        stage_lengths(c, 1, T) || T[c.n_stages] != hop)
+        return fail(AVAE_ESHAPE,
+                    "avae_bigvgan_decode_streaming: output length is not frames x hop for this config");
+    const int halo = halo_frames < 0 ? reach_frames(c) : halo_frames;
+    const int tf = tile_frames < frames ? tile_frames : frames;
+    StreamPlan plan;
+    if (!stream_plan(dec, B, tf, halo, &plan))
+        return fail(AVAE_ESHAPE, "avae_bigvgan_decode_streaming: tile too long");
+    if (!workspace || ws_bytes < plan.total())
+        return fail(AVAE_EWORKSPACE, "avae_bigvgan_decode_streaming: workspace %zu bytes < %zu",
+                    ws_bytes, plan.total());
+    hipStream_t s = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+    float* crop = (float*)ws;
+    float* twave = (float*)(ws + plan.crop_bytes);
+    void* dws = ws + plan.crop_bytes + plan.wave_bytes;
+    const size_t rows = (size_t)B * c.c_in;
+    for (int f0 = 0; f0 < frames; f0 += tf) {
+        const int f1 = f0 + tf < frames ? f0 + tf : frames;
+        const int c0 = f0 - halo > 0 ? f0 - halo : 0;
+        const int c1 = f1 + halo < frames ? f1 + halo : frames;
+        const int cf = c1 - c0;
+        AVAE_TRY(hipMemcpy2DAsync(crop, (size_t)cf * sizeof(float), latent + c0,
+                                  (size_t)frames * sizeof(float), (size_t)cf * sizeof(float), rows,
+                                  hipMemcpyDeviceToDevice, s),
+                 "streaming crop copy");
+        int rc = decode_impl(dec, crop, B, cf, twave, dws, plan.dec_bytes, nullptr, s);
+        if (rc) return rc;
+        const size_t lcrop = (size_t)cf * hop;
+        AVAE_TRY(hipMemcpy2DAsync(wave + (size_t)f0 * hop, (size_t)frames * hop * sizeof(float),
+                                  twave + (size_t)(f0 - c0) * hop, lcrop * sizeof(float),
+                                  (size_t)(f1 - f0) * hop * sizeof(float), (size_t)B,
+                                  hipMemcpyDeviceToDevice, s),
+                 "streaming tile copy");
+    }
+    return AVAE_OK;
+}

@@ -232,6 +232,26 @@ int avae_bigvgan_decode_traced(const avae_decoder* dec, const float* latent, int
                                float* const* stage_out, void* stream);
 
 /*
+ * Time-tiled (streaming) decode for long latents.  The latent is decoded in
+ * tiles of `tile_frames` frames; each tile is decoded from a crop extended by
+ * `halo_frames` frames on each side (clipped at the sequence ends) and only
+ * the tile's own samples are kept.  The decoder is a finite, non-causal
+ * stack of convolutions and resampling filters ([H3] AudioVae::decode), so
+ * with halo_frames >= avae_decoder_reach_frames() every kept sample depends
+ * only on latent frames inside its crop and equals the whole-sequence
+ * decode up to float32 summation order (tile shapes may select different
+ * kernel tilings).  The workspace covers one tile, whatever `frames` is.
+ * Requires an exact hop geometry: output length frames * prod(rates)
+ * (ESHAPE otherwise).  halo_frames < 0 selects avae_decoder_reach_frames().
+ */
+int avae_decoder_reach_frames(const avae_decoder* dec, int* out_frames);
+size_t avae_decoder_streaming_workspace_bytes(const avae_decoder* dec, int B, int tile_frames,
+                                              int halo_frames);
+int avae_bigvgan_decode_streaming(const avae_decoder* dec, const float* latent, int B,
+                                  int frames, float* wave, int tile_frames, int halo_frames,
+                                  void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * Launch profiler, the device-side counterpart of the audio decoder's own
  * phase report ([H3] AVAE_TIME / avae_time_report, phases dec_in, conv_pre,
  * upsamples, resblocks, act_post, conv_post).  Between avae_profile_begin and

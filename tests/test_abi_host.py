@@ -90,3 +90,11 @@ def test_decoder_create_rejects_bad_config():
     assert not h.value
     assert L.avae_decoder_create(None, ctypes.byref(w), ctypes.byref(h)) == -1
     assert L.avae_decoder_workspace_bytes(None, 1, 1) == 0
+
+
+def test_streaming_rejects_bad_arguments():
+    L = avae.lib()
+    fake = ctypes.c_void_p(0x1000)
+    assert L.avae_bigvgan_decode_streaming(None, fake, 1, 1, fake, 1, 0, fake, 16, None) == -1
+    assert L.avae_decoder_streaming_workspace_bytes(None, 1, 1, 0) == 0
+    assert L.avae_decoder_reach_frames(None, None) == -1

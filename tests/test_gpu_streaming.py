@@ -1,0 +1,80 @@
+"""Time-tiled streaming decode (avae_bigvgan_decode_streaming): tiles decoded
+from latent crops with a receptive-field halo reproduce the whole-sequence
+decode, and the oracle on sampled windows."""
+import numpy as np
+import pytest
+
+from bigvgan_waveform_decoder_amd import avae
+from bigvgan_waveform_decoder_amd import workloads as W
+from oracle import avae_oracle as O
+from tests.gpu_util import announce, cuda, cuda_dict, host
+from tests.helpers import decoder_params, decoder_reach_frames, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name,spec,frames,tile", [
+    ("h3-c256", W.scaled_spec(W.H3, 256, final="none"), 90, 17),
+    ("ltx-c128", W.scaled_spec(W.LTX, 128, final="none"), 140, 40),
+])
+def test_streaming_equals_whole_decode(name, spec, frames, tile):
+    announce(f"streaming {name} frames={frames} tile={tile}")
+    wl = 4 if name.startswith("h3") else 5
+    z = W.normal(wl, "latent", [2, spec.c_in, frames])
+    t = W.decoder_tensors(spec, wl)
+    dec = avae.Decoder(spec, cuda_dict(t))
+    assert dec.reach_frames() == decoder_reach_frames(spec)
+    zd = cuda(z)
+    whole = host(dec.decode(zd))
+    tiled = host(dec.decode_streaming(zd, tile))
+    assert tiled.shape == whole.shape == (2, frames * spec.hop)
+    # same arithmetic up to float32 summation order (tile shapes follow T)
+    assert rel_err(tiled, whole) <= 1e-4
+    # and the oracle, on a window in the middle of a tile boundary
+    R = decoder_reach_frames(spec)
+    a = tile - 2
+    lo, hi = max(a - R, 0), min(a + 4 + R, frames)
+    ref = O.decode(z[:1, :, lo:hi], decoder_params(spec, t))[0]
+    off = (a - lo) * spec.hop
+    assert rel_err(tiled[0, a * spec.hop:(a + 4) * spec.hop], ref[off:off + 4 * spec.hop]) <= 1e-3
+
+
+def test_streaming_halo_matters():
+    """With no halo the tile seams differ from the whole decode (the crop
+    edges' padding reaches into the kept samples); with the reach they agree."""
+    announce("streaming halo 0")
+    spec = W.scaled_spec(W.H3, 128, final="none")
+    z = W.normal(4, "latent", [1, spec.c_in, 30])
+    dec = avae.Decoder(spec, cuda_dict(W.decoder_tensors(spec, 4)))
+    zd = cuda(z)
+    whole = host(dec.decode(zd))
+    assert rel_err(host(dec.decode_streaming(zd, 10, halo_frames=0)), whole) > 1e-3
+    assert rel_err(host(dec.decode_streaming(zd, 10)), whole) <= 1e-4
+
+
+def test_streaming_workload4_full_size():
+    """Workload 4's decoder at full size (final map off, so the comparison is
+    not hidden by tanh saturation) in 100-frame tiles with a ragged last tile:
+    the whole-decode result."""
+    announce("streaming workload 4 full size")
+    z, t = W.workload4()
+    spec = W.scaled_spec(W.H3, W.H3.c0, final="none")
+    dec = avae.Decoder(spec, cuda_dict(t))
+    zd = cuda(z[:, :, :370])
+    whole = host(dec.decode(zd))
+    tiled = host(dec.decode_streaming(zd, 100))
+    assert tiled.shape == (2, 370 * spec.hop)
+    # both are float32 decodes of the same arithmetic whose tile shapes (and so
+    # summation orders) follow the sequence length; at full width the growth
+    # over seven stages makes that ~1e-4, inside the decode's 1e-3 bar
+    assert rel_err(tiled, whole) <= 1e-3
+
+
+def test_streaming_rejects_bad_tiles():
+    announce("streaming argument errors")
+    spec = W.scaled_spec(W.H3, 128)
+    dec = avae.Decoder(spec, cuda_dict(W.decoder_tensors(spec, 4)))
+    zd = cuda(W.normal(4, "latent", [1, spec.c_in, 8]))
+    with pytest.raises(avae.AvaeError):
+        dec.decode_streaming(zd, 0)
+    assert dec.streaming_workspace_bytes(1, 4) > dec.streaming_workspace_bytes(1, 4, 0)
