@@ -71,11 +71,42 @@ int conv_out_len(int T, int K, int dil, int pad) { return T + 2 * pad - dil * (K
 
 // One AMP block into y (y = scale*AMP(x) [+ y]); cur, t1, t2 are [B,C,T]
 // scratch buffers.  Activations use `taps`.
+// True if every dilation step of an AMP block of width C and K taps runs as
+// one fused launch (amp_unit.hip).  The kernel takes C <= 32; it is used up
+// to C = 24, the widths where it measured faster than the four separate
+// launches (at 32 channels the separate launches are a few percent faster).
+constexpr int kFuseMaxC = 24;
+bool amp_fusable(int C, int K, int n_dil, const int* dil) {
+    if (C > kFuseMaxC) return false;
+    for (int q = 0; q < n_dil; ++q)
+        if (!avae::amp_unit_supported(C, K, dil[q])) return false;
+    return true;
+}
+
+// One AMP block ([H3] AmpBlock::apply): for each dilation step q,
+// cur <- cur + conv2_q(act(conv1_q(act(cur)))); the last step's result goes
+// through the MRF epilogue (y = cur * out_scale, + y if accumulate).
+// pw1/pw2 (packed weights, or null) select the fused one-launch-per-step
+// path; otherwise each step is act1d, conv1d, act1d, conv1d launches.
 int run_amp(const float* x, float* y, int B, int C, int T, int K, int n_dil, const int* dil,
             const float* const* w1, const float* const* b1, const float* const* w2,
             const float* const* b2, const float* const* la, const float* const* lb,
-            float out_scale, int accumulate, float* cur, float* t1, float* t2,
-            const ActTaps& taps, hipStream_t s) {
+            const float* const* pw1, const float* const* pw2, float out_scale, int accumulate,
+            float* cur, float* t1, float* t2, const ActTaps& taps, hipStream_t s) {
+    if (pw1 && pw2) {
+        float* bufs[2] = {t1, t2};
+        for (int q = 0; q < n_dil; ++q) {
+            const float* src = (q == 0) ? x : bufs[(q - 1) & 1];
+            const bool last = (q == n_dil - 1);
+            float* dst = last ? y : bufs[q & 1];
+            AVAE_TRY(avae::launch_amp_unit(src, dst, pw1[q], b1[q], pw2[q], b2[q], la[2 * q],
+                                           lb[2 * q], la[2 * q + 1], lb[2 * q + 1], B, C, T, K,
+                                           dil[q], last ? out_scale : 1.0f, last ? accumulate : 0,
+                                           taps, s),
+                     "fused AMP unit");
+        }
+        return AVAE_OK;
+    }
     for (int q = 0; q < n_dil; ++q) {
         const float* src = (q == 0) ? x : cur;
         const int d = dil[q];
@@ -179,9 +210,19 @@ extern "C" int avae_convtr1d(const float* x, float* y, int B, int Cin, int Cout,
     return AVAE_OK;
 }
 
+namespace {
+// Packed-weight reserve of the standalone AMP block: room for every
+// dilation step's two packed convolutions at the largest K.
+size_t amp_pack_reserve(int C) {
+    if (C > kFuseMaxC) return 0;
+    const size_t per = avae::amp_unit_packed_floats(C, AVAE_MAX_TAPS);
+    return per ? 2 * AVAE_MAX_DIL * round_up(per * sizeof(float), 256) : 0;
+}
+}  // namespace
+
 extern "C" size_t avae_amp_block_workspace_bytes(int B, int C, int T) {
     if (B < 1 || C < 1 || T < 1) return 0;
-    return 3 * round_up((size_t)B * C * T * sizeof(float), 256);
+    return 3 * round_up((size_t)B * C * T * sizeof(float), 256) + amp_pack_reserve(C);
 }
 
 extern "C" int avae_amp_block(const float* x, float* y, int B, int C, int T, int K, int n_dil,
@@ -211,15 +252,32 @@ extern "C" int avae_amp_block(const float* x, float* y, int B, int C, int T, int
     if (!workspace || ws_bytes < need)
         return fail(AVAE_EWORKSPACE, "avae_amp_block: workspace %zu bytes < %zu needed", ws_bytes,
                     need);
-    const size_t slot = need / 3;
+    const size_t slot = round_up((size_t)B * C * T * sizeof(float), 256);
     char* ws = (char*)workspace;
     float* cur = (float*)ws;
     float* t1 = (float*)(ws + slot);
     float* t2 = (float*)(ws + 2 * slot);
+    hipStream_t s = (hipStream_t)stream;
     avae::prof_set_phase(avae::kPhaseNone);
+    const float* pw1[AVAE_MAX_DIL] = {};
+    const float* pw2[AVAE_MAX_DIL] = {};
+    const bool fused = amp_pack_reserve(C) > 0 && amp_fusable(C, K, n_dil, dil);
+    if (fused) {
+        // pack this call's weights into the reserve (amp_unit.hip layout)
+        char* pk = ws + 3 * slot;
+        const size_t per = round_up(avae::amp_unit_packed_floats(C, K) * sizeof(float), 256);
+        for (int q = 0; q < n_dil; ++q) {
+            float* p1 = (float*)(pk + (2 * q) * per);
+            float* p2 = (float*)(pk + (2 * q + 1) * per);
+            AVAE_TRY(avae::launch_pack_unit_weights(w1[q], p1, C, K, s), "weight packing");
+            AVAE_TRY(avae::launch_pack_unit_weights(w2[q], p2, C, K, s), "weight packing");
+            pw1[q] = p1;
+            pw2[q] = p2;
+        }
+    }
     return run_amp(x, y, B, C, T, K, n_dil, dil, w1, b1 ? b1 : kNull, w2, b2 ? b2 : kNull,
-                   log_alpha, log_beta, out_scale, accumulate, cur, t1, t2,
-                   make_taps(nullptr, nullptr), (hipStream_t)stream);
+                   log_alpha, log_beta, fused ? pw1 : nullptr, fused ? pw2 : nullptr, out_scale,
+                   accumulate, cur, t1, t2, make_taps(nullptr, nullptr), s);
 }
 
 // =========================================================================
@@ -231,6 +289,10 @@ struct avae_decoder {
     avae_weights w;  // pointers into `blob`
     void* blob = nullptr;
     size_t blob_bytes = 0;
+    // packed AMP weights for the stages that run the fused unit (else null)
+    const float* pw1[AVAE_MAX_STAGES][AVAE_MAX_KERNELS][AVAE_MAX_DIL] = {};
+    const float* pw2[AVAE_MAX_STAGES][AVAE_MAX_KERNELS][AVAE_MAX_DIL] = {};
+    void* pblob = nullptr;
     int device = 0;
     ActTaps taps;
 };
@@ -403,6 +465,47 @@ extern "C" int avae_decoder_create(const avae_config* cfg, const avae_weights* w
         *it.first = (const float*)p;
         p += round_up(n * sizeof(float), 256);
     }
+    // Packed copies of the AMP weights of every stage the fused unit takes.
+    size_t pbytes = 0;
+    for (int i = 0; i < c.n_stages; ++i)
+        for (int j = 0; j < c.n_kernels; ++j)
+            if (amp_fusable(c.ch[i + 1], c.rb_k[j], c.n_dil, c.rb_d[j]))
+                pbytes += 2 * c.n_dil *
+                          round_up(avae::amp_unit_packed_floats(c.ch[i + 1], c.rb_k[j]) *
+                                       sizeof(float), 256);
+    if (pbytes) {
+        e = hipMalloc(&d->pblob, pbytes);
+        if (e != hipSuccess) {
+            (void)hipFree(d->blob);
+            delete d;
+            return fail(AVAE_ENOMEM, "avae_decoder_create: hipMalloc(%zu): %s", pbytes,
+                        hipGetErrorString(e));
+        }
+        char* pp = (char*)d->pblob;
+        for (int i = 0; i < c.n_stages && e == hipSuccess; ++i)
+            for (int j = 0; j < c.n_kernels && e == hipSuccess; ++j) {
+                const int co = c.ch[i + 1], K = c.rb_k[j];
+                if (!amp_fusable(co, K, c.n_dil, c.rb_d[j])) continue;
+                const size_t per = round_up(avae::amp_unit_packed_floats(co, K) * sizeof(float), 256);
+                for (int q = 0; q < c.n_dil && e == hipSuccess; ++q) {
+                    float* p1 = (float*)pp;
+                    float* p2 = (float*)(pp + per);
+                    pp += 2 * per;
+                    e = avae::launch_pack_unit_weights(d->w.w1[i][j][q], p1, co, K, nullptr);
+                    if (e == hipSuccess)
+                        e = avae::launch_pack_unit_weights(d->w.w2[i][j][q], p2, co, K, nullptr);
+                    d->pw1[i][j][q] = p1;
+                    d->pw2[i][j][q] = p2;
+                }
+            }
+        if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
+        if (e != hipSuccess) {
+            (void)hipFree(d->pblob);
+            (void)hipFree(d->blob);
+            delete d;
+            return hip_fail(e, "avae_decoder_create: weight packing");
+        }
+    }
     *out = d;
     return AVAE_OK;
 }
@@ -414,6 +517,7 @@ extern "C" void avae_decoder_destroy(avae_decoder* dec) {
         (void)hipGetDevice(&cur);
         (void)hipSetDevice(dec->device);
         (void)hipFree(dec->blob);
+        if (dec->pblob) (void)hipFree(dec->pblob);
         (void)hipSetDevice(cur);
     }
     delete dec;
@@ -496,8 +600,10 @@ int decode_impl(const avae_decoder* dec, const float* latent, int B, int frames,
                  "ConvTranspose1d");
         avae::prof_set_phase(avae::kPhaseResblocks);
         for (int j = 0; j < c.n_kernels; ++j) {
+            const bool fused = dec->pw1[i][j][0] != nullptr;
             int rc = run_amp(X, M, B, co, To, c.rb_k[j], c.n_dil, c.rb_d[j], w.w1[i][j],
                              w.b1[i][j], w.w2[i][j], w.b2[i][j], w.act_la[i][j], w.act_lb[i][j],
+                             fused ? dec->pw1[i][j] : nullptr, fused ? dec->pw2[i][j] : nullptr,
                              inv_nk, j > 0 ? 1 : 0, cur, t1, t2, dec->taps, s);
             if (rc) return rc;
         }

@@ -28,6 +28,7 @@
 // hardware sine is within ~1.3e-7 (measured on MI355X over [0, 1)); the only
 // other error is the float32 rounding of r itself, relative ~1e-7 of the
 // phase, the same order as rounding alpha*v before any float32 sine.
+#include "act_math.h"
 #include "avae_internal.h"
 
 namespace avae {
@@ -37,12 +38,6 @@ constexpr int kThreads = 256;
 constexpr int kTile = 8 * kThreads;        // outputs per block
 constexpr int kX = kTile + 16;             // staged input: x[t0-8 .. t0+kTile+8)
 constexpr int kQ = kTile + 16;             // phase arrays: index j <-> q = t0 - 8 + j
-
-__device__ __forceinline__ float snake_beta(float v, float alpha_rev, float inv_beta) {
-    const float r = v * alpha_rev;
-    const float s = __builtin_amdgcn_sinf(__builtin_amdgcn_fractf(r));
-    return fmaf(s * s, inv_beta, v);
-}
 
 // The doubled-rate pair (2q, 2q+1) from x[q-3 .. q+3], xq pointing at x[q].
 __device__ __forceinline__ void up_pair(const float* xq, const ActTaps& taps, float& e, float& o) {
@@ -254,8 +249,8 @@ __global__ __launch_bounds__(kThreads) void act1d_kernel(
         const int c = row % C;
         if (c != cur_c) {
             cur_c = c;
-            alpha_rev = expf(log_alpha[c]) * 0.15915494309189535f;  // alpha / (2 pi)
-            inv_beta = 1.0f / (expf(log_beta[c]) + 1e-9f);
+            alpha_rev = snake_alpha_rev(log_alpha[c]);
+            inv_beta = snake_inv_beta(log_beta[c]);
         }
         const size_t base = (size_t)row * (size_t)T;
         if (id > first) __syncthreads();  // previous tile done with xs, se, so

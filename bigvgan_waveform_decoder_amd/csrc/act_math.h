@@ -1,0 +1,36 @@
+// Device math shared by the Activation1d kernels (act1d.hip, amp_unit.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace avae {
+
+// SnakeBeta ([H3] = docs.rs page of cortiq_engine/audiovae.rs, item
+// SnakeBeta): v + sin^2(alpha v) / (beta + 1e-9), with alpha_rev =
+// alpha / (2 pi) and inv_beta = 1 / (beta + 1e-9) precomputed per channel.
+// sin(alpha v) = sin(2 pi r), r = v * alpha_rev; v_fract_f32 reduces r to
+// [0, 1) exactly and v_sin_f32 evaluates sin(2 pi r) in revolutions.
+__device__ __forceinline__ float snake_beta(float v, float alpha_rev, float inv_beta) {
+    const float r = v * alpha_rev;
+    const float s = __builtin_amdgcn_sinf(__builtin_amdgcn_fractf(r));
+    return fmaf(s * s, inv_beta, v);
+}
+
+// Per-channel SnakeBeta constants from the stored logarithms.
+__device__ __forceinline__ float snake_alpha_rev(float log_alpha) {
+    return expf(log_alpha) * 0.15915494309189535f;  // alpha / (2 pi)
+}
+__device__ __forceinline__ float snake_inv_beta(float log_beta) {
+    return 1.0f / (expf(log_beta) + 1e-9f);
+}
+
+// Spreads consecutive block ids over the 8 XCDs so that each XCD works
+// through a contiguous range of logical tiles (neighbouring tiles share
+// their halos in that XCD's L2).
+__device__ __forceinline__ int xcd_spread(int bid, int nblk) {
+    const int q = nblk >> 3, r = nblk & 7;
+    const int xcd = bid & 7, idx = bid >> 3;
+    return (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+}
+
+}  // namespace avae

@@ -62,6 +62,20 @@ hipError_t launch_conv_out1(const float* x, float* y, float* pre_final, const fl
                             const float* bias, int B, int Cin, int T, int K, int final_act,
                             hipStream_t stream);
 
+// Fused AMP unit (amp_unit.hip): y = x + conv2(act2(conv1(act1(x)))) for one
+// dilation step, then y * out_scale (+ y_old if accumulate).  Narrow widths
+// only (amp_unit_supported); the weights come packed by
+// launch_pack_unit_weights into amp_unit_packed_floats(C, K) floats.  x and y
+// must not overlap.
+bool amp_unit_supported(int C, int K, int dilation);
+size_t amp_unit_packed_floats(int C, int K);
+hipError_t launch_pack_unit_weights(const float* w, float* wt, int C, int K, hipStream_t s);
+hipError_t launch_amp_unit(const float* x, float* y, const float* wt1, const float* b1,
+                           const float* wt2, const float* b2, const float* la1, const float* lb1,
+                           const float* la2, const float* lb2, int B, int C, int T, int K,
+                           int dilation, float out_scale, int accumulate, const ActTaps& taps,
+                           hipStream_t stream);
+
 // y[b,c,t] = x[b,c,t] * scale[c] + shift[c]
 hipError_t launch_channel_affine(const float* x, float* y, const float* scale,
                                  const float* shift, int B, int C, int T, hipStream_t stream);

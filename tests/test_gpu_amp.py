@@ -51,6 +51,49 @@ def test_amp_block_odd_shapes(C, T, K):
     assert rel_err(y, ref) <= TOL_BLOCK
 
 
+# Widths up to 24 (multiples of 4) run each dilation step as one fused launch
+# (activation, dilated conv, activation, conv, residual).  These cover the
+# tile shapes it picks (1 or 2 channel tiles; 5..11 time tiles per wave),
+# rows shorter than the unit's halo, one-sample rows, and several tiles with
+# a ragged last one; widths 28 and 32 check the separate-launch path at the
+# same sizes.
+FUSED = [
+    (4, 5, 3, (1,)),
+    (12, 1, 11, (1, 3, 5)),
+    (8, 3, 11, (5,)),
+    (12, 5000, 11, (1, 3, 5)),
+    (16, 1500, 7, (1, 3, 5)),
+    (20, 333, 3, (1, 3, 5)),
+    (24, 2000, 11, (1, 3, 5)),
+    (28, 97, 11, (3,)),
+    (32, 700, 7, (1, 3, 5)),
+    (32, 1000, 3, (1, 3, 5)),
+]
+
+
+@pytest.mark.parametrize("C,T,K,dil", FUSED, ids=[f"C{c}-T{t}-K{k}-d{len(d)}" for c, t, k, d in FUSED])
+def test_fused_amp_unit_shapes(C, T, K, dil):
+    announce(f"fused amp C={C} T={T} K={K} dil={dil}")
+    x = W.normal(0, f"famp/{C}/{T}/x", [2, C, T])
+    t = W.amp_tensors(0, f"famp{C}", C, K, dil, weight_var=2.0 / (C * K))
+    y = host(_amp_call(cuda(x), cuda_dict(t), f"famp{C}", K, dil))
+    ref = O.amp_block(x, amp_params(t, f"famp{C}", K, dil))
+    assert rel_err(y, ref) <= TOL_BLOCK
+
+
+def test_fused_amp_unit_accumulate_epilogue():
+    """out <- out + 0.37 * AMP(x) through the fused path's epilogue."""
+    announce("fused amp accumulate")
+    C, T, K, dil = 24, 900, 7, (1, 3, 5)
+    x = W.normal(0, "faccum/x", [2, C, T])
+    o0 = W.normal(0, "faccum/o", [2, C, T])
+    t = W.amp_tensors(0, "faccum", C, K, dil, weight_var=2.0 / (C * K))
+    out = cuda(o0)
+    _amp_call(cuda(x), cuda_dict(t), "faccum", K, dil, out=out, scale=0.37, accumulate=True)
+    ref = o0.astype(np.float64) + 0.37 * O.amp_block(x, amp_params(t, "faccum", K, dil))
+    assert rel_err(host(out), ref) <= TOL_BLOCK
+
+
 def test_mrf_accumulate_matches_oracle():
     """Three blocks accumulated into one output with scale 1/3 = the MRF."""
     announce("mrf accumulate")
