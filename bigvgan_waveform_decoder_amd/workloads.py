@@ -18,6 +18,8 @@ vocoder pages):
      then the MRF of AMP blocks k=(3,7,11) x d=(1,3,5); He weights
   4  full H3-shaped decode: latent [2,32,400] -> [2,320000] at 32 kHz
   5  LTX-shaped vocoder: log-mel [2,64,2000] ~ N(-4,2) -> [2,320000] at 16 kHz
+  6  Music-3 DAV decoder: stereo latent [1,128,862] ~ N(0,1) -> interleaved
+     [1, 2*441344] at 44.1 kHz (10 s); plain-Snake alphas ~ N(1, 0.01)
 """
 from __future__ import annotations
 
@@ -165,8 +167,82 @@ def amp_tensors(workload: int, prefix: str, c: int, k: int, dil: Sequence[int], 
     return t
 
 
+@dataclass
+class DavSpec:
+    """The Music-3 DAV decoder (the H3 page's Music3Dav).  Channel widths are
+    not on the page: c0 halves at every stage, like the H3 decoder."""
+    name: str = "music3-dav"
+    c_side: int = 64             # latent channels per stereo side
+    dec_in: int = 64             # 1-tap projection width
+    c0: int = 1536
+    strides: Tuple[int, ...] = (8, 8, 4, 2)
+    unit_k: int = 7
+    unit_dil: Tuple[int, ...] = (1, 3, 9)
+    k_pre: int = 7
+    k_post: int = 7
+    sample_rate: int = 44100
+
+    @property
+    def up_k(self) -> Tuple[int, ...]:
+        return tuple(2 * s for s in self.strides)
+
+    @property
+    def hop(self) -> int:
+        return int(np.prod(self.strides))
+
+    def widths(self) -> List[int]:
+        return [self.c0 // (2 ** i) for i in range(len(self.strides) + 1)]
+
+
+DAV = DavSpec()
+
+
+def dav_tensors(spec: DavSpec, workload: int, *, alpha_var: float = 0.01,
+                bias_var: float = 0.01) -> Dict[str, np.ndarray]:
+    """All DAV decoder weights by the H3 page's names; He weights, Snake
+    alphas ~ N(1, alpha_var)."""
+    t: Dict[str, np.ndarray] = {}
+    w = spec.widths()
+    cs, d = spec.c_side, spec.dec_in
+
+    def conv(name, cout, cin, k):
+        t[f"{name}.weight"] = normal(workload, f"{name}.weight", [cout, cin, k], 0.0,
+                                     he_var(cin * k))
+        t[f"{name}.bias"] = normal(workload, f"{name}.bias", [cout], 0.0, bias_var)
+
+    def snake_alpha(name, c):
+        t[f"{name}.alpha"] = normal(workload, f"{name}.alpha", [c], 1.0, alpha_var)
+
+    conv("mvae.dec_in_proj", d, cs, 1)
+    conv("mvae.decoder.model.0", w[0], d, spec.k_pre)
+    for i, (s, k) in enumerate(zip(spec.strides, spec.up_k)):
+        p = f"mvae.decoder.model.{i + 1}"
+        ci, co = w[i], w[i + 1]
+        snake_alpha(f"{p}.block.0", ci)
+        t[f"{p}.block.1.weight"] = normal(workload, f"{p}.block.1.weight", [ci, co, k], 0.0,
+                                          he_var(ci * k))
+        t[f"{p}.block.1.bias"] = normal(workload, f"{p}.block.1.bias", [co], 0.0, bias_var)
+        for u in range(len(spec.unit_dil)):
+            q = f"{p}.block.{u + 2}"
+            snake_alpha(f"{q}.block.0", co)
+            conv(f"{q}.block.1", co, co, spec.unit_k)
+            snake_alpha(f"{q}.block.2", co)
+            conv(f"{q}.block.3", co, co, 1)
+    snake_alpha(f"mvae.decoder.model.{len(spec.strides) + 1}", w[-1])
+    conv(f"mvae.decoder.model.{len(spec.strides) + 2}", 1, w[-1], spec.k_post)
+    return t
+
+
+def scaled_dav(c0: int, **kw) -> DavSpec:
+    d = dict(DAV.__dict__)
+    d.update(kw)
+    d["c0"] = c0
+    d["name"] = f"music3-dav-c{c0}"
+    return DavSpec(**d)
+
+
 # --------------------------------------------------------------------------
-# The five workloads
+# The workloads
 # --------------------------------------------------------------------------
 
 def workload1(T: int = 4096, C: int = 32, B: int = 1):
@@ -218,3 +294,9 @@ def scaled_spec(spec: DecoderSpec, c0: int, name: Optional[str] = None, **kw) ->
     d["c0"] = c0
     d["name"] = name or f"{spec.name}-c{c0}"
     return DecoderSpec(**d)
+
+
+def workload6(frames: int = 862, B: int = 1, spec: DavSpec = DAV):
+    """Music-3 DAV decode: stereo latent ~ N(0,1) [B, 2*64, frames] (10 s)."""
+    z = normal(6, "latent", [B, 2 * spec.c_side, frames])
+    return z, dav_tensors(spec, 6)

@@ -17,6 +17,8 @@ Sources (cited by page and item, never by line):
         0.5.74) -- MiniMax-H3 audio VAE decoder, the authority.
   [LTX] docs.rs source page of ``cortiq_engine/ltxaudio.rs`` (cortiq-engine
         0.6.3) -- LTX-2.5 BigVGAN v2 vocoder, second source.
+  The [H3] page also holds the MiniMax-Music-3 DAV decoder (items Snake,
+  DavUnit, DavStage, Music3Dav): the last section of this module.
 
 Readings taken where the pages are silent or disagree are listed in the
 function docstrings (and in the design notes of the repository).
@@ -361,3 +363,119 @@ def decode(latent: np.ndarray, p: DecoderParams, up=None, down=None,
     elif p.final != "none":
         raise ValueError(p.final)
     return y[..., 0, :]
+
+
+# --------------------------------------------------------------------------
+# Music-3 DAV decoder  ([H3] page, items Snake, DavUnit, DavStage, Music3Dav)
+# --------------------------------------------------------------------------
+
+DAV_STRIDES = (8, 8, 4, 2)   # [H3] Music3Dav::STRIDES
+DAV_HOP = 512                # [H3] Music3Dav::HOP = 8 * 8 * 4 * 2
+DAV_UNIT_DILATIONS = (1, 3, 9)  # [H3] DavStage::load
+
+
+def snake(x: np.ndarray, alpha: np.ndarray) -> np.ndarray:
+    """Plain Snake ([H3] ``Snake::apply``), per channel c of ``[..., C, T]``:
+    x + sin^2(alpha_c x) / (alpha_c + 1e-9), alpha used as stored (no
+    exponential, unlike SnakeBeta)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.asarray(alpha, dtype=np.float64)[:, None]
+    return x + np.sin(a * x) ** 2 / (a + 1e-9)
+
+
+@dataclass
+class DavUnitParams:
+    """One residual unit: a1, c1 (k taps at ``dilation``, "same" padding
+    (k-1)/2 * dilation), a2, c2 (1 tap)."""
+    dilation: int
+    a1: np.ndarray
+    w1: np.ndarray            # [C, C, k]
+    b1: Optional[np.ndarray]
+    a2: np.ndarray
+    w2: np.ndarray            # [C, C, 1]
+    b2: Optional[np.ndarray]
+
+
+def dav_unit(x: np.ndarray, p: DavUnitParams) -> np.ndarray:
+    """[H3] ``DavUnit::apply``: x + c2(snake(c1(snake(x, a1)), a2)).  The page
+    loads c1 with padding 3 * dilation for its 7 taps, i.e. "same"."""
+    k = p.w1.shape[2]
+    h = snake(x, p.a1)
+    h = conv1d(h, p.w1, p.b1, dilation=p.dilation, pad=(k - 1) // 2 * p.dilation)
+    h = snake(h, p.a2)
+    return conv1d(h, p.w2, p.b2, dilation=1, pad=0, residual=x)
+
+
+@dataclass
+class DavStageParams:
+    """Snake (alpha over the stage's input channels), a transposed conv at
+    ``stride`` (weight [Cin, Cout, k], padding (k - stride) // 2 as in
+    [H3] ``ConvT1d::load``), then the residual units in order."""
+    stride: int
+    alpha: np.ndarray
+    up_w: np.ndarray
+    up_b: Optional[np.ndarray]
+    units: List[DavUnitParams]
+
+
+def dav_stage(x: np.ndarray, p: DavStageParams) -> np.ndarray:
+    """[H3] ``DavStage::apply``."""
+    h = snake(x, p.alpha)
+    h = convtr1d(h, p.up_w, p.up_b, stride=p.stride)
+    for u in p.units:
+        h = dav_unit(h, u)
+    return h
+
+
+@dataclass
+class DavParams:
+    """Weights of the DAV decoder.  dec_in is the 1-tap input projection of
+    one side's latent, conv_pre and conv_post use "same" padding."""
+    dec_in_w: np.ndarray      # [D, C_side, 1]
+    dec_in_b: Optional[np.ndarray]
+    conv_pre_w: np.ndarray    # [C0, D, k]
+    conv_pre_b: Optional[np.ndarray]
+    stages: List[DavStageParams]
+    post_alpha: np.ndarray
+    conv_post_w: np.ndarray   # [1, C_last, k]
+    conv_post_b: Optional[np.ndarray]
+    trace: List[np.ndarray] = field(default_factory=list)  # filled by dav_decode(record=True)
+
+
+def dav_decode(latent: np.ndarray, p: DavParams, record: bool = False) -> np.ndarray:
+    """[H3] ``Music3Dav::decode``: latent ``[B, 2 C_side, F]`` -> interleaved
+    stereo ``[B, 2 F hop]``.
+
+    The latent channels are a stereo pair: channels [0, C_side) are the left
+    side and [C_side, 2 C_side) the right, each decoded as an independent mono
+    pass: dec_in, conv_pre, the stages, Snake, conv_post, tanh.  The result
+    interleaves the sides sample by sample: out[b, 2 i + side].  With
+    ``record`` the per-stage outputs (conv_pre, each stage) and the
+    pre-tanh conv_post output of the ``[2 B, ...]`` side batch are kept in
+    ``p.trace``.
+    """
+    z = np.asarray(latent, dtype=np.float64)
+    B, C2, F = z.shape
+    cs = p.dec_in_w.shape[1]
+    assert C2 == 2 * cs, "the latent is a stereo pair of sides"
+    x = z.reshape(B * 2, cs, F)          # row 2 b + side
+    x = conv1d(x, p.dec_in_w, p.dec_in_b, dilation=1, pad=0)
+    kp = p.conv_pre_w.shape[2]
+    x = conv1d(x, p.conv_pre_w, p.conv_pre_b, dilation=1, pad=(kp - 1) // 2)
+    if record:
+        p.trace = [x]
+    for st in p.stages:
+        x = dav_stage(x, st)
+        if record:
+            p.trace.append(x)
+    x = snake(x, p.post_alpha)
+    kq = p.conv_post_w.shape[2]
+    y = conv1d(x, p.conv_post_w, p.conv_post_b, dilation=1, pad=(kq - 1) // 2)[:, 0, :]
+    if record:
+        p.trace.append(y)
+    y = np.tanh(y)
+    L = y.shape[-1]
+    out = np.empty((B, 2 * L), dtype=np.float64)
+    out[:, 0::2] = y[0::2]
+    out[:, 1::2] = y[1::2]
+    return out

@@ -81,3 +81,47 @@ def decoder_reach_frames(spec) -> int:
 def amp_reach(k, dil) -> int:
     """Samples an AMP block's output reaches on either side (same rule)."""
     return int(sum(5 + (k - 1) * d // 2 + 5 + (k - 1) // 2 for d in dil))
+
+
+def dav_params(spec, t: Dict[str, np.ndarray]) -> O.DavParams:
+    """The DAV decoder's weights (H3 page names) as oracle parameters."""
+    stages = []
+    for i, s in enumerate(spec.strides):
+        p = f"mvae.decoder.model.{i + 1}"
+        units = []
+        for u, d in enumerate(spec.unit_dil):
+            q = f"{p}.block.{u + 2}"
+            units.append(O.DavUnitParams(
+                dilation=d, a1=f64(t[f"{q}.block.0.alpha"]),
+                w1=f64(t[f"{q}.block.1.weight"]), b1=f64(t[f"{q}.block.1.bias"]),
+                a2=f64(t[f"{q}.block.2.alpha"]),
+                w2=f64(t[f"{q}.block.3.weight"]), b2=f64(t[f"{q}.block.3.bias"])))
+        stages.append(O.DavStageParams(
+            stride=s, alpha=f64(t[f"{p}.block.0.alpha"]), up_w=f64(t[f"{p}.block.1.weight"]),
+            up_b=f64(t[f"{p}.block.1.bias"]), units=units))
+    n = len(spec.strides)
+    return O.DavParams(
+        dec_in_w=f64(t["mvae.dec_in_proj.weight"]), dec_in_b=f64(t["mvae.dec_in_proj.bias"]),
+        conv_pre_w=f64(t["mvae.decoder.model.0.weight"]),
+        conv_pre_b=f64(t["mvae.decoder.model.0.bias"]), stages=stages,
+        post_alpha=f64(t[f"mvae.decoder.model.{n + 1}.alpha"]),
+        conv_post_w=f64(t[f"mvae.decoder.model.{n + 2}.weight"]),
+        conv_post_b=f64(t[f"mvae.decoder.model.{n + 2}.bias"]))
+
+
+def dav_reach_frames(spec) -> int:
+    """Latent frames an output sample of the DAV decoder can depend on, on
+    either side: conv_pre (k-1)/2 frames; per stage a transposed conv
+    (within ceil(k/s) + 1 of its input samples) and the units' dilated convs
+    ((k-1)d/2 samples each, the 1-tap convs and Snake add nothing); conv_post
+    (k-1)/2 output samples; each divided by the upsampling already applied,
+    rounded up plus one frame of slack."""
+    import math
+    reach = (spec.k_pre - 1) / 2.0
+    rate = 1
+    for s, k in zip(spec.strides, spec.up_k):
+        reach += (math.ceil(k / s) + 1) / rate
+        rate *= s
+        reach += sum((spec.unit_k - 1) * d / 2.0 for d in spec.unit_dil) / rate
+    reach += (spec.k_post - 1) / 2.0 / rate
+    return int(math.ceil(reach)) + 1
