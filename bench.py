@@ -34,6 +34,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-frames", type=int, default=120,
                     help="latent frames of the oracle's bounded CPU sample (one pass)")
+    ap.add_argument("--no-dav", action="store_true",
+                    help="skip the Music-3 DAV decoder figure (workload 6)")
     ap.add_argument("--stream-tile", type=int, default=100,
                     help="latent frames per tile of the streaming-decode figure (0: skip it)")
     ap.add_argument("--pmc-calibration", action="store_true",
@@ -155,6 +157,43 @@ def streaming(torch, dec, zd, out, tile, steps):
             "workspace_MB": ws.numel() / 1e6}
 
 
+def dav_figure(torch, avae, W, steps):
+    """The Music-3 DAV decoder on workload 6: stereo latent [1,128,862] ->
+    interleaved [1, 2*441344] at 44.1 kHz (10 s), timed like the main step,
+    with its per-kernel split from the library's launch profiler."""
+    dev = torch.device("cuda:0")
+    z, t = W.workload6()
+    dav = avae.DavDecoder(W.DAV, {k: torch.from_numpy(v).to(dev) for k, v in t.items()})
+    B, _, F = z.shape
+    L = dav.output_length(F)
+    zd = torch.from_numpy(z).to(dev)
+    ws = torch.empty(dav.workspace_bytes(B, F), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, 2 * L), dtype=torch.float32, device=dev)
+    for _ in range(2):
+        dav.decode(zd, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    n = max(steps // 2, 3)
+    e0.record(s)
+    for _ in range(n):
+        dav.decode(zd, out=out, workspace=ws)
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    avae.profile_begin(n * 200 + 64)
+    for _ in range(n):
+        dav.decode(zd, out=out, workspace=ws)
+    kernels, _ = avae.profile_end()
+    top = sorted(kernels.items(), key=lambda kv: -kv[1]["total_ms"])[:6]
+    return {"workload": f"music3-dav decode, latent [{B},128,{F}] -> [{B},{2 * L}] "
+                        f"interleaved stereo at {W.DAV.sample_rate} Hz",
+            "ms": ms, "samples_per_s": out.numel() / (ms / 1e3),
+            "x_realtime": (L / W.DAV.sample_rate) / (ms / 1e3),
+            "kernels_ms": {k: v["total_ms"] / n for k, v in top}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -235,6 +274,8 @@ def main():
                           "ms_per_step": v["total_ms"] / args.steps,
                           "avg_us": 1e3 * v["total_ms"] / max(v["launches"], 1)}
                       for k, v in sorted(kernels.items(), key=lambda kv: -kv[1]["total_ms"])}
+    if not args.no_dav:
+        res["dav"] = dav_figure(torch, avae, W, args.steps)
     if args.stream_tile > 0:
         res["streaming"] = streaming(torch, dec, zd, out, args.stream_tile, args.steps)
     if args.pmc_calibration:

@@ -59,6 +59,28 @@ class avae_weights(ctypes.Structure):
     ]
 
 
+class avae_dav_config(ctypes.Structure):
+    _fields_ = [
+        ("c_side", c_int), ("dec_in_ch", c_int), ("k_pre", c_int), ("k_post", c_int),
+        ("n_stages", c_int), ("ch", c_int * (AVAE_MAX_STAGES + 1)),
+        ("strides", c_int * AVAE_MAX_STAGES), ("up_k", c_int * AVAE_MAX_STAGES),
+        ("unit_k", c_int), ("n_units", c_int), ("unit_dil", c_int * AVAE_MAX_DIL),
+    ]
+
+
+_U2 = (P * AVAE_MAX_DIL) * AVAE_MAX_STAGES
+
+
+class avae_dav_weights(ctypes.Structure):
+    _fields_ = [
+        ("dec_in_w", P), ("dec_in_b", P), ("conv_pre_w", P), ("conv_pre_b", P),
+        ("stage_alpha", P * AVAE_MAX_STAGES), ("up_w", P * AVAE_MAX_STAGES),
+        ("up_b", P * AVAE_MAX_STAGES),
+        ("a1", _U2), ("w1", _U2), ("b1", _U2), ("a2", _U2), ("w2", _U2), ("b2", _U2),
+        ("post_alpha", P), ("conv_post_w", P), ("conv_post_b", P),
+    ]
+
+
 _lib = None
 
 
@@ -100,6 +122,20 @@ def lib() -> ctypes.CDLL:
     L.avae_bigvgan_decode.argtypes = [P, P, c_int, c_int, P, P, c_size_t, P]
     L.avae_bigvgan_decode_traced.restype = c_int
     L.avae_bigvgan_decode_traced.argtypes = [P, P, c_int, c_int, P, P, c_size_t, P, P]
+    L.avae_snake.restype = c_int
+    L.avae_snake.argtypes = [P, P, c_int, c_int, c_int, P, P]
+    L.avae_dav_create.restype = c_int
+    L.avae_dav_create.argtypes = [P, P, P]
+    L.avae_dav_destroy.restype = None
+    L.avae_dav_destroy.argtypes = [P]
+    L.avae_dav_output_length.restype = c_int
+    L.avae_dav_output_length.argtypes = [P, c_int, ctypes.POINTER(c_int)]
+    L.avae_dav_workspace_bytes.restype = c_size_t
+    L.avae_dav_workspace_bytes.argtypes = [P, c_int, c_int]
+    L.avae_dav_decode.restype = c_int
+    L.avae_dav_decode.argtypes = [P, P, c_int, c_int, P, P, c_size_t, P]
+    L.avae_dav_decode_traced.restype = c_int
+    L.avae_dav_decode_traced.argtypes = [P, P, c_int, c_int, P, P, c_size_t, P, P]
     L.avae_decoder_reach_frames.restype = c_int
     L.avae_decoder_reach_frames.argtypes = [P, ctypes.POINTER(c_int)]
     L.avae_decoder_streaming_workspace_bytes.restype = c_size_t
@@ -436,3 +472,109 @@ class Decoder:
             self._h, _dev(latent, "latent"), B, F, _dev(out, "out", (B, L)), int(tile_frames),
             int(halo_frames), workspace.data_ptr(), workspace.numel(), _stream(stream)))
         return out
+
+
+def snake(x, alpha, out=None, stream=None):
+    """avae_snake: plain Snake with alpha as stored; out may be x."""
+    torch = _torch()
+    B, C, T = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _check(lib().avae_snake(_dev(x, "x"), _dev(out, "out", (B, C, T)), B, C, T,
+                            _dev(alpha, "alpha", (C,)), _stream(stream)))
+    return out
+
+
+class DavDecoder:
+    """avae_dav_create / avae_dav_decode over device weight tensors named as on
+    the H3 page (``mvae.dec_in_proj.weight``, ``mvae.decoder.model.{i}...``)."""
+
+    def __init__(self, spec, tensors: Dict[str, "object"]):
+        cfg = avae_dav_config()
+        cfg.c_side, cfg.dec_in_ch = spec.c_side, spec.dec_in
+        cfg.k_pre, cfg.k_post = spec.k_pre, spec.k_post
+        ns = len(spec.strides)
+        cfg.n_stages = ns
+        for i, c in enumerate(spec.widths()):
+            cfg.ch[i] = c
+        for i, (st, k) in enumerate(zip(spec.strides, spec.up_k)):
+            cfg.strides[i], cfg.up_k[i] = st, k
+        cfg.unit_k = spec.unit_k
+        cfg.n_units = len(spec.unit_dil)
+        for u, d in enumerate(spec.unit_dil):
+            cfg.unit_dil[u] = d
+        self.spec, self.cfg = spec, cfg
+        t = tensors
+        g = lambda name: _dev(t[name], name) if name in t else None
+        w = avae_dav_weights()
+        w.dec_in_w, w.dec_in_b = g("mvae.dec_in_proj.weight"), g("mvae.dec_in_proj.bias")
+        w.conv_pre_w, w.conv_pre_b = g("mvae.decoder.model.0.weight"), g("mvae.decoder.model.0.bias")
+        for i in range(ns):
+            p = f"mvae.decoder.model.{i + 1}"
+            w.stage_alpha[i] = g(f"{p}.block.0.alpha")
+            w.up_w[i], w.up_b[i] = g(f"{p}.block.1.weight"), g(f"{p}.block.1.bias")
+            for u in range(len(spec.unit_dil)):
+                q = f"{p}.block.{u + 2}"
+                w.a1[i][u] = g(f"{q}.block.0.alpha")
+                w.w1[i][u], w.b1[i][u] = g(f"{q}.block.1.weight"), g(f"{q}.block.1.bias")
+                w.a2[i][u] = g(f"{q}.block.2.alpha")
+                w.w2[i][u], w.b2[i][u] = g(f"{q}.block.3.weight"), g(f"{q}.block.3.bias")
+        w.post_alpha = g(f"mvae.decoder.model.{ns + 1}.alpha")
+        w.conv_post_w = g(f"mvae.decoder.model.{ns + 2}.weight")
+        w.conv_post_b = g(f"mvae.decoder.model.{ns + 2}.bias")
+        h = P()
+        _check(lib().avae_dav_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(h)))
+        self._h = h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h and _lib is not None:
+            _lib.avae_dav_destroy(h)
+            self._h = None
+
+    def output_length(self, frames: int) -> int:
+        """Samples per side."""
+        n = c_int()
+        _check(lib().avae_dav_output_length(self._h, frames, ctypes.byref(n)))
+        return n.value
+
+    def workspace_bytes(self, B: int, frames: int) -> int:
+        return int(lib().avae_dav_workspace_bytes(self._h, B, frames))
+
+    def stage_shapes(self, B: int, frames: int):
+        """Traced intermediates of the [2B, ...] side batch."""
+        w = self.spec.widths()
+        shapes = [(2 * B, w[0], frames)]
+        T = frames
+        for i, (st, k) in enumerate(zip(self.spec.strides, self.spec.up_k)):
+            T = (T - 1) * st + k - 2 * ((k - st) // 2)
+            shapes.append((2 * B, w[i + 1], T))
+        shapes.append((2 * B, self.output_length(frames)))
+        return shapes
+
+    def decode(self, latent, out=None, workspace=None, stream=None, trace: bool = False):
+        """latent [B, 2 c_side, F] -> interleaved stereo [B, 2 L]."""
+        torch = _torch()
+        B, C, F = latent.shape
+        if C != 2 * self.spec.c_side:
+            raise ValueError(f"latent has {C} channels, the DAV decoder expects "
+                             f"{2 * self.spec.c_side} (two sides)")
+        L = self.output_length(F)
+        if out is None:
+            out = torch.empty((B, 2 * L), device=latent.device, dtype=torch.float32)
+        if workspace is None:
+            workspace = torch.empty(self.workspace_bytes(B, F), dtype=torch.uint8,
+                                    device=latent.device)
+        if not trace:
+            _check(lib().avae_dav_decode(self._h, _dev(latent, "latent"), B, F,
+                                         _dev(out, "out", (B, 2 * L)), workspace.data_ptr(),
+                                         workspace.numel(), _stream(stream)))
+            return out
+        stages = [torch.empty(s, device=latent.device, dtype=torch.float32)
+                  for s in self.stage_shapes(B, F)]
+        arr = (P * len(stages))(*[s.data_ptr() for s in stages])
+        _check(lib().avae_dav_decode_traced(self._h, _dev(latent, "latent"), B, F,
+                                            _dev(out, "out", (B, 2 * L)), workspace.data_ptr(),
+                                            workspace.numel(), ctypes.addressof(arr),
+                                            _stream(stream)))
+        return out, stages

@@ -3,6 +3,7 @@
 // the compute calls never allocate or synchronise.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -620,7 +621,7 @@ int decode_impl(const avae_decoder* dec, const float* latent, int B, int frames,
     avae::prof_set_phase(avae::kPhaseConvPost);
     float* pre = (stage_out && stage_out[c.n_stages + 1]) ? stage_out[c.n_stages + 1] : nullptr;
     AVAE_TRY(avae::launch_conv_out1(t1, wave, pre, w.conv_post_w, w.conv_post_b, B, cl, TL,
-                                    c.k_post, c.final_act, s),
+                                    c.k_post, c.final_act, 0, s),
              "conv_post");
     avae::prof_set_phase(avae::kPhaseNone);
     return AVAE_OK;
@@ -761,4 +762,265 @@ extern "C" int avae_bigvgan_decode_streaming(const avae_decoder* dec, const floa
                  "streaming tile copy");
     }
     return AVAE_OK;
+}
+
+// =========================================================================
+// Plain Snake and the Music-3 DAV decoder
+// =========================================================================
+
+extern "C" int avae_snake(const float* x, float* y, int B, int C, int T, const float* alpha,
+                          void* stream) {
+    if (!x || !y || !alpha) return fail(AVAE_EINVAL, "avae_snake: null pointer");
+    if (B < 1 || C < 1 || T < 1)
+        return fail(AVAE_EINVAL, "avae_snake: B, C, T must be >= 1 (got %d, %d, %d)", B, C, T);
+    avae::prof_set_phase(avae::kPhaseNone);
+    AVAE_TRY(avae::launch_snake(x, y, B, C, T, alpha, (hipStream_t)stream), "avae_snake launch");
+    return AVAE_OK;
+}
+
+struct avae_dav {
+    avae_dav_config cfg;
+    avae_dav_weights w;  // pointers into `blob`
+    void* blob = nullptr;
+    int device = 0;
+};
+
+namespace {
+
+int check_dav_config(const avae_dav_config* c) {
+    if (c->c_side < 1 || c->dec_in_ch < 1) return fail(AVAE_EINVAL, "dav config: c_side/dec_in_ch < 1");
+    if (c->k_pre < 1 || c->k_pre % 2 == 0 || c->k_pre > AVAE_MAX_TAPS || c->k_post < 1 ||
+        c->k_post % 2 == 0 || c->k_post > AVAE_MAX_TAPS)
+        return fail(AVAE_ESHAPE, "dav config: k_pre/k_post must be odd and <= %d", AVAE_MAX_TAPS);
+    if (c->n_stages < 1 || c->n_stages > AVAE_MAX_STAGES)
+        return fail(AVAE_ESHAPE, "dav config: n_stages must be in [1, %d]", AVAE_MAX_STAGES);
+    if (c->unit_k < 1 || c->unit_k % 2 == 0 || c->unit_k > AVAE_MAX_TAPS)
+        return fail(AVAE_ESHAPE, "dav config: unit_k must be odd and <= %d", AVAE_MAX_TAPS);
+    if (c->n_units < 1 || c->n_units > AVAE_MAX_DIL)
+        return fail(AVAE_ESHAPE, "dav config: n_units must be in [1, %d]", AVAE_MAX_DIL);
+    for (int u = 0; u < c->n_units; ++u)
+        if (c->unit_dil[u] < 1 || (long long)(c->unit_k - 1) * c->unit_dil[u] > 4096)
+            return fail(AVAE_ESHAPE, "dav config: bad unit_dil[%d]", u);
+    for (int i = 0; i <= c->n_stages; ++i)
+        if (c->ch[i] < 1) return fail(AVAE_EINVAL, "dav config: ch[%d] < 1", i);
+    if (c->ch[c->n_stages] > 1024)
+        return fail(AVAE_ESHAPE, "dav config: last width %d too wide for conv_post", c->ch[c->n_stages]);
+    for (int i = 0; i < c->n_stages; ++i)
+        if (c->strides[i] < 1 || c->up_k[i] < c->strides[i] || c->up_k[i] > AVAE_MAX_TAPS)
+            return fail(AVAE_ESHAPE, "dav config: stage %d needs 1 <= stride <= up_k <= %d", i,
+                        AVAE_MAX_TAPS);
+    return AVAE_OK;
+}
+
+int dav_lengths(const avae_dav_config& c, int frames, long long* T) {
+    T[0] = frames;
+    for (int i = 0; i < c.n_stages; ++i) {
+        const int p = (c.up_k[i] - c.strides[i]) / 2;
+        T[i + 1] = (T[i] - 1) * c.strides[i] + c.up_k[i] - 2LL * p;
+        if (T[i + 1] < 1 || T[i + 1] > 0x7fffffffLL) return 1;
+    }
+    return 0;
+}
+
+// One workspace slot: the largest [2B, C, T] activation of the decode.
+size_t dav_slot_bytes(const avae_dav_config& c, int B, const long long* T) {
+    const size_t B2 = 2 * (size_t)B;
+    size_t m = B2 * (size_t)std::max(c.dec_in_ch, c.ch[0]) * (size_t)T[0];
+    for (int i = 0; i < c.n_stages; ++i) {
+        m = std::max(m, B2 * (size_t)c.ch[i] * (size_t)T[i]);
+        m = std::max(m, B2 * (size_t)c.ch[i + 1] * (size_t)T[i + 1]);
+    }
+    return round_up(m * sizeof(float), 256);
+}
+
+int dav_decode_impl(const avae_dav* dav, const float* latent, int B, int frames, float* wave,
+                    void* workspace, size_t ws_bytes, float* const* trace, hipStream_t s) {
+    if (!dav || !latent || !wave) return fail(AVAE_EINVAL, "avae_dav_decode: null argument");
+    if (B < 1 || frames < 1) return fail(AVAE_EINVAL, "avae_dav_decode: B, frames must be >= 1");
+    const avae_dav_config& c = dav->cfg;
+    const avae_dav_weights& w = dav->w;
+    long long T[AVAE_MAX_STAGES + 1];
+    if (dav_lengths(c, frames, T)) return fail(AVAE_ESHAPE, "avae_dav_decode: length overflow");
+    if ((long long)2 * B * T[c.n_stages] > 0x7fffffffLL)
+        return fail(AVAE_ESHAPE, "avae_dav_decode: output too long");
+    const size_t slot = dav_slot_bytes(c, B, T);
+    if (!workspace || ws_bytes < 3 * slot)
+        return fail(AVAE_EWORKSPACE, "avae_dav_decode: workspace %zu bytes < %zu needed", ws_bytes,
+                    3 * slot);
+    char* ws = (char*)workspace;
+    float* P0 = (float*)ws;             // the running activation
+    float* P1 = (float*)(ws + slot);    // dec_in output / transposed-conv output
+    float* P2 = (float*)(ws + 2 * slot);  // a unit's first conv output
+    const int B2 = 2 * B;  // row 2b + side: the latent's channel halves are the sides
+    const int F = frames;
+    avae::prof_set_phase(avae::kPhaseDecIn);
+    {
+        ConvEpilogue e{w.dec_in_b, nullptr, 1.0f, 0, nullptr, nullptr};
+        AVAE_TRY(avae::launch_conv1d(latent, P1, w.dec_in_w, B2, c.c_side, c.dec_in_ch, F, F, 1, 1,
+                                     0, e, s),
+                 "dav dec_in");
+    }
+    avae::prof_set_phase(avae::kPhaseConvPre);
+    {
+        ConvEpilogue e{w.conv_pre_b, nullptr, 1.0f, 0, nullptr, nullptr};
+        AVAE_TRY(avae::launch_conv1d(P1, P0, w.conv_pre_w, B2, c.dec_in_ch, c.ch[0], F, F, c.k_pre,
+                                     1, (c.k_pre - 1) / 2, e, s),
+                 "dav conv_pre");
+    }
+    if (trace && trace[0])
+        AVAE_TRY(hipMemcpyAsync(trace[0], P0, (size_t)B2 * c.ch[0] * F * sizeof(float),
+                                hipMemcpyDeviceToDevice, s),
+                 "trace copy");
+    for (int i = 0; i < c.n_stages; ++i) {
+        const int ci = c.ch[i], co = c.ch[i + 1];
+        const int Ti = (int)T[i], To = (int)T[i + 1];
+        avae::prof_set_phase(avae::kPhaseUpsamples);
+        // the stage's Snake is applied as the transposed conv stages its input
+        AVAE_TRY(avae::launch_convtr1d(P0, P1, w.up_w[i], w.up_b[i], B2, ci, co, Ti, To, c.up_k[i],
+                                       c.strides[i], (c.up_k[i] - c.strides[i]) / 2, s,
+                                       w.stage_alpha[i]),
+                 "dav ConvTranspose1d");
+        std::swap(P0, P1);
+        avae::prof_set_phase(avae::kPhaseResblocks);
+        for (int u = 0; u < c.n_units; ++u) {
+            const int d = c.unit_dil[u];
+            // c1: the first Snake on its staged input, the second in its epilogue
+            ConvEpilogue e1{w.b1[i][u], nullptr, 1.0f, 0, w.a2[i][u], w.a1[i][u]};
+            AVAE_TRY(avae::launch_conv1d(P0, P2, w.w1[i][u], B2, co, co, To, To, c.unit_k, d,
+                                         (c.unit_k - 1) / 2 * d, e1, s),
+                     "dav unit conv");
+            // c2 (one tap) plus the residual, in place on the running activation
+            ConvEpilogue e2{w.b2[i][u], P0, 1.0f, 0, nullptr, nullptr};
+            AVAE_TRY(avae::launch_conv1d(P2, P0, w.w2[i][u], B2, co, co, To, To, 1, 1, 0, e2, s),
+                     "dav unit 1-tap conv");
+        }
+        if (trace && trace[1 + i])
+            AVAE_TRY(hipMemcpyAsync(trace[1 + i], P0, (size_t)B2 * co * To * sizeof(float),
+                                    hipMemcpyDeviceToDevice, s),
+                     "trace copy");
+    }
+    const int cl = c.ch[c.n_stages];
+    const int TL = (int)T[c.n_stages];
+    avae::prof_set_phase(avae::kPhaseConvPost);
+    float* pre = (trace && trace[c.n_stages + 1]) ? trace[c.n_stages + 1] : nullptr;
+    // the final Snake is applied as conv_post stages its input
+    AVAE_TRY(avae::launch_conv_out1(P0, wave, pre, w.conv_post_w, w.conv_post_b, B2, cl, TL,
+                                    c.k_post, AVAE_FINAL_TANH, 1, s, w.post_alpha),
+             "dav conv_post");
+    avae::prof_set_phase(avae::kPhaseNone);
+    return AVAE_OK;
+}
+
+}  // namespace
+
+extern "C" int avae_dav_create(const avae_dav_config* cfg, const avae_dav_weights* w,
+                               avae_dav** out) {
+    if (!cfg || !w || !out) return fail(AVAE_EINVAL, "avae_dav_create: null argument");
+    *out = nullptr;
+    int rc = check_dav_config(cfg);
+    if (rc) return rc;
+    const avae_dav_config& c = *cfg;
+    if (!w->dec_in_w || !w->conv_pre_w || !w->post_alpha || !w->conv_post_w)
+        return fail(AVAE_EINVAL, "avae_dav_create: missing dec_in/conv_pre/post weights");
+    for (int i = 0; i < c.n_stages; ++i) {
+        if (!w->stage_alpha[i] || !w->up_w[i])
+            return fail(AVAE_EINVAL, "avae_dav_create: missing stage %d snake/upsampler", i);
+        for (int u = 0; u < c.n_units; ++u)
+            if (!w->a1[i][u] || !w->w1[i][u] || !w->a2[i][u] || !w->w2[i][u])
+                return fail(AVAE_EINVAL, "avae_dav_create: missing unit [%d][%d]", i, u);
+    }
+    avae_dav* d = new (std::nothrow) avae_dav();
+    if (!d) return fail(AVAE_ENOMEM, "avae_dav_create: host allocation failed");
+    d->cfg = c;
+    std::memset(&d->w, 0, sizeof(d->w));
+    BlobPlan plan;
+    plan.add(&d->w.dec_in_w, w->dec_in_w, (size_t)c.dec_in_ch * c.c_side);
+    plan.add(&d->w.dec_in_b, w->dec_in_b, c.dec_in_ch);
+    plan.add(&d->w.conv_pre_w, w->conv_pre_w, (size_t)c.ch[0] * c.dec_in_ch * c.k_pre);
+    plan.add(&d->w.conv_pre_b, w->conv_pre_b, c.ch[0]);
+    for (int i = 0; i < c.n_stages; ++i) {
+        const size_t ci = c.ch[i], co = c.ch[i + 1];
+        plan.add(&d->w.stage_alpha[i], w->stage_alpha[i], ci);
+        plan.add(&d->w.up_w[i], w->up_w[i], ci * co * c.up_k[i]);
+        plan.add(&d->w.up_b[i], w->up_b[i], co);
+        for (int u = 0; u < c.n_units; ++u) {
+            plan.add(&d->w.a1[i][u], w->a1[i][u], co);
+            plan.add(&d->w.w1[i][u], w->w1[i][u], co * co * c.unit_k);
+            plan.add(&d->w.b1[i][u], w->b1[i][u], co);
+            plan.add(&d->w.a2[i][u], w->a2[i][u], co);
+            plan.add(&d->w.w2[i][u], w->w2[i][u], co * co);
+            plan.add(&d->w.b2[i][u], w->b2[i][u], co);
+        }
+    }
+    const size_t cl = c.ch[c.n_stages];
+    plan.add(&d->w.post_alpha, w->post_alpha, cl);
+    plan.add(&d->w.conv_post_w, w->conv_post_w, cl * c.k_post);
+    plan.add(&d->w.conv_post_b, w->conv_post_b, 1);
+    hipError_t e = hipGetDevice(&d->device);
+    if (e != hipSuccess) {
+        delete d;
+        return hip_fail(e, "avae_dav_create: hipGetDevice");
+    }
+    e = hipMalloc(&d->blob, plan.total);
+    if (e != hipSuccess) {
+        delete d;
+        return fail(AVAE_ENOMEM, "avae_dav_create: hipMalloc(%zu): %s", plan.total,
+                    hipGetErrorString(e));
+    }
+    char* p = (char*)d->blob;
+    for (auto& it : plan.items) {
+        const size_t n = it.second.second;
+        e = hipMemcpy(p, it.second.first, n * sizeof(float), hipMemcpyDefault);
+        if (e != hipSuccess) {
+            (void)hipFree(d->blob);
+            delete d;
+            return hip_fail(e, "avae_dav_create: weight copy");
+        }
+        *it.first = (const float*)p;
+        p += round_up(n * sizeof(float), 256);
+    }
+    *out = d;
+    return AVAE_OK;
+}
+
+extern "C" void avae_dav_destroy(avae_dav* dav) {
+    if (!dav) return;
+    if (dav->blob) {
+        int cur = 0;
+        (void)hipGetDevice(&cur);
+        (void)hipSetDevice(dav->device);
+        (void)hipFree(dav->blob);
+        (void)hipSetDevice(cur);
+    }
+    delete dav;
+}
+
+extern "C" int avae_dav_output_length(const avae_dav* dav, int frames, int* out_len) {
+    if (!dav || !out_len) return fail(AVAE_EINVAL, "avae_dav_output_length: null argument");
+    if (frames < 1) return fail(AVAE_EINVAL, "avae_dav_output_length: frames < 1");
+    long long T[AVAE_MAX_STAGES + 1];
+    if (dav_lengths(dav->cfg, frames, T))
+        return fail(AVAE_ESHAPE, "avae_dav_output_length: length overflow");
+    *out_len = (int)T[dav->cfg.n_stages];
+    return AVAE_OK;
+}
+
+extern "C" size_t avae_dav_workspace_bytes(const avae_dav* dav, int B, int frames) {
+    if (!dav || B < 1 || frames < 1) return 0;
+    long long T[AVAE_MAX_STAGES + 1];
+    if (dav_lengths(dav->cfg, frames, T)) return 0;
+    return 3 * dav_slot_bytes(dav->cfg, B, T);
+}
+
+extern "C" int avae_dav_decode(const avae_dav* dav, const float* latent, int B, int frames,
+                               float* wave, void* workspace, size_t ws_bytes, void* stream) {
+    return dav_decode_impl(dav, latent, B, frames, wave, workspace, ws_bytes, nullptr,
+                           (hipStream_t)stream);
+}
+
+extern "C" int avae_dav_decode_traced(const avae_dav* dav, const float* latent, int B, int frames,
+                                      float* wave, void* workspace, size_t ws_bytes,
+                                      float* const* stage_out, void* stream) {
+    return dav_decode_impl(dav, latent, B, frames, wave, workspace, ws_bytes, stage_out,
+                           (hipStream_t)stream);
 }

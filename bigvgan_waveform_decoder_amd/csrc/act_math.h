@@ -16,6 +16,14 @@ __device__ __forceinline__ float snake_beta(float v, float alpha_rev, float inv_
     return fmaf(s * s, inv_beta, v);
 }
 
+// Plain Snake ([H3] page, item Snake, the Music-3 DAV decoder): alpha used
+// as stored, v + sin^2(alpha v) / (alpha + 1e-9), the sine as above.
+__device__ __forceinline__ float snake_plain(float v, float alpha) {
+    const float r = v * (alpha * 0.15915494309189535f);
+    const float s = __builtin_amdgcn_sinf(__builtin_amdgcn_fractf(r));
+    return fmaf(s * s, 1.0f / (alpha + 1e-9f), v);
+}
+
 // Per-channel SnakeBeta constants from the stored logarithms.
 __device__ __forceinline__ float snake_alpha_rev(float log_alpha) {
     return expf(log_alpha) * 0.15915494309189535f;  // alpha / (2 pi)

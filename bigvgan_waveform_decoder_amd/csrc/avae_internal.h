@@ -20,14 +20,16 @@ struct ActTaps {
 };
 
 // Epilogue of the Conv1d kernel:
-//   v   = conv + bias[o] (+ residual[idx])
+//   v   = conv + bias[o], then Snake(v, snake_alpha[o]) if given, (+ residual[idx])
 //   out = v * out_scale (+ out[idx] if accumulate)
 // residual may alias out (same element read then written by one lane).
 struct ConvEpilogue {
-    const float* bias;      // [Cout] or null
-    const float* residual;  // [B, Cout, Tout] or null
+    const float* bias;         // [Cout] or null
+    const float* residual;     // [B, Cout, Tout] or null
     float out_scale;
     int accumulate;
+    const float* snake_alpha;  // [Cout] or null: plain Snake after the bias
+    const float* in_alpha;     // [Cin] or null: plain Snake of the input as it is staged
 };
 
 // Launch profiler (profile.cpp).  prof_pre/prof_post bracket one launch;
@@ -51,16 +53,24 @@ hipError_t launch_conv1d(const float* x, float* y, const float* w, int B, int Ci
                          int T, int Tout, int K, int dilation, int pad,
                          const ConvEpilogue& ep, hipStream_t stream);
 
+// in_alpha: [Cin] or null, plain Snake applied to the input as it is staged.
 hipError_t launch_convtr1d(const float* x, float* y, const float* w, const float* bias,
                            int B, int Cin, int Cout, int Tin, int Tout, int K, int stride,
-                           int pad, hipStream_t stream);
+                           int pad, hipStream_t stream, const float* in_alpha = nullptr);
 
 // Conv1d to a single output channel ("same" padding, odd K) followed by the
 // final nonlinearity (0 none, 1 tanh, 2 clamp to [-1,1]).  pre_final, if not
-// null, also receives the value before the nonlinearity.
+// null, also receives the value before the nonlinearity ([B, T]).  With
+// interleave2, input rows 2b and 2b+1 are the two stereo sides of output
+// row b, written interleaved: y[b][2t + side].
 hipError_t launch_conv_out1(const float* x, float* y, float* pre_final, const float* w,
                             const float* bias, int B, int Cin, int T, int K, int final_act,
-                            hipStream_t stream);
+                            int interleave2, hipStream_t stream,
+                            const float* in_alpha = nullptr);
+
+// Plain Snake (snake.hip): y = x + sin^2(alpha_c x) / (alpha_c + 1e-9).
+hipError_t launch_snake(const float* x, float* y, int B, int C, int T, const float* alpha,
+                        hipStream_t stream);
 
 // Fused AMP unit (amp_unit.hip): y = x + conv2(act2(conv1(act1(x)))) for one
 // dilation step, then y * out_scale (+ y_old if accumulate).  Narrow widths

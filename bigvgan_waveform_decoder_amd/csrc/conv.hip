@@ -25,6 +25,7 @@
 // to time, so consecutive lanes store consecutive samples.
 #include <string>
 
+#include "act_math.h"
 #include "avae_internal.h"
 
 namespace avae {
@@ -110,7 +111,10 @@ __global__ __launch_bounds__(WM * WN * 64) void conv1d_mfma_kernel(
             const int u = e - i * xw;
             const int t = t0 - pad + u;
             float v = 0.f;
-            if (ic0 + i < Cin && t >= 0 && t < T) v = xb[(size_t)(ic0 + i) * T + t];
+            if (ic0 + i < Cin && t >= 0 && t < T) {
+                v = xb[(size_t)(ic0 + i) * T + t];
+                if (ep.in_alpha) v = snake_plain(v, ep.in_alpha[ic0 + i]);
+            }
             Xs[i * xs_stride + u] = v;
         }
         __syncthreads();
@@ -159,6 +163,7 @@ __global__ __launch_bounds__(WM * WN * 64) void conv1d_mfma_kernel(
                     const size_t idx = (size_t)o * Tout + t;
                     float v = acc[a][c][r];
                     if (ep.bias) v += ep.bias[o];
+                    if (ep.snake_alpha) v = snake_plain(v, ep.snake_alpha[o]);
                     if (rb) v += rb[idx];
                     v *= ep.out_scale;
                     if (ep.accumulate) v += yb[idx];
@@ -183,7 +188,12 @@ __global__ __launch_bounds__(WM * WN * 64) void conv1d_mfma_kernel(
 //    channel tiles fastest (0: neighbouring blocks share the staged input)
 //    or time tiles fastest (1: they share one weight slice).  Measured on
 //    MI355X, channel-fastest is equal or better for every decoder shape.
+// Largest dilation a pipelined kernel stages the halo for (its DM template
+// parameter): 5 covers the BigVGAN units (d = 1, 3, 5); a second 7-tap
+// instantiation with DM = 9 takes the DAV units' d = 9 (a wider halo costs
+// the d <= 5 shapes staging work, so they keep DM = 5).
 constexpr int kDilMax = 5;
+constexpr int dil_max(int K) { return K == 7 ? 9 : kDilMax; }
 
 constexpr int xs_stride_const(int xw) {
     return ((xw + 63) / 64 * 64 + 16) - 64 >= xw ? ((xw + 63) / 64 * 64 + 16) - 64
@@ -198,7 +208,7 @@ constexpr int pipe_min_waves() {
     return (BM == 96 || BM == 48 || BM == 32 || (BM == 64 && BN == 64 && KT <= 3)) ? 3 : 1;
 }
 
-template <int BM, int BN, int WM, int WN, int KT, int KC>
+template <int BM, int BN, int WM, int WN, int KT, int KC, int DM, bool SN>
 __global__ __launch_bounds__(WM * WN * 64, (pipe_min_waves<BM, BN, KT>())) void conv1d_pipe_kernel(
     const float* __restrict__ x, float* y, const float* __restrict__ w, int Cin, int Cout,
     int T, int Tout, int dil, int pad, int m_tiles, int n_tiles, int nblk, int flush,
@@ -215,7 +225,7 @@ __global__ __launch_bounds__(WM * WN * 64, (pipe_min_waves<BM, BN, KT>())) void 
     constexpr int WS = (WROW % 8 == 0) ? WROW + 4 : WROW + 8;
     constexpr int WV = WROW / 4;        // float4 per row per chunk
     constexpr int WV_PT = (BM * WV + NT - 1) / NT;
-    constexpr int XW_MAX = BN + (KT - 1) * kDilMax;
+    constexpr int XW_MAX = BN + (KT - 1) * DM;
     constexpr int XS = xs_stride_const(XW_MAX);
     constexpr int X_PT = (XW_MAX + kXLanes - 1) / kXLanes;
     static_assert(WROW % 4 == 0, "float4 weight rows");
@@ -258,6 +268,7 @@ __global__ __launch_bounds__(WM * WN * 64, (pipe_min_waves<BM, BN, KT>())) void 
 
     float4 wr[WV_PT];
     float xr[X_PT];
+    float xa = 1.f;  // Snake alpha of this thread's staged input row
 
     auto gload = [&](int ic0) {
         const int valid_f = (Cin - ic0 < KC ? Cin - ic0 : KC) * KT;  // multiple of 4
@@ -282,6 +293,7 @@ __global__ __launch_bounds__(WM * WN * 64, (pipe_min_waves<BM, BN, KT>())) void 
             if (u < xw && ic < Cin && t >= 0 && t < T) v = xrowp[t];
             xr[r] = v;
         }
+        if (SN && ep.in_alpha) xa = ic < Cin ? ep.in_alpha[ic] : 1.f;
     };
     auto lstore = [&]() {
 #pragma unroll
@@ -292,6 +304,12 @@ __global__ __launch_bounds__(WM * WN * 64, (pipe_min_waves<BM, BN, KT>())) void 
                 const int f4 = e4 - ol * WV;
                 *reinterpret_cast<float4*>(Ws + ol * WS + 4 * f4) = wr[r];
             }
+        }
+        if (SN && ep.in_alpha) {
+            // plain Snake of the input as staged (zero padding stays zero)
+            const float arev = xa * 0.15915494309189535f, inv = 1.0f / (xa + 1e-9f);
+#pragma unroll
+            for (int r = 0; r < X_PT; ++r) xr[r] = snake_beta(xr[r], arev, inv);
         }
 #pragma unroll
         for (int r = 0; r < X_PT; ++r) {
@@ -358,6 +376,7 @@ __global__ __launch_bounds__(WM * WN * 64, (pipe_min_waves<BM, BN, KT>())) void 
                     const size_t idx = (size_t)o * Tout + t;
                     float v = acc[a][cc][r];
                     if (ep.bias) v += ep.bias[o];
+                    if (SN && ep.snake_alpha) v = snake_plain(v, ep.snake_alpha[o]);
                     if (rb) v += rb[idx];
                     v *= ep.out_scale;
                     if (ep.accumulate) v += yb[idx];
@@ -416,7 +435,7 @@ hipError_t run_conv1d(const float* x, float* y, const float* w, int B, int Cin, 
     return e;
 }
 
-template <int BM, int BN, int WM, int WN, int KT>
+template <int BM, int BN, int WM, int WN, int KT, int DM = kDilMax, bool SN = false>
 hipError_t run_conv1d_pipe(const float* x, float* y, const float* w, int B, int Cin, int Cout,
                            int T, int Tout, int dil, int pad, const ConvEpilogue& ep,
                            hipStream_t stream) {
@@ -433,9 +452,11 @@ hipError_t run_conv1d_pipe(const float* x, float* y, const float* w, int B, int 
     static const std::string name = "conv1d_pipe_kernel<" + std::to_string(BM) + "," +
                                     std::to_string(BN) + "," + std::to_string(WM) + "," +
                                     std::to_string(WN) + "," + std::to_string(KT) + "," +
-                                    std::to_string(KC) + ">";
+                                    std::to_string(KC) +
+                                    (DM == kDilMax ? std::string() : ",d" + std::to_string(DM)) +
+                                    (SN ? ",snake" : "") + ">";
     prof_pre(stream);
-    hipLaunchKernelGGL((conv1d_pipe_kernel<BM, BN, WM, WN, KT, KC>), dim3((unsigned)nblk),
+    hipLaunchKernelGGL((conv1d_pipe_kernel<BM, BN, WM, WN, KT, KC, DM, SN>), dim3((unsigned)nblk),
                        dim3(WM * WN * 64), 0, stream, x, y, w, Cin, Cout, T, Tout, dil, pad,
                        m_tiles, n_tiles, (int)nblk, flush, n_fastest, ep);
     const hipError_t e = hipGetLastError();
@@ -453,7 +474,16 @@ hipError_t dispatch_pipe(const float* x, float* y, const float* w, int B, int Ci
     switch (K) {
         case 1: return run_conv1d_pipe<BM, BN, WM, WN, 1>(x, y, w, B, Cin, Cout, T, Tout, dil, pad, ep, stream);
         case 3: return run_conv1d_pipe<BM, BN, WM, WN, 3>(x, y, w, B, Cin, Cout, T, Tout, dil, pad, ep, stream);
-        case 7: return run_conv1d_pipe<BM, BN, WM, WN, 7>(x, y, w, B, Cin, Cout, T, Tout, dil, pad, ep, stream);
+        case 7:
+            // the DAV units' first conv: both Snakes fused (input staging, epilogue)
+            if (ep.in_alpha || ep.snake_alpha) {
+                if (dil > kDilMax)
+                    return run_conv1d_pipe<BM, BN, WM, WN, 7, 9, true>(x, y, w, B, Cin, Cout, T, Tout, dil, pad, ep, stream);
+                return run_conv1d_pipe<BM, BN, WM, WN, 7, kDilMax, true>(x, y, w, B, Cin, Cout, T, Tout, dil, pad, ep, stream);
+            }
+            if (dil > kDilMax)
+                return run_conv1d_pipe<BM, BN, WM, WN, 7, 9>(x, y, w, B, Cin, Cout, T, Tout, dil, pad, ep, stream);
+            return run_conv1d_pipe<BM, BN, WM, WN, 7>(x, y, w, B, Cin, Cout, T, Tout, dil, pad, ep, stream);
         default: return run_conv1d_pipe<BM, BN, WM, WN, 11>(x, y, w, B, Cin, Cout, T, Tout, dil, pad, ep, stream);
     }
 }
@@ -476,9 +506,9 @@ hipError_t dispatch_k(const float* x, float* y, const float* w, int B, int Cin, 
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(WM * WN * 64) void convtr1d_mfma_kernel(
     const float* __restrict__ x, float* __restrict__ y, const float* __restrict__ w,
-    const float* __restrict__ bias, int Cin, int Cout, int Tin, int Tout, int K, int s, int pad,
-    int ntap_max, int m_tiles, int q_tiles, int nblk, int ws_stride, int xs_stride,
-    int flush) {
+    const float* __restrict__ bias, const float* __restrict__ in_alpha, int Cin, int Cout,
+    int Tin, int Tout, int K, int s, int pad, int ntap_max, int m_tiles, int q_tiles, int nblk,
+    int ws_stride, int xs_stride, int flush) {
     constexpr int NT = WM * WN * 64;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int MT = WTM / 16, NTL = WTN / 16;
@@ -537,7 +567,10 @@ __global__ __launch_bounds__(WM * WN * 64) void convtr1d_mfma_kernel(
             const int u = e - i * xw;
             const int t = xbase + u;
             float v = 0.f;
-            if (ic0 + i < Cin && t >= 0 && t < Tin) v = xb[(size_t)(ic0 + i) * Tin + t];
+            if (ic0 + i < Cin && t >= 0 && t < Tin) {
+                v = xb[(size_t)(ic0 + i) * Tin + t];
+                if (in_alpha) v = snake_plain(v, in_alpha[ic0 + i]);
+            }
             Xs[i * xs_stride + u] = v;
         }
         __syncthreads();
@@ -604,8 +637,8 @@ constexpr int kKCT = 16;  // input channels per ConvT K chunk
 template <int WM, int WN, int NTL, int KT, int S>
 __global__ __launch_bounds__(WM * WN * 64) void convtr1d_poly_kernel(
     const float* __restrict__ x, float* __restrict__ y, const float* __restrict__ w,
-    const float* __restrict__ bias, int Cin, int Cout, int Tin, int Tout, int pad, int qlo,
-    int m_tiles, int q_tiles, int nblk, int flush) {
+    const float* __restrict__ bias, const float* __restrict__ in_alpha, int Cin, int Cout,
+    int Tin, int Tout, int pad, int qlo, int m_tiles, int q_tiles, int nblk, int flush) {
     constexpr int NT = WM * WN * 64;
     static_assert(NT == 256, "256 threads");
     constexpr int BMO = 16 * WM;              // output channels per block
@@ -651,6 +684,7 @@ __global__ __launch_bounds__(WM * WN * 64) void convtr1d_poly_kernel(
     const int nch = (Cin + kKCT - 1) / kKCT;
     float4 wr[W_PT];
     float xr[X_PT];
+    float xa = 1.f;  // Snake alpha of this thread's staged input row
 
     auto gload = [&](int ic0) {
 #pragma unroll
@@ -672,6 +706,7 @@ __global__ __launch_bounds__(WM * WN * 64) void convtr1d_poly_kernel(
             if (u < XW && ic < Cin && t >= 0 && t < Tin) v = xb[(size_t)ic * Tin + t];
             xr[k] = v;
         }
+        if (in_alpha) xa = ic < Cin ? in_alpha[ic] : 1.f;
     };
     auto lstore = [&]() {
 #pragma unroll
@@ -681,6 +716,11 @@ __global__ __launch_bounds__(WM * WN * 64) void convtr1d_poly_kernel(
                 const int i = e / WV;
                 *reinterpret_cast<float4*>(Ws + i * RS + 4 * (e - i * WV)) = wr[k];
             }
+        }
+        if (in_alpha) {
+            const float arev = xa * 0.15915494309189535f, inv = 1.0f / (xa + 1e-9f);
+#pragma unroll
+            for (int k = 0; k < X_PT; ++k) xr[k] = snake_beta(xr[k], arev, inv);
         }
 #pragma unroll
         for (int k = 0; k < X_PT; ++k) {
@@ -752,8 +792,9 @@ __global__ __launch_bounds__(WM * WN * 64) void convtr1d_poly_kernel(
 }
 
 template <int WM, int WN, int NTL, int KT, int S>
-hipError_t run_convtr1d_poly(const float* x, float* y, const float* w, const float* bias, int B,
-                             int Cin, int Cout, int Tin, int Tout, int pad, hipStream_t stream) {
+hipError_t run_convtr1d_poly(const float* x, float* y, const float* w, const float* bias,
+                             const float* in_alpha, int B, int Cin, int Cout, int Tin, int Tout,
+                             int pad, hipStream_t stream) {
     constexpr int BMO = 16 * WM;
     constexpr int NQ = 16 * NTL * WN;
     // q = floor((t' + pad) / S) over all outputs t' in [0, Tout)
@@ -770,8 +811,8 @@ hipError_t run_convtr1d_poly(const float* x, float* y, const float* w, const flo
                                     std::to_string(KT) + "," + std::to_string(S) + ">";
     prof_pre(stream);
     hipLaunchKernelGGL((convtr1d_poly_kernel<WM, WN, NTL, KT, S>), dim3((unsigned)nblk),
-                       dim3(WM * WN * 64), 0, stream, x, y, w, bias, Cin, Cout, Tin, Tout, pad,
-                       qlo, m_tiles, q_tiles, (int)nblk, flush);
+                       dim3(WM * WN * 64), 0, stream, x, y, w, bias, in_alpha, Cin, Cout, Tin,
+                       Tout, pad, qlo, m_tiles, q_tiles, (int)nblk, flush);
     const hipError_t e = hipGetLastError();
     prof_post(stream, name.c_str(), 2.0 * B * Cin * Cout * (double)KT * Tin,
               4.0 * ((double)B * Cin * Tin + (double)B * Cout * Tout + (double)Cin * Cout * KT));
@@ -785,8 +826,9 @@ constexpr int kOutChunk = 16;
 
 __global__ __launch_bounds__(kOutThreads) void conv_out1_kernel(
     const float* __restrict__ x, float* __restrict__ y, float* __restrict__ pre,
-    const float* __restrict__ w, const float* __restrict__ bias, int Cin, int T, int K,
-    int final_act, int tiles) {
+    const float* __restrict__ w, const float* __restrict__ bias,
+    const float* __restrict__ in_alpha, int Cin, int T, int K, int final_act, int interleave2,
+    int tiles) {
     extern __shared__ float sm[];
     const int xw = kOutThreads + K - 1;
     float* ws = sm;                 // [Cin*K]
@@ -805,7 +847,10 @@ __global__ __launch_bounds__(kOutThreads) void conv_out1_kernel(
             const int u = e - i * xw;
             const int t = t0 - pad + u;
             float v = 0.f;
-            if (ic0 + i < Cin && t >= 0 && t < T) v = xb[(size_t)(ic0 + i) * T + t];
+            if (ic0 + i < Cin && t >= 0 && t < T) {
+                v = xb[(size_t)(ic0 + i) * T + t];
+                if (in_alpha) v = snake_plain(v, in_alpha[ic0 + i]);
+            }
             xs[i * xw + u] = v;
         }
         __syncthreads();
@@ -820,7 +865,10 @@ __global__ __launch_bounds__(kOutThreads) void conv_out1_kernel(
         float v = acc;
         if (final_act == 1) v = tanhf(v);
         else if (final_act == 2) v = fminf(fmaxf(v, -1.f), 1.f);
-        y[(size_t)b * T + t] = v;
+        // interleave2: rows 2b and 2b+1 are the two sides of output row b
+        const size_t yi = interleave2 ? (size_t)(b >> 1) * 2 * T + 2 * (size_t)t + (b & 1)
+                                      : (size_t)b * T + t;
+        y[yi] = v;
     }
 }
 
@@ -839,7 +887,10 @@ __global__ void channel_affine_kernel(const float* __restrict__ x, float* __rest
 hipError_t launch_conv1d(const float* x, float* y, const float* w, int B, int Cin, int Cout,
                          int T, int Tout, int K, int dilation, int pad, const ConvEpilogue& ep,
                          hipStream_t stream) {
-    const bool pipe_ok = (K == 1 || K == 3 || K == 7 || K == 11) && dilation <= kDilMax &&
+    // Snake in the prologue/epilogue: the 7-tap pipelined kernels, else generic
+    const bool snake = ep.in_alpha || ep.snake_alpha;
+    const bool pipe_ok = (K == 1 || K == 3 || K == 7 || K == 11) && dilation <= dil_max(K) &&
+                         (!snake || K == 7) &&
                          Cin % 4 == 0 && ((uintptr_t)w & 15) == 0;
     if (pipe_ok) {
         auto blocks = [&](int bm, int bn) {
@@ -884,15 +935,19 @@ hipError_t launch_conv1d(const float* x, float* y, const float* w, int B, int Ci
 
 hipError_t launch_convtr1d(const float* x, float* y, const float* w, const float* bias, int B,
                            int Cin, int Cout, int Tin, int Tout, int K, int stride, int pad,
-                           hipStream_t stream) {
+                           hipStream_t stream, const float* in_alpha) {
     // float4 weight slices need Cout*K % 4 == 0 and a 16-byte aligned base
     const bool vec = ((long long)Cout * K) % 4 == 0 && ((uintptr_t)w & 15) == 0;
     if (vec && stride == 5 && K == 11)
-        return run_convtr1d_poly<2, 2, 2, 11, 5>(x, y, w, bias, B, Cin, Cout, Tin, Tout, pad, stream);
+        return run_convtr1d_poly<2, 2, 2, 11, 5>(x, y, w, bias, in_alpha, B, Cin, Cout, Tin, Tout, pad, stream);
     if (vec && stride == 5 && K == 10)
-        return run_convtr1d_poly<2, 2, 2, 10, 5>(x, y, w, bias, B, Cin, Cout, Tin, Tout, pad, stream);
+        return run_convtr1d_poly<2, 2, 2, 10, 5>(x, y, w, bias, in_alpha, B, Cin, Cout, Tin, Tout, pad, stream);
     if (vec && stride == 2 && K == 4)
-        return run_convtr1d_poly<4, 1, 4, 4, 2>(x, y, w, bias, B, Cin, Cout, Tin, Tout, pad, stream);
+        return run_convtr1d_poly<4, 1, 4, 4, 2>(x, y, w, bias, in_alpha, B, Cin, Cout, Tin, Tout, pad, stream);
+    if (vec && stride == 8 && K == 16)
+        return run_convtr1d_poly<2, 2, 1, 16, 8>(x, y, w, bias, in_alpha, B, Cin, Cout, Tin, Tout, pad, stream);
+    if (vec && stride == 4 && K == 8)
+        return run_convtr1d_poly<2, 2, 2, 8, 4>(x, y, w, bias, in_alpha, B, Cin, Cout, Tin, Tout, pad, stream);
     constexpr int BM = 64, BN = 64, WM = 2, WN = 2;
     const int ntap_max = (K + stride - 1) / stride;
     auto fdiv = [](int a, int b) { int q = a / b; if ((a % b != 0) && ((a < 0) != (b < 0))) --q; return q; };
@@ -913,9 +968,9 @@ hipError_t launch_convtr1d(const float* x, float* y, const float* w, const float
     const int flush = 24 / (2 * ntap_max) > 0 ? 24 / (2 * ntap_max) : 1;
     prof_pre(stream);
     hipLaunchKernelGGL((convtr1d_mfma_kernel<BM, BN, WM, WN>), dim3((unsigned)nblk),
-                       dim3(WM * WN * 64), lds, stream, x, y, w, bias, Cin, Cout, Tin, Tout, K,
-                       stride, pad, ntap_max, m_tiles, q_tiles, (int)nblk, ws_stride, xs_stride,
-                       flush);
+                       dim3(WM * WN * 64), lds, stream, x, y, w, bias, in_alpha, Cin, Cout, Tin,
+                       Tout, K, stride, pad, ntap_max, m_tiles, q_tiles, (int)nblk, ws_stride,
+                       xs_stride, flush);
     const hipError_t e = hipGetLastError();
     prof_post(stream, "convtr1d_mfma_kernel<64,64,2,2>", 2.0 * B * Cin * Cout * (double)K * Tin,
               4.0 * ((double)B * Cin * Tin + (double)B * Cout * Tout + (double)Cin * Cout * K));
@@ -924,14 +979,14 @@ hipError_t launch_convtr1d(const float* x, float* y, const float* w, const float
 
 hipError_t launch_conv_out1(const float* x, float* y, float* pre_final, const float* w,
                             const float* bias, int B, int Cin, int T, int K, int final_act,
-                            hipStream_t stream) {
+                            int interleave2, hipStream_t stream, const float* in_alpha) {
     const int tiles = (T + kOutThreads - 1) / kOutThreads;
     const long long nblk = (long long)tiles * B;
     const size_t lds = (size_t)(Cin * K + kOutChunk * (kOutThreads + K - 1)) * sizeof(float);
     if (nblk > 0x7fffffffLL || lds > 64 * 1024) return hipErrorInvalidValue;
     prof_pre(stream);
     hipLaunchKernelGGL(conv_out1_kernel, dim3((unsigned)nblk), dim3(kOutThreads), lds, stream, x,
-                       y, pre_final, w, bias, Cin, T, K, final_act, tiles);
+                       y, pre_final, w, bias, in_alpha, Cin, T, K, final_act, interleave2, tiles);
     const hipError_t e = hipGetLastError();
     prof_post(stream, "conv_out1_kernel", 2.0 * B * Cin * (double)K * T,
               4.0 * ((double)B * Cin * T + (double)B * T * (pre_final ? 2 : 1) + (double)Cin * K));

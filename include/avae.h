@@ -252,6 +252,81 @@ int avae_bigvgan_decode_streaming(const avae_decoder* dec, const float* latent, 
                                   void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Plain Snake ([H3] Snake::apply, the Music-3 DAV decoder's activation):
+ * y[b,c,t] = x + sin^2(alpha[c] x) / (alpha[c] + 1e-9), alpha [C] used as
+ * stored (no exponential, unlike the SnakeBeta of avae_act1d).  x, y
+ * [B, C, T]; y may equal x (pointwise, in place).  EINVAL on null pointers
+ * or sizes < 1.
+ */
+int avae_snake(const float* x, float* y, int B, int C, int T, const float* alpha, void* stream);
+
+/*
+ * The MiniMax-Music-3 DAV decoder ([H3] page, items Music3Dav, DavStage,
+ * DavUnit, Snake).  Per stereo side (a mono pass): dec_in (1-tap conv,
+ * c_side -> dec_in_ch), conv_pre (k_pre taps, "same", -> ch[0]), then per
+ * stage i: Snake(stage_alpha[i]) -> ConvTranspose1d (ch[i] -> ch[i+1],
+ * stride strides[i], up_k[i] taps, padding (up_k - stride)/2) -> n_units
+ * residual units u: x + c2(Snake(c1(Snake(x, a1)), a2)) with c1 unit_k taps
+ * at dilation unit_dil[u] ("same") and c2 one tap; then Snake(post_alpha),
+ * conv_post (k_post taps, "same", -> 1 channel) and tanh.
+ * Weight layouts: Conv1d [Cout, Cin, k], ConvTranspose1d [Cin, Cout, k],
+ * biases [Cout] (may be NULL), alphas [C].  Like avae_decoder, the decoder
+ * keeps a device copy of the weights (host or device pointers accepted).
+ */
+typedef struct avae_dav_config {
+    int c_side;                      /* latent channels per side (latent has 2 c_side) */
+    int dec_in_ch;
+    int k_pre, k_post;               /* odd, <= AVAE_MAX_TAPS */
+    int n_stages;                    /* <= AVAE_MAX_STAGES */
+    int ch[AVAE_MAX_STAGES + 1];
+    int strides[AVAE_MAX_STAGES];
+    int up_k[AVAE_MAX_STAGES];       /* >= stride */
+    int unit_k;                      /* odd */
+    int n_units;                     /* <= AVAE_MAX_DIL */
+    int unit_dil[AVAE_MAX_DIL];
+} avae_dav_config;
+
+typedef struct avae_dav_weights {
+    const float *dec_in_w, *dec_in_b;
+    const float *conv_pre_w, *conv_pre_b;
+    const float *stage_alpha[AVAE_MAX_STAGES];
+    const float *up_w[AVAE_MAX_STAGES], *up_b[AVAE_MAX_STAGES];
+    const float *a1[AVAE_MAX_STAGES][AVAE_MAX_DIL], *w1[AVAE_MAX_STAGES][AVAE_MAX_DIL],
+        *b1[AVAE_MAX_STAGES][AVAE_MAX_DIL];
+    const float *a2[AVAE_MAX_STAGES][AVAE_MAX_DIL], *w2[AVAE_MAX_STAGES][AVAE_MAX_DIL],
+        *b2[AVAE_MAX_STAGES][AVAE_MAX_DIL];
+    const float *post_alpha, *conv_post_w, *conv_post_b;
+} avae_dav_weights;
+
+typedef struct avae_dav avae_dav;
+
+/* EINVAL (null, missing weight, bad size), ESHAPE (caps), ENOMEM, EHIP. */
+int avae_dav_create(const avae_dav_config* cfg, const avae_dav_weights* w, avae_dav** out);
+void avae_dav_destroy(avae_dav* dav);
+/* Samples per side for `frames` latent frames (frames * prod(strides) when
+ * up_k = 2 stride). */
+int avae_dav_output_length(const avae_dav* dav, int frames, int* out_len);
+size_t avae_dav_workspace_bytes(const avae_dav* dav, int B, int frames);
+/*
+ * latent [B, 2 c_side, frames] (channels [0, c_side) the left side, the rest
+ * the right: [H3] Music3Dav::decode folds the 2 c_side latent into two mono
+ * passes) -> wave [B, 2 L], interleaved: wave[b][2 t + side].  The two sides
+ * of all B items run as one batch of 2 B passes.  EWORKSPACE if ws_bytes <
+ * avae_dav_workspace_bytes().
+ */
+int avae_dav_decode(const avae_dav* dav, const float* latent, int B, int frames, float* wave,
+                    void* workspace, size_t ws_bytes, void* stream);
+/*
+ * Same, and copies intermediate results of the [2 B, ...] side batch (row
+ * 2 b + side) into stage_out[0 .. n_stages+1] where non-NULL: [0] conv_pre
+ * output [2B, ch[0], frames], [1+i] stage i output, [n_stages+1] the
+ * conv_post output before tanh [2B, L].
+ */
+int avae_dav_decode_traced(const avae_dav* dav, const float* latent, int B, int frames,
+                           float* wave, void* workspace, size_t ws_bytes,
+                           float* const* stage_out, void* stream);
+
+/*
  * Launch profiler, the device-side counterpart of the audio decoder's own
  * phase report ([H3] AVAE_TIME / avae_time_report, phases dec_in, conv_pre,
  * upsamples, resblocks, act_post, conv_post).  Between avae_profile_begin and
