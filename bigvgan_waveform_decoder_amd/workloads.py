@@ -20,6 +20,9 @@ vocoder pages):
   5  LTX-shaped vocoder: log-mel [2,64,2000] ~ N(-4,2) -> [2,320000] at 16 kHz
   6  Music-3 DAV decoder: stereo latent [1,128,862] ~ N(0,1) -> interleaved
      [1, 2*441344] at 44.1 kHz (10 s); plain-Snake alphas ~ N(1, 0.01)
+  7  LTX bandwidth-extension tail: 16 kHz signal [2,320000] ~ N(0, 0.01)
+     -> 48 kHz [2,960000]; STFT basis DFT x Hann (L = 512), slaney mel basis
+     (64 mels, 0-8 kHz), BWE generator rates (6,5,2,2,2), c0 = 512, He
 """
 from __future__ import annotations
 
@@ -300,3 +303,63 @@ def workload6(frames: int = 862, B: int = 1, spec: DavSpec = DAV):
     """Music-3 DAV decode: stereo latent ~ N(0,1) [B, 2*64, frames] (10 s)."""
     z = normal(6, "latent", [B, 2 * spec.c_side, frames])
     return z, dav_tensors(spec, 6)
+
+
+# --------------------------------------------------------------------------
+# LTX bandwidth-extension tail (the checkpoint's STFT and mel bases are not
+# on the pages: a DFT x Hann basis and a slaney mel basis stand in)
+# --------------------------------------------------------------------------
+
+BWE = DecoderSpec(name="ltx-bwe", c_in=64, c0=512, rates=(6, 5, 2, 2, 2),
+                  up_k=(12, 11, 4, 4, 4), final="none", sample_rate=48000)
+BWE_HOP = 80
+BWE_NFFT = 512
+BWE_MELS = 64
+
+
+def stft_basis(n_fft: int) -> np.ndarray:
+    """[2 (n_fft/2+1), n_fft]: rows r = cos(2 pi r j / n) w(j), rows n/2+1+r =
+    -sin(2 pi r j / n) w(j), w the periodic Hann window (float32)."""
+    nf = n_fft // 2 + 1
+    j = np.arange(n_fft, dtype=np.float64)
+    win = 0.5 - 0.5 * np.cos(2.0 * np.pi * j / n_fft)
+    r = np.arange(nf, dtype=np.float64)[:, None]
+    ang = 2.0 * np.pi * r * j[None, :] / n_fft
+    return np.concatenate([np.cos(ang) * win, -np.sin(ang) * win]).astype(np.float32)
+
+
+def slaney_mel_basis(sr: float, n_fft: int, n_mels: int, fmin: float, fmax: float) -> np.ndarray:
+    """[n_mels, n_fft/2+1] triangular filters on the slaney mel scale with
+    unit-area normalisation (float32)."""
+    nf = n_fft // 2 + 1
+    f_log, m_log, step = 1000.0, 15.0, math.log(6.4) / 27.0
+
+    def hz2mel(f):
+        return np.where(f >= f_log, m_log + np.log(np.maximum(f, 1e-9) / f_log) / step, 3.0 * f / 200.0)
+
+    def mel2hz(m):
+        return np.where(m >= m_log, f_log * np.exp((m - m_log) * step), m * 200.0 / 3.0)
+
+    m0, m1 = hz2mel(np.array(fmin)), hz2mel(np.array(fmax))
+    pts = mel2hz(m0 + (m1 - m0) * np.arange(n_mels + 2) / (n_mels + 1))
+    freqs = sr * np.arange(nf) / n_fft
+    fb = np.zeros((n_mels, nf))
+    for m in range(n_mels):
+        lo, c, hi = pts[m], pts[m + 1], pts[m + 2]
+        up = (freqs - lo) / max(c - lo, 1e-12)
+        dn = (hi - freqs) / max(hi - c, 1e-12)
+        fb[m] = np.maximum(0.0, np.minimum(up, dn)) * (2.0 / (hi - lo))
+    return fb.astype(np.float32)
+
+
+def bwe_tensors(workload: int, spec: DecoderSpec = BWE) -> Dict[str, np.ndarray]:
+    t = decoder_tensors(spec, workload)
+    t["mel_stft.forward_basis"] = stft_basis(BWE_NFFT)
+    t["mel_stft.mel_basis"] = slaney_mel_basis(16000.0, BWE_NFFT, BWE_MELS, 0.0, 8000.0)
+    return t
+
+
+def workload7(T: int = 320000, B: int = 2, spec: DecoderSpec = BWE):
+    """The bandwidth-extension tail on a 16 kHz signal ~ N(0, 0.01) [B, T]."""
+    low = normal(7, "low16k", [B, T], 0.0, 0.01)
+    return low, bwe_tensors(7, spec)

@@ -18,7 +18,9 @@ Sources (cited by page and item, never by line):
   [LTX] docs.rs source page of ``cortiq_engine/ltxaudio.rs`` (cortiq-engine
         0.6.3) -- LTX-2.5 BigVGAN v2 vocoder, second source.
   The [H3] page also holds the MiniMax-Music-3 DAV decoder (items Snake,
-  DavUnit, DavStage, Music3Dav): the last section of this module.
+  DavUnit, DavStage, Music3Dav); the [LTX] page the bandwidth-extension tail
+  (items MelStft, hann_sinc_upsample, AudioStack::decode_from_mel).  Both
+  are sections at the end of this module.
 
 Readings taken where the pages are silent or disagree are listed in the
 function docstrings (and in the design notes of the repository).
@@ -479,3 +481,96 @@ def dav_decode(latent: np.ndarray, p: DavParams, record: bool = False) -> np.nda
     out[:, 0::2] = y[0::2]
     out[:, 1::2] = y[1::2]
     return out
+
+
+# --------------------------------------------------------------------------
+# LTX bandwidth-extension tail  ([LTX] MelStft, hann_sinc_upsample,
+#                               AudioStack::decode_from_mel)
+# --------------------------------------------------------------------------
+
+def mel_stft(x: np.ndarray, forward_basis: np.ndarray, mel_basis: np.ndarray,
+             hop: int) -> np.ndarray:
+    """[LTX] ``MelStft::forward``: causal log-mel of ``x [B, T]`` ->
+    ``[B, n_mels, frames]`` (mel-major, the layout the generator reads).
+
+    forward_basis ``[2 n_freqs, L]`` (rows r: real part, rows n_freqs + r:
+    imaginary part), mel_basis ``[n_mels, n_freqs]``.  The signal is padded
+    with L - hop zeros on the left (causal) and none on the right; frame f
+    starts at f hop of the padded signal; frames = (T + L - hop - L) // hop + 1.
+    Each frame: magnitude sqrt(re^2 + im^2) per frequency, the mel
+    projection, then ln(max(., 1e-5)).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    fb = np.asarray(forward_basis, dtype=np.float64)
+    mb = np.asarray(mel_basis, dtype=np.float64)
+    nf2, L = fb.shape
+    nf = nf2 // 2
+    left = max(L - hop, 0)
+    B, T = x.shape
+    padded = T + left
+    frames = (padded - L) // hop + 1 if padded >= L else 0
+    xp = np.concatenate([np.zeros((B, left)), x], axis=1)
+    out = np.empty((B, mb.shape[0], frames))
+    for f in range(frames):
+        seg = xp[:, f * hop: f * hop + L]            # [B, L]
+        z = seg @ fb.T                               # [B, 2 nf]
+        mag = np.sqrt(z[:, :nf] ** 2 + z[:, nf:] ** 2)
+        out[:, :, f] = np.log(np.maximum(mag @ mb.T, 1e-5))
+    return out
+
+
+def hann_sinc_filter(ratio: int, rolloff: float = 0.99, lpw: float = 6.0) -> np.ndarray:
+    """The x``ratio`` Hann-windowed sinc interpolator of [LTX]
+    ``hann_sinc_upsample``: k = 2 w ratio + 1 taps, w = ceil(lpw / rolloff);
+    tap i at t = (i / ratio - w) * rolloff: sinc(t) cos^2(pi clamp(t) / (2 lpw))
+    * rolloff / ratio (float64; the page rounds it to float32)."""
+    w = math.ceil(lpw / rolloff)
+    k = 2 * w * ratio + 1
+    i = np.arange(k, dtype=np.float64)
+    ta = (i / ratio - w) * rolloff
+    tc = np.clip(ta, -lpw, lpw)
+    win = np.cos(tc * math.pi / lpw / 2.0) ** 2
+    s = np.where(ta == 0.0, 1.0, np.sin(math.pi * ta) / np.where(ta == 0.0, 1.0, math.pi * ta))
+    return s * win * rolloff / ratio
+
+
+def hann_sinc_upsample(x: np.ndarray, ratio: int, filt: Optional[np.ndarray] = None) -> np.ndarray:
+    """[LTX] ``hann_sinc_upsample``: ``x [B, T]`` -> ``[B, ratio T]``.
+    Replicate-pad w samples each side, scale by ``ratio``, transposed FIR
+    with the filter at stride ``ratio``, keep [2 w ratio, full - (k - ratio))."""
+    x = np.asarray(x, dtype=np.float64)
+    if filt is None:
+        filt = hann_sinc_filter(ratio)
+    filt = np.asarray(filt, dtype=np.float64)
+    k = filt.shape[0]
+    w = (k - 1) // (2 * ratio)
+    B, T = x.shape
+    idx = np.clip(np.arange(-w, T + w), 0, T - 1)
+    xp = x[:, idx] * ratio
+    tp = T + 2 * w
+    full = (tp - 1) * ratio + k
+    acc = np.zeros((B, full))
+    for a in range(k):
+        acc[:, a: a + ratio * (tp - 1) + 1: ratio] += xp * filt[a]
+    lo, hi = 2 * w * ratio, full - (k - ratio)
+    return acc[:, lo:hi]
+
+
+def bwe_tail(low: np.ndarray, forward_basis: np.ndarray, mel_basis: np.ndarray, hop: int,
+             bwe: DecoderParams, ratio: int = 3, skip_filter: Optional[np.ndarray] = None
+             ) -> np.ndarray:
+    """[LTX] ``AudioStack::decode_from_mel`` after the first vocoder: the
+    16 kHz ``low [B, T]`` is zero-padded to whole hops, its causal log-mel
+    drives the bandwidth-extension generator (a BigVGAN whose output is a
+    residual, no final nonlinearity), the padded signal is upsampled x``ratio``
+    by the Hann-sinc interpolator, and the sum is clamped to [-1, 1] over
+    min(len(residual), len(skip), ratio T) samples."""
+    low = np.asarray(low, dtype=np.float64)
+    B, T = low.shape
+    rem = T % hop
+    padded = low if rem == 0 else np.concatenate([low, np.zeros((B, hop - rem))], axis=1)
+    m = mel_stft(padded, forward_basis, mel_basis, hop)
+    residual = decode(m, bwe)
+    skip = hann_sinc_upsample(padded, ratio, skip_filter)
+    t = min(residual.shape[-1], skip.shape[-1], T * ratio)
+    return np.clip(residual[:, :t] + skip[:, :t], -1.0, 1.0)
