@@ -34,6 +34,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-frames", type=int, default=120,
                     help="latent frames of the oracle's bounded CPU sample (one pass)")
+    ap.add_argument("--no-bwe", action="store_true",
+                    help="skip the LTX bandwidth-extension tail figure (workload 7)")
     ap.add_argument("--no-dav", action="store_true",
                     help="skip the Music-3 DAV decoder figure (workload 6)")
     ap.add_argument("--stream-tile", type=int, default=100,
@@ -194,6 +196,42 @@ def dav_figure(torch, avae, W, steps):
             "kernels_ms": {k: v["total_ms"] / n for k, v in top}}
 
 
+def bwe_figure(torch, avae, W, steps):
+    """The LTX bandwidth-extension tail on workload 7: 16 kHz [2,320000] ->
+    48 kHz [2,960000] (log-mel, generator, Hann-sinc skip, clamp)."""
+    dev = torch.device("cuda:0")
+    low, t = W.workload7()
+    dec = avae.BweDecoder(W.BWE, {k: torch.from_numpy(v).to(dev) for k, v in t.items()})
+    B, T = low.shape
+    ld = torch.from_numpy(low).to(dev)
+    ws = torch.empty(dec.workspace_bytes(B, T), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, 3 * T), dtype=torch.float32, device=dev)
+    for _ in range(2):
+        dec.decode(ld, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    n = max(steps // 2, 3)
+    e0.record(s)
+    for _ in range(n):
+        dec.decode(ld, out=out, workspace=ws)
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    avae.profile_begin(n * 300 + 64)
+    for _ in range(n):
+        dec.decode(ld, out=out, workspace=ws)
+    kernels, _ = avae.profile_end()
+    top = sorted(kernels.items(), key=lambda kv: -kv[1]["total_ms"])[:6]
+    return {"workload": f"ltx bandwidth extension, [{B},{T}] at 16 kHz -> [{B},{3 * T}] at 48 kHz",
+            "ms": ms, "samples_per_s": out.numel() / (ms / 1e3),
+            "x_realtime": (T / 16000.0) / (ms / 1e3),
+            "kernels_ms": {k: v["total_ms"] / n for k, v in top},
+            "mel_stft_ms": kernels.get("mel_stft_kernel", {}).get("total_ms", 0.0) / n,
+            "combine_ms": kernels.get("bwe_combine_kernel", {}).get("total_ms", 0.0) / n}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -276,6 +314,8 @@ def main():
                       for k, v in sorted(kernels.items(), key=lambda kv: -kv[1]["total_ms"])}
     if not args.no_dav:
         res["dav"] = dav_figure(torch, avae, W, args.steps)
+    if not args.no_bwe:
+        res["bwe"] = bwe_figure(torch, avae, W, args.steps)
     if args.stream_tile > 0:
         res["streaming"] = streaming(torch, dec, zd, out, args.stream_tile, args.steps)
     if args.pmc_calibration:

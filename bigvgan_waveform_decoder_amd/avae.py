@@ -81,6 +81,15 @@ class avae_dav_weights(ctypes.Structure):
     ]
 
 
+class avae_bwe_config(ctypes.Structure):
+    _fields_ = [("gen", avae_config), ("filter_len", c_int), ("hop", c_int), ("n_freqs", c_int),
+                ("n_mels", c_int), ("ratio", c_int)]
+
+
+class avae_bwe_weights(ctypes.Structure):
+    _fields_ = [("gen", avae_weights), ("forward_basis", P), ("mel_basis", P)]
+
+
 _lib = None
 
 
@@ -122,6 +131,20 @@ def lib() -> ctypes.CDLL:
     L.avae_bigvgan_decode.argtypes = [P, P, c_int, c_int, P, P, c_size_t, P]
     L.avae_bigvgan_decode_traced.restype = c_int
     L.avae_bigvgan_decode_traced.argtypes = [P, P, c_int, c_int, P, P, c_size_t, P, P]
+    L.avae_mel_stft.restype = c_int
+    L.avae_mel_stft.argtypes = [P, P, c_int, c_int, P, c_int, c_int, c_int, P, c_int, P]
+    L.avae_hann_sinc_upsample.restype = c_int
+    L.avae_hann_sinc_upsample.argtypes = [P, P, c_int, c_int, c_int, P]
+    L.avae_bwe_create.restype = c_int
+    L.avae_bwe_create.argtypes = [P, P, P]
+    L.avae_bwe_destroy.restype = None
+    L.avae_bwe_destroy.argtypes = [P]
+    L.avae_bwe_workspace_bytes.restype = c_size_t
+    L.avae_bwe_workspace_bytes.argtypes = [P, c_int, c_int]
+    L.avae_bwe_decode.restype = c_int
+    L.avae_bwe_decode.argtypes = [P, P, c_int, c_int, P, P, c_size_t, P]
+    L.avae_bwe_decode_traced.restype = c_int
+    L.avae_bwe_decode_traced.argtypes = [P, P, c_int, c_int, P, P, c_size_t, P, P, P]
     L.avae_snake.restype = c_int
     L.avae_snake.argtypes = [P, P, c_int, c_int, c_int, P, P]
     L.avae_dav_create.restype = c_int
@@ -333,6 +356,56 @@ def amp_block(x, K: int, dil: Sequence[int], w1: List, b1: List, w2: List, b2: L
     return out
 
 
+def _decoder_structs(spec, tensors: Dict[str, "object"]):
+    """avae_config and avae_weights of a BigVGAN decoder spec, weights named
+    as on the H3 page."""
+    cfg = avae_config()
+    cfg.c_in = spec.c_in
+    cfg.dec_in_ch = int(spec.dec_in)
+    cfg.has_latent_affine = 1 if spec.latent_affine else 0
+    cfg.k_pre, cfg.k_post = spec.k_pre, spec.k_post
+    ns = len(spec.rates)
+    if ns > AVAE_MAX_STAGES:
+        raise ValueError("too many stages")
+    cfg.n_stages = ns
+    for i, c in enumerate(spec.widths()):
+        cfg.ch[i] = c
+    for i, (r, k) in enumerate(zip(spec.rates, spec.up_k)):
+        cfg.rates[i], cfg.up_k[i] = r, k
+    nk = len(spec.rb_k)
+    cfg.n_kernels = nk
+    nd = len(spec.rb_d[0])
+    cfg.n_dil = nd
+    for j in range(nk):
+        cfg.rb_k[j] = spec.rb_k[j]
+        if len(spec.rb_d[j]) != nd:
+            raise ValueError("every AMP block needs the same number of dilations")
+        for q in range(nd):
+            cfg.rb_d[j][q] = spec.rb_d[j][q]
+    cfg.final_act = FINAL[spec.final]
+    t = tensors
+    g = lambda name: _dev(t[name], name) if name in t else None
+    w = avae_weights()
+    w.latent_mean, w.latent_std = g("latents_mean"), g("latents_std")
+    w.dec_in_w, w.dec_in_b = g("dec_in.weight"), g("dec_in.bias")
+    w.conv_pre_w, w.conv_pre_b = g("conv_pre.weight"), g("conv_pre.bias")
+    for i in range(ns):
+        w.up_w[i], w.up_b[i] = g(f"ups.{i}.weight"), g(f"ups.{i}.bias")
+        for j in range(nk):
+            p = f"resblocks.{i * nk + j}"
+            for q in range(nd):
+                w.w1[i][j][q] = g(f"{p}.convs1.{q}.weight")
+                w.b1[i][j][q] = g(f"{p}.convs1.{q}.bias")
+                w.w2[i][j][q] = g(f"{p}.convs2.{q}.weight")
+                w.b2[i][j][q] = g(f"{p}.convs2.{q}.bias")
+            for q in range(2 * nd):
+                w.act_la[i][j][q] = g(f"{p}.activations.{q}.act.alpha")
+                w.act_lb[i][j][q] = g(f"{p}.activations.{q}.act.beta")
+    w.post_la, w.post_lb = g("activation_post.act.alpha"), g("activation_post.act.beta")
+    w.conv_post_w, w.conv_post_b = g("conv_post.weight"), g("conv_post.bias")
+    return cfg, w
+
+
 class Decoder:
     """avae_decoder_create / avae_bigvgan_decode over device weight tensors
     named as on the H3 page (``conv_pre.weight``, ``ups.{i}.weight``,
@@ -340,52 +413,9 @@ class Decoder:
     ``resblocks.{..}.activations.{q}.act.alpha`` ...)."""
 
     def __init__(self, spec, tensors: Dict[str, "object"]):
-        cfg = avae_config()
-        cfg.c_in = spec.c_in
-        cfg.dec_in_ch = int(spec.dec_in)
-        cfg.has_latent_affine = 1 if spec.latent_affine else 0
-        cfg.k_pre, cfg.k_post = spec.k_pre, spec.k_post
-        ns = len(spec.rates)
-        if ns > AVAE_MAX_STAGES:
-            raise ValueError("too many stages")
-        cfg.n_stages = ns
-        for i, c in enumerate(spec.widths()):
-            cfg.ch[i] = c
-        for i, (r, k) in enumerate(zip(spec.rates, spec.up_k)):
-            cfg.rates[i], cfg.up_k[i] = r, k
-        nk = len(spec.rb_k)
-        cfg.n_kernels = nk
-        nd = len(spec.rb_d[0])
-        cfg.n_dil = nd
-        for j in range(nk):
-            cfg.rb_k[j] = spec.rb_k[j]
-            if len(spec.rb_d[j]) != nd:
-                raise ValueError("every AMP block needs the same number of dilations")
-            for q in range(nd):
-                cfg.rb_d[j][q] = spec.rb_d[j][q]
-        cfg.final_act = FINAL[spec.final]
+        cfg, w = _decoder_structs(spec, tensors)
         self.spec = spec
         self.cfg = cfg
-        t = tensors
-        g = lambda name: _dev(t[name], name) if name in t else None
-        w = avae_weights()
-        w.latent_mean, w.latent_std = g("latents_mean"), g("latents_std")
-        w.dec_in_w, w.dec_in_b = g("dec_in.weight"), g("dec_in.bias")
-        w.conv_pre_w, w.conv_pre_b = g("conv_pre.weight"), g("conv_pre.bias")
-        for i in range(ns):
-            w.up_w[i], w.up_b[i] = g(f"ups.{i}.weight"), g(f"ups.{i}.bias")
-            for j in range(nk):
-                p = f"resblocks.{i * nk + j}"
-                for q in range(nd):
-                    w.w1[i][j][q] = g(f"{p}.convs1.{q}.weight")
-                    w.b1[i][j][q] = g(f"{p}.convs1.{q}.bias")
-                    w.w2[i][j][q] = g(f"{p}.convs2.{q}.weight")
-                    w.b2[i][j][q] = g(f"{p}.convs2.{q}.bias")
-                for q in range(2 * nd):
-                    w.act_la[i][j][q] = g(f"{p}.activations.{q}.act.alpha")
-                    w.act_lb[i][j][q] = g(f"{p}.activations.{q}.act.beta")
-        w.post_la, w.post_lb = g("activation_post.act.alpha"), g("activation_post.act.beta")
-        w.conv_post_w, w.conv_post_b = g("conv_post.weight"), g("conv_post.bias")
         h = P()
         _check(lib().avae_decoder_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(h)))
         self._h = h
@@ -578,3 +608,86 @@ class DavDecoder:
                                             workspace.numel(), ctypes.addressof(arr),
                                             _stream(stream)))
         return out, stages
+
+
+def mel_stft(x, forward_basis, mel_basis, hop: int, out=None, stream=None):
+    """avae_mel_stft: x [B, T] -> causal log-mel [B, n_mels, T // hop]."""
+    torch = _torch()
+    B, T = x.shape
+    nf2, L = forward_basis.shape
+    n_mels, nf = mel_basis.shape
+    if nf2 != 2 * nf:
+        raise ValueError("forward_basis needs 2 n_freqs rows")
+    frames = T // hop
+    if out is None:
+        out = torch.empty((B, n_mels, frames), device=x.device, dtype=torch.float32)
+    _check(lib().avae_mel_stft(_dev(x, "x"), _dev(out, "out", (B, n_mels, frames)), B, T,
+                               _dev(forward_basis, "forward_basis"), nf, L, hop,
+                               _dev(mel_basis, "mel_basis"), n_mels, _stream(stream)))
+    return out
+
+
+def hann_sinc_upsample(x, ratio: int = 3, out=None, stream=None):
+    """avae_hann_sinc_upsample: x [B, T] -> [B, ratio T]."""
+    torch = _torch()
+    B, T = x.shape
+    if out is None:
+        out = torch.empty((B, ratio * T), device=x.device, dtype=torch.float32)
+    _check(lib().avae_hann_sinc_upsample(_dev(x, "x"), _dev(out, "out", (B, ratio * T)), B, T,
+                                         ratio, _stream(stream)))
+    return out
+
+
+class BweDecoder:
+    """avae_bwe_create / avae_bwe_decode: the bandwidth-extension tail, the
+    generator's weights named as for Decoder, the bases as
+    ``mel_stft.forward_basis`` [2 nf, L] and ``mel_stft.mel_basis`` [n_mels, nf]."""
+
+    def __init__(self, spec, tensors: Dict[str, "object"], hop: int = 80, ratio: int = 3):
+        gcfg, gw = _decoder_structs(spec, tensors)
+        fb, mb = tensors["mel_stft.forward_basis"], tensors["mel_stft.mel_basis"]
+        cfg = avae_bwe_config()
+        cfg.gen = gcfg
+        cfg.filter_len, cfg.hop, cfg.ratio = fb.shape[1], hop, ratio
+        cfg.n_mels, cfg.n_freqs = mb.shape
+        w = avae_bwe_weights()
+        w.gen = gw
+        w.forward_basis, w.mel_basis = _dev(fb, "forward_basis"), _dev(mb, "mel_basis")
+        self.spec, self.cfg = spec, cfg
+        h = P()
+        _check(lib().avae_bwe_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(h)))
+        self._h = h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h and _lib is not None:
+            _lib.avae_bwe_destroy(h)
+            self._h = None
+
+    def workspace_bytes(self, B: int, T: int) -> int:
+        return int(lib().avae_bwe_workspace_bytes(self._h, B, T))
+
+    def decode(self, low, out=None, workspace=None, stream=None, trace: bool = False):
+        """low [B, T] at the input rate -> [B, ratio T]; trace=True also
+        returns the log-mel and the generator's residual."""
+        torch = _torch()
+        B, T = low.shape
+        r, hop = self.cfg.ratio, self.cfg.hop
+        if out is None:
+            out = torch.empty((B, r * T), device=low.device, dtype=torch.float32)
+        if workspace is None:
+            workspace = torch.empty(self.workspace_bytes(B, T), dtype=torch.uint8,
+                                    device=low.device)
+        if not trace:
+            _check(lib().avae_bwe_decode(self._h, _dev(low, "low"), B, T,
+                                         _dev(out, "out", (B, r * T)), workspace.data_ptr(),
+                                         workspace.numel(), _stream(stream)))
+            return out
+        frames = -(-T // hop)
+        mel = torch.empty((B, self.cfg.n_mels, frames), device=low.device, dtype=torch.float32)
+        res = torch.empty((B, frames * hop * r), device=low.device, dtype=torch.float32)
+        _check(lib().avae_bwe_decode_traced(self._h, _dev(low, "low"), B, T,
+                                            _dev(out, "out", (B, r * T)), workspace.data_ptr(),
+                                            workspace.numel(), mel.data_ptr(), res.data_ptr(),
+                                            _stream(stream)))
+        return out, mel, res

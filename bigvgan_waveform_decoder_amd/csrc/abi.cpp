@@ -1024,3 +1024,213 @@ extern "C" int avae_dav_decode_traced(const avae_dav* dav, const float* latent, 
     return dav_decode_impl(dav, latent, B, frames, wave, workspace, ws_bytes, stage_out,
                            (hipStream_t)stream);
 }
+
+// =========================================================================
+// LTX bandwidth-extension tail
+// =========================================================================
+
+namespace {
+
+constexpr double kHannRolloff = 0.99;  // [LTX] hann_sinc_upsample
+constexpr double kHannZeros = 6.0;
+
+int check_mel_shape(int n_freqs, int filter_len, int hop, int n_mels) {
+    if (n_freqs < 1 || filter_len < 1 || hop < 1 || n_mels < 1)
+        return fail(AVAE_EINVAL, "mel: sizes must be >= 1");
+    if (filter_len < hop || filter_len % 32 != 0 || n_freqs > 384 || filter_len > 4096)
+        return fail(AVAE_ESHAPE, "mel: need filter_len >= hop, filter_len %% 32 == 0, "
+                                 "n_freqs <= 384, filter_len <= 4096");
+    return AVAE_OK;
+}
+
+std::vector<float> hann_taps(int ratio) {
+    const int k = avae::design_hann_sinc(ratio, kHannRolloff, kHannZeros, nullptr);
+    std::vector<double> d(k);
+    avae::design_hann_sinc(ratio, kHannRolloff, kHannZeros, d.data());
+    std::vector<float> f(k);
+    for (int i = 0; i < k; ++i) f[i] = (float)d[i];  // the page rounds its taps to float32
+    return f;
+}
+
+}  // namespace
+
+extern "C" int avae_mel_stft(const float* x, float* out, int B, int T, const float* forward_basis,
+                             int n_freqs, int filter_len, int hop, const float* mel_basis,
+                             int n_mels, void* stream) {
+    if (!x || !out || !forward_basis || !mel_basis)
+        return fail(AVAE_EINVAL, "avae_mel_stft: null pointer");
+    if (B < 1 || T < 1) return fail(AVAE_EINVAL, "avae_mel_stft: B, T must be >= 1");
+    int rc = check_mel_shape(n_freqs, filter_len, hop, n_mels);
+    if (rc) return rc;
+    const int frames = T / hop;
+    if (frames < 1) return fail(AVAE_ESHAPE, "avae_mel_stft: T < hop gives no frame");
+    avae::prof_set_phase(avae::kPhaseNone);
+    AVAE_TRY(avae::launch_mel_stft(x, out, B, T, frames, forward_basis, n_freqs, filter_len, hop,
+                                   mel_basis, n_mels, (hipStream_t)stream),
+             "avae_mel_stft launch");
+    return AVAE_OK;
+}
+
+extern "C" int avae_hann_sinc_upsample(const float* x, float* y, int B, int T, int ratio,
+                                       void* stream) {
+    if (!x || !y) return fail(AVAE_EINVAL, "avae_hann_sinc_upsample: null pointer");
+    if (B < 1 || T < 1 || ratio < 1 || ratio > 4)
+        return fail(AVAE_EINVAL, "avae_hann_sinc_upsample: B, T >= 1 and ratio in [1, 4]");
+    if ((long long)T * ratio > 0x7fffffffLL)
+        return fail(AVAE_ESHAPE, "avae_hann_sinc_upsample: output too long");
+    const std::vector<float> taps = hann_taps(ratio);
+    avae::prof_set_phase(avae::kPhaseNone);
+    AVAE_TRY(avae::launch_bwe_combine(x, nullptr, y, B, T, T, 0, T * ratio, ratio, taps.data(),
+                                      (int)taps.size(), 0, (hipStream_t)stream),
+             "avae_hann_sinc_upsample launch");
+    return AVAE_OK;
+}
+
+struct avae_bwe {
+    avae_bwe_config cfg;
+    avae_decoder* gen = nullptr;
+    void* blob = nullptr;  // forward_basis, mel_basis
+    const float* basis = nullptr;
+    const float* mel = nullptr;
+    std::vector<float> taps;
+    int device = 0;
+};
+
+namespace {
+
+struct BwePlan {
+    int frames, Tp;
+    long long Lres;
+    size_t mel_bytes, res_bytes, gen_bytes;
+    size_t total() const { return mel_bytes + res_bytes + gen_bytes; }
+};
+
+bool bwe_plan(const avae_bwe* bwe, int B, int T, BwePlan* p) {
+    const avae_bwe_config& c = bwe->cfg;
+    p->frames = (T + c.hop - 1) / c.hop;
+    p->Tp = p->frames * c.hop;
+    p->Lres = (long long)p->Tp * c.ratio;
+    if (p->Lres > 0x7fffffffLL) return false;
+    p->mel_bytes = round_up((size_t)B * c.n_mels * p->frames * sizeof(float), 256);
+    p->res_bytes = round_up((size_t)B * (size_t)p->Lres * sizeof(float), 256);
+    p->gen_bytes = avae_decoder_workspace_bytes(bwe->gen, B, p->frames);
+    return p->gen_bytes > 0;
+}
+
+int bwe_decode_impl(const avae_bwe* bwe, const float* low, int B, int T, float* out,
+                    void* workspace, size_t ws_bytes, float* mel_out, float* resid_out,
+                    hipStream_t s) {
+    if (!bwe || !low || !out) return fail(AVAE_EINVAL, "avae_bwe_decode: null argument");
+    if (B < 1 || T < 1) return fail(AVAE_EINVAL, "avae_bwe_decode: B, T must be >= 1");
+    const avae_bwe_config& c = bwe->cfg;
+    BwePlan p;
+    if (!bwe_plan(bwe, B, T, &p) || (long long)T * c.ratio > 0x7fffffffLL)
+        return fail(AVAE_ESHAPE, "avae_bwe_decode: length overflow");
+    if (!workspace || ws_bytes < p.total())
+        return fail(AVAE_EWORKSPACE, "avae_bwe_decode: workspace %zu bytes < %zu needed", ws_bytes,
+                    p.total());
+    char* ws = (char*)workspace;
+    float* mel = (float*)ws;
+    float* res = (float*)(ws + p.mel_bytes);
+    void* gws = ws + p.mel_bytes + p.res_bytes;
+    avae::prof_set_phase(avae::kPhaseNone);
+    AVAE_TRY(avae::launch_mel_stft(low, mel, B, T, p.frames, bwe->basis, c.n_freqs, c.filter_len,
+                                   c.hop, bwe->mel, c.n_mels, s),
+             "bwe mel");
+    if (mel_out)
+        AVAE_TRY(hipMemcpyAsync(mel_out, mel, (size_t)B * c.n_mels * p.frames * sizeof(float),
+                                hipMemcpyDeviceToDevice, s),
+                 "trace copy");
+    int rc = decode_impl(bwe->gen, mel, B, p.frames, res, gws, p.gen_bytes, nullptr, s);
+    if (rc) return rc;
+    if (resid_out)
+        AVAE_TRY(hipMemcpyAsync(resid_out, res, (size_t)B * p.Lres * sizeof(float),
+                                hipMemcpyDeviceToDevice, s),
+                 "trace copy");
+    avae::prof_set_phase(avae::kPhaseNone);
+    AVAE_TRY(avae::launch_bwe_combine(low, res, out, B, T, p.Tp, (int)p.Lres, T * c.ratio, c.ratio,
+                                      bwe->taps.data(), (int)bwe->taps.size(), 1, s),
+             "bwe combine");
+    return AVAE_OK;
+}
+
+}  // namespace
+
+extern "C" int avae_bwe_create(const avae_bwe_config* cfg, const avae_bwe_weights* w,
+                               avae_bwe** out) {
+    if (!cfg || !w || !out) return fail(AVAE_EINVAL, "avae_bwe_create: null argument");
+    *out = nullptr;
+    const avae_bwe_config& c = *cfg;
+    int rc = check_mel_shape(c.n_freqs, c.filter_len, c.hop, c.n_mels);
+    if (rc) return rc;
+    if (c.ratio < 1 || c.ratio > 4) return fail(AVAE_EINVAL, "avae_bwe_create: ratio in [1, 4]");
+    if (!w->forward_basis || !w->mel_basis)
+        return fail(AVAE_EINVAL, "avae_bwe_create: missing STFT or mel basis");
+    if (c.gen.c_in != c.n_mels || c.gen.dec_in_ch != 0 || c.gen.has_latent_affine)
+        return fail(AVAE_ESHAPE, "avae_bwe_create: the generator reads the n_mels log-mel directly");
+    rc = check_config(&c.gen);
+    if (rc) return rc;
+    long long T[AVAE_MAX_STAGES + 1];
+    if (stage_lengths(c.gen, 1, T) || T[c.gen.n_stages] != (long long)c.hop * c.ratio ||
+        stage_lengths(c.gen, 2, T) || T[c.gen.n_stages] != 2LL * c.hop * c.ratio)
+        return fail(AVAE_ESHAPE, "avae_bwe_create: the generator must give hop * ratio samples a frame");
+    avae_bwe* b = new (std::nothrow) avae_bwe();
+    if (!b) return fail(AVAE_ENOMEM, "avae_bwe_create: host allocation failed");
+    b->cfg = c;
+    b->taps = hann_taps(c.ratio);
+    rc = avae_decoder_create(&c.gen, &w->gen, &b->gen);
+    if (rc) {
+        delete b;
+        return rc;
+    }
+    const size_t nb = (size_t)2 * c.n_freqs * c.filter_len, nm = (size_t)c.n_mels * c.n_freqs;
+    const size_t bb = round_up(nb * sizeof(float), 256);
+    hipError_t e = hipGetDevice(&b->device);
+    if (e == hipSuccess) e = hipMalloc(&b->blob, bb + nm * sizeof(float));
+    if (e == hipSuccess) e = hipMemcpy(b->blob, w->forward_basis, nb * sizeof(float), hipMemcpyDefault);
+    if (e == hipSuccess)
+        e = hipMemcpy((char*)b->blob + bb, w->mel_basis, nm * sizeof(float), hipMemcpyDefault);
+    if (e != hipSuccess) {
+        if (b->blob) (void)hipFree(b->blob);
+        avae_decoder_destroy(b->gen);
+        delete b;
+        return hip_fail(e, "avae_bwe_create: basis copy");
+    }
+    b->basis = (const float*)b->blob;
+    b->mel = (const float*)((char*)b->blob + bb);
+    *out = b;
+    return AVAE_OK;
+}
+
+extern "C" void avae_bwe_destroy(avae_bwe* bwe) {
+    if (!bwe) return;
+    avae_decoder_destroy(bwe->gen);
+    if (bwe->blob) {
+        int cur = 0;
+        (void)hipGetDevice(&cur);
+        (void)hipSetDevice(bwe->device);
+        (void)hipFree(bwe->blob);
+        (void)hipSetDevice(cur);
+    }
+    delete bwe;
+}
+
+extern "C" size_t avae_bwe_workspace_bytes(const avae_bwe* bwe, int B, int T) {
+    if (!bwe || B < 1 || T < 1) return 0;
+    BwePlan p;
+    if (!bwe_plan(bwe, B, T, &p)) return 0;
+    return p.total();
+}
+
+extern "C" int avae_bwe_decode(const avae_bwe* bwe, const float* low, int B, int T, float* out,
+                               void* workspace, size_t ws_bytes, void* stream) {
+    return bwe_decode_impl(bwe, low, B, T, out, workspace, ws_bytes, nullptr, nullptr,
+                           (hipStream_t)stream);
+}
+
+extern "C" int avae_bwe_decode_traced(const avae_bwe* bwe, const float* low, int B, int T,
+                                      float* out, void* workspace, size_t ws_bytes,
+                                      float* mel_out, float* resid_out, void* stream) {
+    return bwe_decode_impl(bwe, low, B, T, out, workspace, ws_bytes, mel_out, resid_out,
+                           (hipStream_t)stream);
+}

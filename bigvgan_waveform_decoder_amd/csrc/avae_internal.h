@@ -43,6 +43,9 @@ void prof_post(hipStream_t s, const char* name, double flops, double bytes);
 
 // Host-side float64 Kaiser-sinc design (filter_design.cpp).
 void design_kaiser_sinc(double cutoff, double half_width, int taps, double* out);
+// Host-side float64 Hann-sinc interpolator taps; returns the tap count
+// (out may be null to query it).
+int design_hann_sinc(int ratio, double rolloff, double lpw, double* out);
 
 hipError_t launch_act1d(const float* x, float* y, int B, int C, int T,
                         const float* log_alpha, const float* log_beta,
@@ -85,6 +88,19 @@ hipError_t launch_amp_unit(const float* x, float* y, const float* wt1, const flo
                            const float* la2, const float* lb2, int B, int C, int T, int K,
                            int dilation, float out_scale, int accumulate, const ActTaps& taps,
                            hipStream_t stream);
+
+// Causal log-mel (bwe.hip): x [B, T] (zero beyond T) -> out [B, n_mels,
+// frames], frame f covering padded samples [f hop, f hop + L) with L - hop
+// zeros on the left; basis [2 nf, L], mel [n_mels, nf].
+hipError_t launch_mel_stft(const float* x, float* out, int B, int T, int frames,
+                           const float* basis, int nf, int L, int hop, const float* mel,
+                           int n_mels, hipStream_t stream);
+// out[b, t] (t < Lout) = [clamp](resid[b, t] + skip(t)), skip the x`ratio`
+// interpolation (k host taps) of x zero-extended from T to Tp samples and
+// replicate-padded; resid may be null (skip alone).
+hipError_t launch_bwe_combine(const float* x, const float* resid, float* out, int B, int T,
+                              int Tp, int Lres, int Lout, int ratio, const float* taps_host,
+                              int k, int do_clamp, hipStream_t stream);
 
 // y[b,c,t] = x[b,c,t] * scale[c] + shift[c]
 hipError_t launch_channel_affine(const float* x, float* y, const float* scale,

@@ -53,4 +53,24 @@ void design_kaiser_sinc(double cutoff, double half_width, int taps, double* out)
     for (int i = 0; i < taps; ++i) out[i] /= total;
 }
 
+// The x`ratio` Hann-windowed sinc interpolator of the LTX bandwidth
+// extension ([LTX] hann_sinc_upsample): w = ceil(lpw / rolloff) input samples
+// each side, k = 2 w ratio + 1 taps; tap i sits at t = (i/ratio - w) rolloff
+// and is sinc(t) cos^2(pi clamp(t, -lpw, lpw) / (2 lpw)) rolloff / ratio.
+// Returns k (out must hold it).
+int design_hann_sinc(int ratio, double rolloff, double lpw, double* out) {
+    const double pi = 3.14159265358979323846;
+    const int w = (int)std::ceil(lpw / rolloff);
+    const int k = 2 * w * ratio + 1;
+    if (!out) return k;
+    for (int i = 0; i < k; ++i) {
+        const double t = ((double)i / ratio - w) * rolloff;
+        const double tc = std::fmin(std::fmax(t, -lpw), lpw);
+        const double c = std::cos(tc * pi / lpw / 2.0);
+        const double sinc = (t == 0.0) ? 1.0 : std::sin(pi * t) / (pi * t);
+        out[i] = sinc * c * c * rolloff / ratio;
+    }
+    return k;
+}
+
 }  // namespace avae

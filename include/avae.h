@@ -327,6 +327,58 @@ int avae_dav_decode_traced(const avae_dav* dav, const float* latent, int B, int 
                            float* const* stage_out, void* stream);
 
 /*
+ * LTX bandwidth-extension tail ([LTX] page, items MelStft, hann_sinc_upsample,
+ * AudioStack::decode_from_mel).
+ *
+ * avae_mel_stft: causal log-mel of x [B, T] -> out [B, n_mels, frames] with
+ * frames = floor(T / hop): frame f is the STFT (as a product with
+ * forward_basis [2 n_freqs, filter_len]: rows r real, rows n_freqs + r
+ * imaginary) of samples [f hop - (filter_len - hop), f hop + hop) of x, zero
+ * outside [0, T); then sqrt(re^2 + im^2), the mel projection mel_basis
+ * [n_mels, n_freqs] and ln(max(., 1e-5)).  Needs filter_len >= hop,
+ * filter_len % 32 == 0, n_freqs <= 384 (ESHAPE).  Device pointers.
+ *
+ * avae_hann_sinc_upsample: y [B, ratio T] = the x`ratio` Hann-windowed sinc
+ * interpolation of x [B, T] (rolloff 0.99, 6 zero crossings: 2 w ratio + 1
+ * taps with w = 7, designed on the host in float64), replicate-padded at
+ * both ends.  ratio in [1, 4].
+ *
+ * avae_bwe_*: the whole tail.  The 16 kHz signal low [B, T] is zero-padded to
+ * Tp = ceil(T / hop) hop samples, its log-mel (Tp / hop frames) drives the
+ * extension generator (a BigVGAN decoder, cfg.gen / w.gen exactly as for
+ * avae_decoder_create, whose hop prod(rates) must equal hop * ratio and whose
+ * final_act is the caller's: the [LTX] page adds its output as a residual),
+ * and out [B, ratio T] = clamp(residual + hann_sinc_upsample(padded), -1, 1).
+ * avae_bwe_decode_traced also copies the log-mel [B, n_mels, Tp / hop] and
+ * the residual [B, Tp * ratio] where non-NULL.
+ */
+int avae_mel_stft(const float* x, float* out, int B, int T, const float* forward_basis,
+                  int n_freqs, int filter_len, int hop, const float* mel_basis, int n_mels,
+                  void* stream);
+int avae_hann_sinc_upsample(const float* x, float* y, int B, int T, int ratio, void* stream);
+
+typedef struct avae_bwe_config {
+    avae_config gen;
+    int filter_len, hop, n_freqs, n_mels, ratio;
+} avae_bwe_config;
+
+typedef struct avae_bwe_weights {
+    avae_weights gen;
+    const float *forward_basis, *mel_basis;
+} avae_bwe_weights;
+
+typedef struct avae_bwe avae_bwe;
+
+int avae_bwe_create(const avae_bwe_config* cfg, const avae_bwe_weights* w, avae_bwe** out);
+void avae_bwe_destroy(avae_bwe* bwe);
+size_t avae_bwe_workspace_bytes(const avae_bwe* bwe, int B, int T);
+int avae_bwe_decode(const avae_bwe* bwe, const float* low, int B, int T, float* out,
+                    void* workspace, size_t ws_bytes, void* stream);
+int avae_bwe_decode_traced(const avae_bwe* bwe, const float* low, int B, int T, float* out,
+                           void* workspace, size_t ws_bytes, float* mel_out, float* resid_out,
+                           void* stream);
+
+/*
  * Launch profiler, the device-side counterpart of the audio decoder's own
  * phase report ([H3] AVAE_TIME / avae_time_report, phases dec_in, conv_pre,
  * upsamples, resblocks, act_post, conv_post).  Between avae_profile_begin and
