@@ -98,3 +98,40 @@ def test_streaming_rejects_bad_arguments():
     assert L.avae_bigvgan_decode_streaming(None, fake, 1, 1, fake, 1, 0, fake, 16, None) == -1
     assert L.avae_decoder_streaming_workspace_bytes(None, 1, 1, 0) == 0
     assert L.avae_decoder_reach_frames(None, None) == -1
+
+
+def test_dav_bwe_and_tail_ops_reject_bad_arguments():
+    """The DAV decoder, the extension tail and their single ops check their
+    arguments before any device work (this runs where there is no GPU)."""
+    L = avae.lib()
+    fake = ctypes.c_void_p(0x1000)
+    assert L.avae_snake(None, fake, 1, 1, 1, fake, None) == -1
+    assert L.avae_snake(fake, fake, 0, 1, 1, fake, None) == -1
+    assert L.avae_mel_stft(fake, fake, 1, 800, fake, 257, 512, 80, None, 64, None) == -1
+    # filter shorter than the hop, and a filter length that is not a multiple of 32
+    assert L.avae_mel_stft(fake, fake, 1, 800, fake, 257, 64, 80, fake, 64, None) == -2
+    assert L.avae_mel_stft(fake, fake, 1, 800, fake, 257, 500, 80, fake, 64, None) == -2
+    assert L.avae_mel_stft(fake, fake, 1, 40, fake, 257, 512, 80, fake, 64, None) == -2
+    assert L.avae_hann_sinc_upsample(fake, fake, 1, 10, 0, None) == -1
+    assert L.avae_hann_sinc_upsample(fake, fake, 1, 10, 5, None) == -1
+    cfg = avae.avae_dav_config()
+    h = ctypes.c_void_p()
+    assert L.avae_dav_create(ctypes.byref(cfg), ctypes.byref(avae.avae_dav_weights()),
+                             ctypes.byref(h)) in (-1, -2)
+    assert not h.value
+    assert L.avae_dav_workspace_bytes(None, 1, 1) == 0
+    assert L.avae_dav_decode(None, fake, 1, 1, fake, fake, 16, None) == -1
+    bcfg = avae.avae_bwe_config()
+    assert L.avae_bwe_create(ctypes.byref(bcfg), ctypes.byref(avae.avae_bwe_weights()),
+                             ctypes.byref(h)) in (-1, -2)
+    assert L.avae_bwe_workspace_bytes(None, 1, 1) == 0
+    assert L.avae_bwe_decode(None, fake, 1, 1, fake, fake, 16, None) == -1
+
+
+def test_kernel_names_in_the_profiler_are_stable():
+    """bench.py's traffic lookup keys on the library's kernel names."""
+    import json
+    d = json.load(open(os.path.join(ROOT, "profiles", "pmc_traffic.json")))
+    for name, e in d["kernels"].items():
+        assert re.match(r"conv1d_pipe_kernel<\d+,\d+,\d+,\d+,\d+,\d+>$", name), name
+        assert os.path.exists(os.path.join(ROOT, e["source"]))
