@@ -127,6 +127,8 @@ def lib() -> ctypes.CDLL:
     L.avae_decoder_output_length.argtypes = [P, c_int, ctypes.POINTER(c_int)]
     L.avae_decoder_workspace_bytes.restype = c_size_t
     L.avae_decoder_workspace_bytes.argtypes = [P, c_int, c_int]
+    L.avae_decoder_set_concurrent.restype = c_int
+    L.avae_decoder_set_concurrent.argtypes = [P, c_int]
     L.avae_bigvgan_decode.restype = c_int
     L.avae_bigvgan_decode.argtypes = [P, P, c_int, c_int, P, P, c_size_t, P]
     L.avae_bigvgan_decode_traced.restype = c_int
@@ -433,6 +435,11 @@ class Decoder:
 
     def workspace_bytes(self, B: int, frames: int) -> int:
         return int(lib().avae_decoder_workspace_bytes(self._h, B, frames))
+
+    def set_concurrent(self, on: bool) -> None:
+        """Run a stage's AMP blocks overlapped on side streams (default) or
+        one after the other on the caller's stream."""
+        _check(lib().avae_decoder_set_concurrent(self._h, 1 if on else 0))
 
     def stage_shapes(self, B: int, frames: int):
         """Shapes of the traced intermediates (conv_pre, each stage, pre-final)."""

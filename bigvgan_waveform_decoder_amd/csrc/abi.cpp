@@ -294,6 +294,19 @@ struct avae_decoder {
     const float* pw1[AVAE_MAX_STAGES][AVAE_MAX_KERNELS][AVAE_MAX_DIL] = {};
     const float* pw2[AVAE_MAX_STAGES][AVAE_MAX_KERNELS][AVAE_MAX_DIL] = {};
     void* pblob = nullptr;
+    // The AMP blocks of a stage are independent (they all read the ConvT
+    // output): blocks 1.. run on side streams forked from and joined back to
+    // the caller's stream with events, so one block's last partial wave of
+    // workgroups overlaps the others' work.
+    // The side streams and events belong to the decoder, so the enqueue of
+    // one stage's fork .. join is held under `mu`: calls from several host
+    // threads stay correct (their side work queues up on the same streams).
+    hipStream_t side[AVAE_MAX_KERNELS - 1] = {};
+    hipEvent_t fork = nullptr;
+    hipEvent_t join[AVAE_MAX_KERNELS - 1] = {};
+    bool has_side = false;     // streams and events exist (n_kernels > 1)
+    bool concurrent = false;   // use them (avae_decoder_set_concurrent)
+    mutable std::mutex mu;
     int device = 0;
     ActTaps taps;
 };
@@ -507,20 +520,32 @@ extern "C" int avae_decoder_create(const avae_config* cfg, const avae_weights* w
             return hip_fail(e, "avae_decoder_create: weight packing");
         }
     }
+    // side streams and events for the concurrent MRF blocks (non-blocking:
+    // no implicit ordering with the null stream; default priority)
+    if (c.n_kernels > 1) {
+        bool ok = hipEventCreateWithFlags(&d->fork, hipEventDisableTiming) == hipSuccess;
+        for (int j = 0; ok && j < c.n_kernels - 1; ++j)
+            ok = hipStreamCreateWithFlags(&d->side[j], hipStreamNonBlocking) == hipSuccess &&
+                 hipEventCreateWithFlags(&d->join[j], hipEventDisableTiming) == hipSuccess;
+        d->has_side = d->concurrent = ok;
+    }
     *out = d;
     return AVAE_OK;
 }
 
 extern "C" void avae_decoder_destroy(avae_decoder* dec) {
     if (!dec) return;
-    if (dec->blob) {
-        int cur = 0;
-        (void)hipGetDevice(&cur);
-        (void)hipSetDevice(dec->device);
-        (void)hipFree(dec->blob);
-        if (dec->pblob) (void)hipFree(dec->pblob);
-        (void)hipSetDevice(cur);
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    (void)hipSetDevice(dec->device);
+    for (int j = 0; j < AVAE_MAX_KERNELS - 1; ++j) {
+        if (dec->side[j]) (void)hipStreamDestroy(dec->side[j]);
+        if (dec->join[j]) (void)hipEventDestroy(dec->join[j]);
     }
+    if (dec->fork) (void)hipEventDestroy(dec->fork);
+    if (dec->blob) (void)hipFree(dec->blob);
+    if (dec->pblob) (void)hipFree(dec->pblob);
+    (void)hipSetDevice(cur);
     delete dec;
 }
 
@@ -534,11 +559,30 @@ extern "C" int avae_decoder_output_length(const avae_decoder* dec, int frames, i
     return AVAE_OK;
 }
 
+namespace {
+// Workspace slots: M and X, then per AMP block its own three scratch slots
+// and (blocks after the first) its own output, when the blocks run
+// concurrently; M, X and one block's scratch otherwise.
+int decode_slots(const avae_decoder* dec) {
+    return dec->has_side ? 1 + 4 * dec->cfg.n_kernels : 5;
+}
+}  // namespace
+
+extern "C" int avae_decoder_set_concurrent(avae_decoder* dec, int on) {
+    if (!dec) return fail(AVAE_EINVAL, "avae_decoder_set_concurrent: null decoder");
+    if (on && !dec->has_side)
+        return fail(AVAE_EINVAL, "avae_decoder_set_concurrent: this decoder has %s",
+                    dec->cfg.n_kernels > 1 ? "no side streams (creation failed)"
+                                           : "a single AMP block per stage");
+    dec->concurrent = on != 0;
+    return AVAE_OK;
+}
+
 extern "C" size_t avae_decoder_workspace_bytes(const avae_decoder* dec, int B, int frames) {
     if (!dec || B < 1 || frames < 1) return 0;
     long long T[AVAE_MAX_STAGES + 1];
     if (stage_lengths(dec->cfg, frames, T)) return 0;
-    return 5 * decode_slot_bytes(dec->cfg, B, T);
+    return decode_slots(dec) * decode_slot_bytes(dec->cfg, B, T);
 }
 
 namespace {
@@ -553,9 +597,10 @@ int decode_impl(const avae_decoder* dec, const float* latent, int B, int frames,
     if (stage_lengths(c, frames, T))
         return fail(AVAE_ESHAPE, "avae_bigvgan_decode: length overflow");
     const size_t slot = decode_slot_bytes(c, B, T);
-    if (!workspace || ws_bytes < 5 * slot)
+    const size_t need = decode_slots(dec) * slot;
+    if (!workspace || ws_bytes < need)
         return fail(AVAE_EWORKSPACE, "avae_bigvgan_decode: workspace %zu bytes < %zu needed",
-                    ws_bytes, 5 * slot);
+                    ws_bytes, need);
     char* ws = (char*)workspace;
     float* M = (float*)(ws + 0 * slot);   // stage input/output (MRF accumulator)
     float* X = (float*)(ws + 1 * slot);   // ConvT output: every AMP block's input
@@ -600,13 +645,44 @@ int decode_impl(const avae_decoder* dec, const float* latent, int B, int frames,
                                        c.rates[i], pad, s),
                  "ConvTranspose1d");
         avae::prof_set_phase(avae::kPhaseResblocks);
-        for (int j = 0; j < c.n_kernels; ++j) {
-            const bool fused = dec->pw1[i][j][0] != nullptr;
-            int rc = run_amp(X, M, B, co, To, c.rb_k[j], c.n_dil, c.rb_d[j], w.w1[i][j],
-                             w.b1[i][j], w.w2[i][j], w.b2[i][j], w.act_la[i][j], w.act_lb[i][j],
-                             fused ? dec->pw1[i][j] : nullptr, fused ? dec->pw2[i][j] : nullptr,
-                             inv_nk, j > 0 ? 1 : 0, cur, t1, t2, dec->taps, s);
-            if (rc) return rc;
+        if (dec->concurrent) {
+            std::lock_guard<std::mutex> lk(dec->mu);
+            // fork: every block waits for the ConvT output X
+            AVAE_TRY(hipEventRecord(dec->fork, s), "fork event");
+            for (int k = 1; k < c.n_kernels; ++k)
+                AVAE_TRY(hipStreamWaitEvent(dec->side[k - 1], dec->fork, 0), "fork wait");
+            float* outs[AVAE_MAX_KERNELS] = {M};
+            for (int k = 1; k < c.n_kernels; ++k) outs[k] = (float*)(ws + (size_t)(1 + 3 * c.n_kernels + k) * slot);
+            for (int k = 0; k < c.n_kernels; ++k) {
+                hipStream_t sk = k == 0 ? s : dec->side[k - 1];
+                float* sc = (float*)(ws + (size_t)(2 + 3 * k) * slot);
+                float* s1 = (float*)(ws + (size_t)(3 + 3 * k) * slot);
+                float* s2 = (float*)(ws + (size_t)(4 + 3 * k) * slot);
+                const bool fused = dec->pw1[i][k][0] != nullptr;
+                int rc = run_amp(X, outs[k], B, co, To, c.rb_k[k], c.n_dil, c.rb_d[k], w.w1[i][k],
+                                 w.b1[i][k], w.w2[i][k], w.b2[i][k], w.act_la[i][k],
+                                 w.act_lb[i][k], fused ? dec->pw1[i][k] : nullptr,
+                                 fused ? dec->pw2[i][k] : nullptr, inv_nk, 0, sc, s1, s2,
+                                 dec->taps, sk);
+                if (rc) return rc;
+            }
+            // join, then M = block 0 + the others (each already scaled by 1/nk)
+            for (int k = 1; k < c.n_kernels; ++k) {
+                AVAE_TRY(hipEventRecord(dec->join[k - 1], dec->side[k - 1]), "join event");
+                AVAE_TRY(hipStreamWaitEvent(s, dec->join[k - 1], 0), "join wait");
+            }
+            AVAE_TRY(avae::launch_sum_into(M, outs + 1, c.n_kernels - 1, (size_t)B * co * To, s),
+                     "MRF sum");
+        } else {
+            for (int j = 0; j < c.n_kernels; ++j) {
+                const bool fused = dec->pw1[i][j][0] != nullptr;
+                int rc = run_amp(X, M, B, co, To, c.rb_k[j], c.n_dil, c.rb_d[j], w.w1[i][j],
+                                 w.b1[i][j], w.w2[i][j], w.b2[i][j], w.act_la[i][j],
+                                 w.act_lb[i][j], fused ? dec->pw1[i][j] : nullptr,
+                                 fused ? dec->pw2[i][j] : nullptr, inv_nk, j > 0 ? 1 : 0, cur,
+                                 t1, t2, dec->taps, s);
+                if (rc) return rc;
+            }
         }
         if (stage_out && stage_out[1 + i])
             AVAE_TRY(hipMemcpyAsync(stage_out[1 + i], M, (size_t)B * co * To * sizeof(float),
@@ -693,7 +769,7 @@ bool stream_plan(const avae_decoder* dec, int B, int tile_frames, int halo, Stre
     if (stage_lengths(c, (int)cf, T)) return false;
     p->crop_bytes = round_up((size_t)B * c.c_in * cf * sizeof(float), 256);
     p->wave_bytes = round_up((size_t)B * T[c.n_stages] * sizeof(float), 256);
-    p->dec_bytes = 5 * decode_slot_bytes(c, B, T);
+    p->dec_bytes = decode_slots(dec) * decode_slot_bytes(c, B, T);
     return true;
 }
 

@@ -102,6 +102,10 @@ hipError_t launch_bwe_combine(const float* x, const float* resid, float* out, in
                               int Tp, int Lres, int Lout, int ratio, const float* taps_host,
                               int k, int do_clamp, hipStream_t stream);
 
+// y[i] += x[0][i] + ... + x[n-1][i] for i < count (n <= 3): the MRF sum of
+// AMP blocks that ran concurrently into separate buffers.
+hipError_t launch_sum_into(float* y, float* const* x, int n, size_t count, hipStream_t stream);
+
 // y[b,c,t] = x[b,c,t] * scale[c] + shift[c]
 hipError_t launch_channel_affine(const float* x, float* y, const float* scale,
                                  const float* shift, int B, int C, int T, hipStream_t stream);

@@ -23,6 +23,7 @@
 // and B[l/16][l%16]; the 4 accumulator registers of lane l hold
 // D[4*(l/16) + r][l%16], r = 0..3.  Rows map to output channels and columns
 // to time, so consecutive lanes store consecutive samples.
+#include <algorithm>
 #include <string>
 
 #include "act_math.h"
@@ -990,6 +991,40 @@ hipError_t launch_conv_out1(const float* x, float* y, float* pre_final, const fl
     const hipError_t e = hipGetLastError();
     prof_post(stream, "conv_out1_kernel", 2.0 * B * Cin * (double)K * T,
               4.0 * ((double)B * Cin * T + (double)B * T * (pre_final ? 2 : 1) + (double)Cin * K));
+    return e;
+}
+
+__global__ __launch_bounds__(256) void sum_into_kernel(float* __restrict__ y, const float* __restrict__ a,
+                                                      const float* __restrict__ b,
+                                                      const float* __restrict__ c, size_t n4,
+                                                      int n) {
+    // float4 elements; the buffers are 256-byte aligned workspace slots
+    for (size_t i = blockIdx.x * (size_t)256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+        float4 v = reinterpret_cast<float4*>(y)[i];
+        const float4 p = reinterpret_cast<const float4*>(a)[i];
+        v.x += p.x; v.y += p.y; v.z += p.z; v.w += p.w;
+        if (n > 1) {
+            const float4 q = reinterpret_cast<const float4*>(b)[i];
+            v.x += q.x; v.y += q.y; v.z += q.z; v.w += q.w;
+        }
+        if (n > 2) {
+            const float4 q = reinterpret_cast<const float4*>(c)[i];
+            v.x += q.x; v.y += q.y; v.z += q.z; v.w += q.w;
+        }
+        reinterpret_cast<float4*>(y)[i] = v;
+    }
+}
+
+hipError_t launch_sum_into(float* y, float* const* x, int n, size_t count, hipStream_t stream) {
+    if (n < 1) return hipSuccess;
+    if (n > 3 || count % 4 != 0) return hipErrorInvalidValue;
+    const size_t n4 = count / 4;
+    const unsigned blocks = (unsigned)std::min<size_t>((n4 + 255) / 256, 8192);
+    prof_pre(stream);
+    hipLaunchKernelGGL(sum_into_kernel, dim3(blocks), dim3(256), 0, stream, y, x[0],
+                       n > 1 ? x[1] : nullptr, n > 2 ? x[2] : nullptr, n4, n);
+    const hipError_t e = hipGetLastError();
+    prof_post(stream, "sum_into_kernel", (double)n * count, 4.0 * (n + 2) * count);
     return e;
 }
 

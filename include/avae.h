@@ -206,14 +206,32 @@ void avae_decoder_destroy(avae_decoder* dec);
 int avae_decoder_output_length(const avae_decoder* dec, int frames, int* out_len);
 
 /* Workspace bytes avae_bigvgan_decode needs for B passes of `frames` frames
- * (0 on invalid arguments). */
+ * (0 on invalid arguments).  The figure does not depend on the concurrency
+ * setting below. */
 size_t avae_decoder_workspace_bytes(const avae_decoder* dec, int B, int frames);
+
+/*
+ * The AMP blocks of one multi-receptive-field stage ([H3] AudioVae::decode:
+ * the stage's AmpBlock outputs are summed, then scaled by 1/n_kernels) all
+ * read the same upsampled input and are independent of each other.  With `on` (the default when the config has
+ * more than one kernel size), blocks 1.. are enqueued on side streams the
+ * decoder owns, forked from the caller's stream after the upsampling and
+ * joined back to it (events) before their sum, so their kernels overlap on
+ * the GPU; with `on` = 0 every block runs on the caller's stream, one after
+ * the other.  The two settings compute the same sums in the same order up
+ * to the rounding of one multiply-add per block.  Takes effect for calls
+ * made after it returns; not to be called while another host thread decodes
+ * with this decoder.  Errors: EINVAL (null decoder, or `on` with a single
+ * kernel size or side streams that could not be created).
+ */
+int avae_decoder_set_concurrent(avae_decoder* dec, int on);
 
 /*
  * Decode: latent [B, c_in, frames] -> wave [B, L] float32, L from
  * avae_decoder_output_length; each row is an independent mono pass.
  * Concurrent calls on different streams are safe with separate workspaces
- * (the decoder is read-only here).
+ * (the weights are read-only here; the enqueue of a stage's concurrent AMP
+ * blocks on the decoder's side streams is serialized by a host mutex).
  * Errors: EINVAL, ESHAPE, EWORKSPACE, EHIP.
  */
 int avae_bigvgan_decode(const avae_decoder* dec, const float* latent, int B, int frames,

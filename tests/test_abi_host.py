@@ -90,6 +90,7 @@ def test_decoder_create_rejects_bad_config():
     assert not h.value
     assert L.avae_decoder_create(None, ctypes.byref(w), ctypes.byref(h)) == -1
     assert L.avae_decoder_workspace_bytes(None, 1, 1) == 0
+    assert L.avae_decoder_set_concurrent(None, 1) == -1
 
 
 def test_streaming_rejects_bad_arguments():

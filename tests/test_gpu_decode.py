@@ -85,6 +85,64 @@ def test_decode_batched_equals_single_and_deterministic():
     assert np.max(np.abs(a[0] - a[1])) > 0
 
 
+def test_decode_concurrent_blocks_match_serial():
+    """A stage's AMP blocks overlapped on the decoder's side streams give the
+    serial result at every stage boundary up to the rounding of the block
+    sum (one multiply-add per block, an ulp or so), which the later stages'
+    gain carries forward (1.3e-5 at the last boundary of this spec; bar
+    1e-4, ten times under the oracle bar), and repeat bit for bit."""
+    announce("decode concurrent vs serial AMP blocks")
+    spec = W.scaled_spec(W.H3, 128)
+    z = cuda(W.normal(4, "latent", [2, spec.c_in, 6]))
+    dec = avae.Decoder(spec, cuda_dict(W.decoder_tensors(spec, 4)))
+    wc, sc = dec.decode(z, trace=True)
+    wc2 = dec.decode(z)
+    np.testing.assert_array_equal(host(wc), host(wc2))
+    dec.set_concurrent(False)
+    _, ss = dec.decode(z, trace=True)
+    for i, (a, b) in enumerate(zip(sc, ss)):
+        assert rel_err(host(a), host(b)) <= 1e-4, i
+    dec.set_concurrent(True)
+    np.testing.assert_array_equal(host(dec.decode(z)), host(wc))
+
+
+def test_decode_from_two_host_threads():
+    """Two host threads decode with one decoder on their own streams and
+    workspaces at the same time; each gets the single-threaded result."""
+    import threading
+    announce("decode from two host threads")
+    spec = W.scaled_spec(W.H3, 128)
+    dec = avae.Decoder(spec, cuda_dict(W.decoder_tensors(spec, 4)))
+    zs = [cuda(W.normal(40 + r, "latent", [1, spec.c_in, 5])) for r in range(2)]
+    refs = [host(dec.decode(z)) for z in zs]
+    got = [[], []]
+    errs = []
+
+    def run(r):
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                ws = torch.empty(dec.workspace_bytes(1, 5), dtype=torch.uint8, device="cuda:0")
+                out = torch.empty((1, dec.output_length(5)), device="cuda:0")
+                for _ in range(4):
+                    dec.decode(zs[r], out=out, workspace=ws, stream=st)
+                    got[r].append(out.clone())
+            st.synchronize()
+        except Exception as e:  # reported by the main thread
+            errs.append(e)
+
+    th = [threading.Thread(target=run, args=(r,)) for r in range(2)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join(timeout=60)
+    assert not errs, errs
+    for r in range(2):
+        assert len(got[r]) == 4
+        for g in got[r]:
+            np.testing.assert_array_equal(host(g), refs[r])
+
+
 _FULL = {}
 
 
