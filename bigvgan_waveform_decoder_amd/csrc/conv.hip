@@ -51,6 +51,63 @@ __device__ __forceinline__ int floor_div(int a, int b) {
     return q;
 }
 
+// Conv1d epilogue for an MT x NTL grid of 16x16 accumulator tiles whose
+// top-left output is (o_base, t_base): bias, optional plain Snake, optional
+// residual, scale, optional accumulate.  Every input of the epilogue is
+// loaded before the first store: a store may alias the residual (the same
+// element, read and written by the same lane), so a load issued after a
+// store would wait for it, one memory latency per element.
+template <int MT, int NTL, bool SN>
+__device__ __forceinline__ void conv_epilogue(const f32x4 (&acc)[MT][NTL], float* y, int Cout,
+                                              int Tout, int b, int o_base, int t_base, int l16,
+                                              int g, const ConvEpilogue& ep) {
+    float* yb = y + (size_t)b * Cout * Tout;
+    const float* rb = ep.residual ? ep.residual + (size_t)b * Cout * Tout : nullptr;
+    float bias[MT][4], alpha[MT][4];
+    float res[MT][NTL][4], old[MT][NTL][4];
+#pragma unroll
+    for (int a = 0; a < MT; ++a)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int o = o_base + a * 16 + g * 4 + r;
+            bias[a][r] = (ep.bias && o < Cout) ? ep.bias[o] : 0.f;
+            alpha[a][r] = (SN && ep.snake_alpha && o < Cout) ? ep.snake_alpha[o] : 1.f;
+        }
+#pragma unroll
+    for (int a = 0; a < MT; ++a)
+#pragma unroll
+        for (int cc = 0; cc < NTL; ++cc) {
+            const int t = t_base + cc * 16 + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int o = o_base + a * 16 + g * 4 + r;
+                const bool ok = o < Cout && t < Tout;
+                const size_t idx = (size_t)o * Tout + t;
+                res[a][cc][r] = (rb && ok) ? rb[idx] : 0.f;
+                old[a][cc][r] = (ep.accumulate && ok) ? yb[idx] : 0.f;
+            }
+        }
+#pragma unroll
+    for (int a = 0; a < MT; ++a)
+#pragma unroll
+        for (int cc = 0; cc < NTL; ++cc) {
+            const int t = t_base + cc * 16 + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int o = o_base + a * 16 + g * 4 + r;
+                if (o < Cout && t < Tout) {
+                    float v = acc[a][cc][r];
+                    if (ep.bias) v += bias[a][r];
+                    if (SN && ep.snake_alpha) v = snake_plain(v, alpha[a][r]);
+                    if (rb) v += res[a][cc][r];
+                    v *= ep.out_scale;
+                    if (ep.accumulate) v += old[a][cc][r];
+                    yb[(size_t)o * Tout + t] = v;
+                }
+            }
+        }
+}
+
 // ------------------------------------------------------------------ Conv1d
 
 template <int BM, int BN, int WM, int WN, int KT>
@@ -150,29 +207,7 @@ __global__ __launch_bounds__(WM * WN * 64) void conv1d_mfma_kernel(
         __syncthreads();
     }
 
-    float* yb = y + (size_t)b * Cout * Tout;
-    const float* rb = ep.residual ? ep.residual + (size_t)b * Cout * Tout : nullptr;
-#pragma unroll
-    for (int a = 0; a < MT; ++a) {
-#pragma unroll
-        for (int c = 0; c < NTL; ++c) {
-            const int t = t0 + wn0 + c * 16 + l16;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int o = o0 + wm0 + a * 16 + g * 4 + r;
-                if (o < Cout && t < Tout) {
-                    const size_t idx = (size_t)o * Tout + t;
-                    float v = acc[a][c][r];
-                    if (ep.bias) v += ep.bias[o];
-                    if (ep.snake_alpha) v = snake_plain(v, ep.snake_alpha[o]);
-                    if (rb) v += rb[idx];
-                    v *= ep.out_scale;
-                    if (ep.accumulate) v += yb[idx];
-                    yb[idx] = v;
-                }
-            }
-        }
-    }
+    conv_epilogue<MT, NTL, true>(acc, y, Cout, Tout, b, o0 + wm0, t0 + wn0, l16, g, ep);
 }
 
 // Pipelined Conv1d for the decoder's shapes (K in {1,3,7,11}, dilation <= 5,
@@ -363,29 +398,7 @@ __global__ __launch_bounds__(WM * WN * 64, (pipe_min_waves<BM, BN, KT>())) void 
         }
     }
 
-    float* yb = y + (size_t)b * Cout * Tout;
-    const float* rb = ep.residual ? ep.residual + (size_t)b * Cout * Tout : nullptr;
-#pragma unroll
-    for (int a = 0; a < MT; ++a) {
-#pragma unroll
-        for (int cc = 0; cc < NTL; ++cc) {
-            const int t = t0 + wn0 + cc * 16 + l16;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int o = o0 + wm0 + a * 16 + g * 4 + r;
-                if (o < Cout && t < Tout) {
-                    const size_t idx = (size_t)o * Tout + t;
-                    float v = acc[a][cc][r];
-                    if (ep.bias) v += ep.bias[o];
-                    if (SN && ep.snake_alpha) v = snake_plain(v, ep.snake_alpha[o]);
-                    if (rb) v += rb[idx];
-                    v *= ep.out_scale;
-                    if (ep.accumulate) v += yb[idx];
-                    yb[idx] = v;
-                }
-            }
-        }
-    }
+    conv_epilogue<MT, NTL, SN>(acc, y, Cout, Tout, b, o0 + wm0, t0 + wn0, l16, g, ep);
 }
 
 struct ConvTile {
@@ -468,10 +481,206 @@ hipError_t run_conv1d_pipe(const float* x, float* y, const float* w, int B, int 
     return e;
 }
 
+// Conv1d with the weight tiles staged by LDS DMA (global_load_lds_dwordx4:
+// each lane's 16 bytes go straight from global memory to LDS, no registers,
+// no LDS store instructions) into two LDS buffers, so the next K chunk's
+// weights stream in during the whole MFMA work on the current chunk, with one
+// barrier per chunk.  The input window keeps the register path (its zero
+// padding at the sequence ends needs a select), double-buffered in LDS too.
+// Same GEMM, LDS layouts (padded weight rows), blocked accumulation and
+// epilogue as conv1d_pipe_kernel.  Cin must be a multiple of KC.
+template <int BM, int BN, int WM, int WN, int KT, int KC, int DM>
+__global__ __launch_bounds__(WM * WN * 64, 2) void conv1d_dma_kernel(
+    const float* __restrict__ x, float* y, const float* __restrict__ w, int Cin, int Cout,
+    int T, int Tout, int dil, int pad, int m_tiles, int n_tiles, int nblk, int flush,
+    ConvEpilogue ep) {
+    constexpr int NT = WM * WN * 64;
+    static_assert(NT == 256, "256 threads");
+    constexpr int kXLanes = NT / KC;  // lanes per staged input row
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int MT = WTM / 16, NTL = WTN / 16;
+    constexpr int WROW = KC * KT;                          // weight floats per row per chunk
+    constexpr int WS = (WROW % 8 == 0) ? WROW + 4 : WROW + 8;  // padded LDS row (floats)
+    constexpr int GR = WS / 4, GV = WROW / 4;              // 16-byte granules per row
+    constexpr int NI = (BM * GR + NT - 1) / NT;            // DMA instructions per thread
+    constexpr int WBUF = NI * NT * 4;                      // floats per weight buffer
+    constexpr int XW_MAX = BN + (KT - 1) * DM;
+    constexpr int XS = xs_stride_const(XW_MAX);
+    constexpr int X_PT = (XW_MAX + kXLanes - 1) / kXLanes;
+    static_assert(WROW % 4 == 0, "float4 weight rows");
+
+    // two buffers as separate arrays: the compiler then sees that the DMA
+    // into one cannot alias the LDS reads of the other, and does not wait
+    // for the DMA before the MFMA work of the current chunk
+    __shared__ __align__(16) float WsA[WBUF];
+    __shared__ __align__(16) float WsB[WBUF];
+    __shared__ __align__(16) float XsA[KC * XS];
+    __shared__ __align__(16) float XsB[KC * XS];
+
+    const int lid = xcd_remap(blockIdx.x, nblk);
+    const int mt_i = lid % m_tiles;
+    const int rest = lid / m_tiles;
+    const int nt_i = rest % n_tiles;
+    const int b = rest / n_tiles;
+    const int o0 = mt_i * BM, t0 = nt_i * BN;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm0 = (wid / WN) * WTM, wn0 = (wid % WN) * WTN;
+    const int l16 = lane & 15, g = lane >> 4;
+    const int xrow = tid / kXLanes, xcol = tid % kXLanes;
+
+    f32x4 acc[MT][NTL], part[MT][NTL];
+#pragma unroll
+    for (int a = 0; a < MT; ++a)
+#pragma unroll
+        for (int c = 0; c < NTL; ++c) {
+            acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+            part[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+
+    // Granule q = i*NT + tid of the padded [BM][GR] tile: row q / GR, float4
+    // q % GR of that row's chunk.  Pad granules, rows past the tile and rows
+    // past Cout fetch an in-bounds float4 of row o0 (never read, or masked by
+    // the epilogue).
+    int woff[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int q = i * NT + tid;
+        const int row = q / GR;
+        int f4 = q - row * GR;
+        int o = o0 + row;
+        if (row >= BM || o >= Cout) o = o0;
+        if (f4 >= GV) f4 = 0;
+        woff[i] = o * Cin * KT + 4 * f4;
+    }
+    const int xw = BN + (KT - 1) * dil;
+    const float* xb = x + (size_t)b * Cin * T;
+    const int nch = Cin / KC;
+    float xr[X_PT];
+
+    auto dma_w = [&](int ic0, float* wbuf) {
+        const float* wc = w + (size_t)ic0 * KT;
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            // (void pointers: without the casts the host pass of this
+            // kernel fails silently and its launch stub goes missing)
+            __builtin_amdgcn_global_load_lds((const void*)(wc + woff[i]),
+                                             (void*)(wbuf + (i * NT + wid * 64) * 4), 16, 0, 0);
+    };
+    auto gx = [&](int ic0) {
+        const float* xrowp = xb + (size_t)(ic0 + xrow) * T;
+#pragma unroll
+        for (int r = 0; r < X_PT; ++r) {
+            const int u = xcol + r * kXLanes;
+            const int t = t0 - pad + u;
+            float v = 0.f;
+            if (u < xw && t >= 0 && t < T) v = xrowp[t];
+            xr[r] = v;
+        }
+    };
+    auto sx = [&](float* xbuf) {
+#pragma unroll
+        for (int r = 0; r < X_PT; ++r) {
+            const int u = xcol + r * kXLanes;
+            if (u < xw) xbuf[xrow * XS + u] = xr[r];
+        }
+    };
+    // one chunk: start staging chunk c+1 into (Wn, Xn), MFMA work on chunk c
+    // from (Wc, Xc), store the input window, barrier
+    auto step = [&](int c, const float* Wc, const float* Xc, float* Wn, float* Xn) {
+        if (c + 1 < nch) {
+            dma_w((c + 1) * KC, Wn);
+            gx((c + 1) * KC);
+        }
+        constexpr int kTapUnroll = BM >= 48 ? 4 : 1;
+#pragma unroll kTapUnroll
+        for (int j = 0; j < KT; ++j) {
+#pragma unroll
+            for (int kk = 0; kk < KC / 4; ++kk) {
+                float av[MT], bv[NTL];
+#pragma unroll
+                for (int a = 0; a < MT; ++a)
+                    av[a] = Wc[(wm0 + a * 16 + l16) * WS + (kk * 4 + g) * KT + j];
+#pragma unroll
+                for (int cc = 0; cc < NTL; ++cc)
+                    bv[cc] = Xc[(kk * 4 + g) * XS + wn0 + cc * 16 + l16 + j * dil];
+#pragma unroll
+                for (int a = 0; a < MT; ++a)
+#pragma unroll
+                    for (int cc = 0; cc < NTL; ++cc)
+                        part[a][cc] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a], bv[cc],
+                                                                           part[a][cc], 0, 0, 0);
+            }
+        }
+        if ((c + 1) % flush == 0 || c + 1 == nch) {
+#pragma unroll
+            for (int a = 0; a < MT; ++a)
+#pragma unroll
+                for (int cc = 0; cc < NTL; ++cc) {
+                    acc[a][cc] += part[a][cc];
+                    part[a][cc] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+        }
+        if (c + 1 < nch) sx(Xn);
+        // the barrier also waits for this wave's DMA of chunk c+1
+        __syncthreads();
+    };
+
+    dma_w(0, WsA);
+    gx(0);
+    sx(XsA);
+    __syncthreads();
+    for (int c = 0; c < nch; c += 2) {
+        step(c, WsA, XsA, WsB, XsB);
+        if (c + 1 < nch) step(c + 1, WsB, XsB, WsA, XsA);
+    }
+
+    conv_epilogue<MT, NTL, false>(acc, y, Cout, Tout, b, o0 + wm0, t0 + wn0, l16, g, ep);
+}
+
+template <int BM, int BN, int WM, int WN, int KT>
+hipError_t run_conv1d_dma(const float* x, float* y, const float* w, int B, int Cin, int Cout,
+                          int T, int Tout, int dil, int pad, const ConvEpilogue& ep,
+                          hipStream_t stream) {
+    constexpr int KC = KT <= 3 ? 16 : 8;
+    const int m_tiles = (Cout + BM - 1) / BM;
+    const int n_tiles = (Tout + BN - 1) / BN;
+    const long long nblk = (long long)m_tiles * n_tiles * B;
+    if (nblk > 0x7fffffffLL || Cin % KC != 0 || (long long)Cout * Cin * KT >= (1LL << 31))
+        return hipErrorInvalidValue;
+    const int flush = (24 / ((KC / 4) * KT)) > 0 ? 24 / ((KC / 4) * KT) : 1;
+    static const std::string name = "conv1d_dma_kernel<" + std::to_string(BM) + "," +
+                                    std::to_string(BN) + "," + std::to_string(WM) + "," +
+                                    std::to_string(WN) + "," + std::to_string(KT) + "," +
+                                    std::to_string(KC) + ">";
+    prof_pre(stream);
+    hipLaunchKernelGGL((conv1d_dma_kernel<BM, BN, WM, WN, KT, KC, kDilMax>), dim3((unsigned)nblk),
+                       dim3(WM * WN * 64), 0, stream, x, y, w, Cin, Cout, T, Tout, dil, pad,
+                       m_tiles, n_tiles, (int)nblk, flush, ep);
+    const hipError_t e = hipGetLastError();
+    const double out_n = (double)B * Cout * Tout;
+    prof_post(stream, name.c_str(), 2.0 * out_n * Cin * KT,
+              4.0 * ((double)B * Cin * T + out_n * (1 + (ep.residual ? 1 : 0) + ep.accumulate) +
+                     (double)Cout * Cin * KT));
+    return e;
+}
+
 template <int BM, int BN, int WM, int WN>
 hipError_t dispatch_pipe(const float* x, float* y, const float* w, int B, int Cin, int Cout,
                          int T, int Tout, int K, int dil, int pad, const ConvEpilogue& ep,
                          hipStream_t stream) {
+    if constexpr (BM == 64) {
+      if (!ep.in_alpha && !ep.snake_alpha && dil <= kDilMax &&
+          Cin % (K <= 3 ? 16 : 8) == 0 && (long long)Cout * Cin * K < (1LL << 31)) {
+        switch (K) {
+            case 1: return run_conv1d_dma<BM, BN, WM, WN, 1>(x, y, w, B, Cin, Cout, T, Tout, dil, pad, ep, stream);
+            case 3: return run_conv1d_dma<BM, BN, WM, WN, 3>(x, y, w, B, Cin, Cout, T, Tout, dil, pad, ep, stream);
+            case 7: return run_conv1d_dma<BM, BN, WM, WN, 7>(x, y, w, B, Cin, Cout, T, Tout, dil, pad, ep, stream);
+            default: return run_conv1d_dma<BM, BN, WM, WN, 11>(x, y, w, B, Cin, Cout, T, Tout, dil, pad, ep, stream);
+        }
+      }
+    }
     switch (K) {
         case 1: return run_conv1d_pipe<BM, BN, WM, WN, 1>(x, y, w, B, Cin, Cout, T, Tout, dil, pad, ep, stream);
         case 3: return run_conv1d_pipe<BM, BN, WM, WN, 3>(x, y, w, B, Cin, Cout, T, Tout, dil, pad, ep, stream);
@@ -773,6 +982,14 @@ __global__ __launch_bounds__(WM * WN * 64) void convtr1d_poly_kernel(
     }
 
     float* yb = y + (size_t)b * Cout * Tout;
+    // bias loaded before the first store (a store could alias it, which
+    // would make every later load wait for it)
+    float bv[4];
+#pragma unroll
+    for (int ri = 0; ri < 4; ++ri) {
+        const int o = o0 + wm * 16 + g * 4 + ri;
+        bv[ri] = (bias && o < Cout) ? bias[o] : 0.f;
+    }
 #pragma unroll
     for (int r = 0; r < S; ++r) {
 #pragma unroll
@@ -784,7 +1001,7 @@ __global__ __launch_bounds__(WM * WN * 64) void convtr1d_poly_kernel(
                 const int o = o0 + wm * 16 + g * 4 + ri;
                 if (o < Cout && t >= 0 && t < Tout) {
                     float v = acc[r][cc][ri];
-                    if (bias) v += bias[o];
+                    if (bias) v += bv[ri];
                     yb[(size_t)o * Tout + t] = v;
                 }
             }

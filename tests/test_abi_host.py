@@ -134,5 +134,5 @@ def test_kernel_names_in_the_profiler_are_stable():
     import json
     d = json.load(open(os.path.join(ROOT, "profiles", "pmc_traffic.json")))
     for name, e in d["kernels"].items():
-        assert re.match(r"conv1d_pipe_kernel<\d+,\d+,\d+,\d+,\d+,\d+>$", name), name
+        assert re.match(r"conv1d_(pipe|dma)_kernel<\d+,\d+,\d+,\d+,\d+,\d+>$", name), name
         assert os.path.exists(os.path.join(ROOT, e["source"]))
