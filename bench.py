@@ -339,7 +339,7 @@ def main():
             "avg_launch_us": avg * 1e6,
             "achieved": k["flops"] / k["launches"] / avg / 1e12
             if res["roofline"]["unit"] == "TFLOP/s" else k["bytes"] / k["launches"] / avg / 1e9}
-    acts = [v for k, v in kernels.items() if k.startswith("act1d")]
+    acts = [v for k, v in iso.items() if k.startswith("act1d")]
     if acts:
         ab = sum(v["bytes"] for v in acts)
         at = sum(v["total_ms"] for v in acts)

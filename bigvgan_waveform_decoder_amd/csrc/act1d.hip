@@ -80,28 +80,27 @@ __device__ __forceinline__ void load12(const float* p, float* w) {
     w[8] = c.x; w[9] = c.y; w[10] = c.z; w[11] = c.w;
 }
 
-struct XPrefetch {
-    float4 a, b, c;
-};
-
-// Loads the interior tile's input window x[t0-8 .. t0+kTile+8) (16-byte
-// aligned) into registers: two float4 per thread plus four for the tail.
+// The interior tile's input window x[t0-8 .. t0+kTile+8) (16-byte aligned)
+// is two float4 per thread plus four for the tail, held in registers
+// between the load and the LDS store so that its latency overlaps the
+// previous tile's compute.  (Plain register variables: passed as a struct
+// by reference, the window was kept in scratch memory and every prefetch
+// waited for its load.)
 __device__ __forceinline__ void act1d_interior_load(const float* __restrict__ xrow, int t0,
-                                                    XPrefetch& p) {
+                                                    float4& a, float4& b, float4& c) {
     const int tid = threadIdx.x;
     const float4* src = reinterpret_cast<const float4*>(xrow + t0 - 8);
-    p.a = src[tid];
-    p.b = src[tid + kThreads];
-    p.c = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (tid < 4) p.c = src[tid + 2 * kThreads];
+    a = src[tid];
+    b = src[tid + kThreads];
+    c = (tid < 4) ? src[tid + 2 * kThreads] : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-__device__ __forceinline__ void act1d_interior_stage(const XPrefetch& p, float* xs) {
+__device__ __forceinline__ void act1d_interior_stage(float4 a, float4 b, float4 c, float* xs) {
     const int tid = threadIdx.x;
     float4* dst = reinterpret_cast<float4*>(xs);
-    dst[tid] = p.a;
-    dst[tid + kThreads] = p.b;
-    if (tid < 4) dst[tid + 2 * kThreads] = p.c;
+    dst[tid] = a;
+    dst[tid + kThreads] = b;
+    if (tid < 4) dst[tid + 2 * kThreads] = c;
 }
 
 // Interior tile compute (input already staged in xs): every output exists
@@ -235,11 +234,11 @@ __global__ __launch_bounds__(kThreads) void act1d_kernel(
     const int last = min(first + per_block, total);
     auto interior = [&](int t0) { return vec_ok && t0 >= 8 && t0 + kTile + 8 <= T; };
 
-    XPrefetch pf;
+    float4 pa = make_float4(0.f, 0.f, 0.f, 0.f), pb = pa, pc = pa;
     {
         const int row = first / tiles;
         const int t0 = (first - row * tiles) * kTile;
-        if (interior(t0)) act1d_interior_load(x + (size_t)row * T, t0, pf);
+        if (interior(t0)) act1d_interior_load(x + (size_t)row * T, t0, pa, pb, pc);
     }
     int cur_c = -1;
     float alpha_rev = 0.f, inv_beta = 0.f;
@@ -255,11 +254,11 @@ __global__ __launch_bounds__(kThreads) void act1d_kernel(
         const size_t base = (size_t)row * (size_t)T;
         if (id > first) __syncthreads();  // previous tile done with xs, se, so
         if (interior(t0)) {
-            act1d_interior_stage(pf, xs);
+            act1d_interior_stage(pa, pb, pc, xs);
             if (id + 1 < last) {
                 const int nrow = (id + 1) / tiles;
                 const int nt0 = (id + 1 - nrow * tiles) * kTile;
-                if (interior(nt0)) act1d_interior_load(x + (size_t)nrow * T, nt0, pf);
+                if (interior(nt0)) act1d_interior_load(x + (size_t)nrow * T, nt0, pa, pb, pc);
             }
             __syncthreads();
             act1d_interior_compute(y + base, t0, alpha_rev, inv_beta, taps, xs, se, so);
@@ -267,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void act1d_kernel(
             if (id + 1 < last) {
                 const int nrow = (id + 1) / tiles;
                 const int nt0 = (id + 1 - nrow * tiles) * kTile;
-                if (interior(nt0)) act1d_interior_load(x + (size_t)nrow * T, nt0, pf);
+                if (interior(nt0)) act1d_interior_load(x + (size_t)nrow * T, nt0, pa, pb, pc);
             }
             act1d_tile_edge(x + base, y + base, T, t0, alpha_rev, inv_beta, taps, xs, se, so);
         }

@@ -489,6 +489,9 @@ hipError_t run_conv1d_pipe(const float* x, float* y, const float* w, int B, int 
 // padding at the sequence ends needs a select), double-buffered in LDS too.
 // Same GEMM, LDS layouts (padded weight rows), blocked accumulation and
 // epilogue as conv1d_pipe_kernel.  Cin must be a multiple of KC.
+// (Used for the 64-row tiles.  On the 96- and 48-row tiles it measured
+// slower than the register-prefetch kernel for 11 taps and within a few
+// percent either way otherwise, so those keep conv1d_pipe_kernel.)
 template <int BM, int BN, int WM, int WN, int KT, int KC, int DM>
 __global__ __launch_bounds__(WM * WN * 64, 2) void conv1d_dma_kernel(
     const float* __restrict__ x, float* y, const float* __restrict__ w, int Cin, int Cout,
@@ -502,8 +505,9 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void conv1d_dma_kernel(
     constexpr int WROW = KC * KT;                          // weight floats per row per chunk
     constexpr int WS = (WROW % 8 == 0) ? WROW + 4 : WROW + 8;  // padded LDS row (floats)
     constexpr int GR = WS / 4, GV = WROW / 4;              // 16-byte granules per row
-    constexpr int NI = (BM * GR + NT - 1) / NT;            // DMA instructions per thread
-    constexpr int WBUF = NI * NT * 4;                      // floats per weight buffer
+    constexpr int NG = BM * GR;                            // granules per weight buffer
+    constexpr int NI = (NG + NT - 1) / NT;                 // DMA instructions per thread
+    constexpr int WBUF = NG * 4;                           // floats per weight buffer
     constexpr int XW_MAX = BN + (KT - 1) * DM;
     constexpr int XS = xs_stride_const(XW_MAX);
     constexpr int X_PT = (XW_MAX + kXLanes - 1) / kXLanes;
@@ -540,9 +544,9 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void conv1d_dma_kernel(
         }
 
     // Granule q = i*NT + tid of the padded [BM][GR] tile: row q / GR, float4
-    // q % GR of that row's chunk.  Pad granules, rows past the tile and rows
-    // past Cout fetch an in-bounds float4 of row o0 (never read, or masked by
-    // the epilogue).
+    // q % GR of that row's chunk.  Pad granules and rows past Cout fetch an
+    // in-bounds float4 of row o0 (never read, or masked by the epilogue);
+    // lanes past the tile (q >= NG, last instruction only) issue no DMA.
     int woff[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -563,10 +567,12 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void conv1d_dma_kernel(
         const float* wc = w + (size_t)ic0 * KT;
 #pragma unroll
         for (int i = 0; i < NI; ++i)
-            // (void pointers: without the casts the host pass of this
-            // kernel fails silently and its launch stub goes missing)
-            __builtin_amdgcn_global_load_lds((const void*)(wc + woff[i]),
-                                             (void*)(wbuf + (i * NT + wid * 64) * 4), 16, 0, 0);
+            if ((i + 1) * NT <= NG || i * NT + tid < NG)
+                // (void pointers: without the casts the host pass of this
+                // kernel fails silently and its launch stub goes missing)
+                __builtin_amdgcn_global_load_lds((const void*)(wc + woff[i]),
+                                                 (void*)(wbuf + (i * NT + wid * 64) * 4), 16, 0,
+                                                 0);
     };
     auto gx = [&](int ic0) {
         const float* xrowp = xb + (size_t)(ic0 + xrow) * T;
