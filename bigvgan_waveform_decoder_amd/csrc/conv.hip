@@ -492,7 +492,7 @@ hipError_t run_conv1d_pipe(const float* x, float* y, const float* w, int B, int 
 // (Used for the 64-row tiles.  On the 96- and 48-row tiles it measured
 // slower than the register-prefetch kernel for 11 taps and within a few
 // percent either way otherwise, so those keep conv1d_pipe_kernel.)
-template <int BM, int BN, int WM, int WN, int KT, int KC, int DM>
+template <int BM, int BN, int WM, int WN, int KT, int KC, int DM, bool SN>
 __global__ __launch_bounds__(WM * WN * 64, 2) void conv1d_dma_kernel(
     const float* __restrict__ x, float* y, const float* __restrict__ w, int Cin, int Cout,
     int T, int Tout, int dil, int pad, int m_tiles, int n_tiles, int nblk, int flush,
@@ -562,6 +562,7 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void conv1d_dma_kernel(
     const float* xb = x + (size_t)b * Cin * T;
     const int nch = Cin / KC;
     float xr[X_PT];
+    float xa = 1.f;  // Snake alpha of this thread's staged input row
 
     auto dma_w = [&](int ic0, float* wbuf) {
         const float* wc = w + (size_t)ic0 * KT;
@@ -576,6 +577,7 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void conv1d_dma_kernel(
     };
     auto gx = [&](int ic0) {
         const float* xrowp = xb + (size_t)(ic0 + xrow) * T;
+        if (SN && ep.in_alpha) xa = ep.in_alpha[ic0 + xrow];
 #pragma unroll
         for (int r = 0; r < X_PT; ++r) {
             const int u = xcol + r * kXLanes;
@@ -586,6 +588,12 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void conv1d_dma_kernel(
         }
     };
     auto sx = [&](float* xbuf) {
+        if (SN && ep.in_alpha) {
+            // plain Snake of the input as staged (zero padding stays zero)
+            const float arev = xa * 0.15915494309189535f, inv = 1.0f / (xa + 1e-9f);
+#pragma unroll
+            for (int r = 0; r < X_PT; ++r) xr[r] = snake_beta(xr[r], arev, inv);
+        }
 #pragma unroll
         for (int r = 0; r < X_PT; ++r) {
             const int u = xcol + r * kXLanes;
@@ -642,10 +650,10 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void conv1d_dma_kernel(
         if (c + 1 < nch) step(c + 1, WsB, XsB, WsA, XsA);
     }
 
-    conv_epilogue<MT, NTL, false>(acc, y, Cout, Tout, b, o0 + wm0, t0 + wn0, l16, g, ep);
+    conv_epilogue<MT, NTL, SN>(acc, y, Cout, Tout, b, o0 + wm0, t0 + wn0, l16, g, ep);
 }
 
-template <int BM, int BN, int WM, int WN, int KT>
+template <int BM, int BN, int WM, int WN, int KT, int DM = kDilMax, bool SN = false>
 hipError_t run_conv1d_dma(const float* x, float* y, const float* w, int B, int Cin, int Cout,
                           int T, int Tout, int dil, int pad, const ConvEpilogue& ep,
                           hipStream_t stream) {
@@ -659,9 +667,11 @@ hipError_t run_conv1d_dma(const float* x, float* y, const float* w, int B, int C
     static const std::string name = "conv1d_dma_kernel<" + std::to_string(BM) + "," +
                                     std::to_string(BN) + "," + std::to_string(WM) + "," +
                                     std::to_string(WN) + "," + std::to_string(KT) + "," +
-                                    std::to_string(KC) + ">";
+                                    std::to_string(KC) +
+                                    (DM == kDilMax ? std::string() : ",d" + std::to_string(DM)) +
+                                    (SN ? ",snake" : "") + ">";
     prof_pre(stream);
-    hipLaunchKernelGGL((conv1d_dma_kernel<BM, BN, WM, WN, KT, KC, kDilMax>), dim3((unsigned)nblk),
+    hipLaunchKernelGGL((conv1d_dma_kernel<BM, BN, WM, WN, KT, KC, DM, SN>), dim3((unsigned)nblk),
                        dim3(WM * WN * 64), 0, stream, x, y, w, Cin, Cout, T, Tout, dil, pad,
                        m_tiles, n_tiles, (int)nblk, flush, ep);
     const hipError_t e = hipGetLastError();
@@ -677,12 +687,20 @@ hipError_t dispatch_pipe(const float* x, float* y, const float* w, int B, int Ci
                          int T, int Tout, int K, int dil, int pad, const ConvEpilogue& ep,
                          hipStream_t stream) {
     if constexpr (BM == 64) {
-      if (!ep.in_alpha && !ep.snake_alpha && dil <= kDilMax &&
-          Cin % (K <= 3 ? 16 : 8) == 0 && (long long)Cout * Cin * K < (1LL << 31)) {
+      if (Cin % (K <= 3 ? 16 : 8) == 0 && (long long)Cout * Cin * K < (1LL << 31)) {
         switch (K) {
             case 1: return run_conv1d_dma<BM, BN, WM, WN, 1>(x, y, w, B, Cin, Cout, T, Tout, dil, pad, ep, stream);
             case 3: return run_conv1d_dma<BM, BN, WM, WN, 3>(x, y, w, B, Cin, Cout, T, Tout, dil, pad, ep, stream);
-            case 7: return run_conv1d_dma<BM, BN, WM, WN, 7>(x, y, w, B, Cin, Cout, T, Tout, dil, pad, ep, stream);
+            case 7:
+                // the DAV units' first conv: both Snakes fused (input staging, epilogue)
+                if (ep.in_alpha || ep.snake_alpha) {
+                    if (dil > kDilMax)
+                        return run_conv1d_dma<BM, BN, WM, WN, 7, 9, true>(x, y, w, B, Cin, Cout, T, Tout, dil, pad, ep, stream);
+                    return run_conv1d_dma<BM, BN, WM, WN, 7, kDilMax, true>(x, y, w, B, Cin, Cout, T, Tout, dil, pad, ep, stream);
+                }
+                if (dil > kDilMax)
+                    return run_conv1d_dma<BM, BN, WM, WN, 7, 9>(x, y, w, B, Cin, Cout, T, Tout, dil, pad, ep, stream);
+                return run_conv1d_dma<BM, BN, WM, WN, 7>(x, y, w, B, Cin, Cout, T, Tout, dil, pad, ep, stream);
             default: return run_conv1d_dma<BM, BN, WM, WN, 11>(x, y, w, B, Cin, Cout, T, Tout, dil, pad, ep, stream);
         }
       }
