@@ -1033,6 +1033,188 @@ __global__ __launch_bounds__(WM * WN * 64) void convtr1d_poly_kernel(
     }
 }
 
+// convtr1d_poly_kernel with the weight slices staged by LDS DMA
+// (global_load_lds_dwordx4) into two LDS buffers, as in conv1d_dma_kernel:
+// the next K chunk's weights stream in during the MFMA work on the current
+// chunk, one barrier per chunk; the input window keeps the register path
+// (zero padding, optional Snake), also double-buffered.  Cin must be a
+// multiple of kKCT.  Same GEMM, LDS layouts and summation order.
+template <int WM, int WN, int NTL, int KT, int S>
+__global__ __launch_bounds__(WM * WN * 64) void convtr1d_dma_kernel(
+    const float* __restrict__ x, float* __restrict__ y, const float* __restrict__ w,
+    const float* __restrict__ bias, const float* __restrict__ in_alpha, int Cin, int Cout,
+    int Tin, int Tout, int pad, int qlo, int m_tiles, int q_tiles, int nblk, int flush) {
+    constexpr int NT = WM * WN * 64;
+    static_assert(NT == 256, "256 threads");
+    constexpr int BMO = 16 * WM;              // output channels per block
+    constexpr int NQ = 16 * NTL * WN;         // q positions per block
+    constexpr int NTAP = (KT + S - 1) / S;    // taps of the longest phase
+    constexpr int WROW = BMO * KT;            // weight floats per input channel
+    constexpr int RS = (WROW % 32 <= 16) ? WROW - WROW % 32 + 16 : WROW - WROW % 32 + 48;
+    static_assert(WROW % 4 == 0 && RS % 4 == 0, "float4 weight slices");
+    constexpr int GR = RS / 4, GV = WROW / 4; // 16-byte granules per row: padded, valid
+    constexpr int NG = kKCT * GR;             // granules per weight buffer
+    constexpr int NI = (NG + NT - 1) / NT;    // DMA instructions per thread
+    constexpr int XW = NQ + NTAP - 1;
+    constexpr int XS = xs_stride_const(XW);
+    constexpr int XR = NT / kKCT;             // lanes per staged input row
+    constexpr int X_PT = (XW + XR - 1) / XR;
+
+    __shared__ __align__(16) float WsA[NG * 4];
+    __shared__ __align__(16) float WsB[NG * 4];
+    __shared__ __align__(16) float XsA[kKCT * XS];
+    __shared__ __align__(16) float XsB[kKCT * XS];
+
+    const int lid = xcd_remap(blockIdx.x, nblk);
+    const int qt = lid % q_tiles;
+    const int rest = lid / q_tiles;
+    const int mt_i = rest % m_tiles;
+    const int b = rest / m_tiles;
+    const int o0 = mt_i * BMO;
+    const int q0 = qlo + qt * NQ;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wid / WN, wn0 = (wid % WN) * (16 * NTL);
+    const int l16 = lane & 15, g = lane >> 4;
+    const int xrow = tid / XR, xcol = tid % XR;
+
+    f32x4 acc[S][NTL], part[S][NTL];
+#pragma unroll
+    for (int r = 0; r < S; ++r)
+#pragma unroll
+        for (int c = 0; c < NTL; ++c) {
+            acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+            part[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+
+    // Granule q = i*NT + tid of the padded [kKCT][GR] buffer: input channel
+    // q / GR, float4 q % GR of its [BMO x KT] slice.  Pad granules and
+    // granules past Cout re-fetch the slice's first float4 (in bounds; never
+    // read, or masked by the epilogue); lanes past the buffer issue no DMA.
+    int woff[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int q = i * NT + tid;
+        const int ic = q / GR;
+        int f = q - ic * GR;
+        if (f >= GV || o0 * KT + 4 * f >= Cout * KT) f = 0;
+        woff[i] = (ic < kKCT ? ic : 0) * Cout * KT + o0 * KT + 4 * f;
+    }
+    const float* xb = x + (size_t)b * Cin * Tin;
+    const int xbase = q0 - (NTAP - 1);
+    const int nch = Cin / kKCT;
+    float xr[X_PT];
+    float xa = 1.f;  // Snake alpha of this thread's staged input row
+
+    auto dma_w = [&](int ic0, float* wbuf) {
+        const float* wc = w + (size_t)ic0 * Cout * KT;
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            if ((i + 1) * NT <= NG || i * NT + tid < NG)
+                __builtin_amdgcn_global_load_lds((const void*)(wc + woff[i]),
+                                                 (void*)(wbuf + (i * NT + wid * 64) * 4), 16, 0,
+                                                 0);
+    };
+    auto gx = [&](int ic0) {
+        const int ic = ic0 + xrow;
+#pragma unroll
+        for (int k = 0; k < X_PT; ++k) {
+            const int u = xcol + k * XR;
+            const int t = xbase + u;
+            float v = 0.f;
+            if (u < XW && t >= 0 && t < Tin) v = xb[(size_t)ic * Tin + t];
+            xr[k] = v;
+        }
+        if (in_alpha) xa = in_alpha[ic];
+    };
+    auto sx = [&](float* xbuf) {
+        if (in_alpha) {
+            const float arev = xa * 0.15915494309189535f, inv = 1.0f / (xa + 1e-9f);
+#pragma unroll
+            for (int k = 0; k < X_PT; ++k) xr[k] = snake_beta(xr[k], arev, inv);
+        }
+#pragma unroll
+        for (int k = 0; k < X_PT; ++k) {
+            const int u = xcol + k * XR;
+            if (u < XW) xbuf[xrow * XS + u] = xr[k];
+        }
+    };
+    auto step = [&](int c, const float* Wc, const float* Xc, float* Wn, float* Xn) {
+        if (c + 1 < nch) {
+            dma_w((c + 1) * kKCT, Wn);
+            gx((c + 1) * kKCT);
+        }
+#pragma unroll
+        for (int m = 0; m < NTAP; ++m) {
+#pragma unroll 1
+            for (int kk = 0; kk < kKCT / 4; ++kk) {
+                float bv[NTL];
+#pragma unroll
+                for (int cc = 0; cc < NTL; ++cc)
+                    bv[cc] = Xc[(kk * 4 + g) * XS + wn0 + cc * 16 + l16 + (NTAP - 1 - m)];
+#pragma unroll
+                for (int r = 0; r < S; ++r) {
+                    if (r + S * m < KT) {
+                        const float av =
+                            Wc[(kk * 4 + g) * RS + (wm * 16 + l16) * KT + r + S * m];
+#pragma unroll
+                        for (int cc = 0; cc < NTL; ++cc)
+                            part[r][cc] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                av, bv[cc], part[r][cc], 0, 0, 0);
+                    }
+                }
+            }
+        }
+        if ((c + 1) % flush == 0 || c + 1 == nch) {
+#pragma unroll
+            for (int r = 0; r < S; ++r)
+#pragma unroll
+                for (int cc = 0; cc < NTL; ++cc) {
+                    acc[r][cc] += part[r][cc];
+                    part[r][cc] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+        }
+        if (c + 1 < nch) sx(Xn);
+        // the barrier also waits for this wave's DMA of chunk c+1
+        __syncthreads();
+    };
+
+    dma_w(0, WsA);
+    gx(0);
+    sx(XsA);
+    __syncthreads();
+    for (int c = 0; c < nch; c += 2) {
+        step(c, WsA, XsA, WsB, XsB);
+        if (c + 1 < nch) step(c + 1, WsB, XsB, WsA, XsA);
+    }
+
+    float* yb = y + (size_t)b * Cout * Tout;
+    float bvv[4];
+#pragma unroll
+    for (int ri = 0; ri < 4; ++ri) {
+        const int o = o0 + wm * 16 + g * 4 + ri;
+        bvv[ri] = (bias && o < Cout) ? bias[o] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < S; ++r) {
+#pragma unroll
+        for (int cc = 0; cc < NTL; ++cc) {
+            const int q = q0 + wn0 + cc * 16 + l16;
+            const int t = q * S + r - pad;
+#pragma unroll
+            for (int ri = 0; ri < 4; ++ri) {
+                const int o = o0 + wm * 16 + g * 4 + ri;
+                if (o < Cout && t >= 0 && t < Tout) {
+                    float v = acc[r][cc][ri];
+                    if (bias) v += bvv[ri];
+                    yb[(size_t)o * Tout + t] = v;
+                }
+            }
+        }
+    }
+}
+
 template <int WM, int WN, int NTL, int KT, int S>
 hipError_t run_convtr1d_poly(const float* x, float* y, const float* w, const float* bias,
                              const float* in_alpha, int B, int Cin, int Cout, int Tin, int Tout,
@@ -1048,13 +1230,23 @@ hipError_t run_convtr1d_poly(const float* x, float* y, const float* w, const flo
     if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
     constexpr int NTAP = (KT + S - 1) / S;
     const int flush = 24 / (NTAP * (kKCT / 4)) > 0 ? 24 / (NTAP * (kKCT / 4)) : 1;
-    static const std::string name = "convtr1d_poly_kernel<" + std::to_string(WM) + "," +
-                                    std::to_string(WN) + "," + std::to_string(NTL) + "," +
-                                    std::to_string(KT) + "," + std::to_string(S) + ">";
+    // LDS-DMA staging when every K chunk is full and the offsets fit in int
+    const bool dma = Cin % kKCT == 0 && (long long)Cin * Cout * KT < (1LL << 31);
+    static const std::string tile = std::to_string(WM) + "," + std::to_string(WN) + "," +
+                                    std::to_string(NTL) + "," + std::to_string(KT) + "," +
+                                    std::to_string(S) + ">";
+    static const std::string name_poly = "convtr1d_poly_kernel<" + tile;
+    static const std::string name_dma = "convtr1d_dma_kernel<" + tile;
     prof_pre(stream);
-    hipLaunchKernelGGL((convtr1d_poly_kernel<WM, WN, NTL, KT, S>), dim3((unsigned)nblk),
-                       dim3(WM * WN * 64), 0, stream, x, y, w, bias, in_alpha, Cin, Cout, Tin,
-                       Tout, pad, qlo, m_tiles, q_tiles, (int)nblk, flush);
+    if (dma)
+        hipLaunchKernelGGL((convtr1d_dma_kernel<WM, WN, NTL, KT, S>), dim3((unsigned)nblk),
+                           dim3(WM * WN * 64), 0, stream, x, y, w, bias, in_alpha, Cin, Cout, Tin,
+                           Tout, pad, qlo, m_tiles, q_tiles, (int)nblk, flush);
+    else
+        hipLaunchKernelGGL((convtr1d_poly_kernel<WM, WN, NTL, KT, S>), dim3((unsigned)nblk),
+                           dim3(WM * WN * 64), 0, stream, x, y, w, bias, in_alpha, Cin, Cout, Tin,
+                           Tout, pad, qlo, m_tiles, q_tiles, (int)nblk, flush);
+    const std::string& name = dma ? name_dma : name_poly;
     const hipError_t e = hipGetLastError();
     prof_post(stream, name.c_str(), 2.0 * B * Cin * Cout * (double)KT * Tin,
               4.0 * ((double)B * Cin * Tin + (double)B * Cout * Tout + (double)Cin * Cout * KT));
