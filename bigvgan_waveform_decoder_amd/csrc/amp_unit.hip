@@ -53,7 +53,8 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kUT = 256;              // threads per block (4 waves)
-constexpr int kRun = 16;              // activation outputs per thread run
+constexpr int kRun = 16;              // activation outputs per thread run (default)
+constexpr int kRunMax = 24;           // longest run length act_stage picks
 constexpr int kLdsBudget = 80 * 1024; // two blocks per CU
 constexpr int kXR = 48;               // staged x values per thread (bound)
 
@@ -176,19 +177,20 @@ __device__ __forceinline__ void act_run(const float* __restrict__ src, int ss,
     }
 }
 
-// The activation over all C rows of a range: runs of kRun outputs, one per
+// The activation over all C rows of a range: runs of R outputs, one per
 // thread per pass.
-__device__ __forceinline__ void act_stage(const float* __restrict__ src, int ss,
-                                          float* __restrict__ dst, int ds, int C, int Nd, int og,
-                                          int T, bool edge, const float* arev, const float* ibeta,
-                                          const ActTaps& taps) {
-    const int runs = (Nd + kRun - 1) / kRun;
+template <int R>
+__device__ __forceinline__ void act_pass(const float* __restrict__ src, int ss,
+                                         float* __restrict__ dst, int ds, int C, int Nd, int og,
+                                         int T, bool edge, const float* arev, const float* ibeta,
+                                         const ActTaps& taps) {
+    const int runs = (Nd + R - 1) / R;
     const int items = C * runs;
     // (c, run) of item it, advanced by kUT items per pass without a division
     const int add_c = kUT / runs, add_r = kUT - add_c * runs;
     int c = threadIdx.x / runs, run = threadIdx.x - c * runs;
     for (int it = threadIdx.x; it < items; it += kUT) {
-        act_run<kRun>(src, ss, dst, ds, c, run * kRun, Nd, og, T, edge, arev, ibeta, taps);
+        act_run<R>(src, ss, dst, ds, c, run * R, Nd, og, T, edge, arev, ibeta, taps);
         c += add_c;
         run += add_r;
         if (run >= runs) {
@@ -196,6 +198,28 @@ __device__ __forceinline__ void act_stage(const float* __restrict__ src, int ss,
             ++c;
         }
     }
+}
+
+// The run length is chosen per range: a pass over the block costs about one
+// run (R outputs from R + 5 doubled-rate pairs), and C * ceil(Nd / R) runs
+// take ceil(C * ceil(Nd / R) / 256) passes; a range just over a multiple of
+// 256 runs of 16 would leave most threads idle in its last pass, so runs of
+// 20 or 24 are taken when they need fewer pass-pairs.
+__device__ __forceinline__ void act_stage(const float* __restrict__ src, int ss,
+                                          float* __restrict__ dst, int ds, int C, int Nd, int og,
+                                          int T, bool edge, const float* arev, const float* ibeta,
+                                          const ActTaps& taps) {
+    auto cost = [&](int R) {
+        const int items = C * ((Nd + R - 1) / R);
+        return ((items + kUT - 1) / kUT) * (R + 5);
+    };
+    const int c16 = cost(16), c20 = cost(20), c24 = cost(24);
+    if (c20 < c16 && c20 <= c24)
+        act_pass<20>(src, ss, dst, ds, C, Nd, og, T, edge, arev, ibeta, taps);
+    else if (c24 < c16)
+        act_pass<24>(src, ss, dst, ds, C, Nd, og, T, edge, arev, ibeta, taps);
+    else
+        act_pass<16>(src, ss, dst, ds, C, Nd, og, T, edge, arev, ibeta, taps);
 }
 
 typedef const float __attribute__((address_space(1))) gfloat;
@@ -486,7 +510,7 @@ bool plan_unit(int C, int K, int d, UnitPlan* p) {
         const int TT = (N1r - 2 * h2 - 10) / 16 * 16;
         if (TT < 32) continue;
         const int NX = TT + 2 * H;
-        const int SP = stride16(std::max(NX + kRun + 4, N1r));
+        const int SP = stride16(std::max(NX + kRunMax + 4, N1r));
         const int SQ = stride16(N1r + 2 * h1);
         const size_t lds = ((size_t)C * (SP + SQ) + 4 * (size_t)C) * sizeof(float);
         if (lds > (size_t)kLdsBudget) continue;
