@@ -35,6 +35,9 @@ CONV_CASES = [
     (2, 512, 512, 700, 11, 3, None, False),
     (1, 768, 768, 260, 11, 5, None, True),  # H3 stage-1 width, long K
     (2, 1, 3, 33, 1, 1, None, False),
+    (2, 48, 70, 300, 3, 2, None, True),     # LDS-DMA staging, Cout tail in a 64-row tile
+    (1, 64, 100, 200, 7, 9, None, False),   # 7 taps at dilation 9 (wider staged halo)
+    (1, 36, 64, 300, 11, 1, None, False),   # Cin not a multiple of 8: register staging
 ]
 
 
@@ -101,6 +104,9 @@ CONVT_CASES = [
     (1, 4, 4, 6, 4, 2, 0),
     (1, 12, 6, 300, 11, 5, 4),
     (2, 96, 48, 1000, 4, 2, -1),
+    (1, 32, 40, 50, 16, 8, -1),    # LDS-DMA staging, Cout tail in a 32-channel tile
+    (2, 48, 20, 77, 8, 4, -1),
+    (1, 16, 33, 29, 11, 5, -1),    # Cout*K not a multiple of 4: generic kernel
 ]
 
 
