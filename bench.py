@@ -132,7 +132,80 @@ def act1d_standalone(torch, avae, W, steps):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / n
     gbps = 8.0 * x.size / (ms / 1e3) / 1e9
-    return {"shape": list(x.shape), "ms": ms, "GBps": gbps, "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS}
+    # a plain device-to-device copy of the same tensor: the HBM rate this
+    # machine delivers to a read-once / write-once stream
+    for _ in range(3):
+        yd.copy_(xd)
+    torch.cuda.synchronize()
+    e0.record(s)
+    for _ in range(n):
+        yd.copy_(xd)
+    e1.record(s)
+    torch.cuda.synchronize()
+    copy_gbps = 8.0 * x.size / (e0.elapsed_time(e1) / n / 1e3) / 1e9
+    return {"shape": list(x.shape), "ms": ms, "GBps": gbps, "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS,
+            "copy_GBps": copy_gbps, "frac_of_copy": gbps / copy_gbps}
+
+
+def mfma_probe(torch, avae):
+    """The FP32 rate the matrix cores deliver (avae_probe_mfma, no memory
+    traffic): 16 independent accumulator chains per wave at one wave per SIMD
+    (the instruction's full rate), and 8 chains at two waves per SIMD (the
+    shape of the convolution kernels' work).  Each grid is exactly one
+    resident wave of blocks (256 CUs x waves per SIMD), so no partial second
+    round skews the rate, and a warm-up launch of a few ms comes first."""
+    dev = torch.device("cuda:0")
+    s = torch.cuda.current_stream()
+    out = {}
+    for key, chains, blocks, iters in (("16_chains_1_wave_per_simd", 16, 256, 20000),
+                                       ("8_chains_2_waves_per_simd", 8, 512, 10000)):
+        sink = torch.empty(blocks * 256, device=dev)
+        avae.probe_mfma(chains, blocks, iters, sink)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        avae.probe_mfma(chains, blocks, iters, sink)
+        e1.record(s)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        out[key] = blocks * 4.0 * iters * chains * 2048.0 / (ms / 1e3) / 1e12
+    out["unit"] = "TFLOP/s"
+    return out
+
+
+def roofline_sum(kernels, steps):
+    """Sum over the decode's kernels of max(flops / MFMA peak, bytes / HBM
+    peak), per step (aggregated per kernel name; every launch of a name has
+    the same bound)."""
+    t = 0.0
+    for k in kernels.values():
+        t += max(k["flops"] / (FP32_MFMA_PEAK_TFLOPS * 1e12), k["bytes"] / (HBM_PEAK_GBPS * 1e9))
+    return t * 1e3 / steps
+
+
+def cpu_amp_block_one_core(W):
+    """The oracle on workload 1 (one AMP block, [1, 32, 4096]) on one core."""
+    import numpy as np
+    from oracle import avae_oracle as O
+    from tests.helpers import amp_params
+    x, t = W.workload1()
+    p = amp_params(t, "block", 3, (1, 3, 5))
+    xs = np.asarray(x, np.float64)
+    try:
+        from threadpoolctl import threadpool_limits
+        ctx = threadpool_limits(1)
+    except Exception:
+        ctx = None
+    t0 = time.perf_counter()
+    if ctx is not None:
+        with ctx:
+            O.amp_block(xs, p)
+    else:
+        O.amp_block(xs, p)
+    dt = time.perf_counter() - t0
+    return {"workload": "one AMP block, [1,32,4096], k=3, d=(1,3,5)", "seconds": dt,
+            "samples_per_s": x.shape[-1] / dt, "cores": 1}
 
 
 def streaming(torch, dec, zd, out, tile, steps):
@@ -330,6 +403,17 @@ def main():
         iso, _ = profiled()
         dec.set_concurrent(True)
     res["roofline"] = roofline(iso, args.steps)
+    probe = mfma_probe(torch, avae)
+    res["mfma_probe"] = probe
+    if res["roofline"]["unit"] == "TFLOP/s":
+        res["roofline"]["frac_of_probe_peak"] = (res["roofline"]["achieved"] /
+                                                 probe["16_chains_1_wave_per_simd"])
+    # roofline sum over the decode's kernels vs the timed step (and vs the
+    # single-stream step, whose launches are the same ones one after another)
+    t_roof = roofline_sum(iso, args.steps)
+    single_ms = ms if args.serial_mrf else res["single_stream"]["ms_per_step"]
+    res["decode_roofline_sum"] = {"ms": t_roof, "frac_of_timed": t_roof / ms,
+                                  "frac_of_single_stream": t_roof / single_ms}
     res["roofline"]["measured"] = "AMP blocks serialized for this pass: each launch alone on the GPU"
     kname = res["roofline"]["kernel"]
     if kname in kernels and not args.serial_mrf:
@@ -361,8 +445,27 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         res["pmc_calibration_copy_bytes"] = src.numel() * 4
+    # the same step with the latent coming from pinned host memory and the
+    # waveform going back to it (PCIe both ways), for context
+    zh = torch.from_numpy(z).pin_memory()
+    oh = torch.empty((B, L), dtype=torch.float32).pin_memory()
+    for _ in range(2):
+        zd.copy_(zh, non_blocking=True)
+        dec.decode(zd, out=out, workspace=ws)
+        oh.copy_(out, non_blocking=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        zd.copy_(zh, non_blocking=True)
+        dec.decode(zd, out=out, workspace=ws)
+        oh.copy_(out, non_blocking=True)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    msh = e0.elapsed_time(e1) / args.steps
+    res["with_host_copies"] = {"ms_per_step": msh, "samples_per_s": B * L / (msh / 1e3)}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(spec, z, t, args.cpu_frames)
+        res["cpu_amp_block_one_core"] = cpu_amp_block_one_core(W)
     print(json.dumps(res), flush=True)
 
 

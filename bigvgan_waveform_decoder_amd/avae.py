@@ -129,6 +129,8 @@ def lib() -> ctypes.CDLL:
     L.avae_decoder_workspace_bytes.argtypes = [P, c_int, c_int]
     L.avae_decoder_set_concurrent.restype = c_int
     L.avae_decoder_set_concurrent.argtypes = [P, c_int]
+    L.avae_probe_mfma.restype = c_int
+    L.avae_probe_mfma.argtypes = [c_int, c_int, c_int, P, P]
     L.avae_bigvgan_decode.restype = c_int
     L.avae_bigvgan_decode.argtypes = [P, P, c_int, c_int, P, P, c_size_t, P]
     L.avae_bigvgan_decode_traced.restype = c_int
@@ -510,6 +512,13 @@ class Decoder:
             int(halo_frames), workspace.data_ptr(), workspace.numel(), _stream(stream)))
         return out
 
+
+
+def probe_mfma(chains: int, blocks: int, iters: int, sink, stream=None) -> None:
+    """avae_probe_mfma: a pure FP32-MFMA loop (measurement aid); the caller
+    times it.  flops = blocks * 4 * iters * chains * 2048."""
+    _check(lib().avae_probe_mfma(chains, blocks, iters, _dev(sink, "sink", (blocks * 256,)),
+                                 _stream(stream)))
 
 def snake(x, alpha, out=None, stream=None):
     """avae_snake: plain Snake with alpha as stored; out may be x."""

@@ -844,6 +844,17 @@ extern "C" int avae_bigvgan_decode_streaming(const avae_decoder* dec, const floa
 // Plain Snake and the Music-3 DAV decoder
 // =========================================================================
 
+extern "C" int avae_probe_mfma(int chains, int blocks, int iters, float* sink, void* stream) {
+    if (!sink) return fail(AVAE_EINVAL, "avae_probe_mfma: sink is null");
+    if ((chains != 8 && chains != 16) || blocks < 1 || iters < 1)
+        return fail(AVAE_EINVAL, "avae_probe_mfma: chains must be 8 or 16, blocks and iters >= 1 "
+                                 "(got %d, %d, %d)", chains, blocks, iters);
+    avae::prof_set_phase(avae::kPhaseNone);
+    AVAE_TRY(avae::launch_mfma_probe(chains, blocks, iters, sink, (hipStream_t)stream),
+             "avae_probe_mfma launch");
+    return AVAE_OK;
+}
+
 extern "C" int avae_snake(const float* x, float* y, int B, int C, int T, const float* alpha,
                           void* stream) {
     if (!x || !y || !alpha) return fail(AVAE_EINVAL, "avae_snake: null pointer");

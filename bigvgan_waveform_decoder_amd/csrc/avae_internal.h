@@ -106,6 +106,11 @@ hipError_t launch_bwe_combine(const float* x, const float* resid, float* out, in
 // AMP blocks that ran concurrently into separate buffers.
 hipError_t launch_sum_into(float* y, float* const* x, int n, size_t count, hipStream_t stream);
 
+// Matrix-core throughput probe (probe.hip): `blocks` workgroups of 256
+// threads, each wave running `chains` (8 or 16) independent FP32 MFMA
+// accumulator chains for `iters` iterations; sink gets blocks*256 floats.
+hipError_t launch_mfma_probe(int chains, int blocks, int iters, float* sink, hipStream_t s);
+
 // y[b,c,t] = x[b,c,t] * scale[c] + shift[c]
 hipError_t launch_channel_affine(const float* x, float* y, const float* scale,
                                  const float* shift, int B, int C, int T, hipStream_t stream);

@@ -1,0 +1,46 @@
+// Matrix-core throughput probe: a measurement aid for the convolution
+// kernels' roofline, not part of the decode path.  Every wave runs N
+// independent v_mfma_f32_16x16x4_f32 accumulator chains (the instruction
+// the convolutions use) with no memory traffic inside the loop, so the
+// achieved rate is what the matrix cores deliver for that many independent
+// chains per wave at the occupancy the grid gives.
+#include "avae_internal.h"
+
+namespace avae {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int N>
+__global__ __launch_bounds__(256) void mfma_probe_kernel(float* __restrict__ sink, int iters) {
+    f32x4 acc[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // operands that the compiler cannot fold; tiny so the sums stay finite
+    const float a = (float)threadIdx.x * 1e-6f, b = (float)blockIdx.x * 1e-6f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[i], 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < N; ++i) s += acc[i][0] + acc[i][1] + acc[i][2] + acc[i][3];
+    sink[(size_t)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+}  // namespace
+
+hipError_t launch_mfma_probe(int chains, int blocks, int iters, float* sink, hipStream_t s) {
+    prof_pre(s);
+    if (chains == 16)
+        hipLaunchKernelGGL(mfma_probe_kernel<16>, dim3(blocks), dim3(256), 0, s, sink, iters);
+    else
+        hipLaunchKernelGGL(mfma_probe_kernel<8>, dim3(blocks), dim3(256), 0, s, sink, iters);
+    const hipError_t e = hipGetLastError();
+    prof_post(s, chains == 16 ? "mfma_probe_kernel<16>" : "mfma_probe_kernel<8>",
+              (double)blocks * 4 * iters * chains * 2048.0, 4.0 * blocks * 256);
+    return e;
+}
+
+}  // namespace avae

@@ -422,6 +422,19 @@ int avae_profile_entry(int i, char* name, int name_len, long long* launches, dou
                        double* flops, double* bytes);
 int avae_profile_phases(double* ms6);
 
+/*
+ * Matrix-core throughput probe, a measurement aid for the convolutions'
+ * roofline (not part of any decode).  Launches `blocks` workgroups of 256
+ * threads on `stream`; every wave runs `chains` (8 or 16) independent
+ * v_mfma_f32_16x16x4_f32 accumulator chains for `iters` iterations with no
+ * memory traffic in the loop: blocks * 4 * iters * chains * 2048 flops.
+ * `sink` is a device buffer of blocks * 256 floats that receives the sums
+ * (so the work is kept).  The caller times it (hipEvents on `stream`);
+ * with 256 * n blocks each SIMD holds n waves.  Errors: EINVAL (null sink,
+ * chains not 8 or 16, blocks or iters < 1), EHIP.
+ */
+int avae_probe_mfma(int chains, int blocks, int iters, float* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

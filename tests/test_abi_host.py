@@ -91,6 +91,10 @@ def test_decoder_create_rejects_bad_config():
     assert L.avae_decoder_create(None, ctypes.byref(w), ctypes.byref(h)) == -1
     assert L.avae_decoder_workspace_bytes(None, 1, 1) == 0
     assert L.avae_decoder_set_concurrent(None, 1) == -1
+    fake = ctypes.c_void_p(0x1000)
+    assert L.avae_probe_mfma(8, 1, 1, None, None) == -1
+    assert L.avae_probe_mfma(7, 1, 1, fake, None) == -1
+    assert L.avae_probe_mfma(16, 0, 1, fake, None) == -1
 
 
 def test_streaming_rejects_bad_arguments():

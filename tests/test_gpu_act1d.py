@@ -81,3 +81,14 @@ def test_act1d_deterministic():
     a = host(avae.act1d(cuda(x), cuda(la), cuda(lb)))
     b = host(avae.act1d(cuda(x), cuda(la), cuda(lb)))
     np.testing.assert_array_equal(a, b)
+
+
+def test_mfma_probe_runs_and_sums_are_finite():
+    """The matrix-core probe bench.py times: it runs for both chain counts
+    and writes one finite sum per thread."""
+    import torch
+    announce("mfma probe")
+    for chains in (8, 16):
+        sink = torch.full((4 * 256,), float("nan"), device="cuda:0")
+        avae.probe_mfma(chains, 4, 10, sink)
+        assert np.all(np.isfinite(host(sink)))
