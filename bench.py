@@ -34,6 +34,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-frames", type=int, default=120,
                     help="latent frames of the oracle's bounded CPU sample (one pass)")
+    ap.add_argument("--no-other", action="store_true",
+                    help="skip the other full decoder config's figure (workload 5 or 4)")
     ap.add_argument("--no-bwe", action="store_true",
                     help="skip the LTX bandwidth-extension tail figure (workload 7)")
     ap.add_argument("--no-dav", action="store_true",
@@ -206,6 +208,37 @@ def cpu_amp_block_one_core(W):
     dt = time.perf_counter() - t0
     return {"workload": "one AMP block, [1,32,4096], k=3, d=(1,3,5)", "seconds": dt,
             "samples_per_s": x.shape[-1] / dt, "cores": 1}
+
+
+def other_decoder(torch, avae, W, which, steps):
+    """The other full decoder config, timed like the main step: workload 5
+    (LTX-2.5-shaped, [2,64,2000] log-mel -> [2,320000] at 16 kHz) when the
+    main step is workload 4, and the reverse."""
+    dev = torch.device("cuda:0")
+    z, t = W.workload5() if which == 5 else W.workload4()
+    spec = W.LTX if which == 5 else W.H3
+    dec = avae.Decoder(spec, {k: torch.from_numpy(v).to(dev) for k, v in t.items()})
+    B, _, F = z.shape
+    L = dec.output_length(F)
+    zd = torch.from_numpy(z).to(dev)
+    ws = torch.empty(dec.workspace_bytes(B, F), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, L), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        dec.decode(zd, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(steps):
+        dec.decode(zd, out=out, workspace=ws)
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"workload": f"{spec.name} decode, latent [{B},{spec.c_in},{F}] -> wave [{B},{L}] "
+                        f"at {spec.sample_rate} Hz",
+            "ms": ms, "samples_per_s": B * L / (ms / 1e3),
+            "x_realtime": (L / spec.sample_rate) / (ms / 1e3)}
 
 
 def streaming(torch, dec, zd, out, tile, steps):
@@ -437,6 +470,9 @@ def main():
         res["dav"] = dav_figure(torch, avae, W, args.steps)
     if not args.no_bwe:
         res["bwe"] = bwe_figure(torch, avae, W, args.steps)
+    if not args.no_other:
+        res["other_decoder"] = other_decoder(torch, avae, W, 5 if args.workload == 4 else 4,
+                                             args.steps)
     if args.stream_tile > 0:
         res["streaming"] = streaming(torch, dec, zd, out, args.stream_tile, args.steps)
     if args.pmc_calibration:
