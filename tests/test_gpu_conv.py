@@ -105,6 +105,7 @@ CONVT_CASES = [
     (1, 12, 6, 300, 11, 5, 4),
     (2, 96, 48, 1000, 4, 2, -1),
     (1, 32, 40, 50, 16, 8, -1),    # LDS-DMA staging, Cout tail in a 32-channel tile
+    (1, 32, 20, 50, 11, 5, -1),    # short input: 16-channel tiles, LDS-DMA, Cout tail
     (2, 48, 20, 77, 8, 4, -1),
     (1, 16, 33, 29, 11, 5, -1),    # Cout*K not a multiple of 4: generic kernel
 ]
