@@ -262,7 +262,11 @@ def streaming(torch, dec, zd, out, tile, steps):
     ms = e0.elapsed_time(e1) / n
     R = dec.reach_frames()
     tiles = -(-F // tile)
-    decoded = sum(min(F, (i + 1) * tile + R) - max(0, i * tile - R) for i in range(tiles))
+    # the end tiles decode min(tile + R, F) frames, inner tiles min(tile + 2 R, F)
+    if tiles == 1:
+        decoded = F
+    else:
+        decoded = 2 * min(tile + R, F) + (tiles - 2) * min(tile + 2 * R, F)
     return {"tile_frames": tile, "halo_frames": R, "tiles": tiles, "ms": ms,
             "samples_per_s": out.numel() / (ms / 1e3), "decoded_frames_ratio": decoded / F,
             "workspace_MB": ws.numel() / 1e6}

@@ -756,6 +756,10 @@ long long hop_of(const avae_config& c) {
 }
 
 // The streaming workspace: latent crop, tile waveform, decode workspace.
+// Tiles decoded together in one batched pass (their crops stacked along the
+// batch axis): the workspace covers this many tiles.
+constexpr int kTileBatch = 4;
+
 struct StreamPlan {
     size_t crop_bytes, wave_bytes, dec_bytes;
     size_t total() const { return crop_bytes + wave_bytes + dec_bytes; }
@@ -765,11 +769,13 @@ bool stream_plan(const avae_decoder* dec, int B, int tile_frames, int halo, Stre
     const avae_config& c = dec->cfg;
     const long long cf = (long long)tile_frames + 2LL * halo;
     if (cf > 0x3fffffffLL) return false;
+    if ((long long)B * kTileBatch > 0x7fffffffLL / 2) return false;
+    const int rows = B * kTileBatch;
     long long T[AVAE_MAX_STAGES + 1];
     if (stage_lengths(c, (int)cf, T)) return false;
-    p->crop_bytes = round_up((size_t)B * c.c_in * cf * sizeof(float), 256);
-    p->wave_bytes = round_up((size_t)B * T[c.n_stages] * sizeof(float), 256);
-    p->dec_bytes = decode_slots(dec) * decode_slot_bytes(c, B, T);
+    p->crop_bytes = round_up((size_t)rows * c.c_in * cf * sizeof(float), 256);
+    p->wave_bytes = round_up((size_t)rows * T[c.n_stages] * sizeof(float), 256);
+    p->dec_bytes = decode_slots(dec) * decode_slot_bytes(c, rows, T);
     return true;
 }
 
@@ -819,23 +825,79 @@ extern "C" int avae_bigvgan_decode_streaming(const avae_decoder* dec, const floa
     float* twave = (float*)(ws + plan.crop_bytes);
     void* dws = ws + plan.crop_bytes + plan.wave_bytes;
     const size_t rows = (size_t)B * c.c_in;
-    for (int f0 = 0; f0 < frames; f0 += tf) {
-        const int f1 = f0 + tf < frames ? f0 + tf : frames;
-        const int c0 = f0 - halo > 0 ? f0 - halo : 0;
-        const int c1 = f1 + halo < frames ? f1 + halo : frames;
-        const int cf = c1 - c0;
-        AVAE_TRY(hipMemcpy2DAsync(crop, (size_t)cf * sizeof(float), latent + c0,
-                                  (size_t)frames * sizeof(float), (size_t)cf * sizeof(float), rows,
-                                  hipMemcpyDeviceToDevice, s),
-                 "streaming crop copy");
-        int rc = decode_impl(dec, crop, B, cf, twave, dws, plan.dec_bytes, nullptr, s);
+    // Tile i keeps frames [i tf, min((i+1) tf, frames)).  Its crop: the
+    // first tile [0, tf + halo), the last tile the final tf + halo frames,
+    // an inner tile tf + 2 halo frames centred on it (slid inward when the
+    // halo reaches past an end), every length clipped to the sequence; each
+    // kept frame has at least `halo` frames of context on every side that is
+    // not a true end.  So there are at most two crop lengths, and tiles of
+    // one length stack along the batch axis, up to kTileBatch per pass.
+    const int ntiles = (frames + tf - 1) / tf;
+    const int len_edge = (int)std::min<long long>((long long)tf + halo, frames);
+    const int len_mid = (int)std::min<long long>((long long)tf + 2LL * halo, frames);
+    auto crop_of = [&](int i, int* c0, int* len) {
+        if (ntiles == 1) {
+            *c0 = 0;
+            *len = frames;
+        } else if (i == 0) {
+            *c0 = 0;
+            *len = len_edge;
+        } else if (i == ntiles - 1) {
+            *c0 = frames - len_edge;
+            *len = len_edge;
+        } else {
+            *c0 = std::max(0, std::min(i * tf - halo, frames - len_mid));
+            *len = len_mid;
+        }
+    };
+    for (int pass = 0; pass < 2; ++pass) {
+        // pass 0: the end tiles (and a single whole-sequence tile), pass 1: inner tiles
+        int group[kTileBatch];
+        int ng = 0, glen = 0;
+        auto flush = [&]() -> int {
+            if (ng == 0) return AVAE_OK;
+            for (int g = 0; g < ng; ++g) {
+                int c0, len;
+                crop_of(group[g], &c0, &len);
+                AVAE_TRY(hipMemcpy2DAsync(crop + (size_t)g * rows * len, (size_t)len * sizeof(float),
+                                          latent + c0, (size_t)frames * sizeof(float),
+                                          (size_t)len * sizeof(float), rows,
+                                          hipMemcpyDeviceToDevice, s),
+                         "streaming crop copy");
+            }
+            int rc = decode_impl(dec, crop, B * ng, glen, twave, dws, plan.dec_bytes, nullptr, s);
+            if (rc) return rc;
+            const size_t lcrop = (size_t)glen * hop;
+            for (int g = 0; g < ng; ++g) {
+                int c0, len;
+                crop_of(group[g], &c0, &len);
+                const int f0 = group[g] * tf;
+                const int f1 = std::min(f0 + tf, frames);
+                AVAE_TRY(hipMemcpy2DAsync(wave + (size_t)f0 * hop,
+                                          (size_t)frames * hop * sizeof(float),
+                                          twave + (size_t)g * B * lcrop + (size_t)(f0 - c0) * hop,
+                                          lcrop * sizeof(float),
+                                          (size_t)(f1 - f0) * hop * sizeof(float), (size_t)B,
+                                          hipMemcpyDeviceToDevice, s),
+                         "streaming tile copy");
+            }
+            ng = 0;
+            return AVAE_OK;
+        };
+        for (int i = 0; i < ntiles; ++i) {
+            const bool end_tile = (i == 0 || i == ntiles - 1);
+            if (end_tile != (pass == 0)) continue;
+            int c0, len;
+            crop_of(i, &c0, &len);
+            if (ng == kTileBatch || (ng > 0 && len != glen)) {
+                int rc = flush();
+                if (rc) return rc;
+            }
+            glen = len;
+            group[ng++] = i;
+        }
+        int rc = flush();
         if (rc) return rc;
-        const size_t lcrop = (size_t)cf * hop;
-        AVAE_TRY(hipMemcpy2DAsync(wave + (size_t)f0 * hop, (size_t)frames * hop * sizeof(float),
-                                  twave + (size_t)(f0 - c0) * hop, lcrop * sizeof(float),
-                                  (size_t)(f1 - f0) * hop * sizeof(float), (size_t)B,
-                                  hipMemcpyDeviceToDevice, s),
-                 "streaming tile copy");
     }
     return AVAE_OK;
 }

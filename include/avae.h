@@ -251,14 +251,19 @@ int avae_bigvgan_decode_traced(const avae_decoder* dec, const float* latent, int
 
 /*
  * Time-tiled (streaming) decode for long latents.  The latent is decoded in
- * tiles of `tile_frames` frames; each tile is decoded from a crop extended by
- * `halo_frames` frames on each side (clipped at the sequence ends) and only
- * the tile's own samples are kept.  The decoder is a finite, non-causal
- * stack of convolutions and resampling filters ([H3] AudioVae::decode), so
- * with halo_frames >= avae_decoder_reach_frames() every kept sample depends
- * only on latent frames inside its crop and equals the whole-sequence
- * decode up to float32 summation order (tile shapes may select different
- * kernel tilings).  The workspace covers one tile, whatever `frames` is.
+ * tiles of `tile_frames` frames; each tile is decoded from a crop with
+ * `halo_frames` frames of context on every side that is not a sequence end
+ * (the first and last tiles: tile_frames + halo_frames frames at their end
+ * of the sequence; inner tiles: tile_frames + 2 halo_frames around them;
+ * clipped to the sequence) and only the tile's own samples are kept.  Tiles
+ * whose crops have the same length are stacked along the batch axis, up to
+ * four per decode pass.  The decoder is a
+ * finite, non-causal stack of convolutions and resampling filters ([H3]
+ * AudioVae::decode), so with halo_frames >= avae_decoder_reach_frames()
+ * every kept sample depends only on latent frames inside its crop and
+ * equals the whole-sequence decode up to float32 summation order (tile
+ * shapes may select different kernel tilings).  The workspace covers four
+ * tiles, whatever `frames` is.
  * Requires an exact hop geometry: output length frames * prod(rates)
  * (ESHAPE otherwise).  halo_frames < 0 selects avae_decoder_reach_frames().
  */

@@ -16,6 +16,8 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("name,spec,frames,tile", [
     ("h3-c256", W.scaled_spec(W.H3, 256, final="none"), 90, 17),
     ("ltx-c128", W.scaled_spec(W.LTX, 128, final="none"), 140, 40),
+    # 15 tiles: 13 inner crops in four batched passes, a ragged last tile
+    ("h3-c128-many", W.scaled_spec(W.H3, 128, final="none"), 160, 11),
 ])
 def test_streaming_equals_whole_decode(name, spec, frames, tile):
     announce(f"streaming {name} frames={frames} tile={tile}")
