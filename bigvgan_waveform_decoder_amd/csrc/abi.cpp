@@ -651,8 +651,10 @@ int decode_impl(const avae_decoder* dec, const float* latent, int B, int frames,
             AVAE_TRY(hipEventRecord(dec->fork, s), "fork event");
             for (int k = 1; k < c.n_kernels; ++k)
                 AVAE_TRY(hipStreamWaitEvent(dec->side[k - 1], dec->fork, 0), "fork wait");
+            // block 0 writes M; block k >= 1 its own slot after the scratch slots
             float* outs[AVAE_MAX_KERNELS] = {M};
-            for (int k = 1; k < c.n_kernels; ++k) outs[k] = (float*)(ws + (size_t)(1 + 3 * c.n_kernels + k) * slot);
+            for (int k = 1; k < c.n_kernels; ++k)
+                outs[k] = (float*)(ws + (size_t)(1 + 3 * c.n_kernels + k) * slot);
             for (int k = 0; k < c.n_kernels; ++k) {
                 hipStream_t sk = k == 0 ? s : dec->side[k - 1];
                 float* sc = (float*)(ws + (size_t)(2 + 3 * k) * slot);
