@@ -865,7 +865,8 @@ __global__ __launch_bounds__(WM * WN * 64) void convtr1d_mfma_kernel(
 // MFMAs.  The input window x[q0-NTAP+1 .. q0+NQ) and the weight slice
 // w[ic][o0 .. o0+BMo)[0 .. K) (contiguous in the caller's [Cin, Cout, K]
 // layout) are staged once per K chunk for all phases, with the next chunk
-// prefetched into registers during the MFMA work, as in conv1d_pipe_kernel.
+// prefetched into registers during the MFMA work, as in conv1d_pipe_kernel
+// (convtr1d_dma_kernel below stages the weights by LDS DMA instead).
 constexpr int kKCT = 16;  // input channels per ConvT K chunk
 
 template <int WM, int WN, int NTL, int KT, int S>
@@ -1321,7 +1322,8 @@ __global__ void channel_affine_kernel(const float* __restrict__ x, float* __rest
 hipError_t launch_conv1d(const float* x, float* y, const float* w, int B, int Cin, int Cout,
                          int T, int Tout, int K, int dilation, int pad, const ConvEpilogue& ep,
                          hipStream_t stream) {
-    // Snake in the prologue/epilogue: the 7-tap pipelined kernels, else generic
+    // Snake in the prologue/epilogue: the 7-tap staged kernels (LDS-DMA or
+    // register prefetch), else the generic one
     const bool snake = ep.in_alpha || ep.snake_alpha;
     const bool pipe_ok = (K == 1 || K == 3 || K == 7 || K == 11) && dilation <= dil_max(K) &&
                          (!snake || K == 7) &&
