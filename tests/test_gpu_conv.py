@@ -132,3 +132,62 @@ def test_convtr1d_full_size_workload3():
     ref = O.convtr1d(x, t["ups.0.weight"], t["ups.0.bias"], stride=5)
     assert y.shape == (2, 512, 40001)
     assert rel_err(y, ref) <= TOL
+
+
+def _random_conv_cases(n, seed):
+    """Seeded shapes spread over the dispatch branches: tile rows 16/32/48/64/96,
+    K in and outside the specialised set, dilations up to the staged halo,
+    channel counts that are and are not multiples of the staging chunks."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        K = int(rng.choice([1, 3, 5, 7, 11]))
+        d = int(rng.integers(1, 10 if K == 7 else 6))
+        Cin = int(rng.choice([4, 8, 12, 16, 24, 32, 40, 48, 64, 72, 96, 128]))
+        Cout = int(rng.choice([1, 5, 16, 24, 33, 48, 64, 70, 96, 128, 192]))
+        T = int(rng.integers(max(1, (K - 1) * d // 2 + 1), 700))
+        out.append((int(rng.integers(1, 3)), Cin, Cout, T, K, d, bool(rng.integers(0, 2))))
+    return out
+
+
+RANDOM_CONV = _random_conv_cases(24, 20261203)
+
+
+@pytest.mark.parametrize("B,Cin,Cout,T,K,d,res", RANDOM_CONV)
+def test_conv1d_random_shapes(B, Cin, Cout, T, K, d, res):
+    announce(f"conv1d random B={B} Cin={Cin} Cout={Cout} T={T} K={K} d={d} res={res}")
+    x, w, b = _conv_inputs(f"rnd-{B}-{Cin}-{Cout}-{T}-{K}-{d}", B, Cin, Cout, T, K)
+    r = W.normal(0, f"conv/rnd-{Cin}-{Cout}-{T}-{K}/res", [B, Cout, T]) if res else None
+    y = host(avae.conv1d(cuda(x), cuda(w), cuda(b), dilation=d,
+                         residual=cuda(r) if res else None))
+    ref = O.conv1d(x, w, b, dilation=d, pad=(K * d - d) // 2, residual=r)
+    assert rel_err(y, ref) <= TOL
+
+
+def _random_convt_cases(n, seed):
+    """Seeded (K, stride) pairs of the specialised kernels and others, with
+    Cin on and off the 16-channel chunk and Cout tails."""
+    rng = np.random.default_rng(seed)
+    pairs = [(11, 5), (10, 5), (4, 2), (16, 8), (8, 4), (3, 1), (6, 3), (5, 2)]
+    out = []
+    for _ in range(n):
+        K, s = pairs[int(rng.integers(0, len(pairs)))]
+        out.append((int(rng.integers(1, 3)), int(rng.choice([8, 16, 24, 32, 48, 64])),
+                    int(rng.choice([4, 12, 16, 20, 32, 40, 64, 100])),
+                    int(rng.integers(1, 300)), K, s))
+    return out
+
+
+RANDOM_CONVT = _random_convt_cases(16, 20261204)
+
+
+@pytest.mark.parametrize("B,Cin,Cout,Tin,K,s", RANDOM_CONVT)
+def test_convtr1d_random_shapes(B, Cin, Cout, Tin, K, s):
+    announce(f"convtr1d random B={B} Cin={Cin} Cout={Cout} Tin={Tin} K={K} s={s}")
+    x = W.normal(0, f"convt/rnd-{Cin}-{Cout}-{Tin}/x", [B, Cin, Tin])
+    w = W.normal(0, f"convt/rnd-{Cin}-{Cout}-{Tin}/w", [Cin, Cout, K], 0.0, 2.0 / (Cin * K))
+    b = W.normal(0, f"convt/rnd-{Cin}-{Cout}-{Tin}/b", [Cout], 0.0, 0.01)
+    y = host(avae.convtr1d(cuda(x), cuda(w), cuda(b), stride=s))
+    ref = O.convtr1d(x, w, b, stride=s, pad=(K - s) // 2)
+    assert y.shape == ref.shape
+    assert rel_err(y, ref) <= TOL
