@@ -487,6 +487,12 @@ hipError_t run_conv1d_pipe(const float* x, float* y, const float* w, int B, int 
 // weights stream in during the whole MFMA work on the current chunk, with one
 // barrier per chunk.  The input window keeps the register path (its zero
 // padding at the sequence ends needs a select), double-buffered in LDS too.
+// The staging loads of the next chunk are spread over the k-steps of the
+// current one, each pinned between two groups of MFMAs by a scheduling
+// barrier (left alone, the compiler sinks them all to the end of the chunk,
+// just before the barrier that waits for them); the loads are branch-free
+// (every lane of the last DMA instruction has an LDS slot, input offsets are
+// clamped and out-of-range samples zeroed when stored).
 // Same GEMM, LDS layouts (padded weight rows), blocked accumulation and
 // epilogue as conv1d_pipe_kernel.  Cin must be a multiple of KC.
 // (Used for the 64-row tiles.  On the 96- and 48-row tiles it measured
@@ -507,15 +513,13 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void conv1d_dma_kernel(
     constexpr int GR = WS / 4, GV = WROW / 4;              // 16-byte granules per row
     constexpr int NG = BM * GR;                            // granules per weight buffer
     constexpr int NI = (NG + NT - 1) / NT;                 // DMA instructions per thread
-    constexpr int WBUF = NG * 4;                           // floats per weight buffer
+    constexpr int WBUF = NI * NT * 4;                      // floats per weight buffer (every lane has a slot)
     constexpr int XW_MAX = BN + (KT - 1) * DM;
     constexpr int XS = xs_stride_const(XW_MAX);
     constexpr int X_PT = (XW_MAX + kXLanes - 1) / kXLanes;
     static_assert(WROW % 4 == 0, "float4 weight rows");
+    static_assert(X_PT * kXLanes <= XS, "unconditional input stores stay inside the row");
 
-    // two buffers as separate arrays: the compiler then sees that the DMA
-    // into one cannot alias the LDS reads of the other, and does not wait
-    // for the DMA before the MFMA work of the current chunk
     __shared__ __align__(16) float WsA[WBUF];
     __shared__ __align__(16) float WsB[WBUF];
     __shared__ __align__(16) float XsA[KC * XS];
@@ -543,11 +547,7 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void conv1d_dma_kernel(
             part[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 
-    // Granule q = i*NT + tid of the padded [BM][GR] tile: row q / GR, float4
-    // q % GR of that row's chunk.  Pad granules and rows past Cout fetch an
-    // in-bounds float4 of row o0 (never read, or masked by the epilogue);
-    // lanes past the tile (q >= NG, last instruction only) issue no DMA.
-    int woff[NI];
+    unsigned woff[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int q = i * NT + tid;
@@ -556,59 +556,52 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void conv1d_dma_kernel(
         int o = o0 + row;
         if (row >= BM || o >= Cout) o = o0;
         if (f4 >= GV) f4 = 0;
-        woff[i] = o * Cin * KT + 4 * f4;
+        woff[i] = (unsigned)(o * Cin * KT + 4 * f4);
     }
     const int xw = BN + (KT - 1) * dil;
     const float* xb = x + (size_t)b * Cin * T;
     const int nch = Cin / KC;
+    // clamped input offsets (the loads never leave the row; out-of-range
+    // samples are zeroed when stored)
+    int xoff[X_PT];
+    bool xin[X_PT];
+#pragma unroll
+    for (int r = 0; r < X_PT; ++r) {
+        const int u = xcol + r * kXLanes;
+        const int t = t0 - pad + u;
+        xin[r] = u < xw && t >= 0 && t < T;
+        xoff[r] = min(max(t, 0), T - 1);
+    }
     float xr[X_PT];
-    float xa = 1.f;  // Snake alpha of this thread's staged input row
+    float xa = 1.f;
 
-    auto dma_w = [&](int ic0, float* wbuf) {
-        const float* wc = w + (size_t)ic0 * KT;
-#pragma unroll
-        for (int i = 0; i < NI; ++i)
-            if ((i + 1) * NT <= NG || i * NT + tid < NG)
-                // (void pointers: without the casts the host pass of this
-                // kernel fails silently and its launch stub goes missing)
-                __builtin_amdgcn_global_load_lds((const void*)(wc + woff[i]),
-                                                 (void*)(wbuf + (i * NT + wid * 64) * 4), 16, 0,
-                                                 0);
+    auto dma_one = [&](const float* wc, float* wbuf, int i) {
+        __builtin_amdgcn_global_load_lds((const void*)(wc + woff[i]),
+                                         (void*)(wbuf + (i * NT + wid * 64) * 4), 16, 0, 0);
     };
-    auto gx = [&](int ic0) {
-        const float* xrowp = xb + (size_t)(ic0 + xrow) * T;
-        if (SN && ep.in_alpha) xa = ep.in_alpha[ic0 + xrow];
-#pragma unroll
-        for (int r = 0; r < X_PT; ++r) {
-            const int u = xcol + r * kXLanes;
-            const int t = t0 - pad + u;
-            float v = 0.f;
-            if (u < xw && t >= 0 && t < T) v = xrowp[t];
-            xr[r] = v;
-        }
-    };
+    auto gx_one = [&](const float* xrowp, int r) { xr[r] = xrowp[xoff[r]]; };
     auto sx = [&](float* xbuf) {
-        if (SN && ep.in_alpha) {
-            // plain Snake of the input as staged (zero padding stays zero)
-            const float arev = xa * 0.15915494309189535f, inv = 1.0f / (xa + 1e-9f);
-#pragma unroll
-            for (int r = 0; r < X_PT; ++r) xr[r] = snake_beta(xr[r], arev, inv);
-        }
+        const float arev = xa * 0.15915494309189535f, inv = 1.0f / (xa + 1e-9f);
 #pragma unroll
         for (int r = 0; r < X_PT; ++r) {
-            const int u = xcol + r * kXLanes;
-            if (u < xw) xbuf[xrow * XS + u] = xr[r];
+            float v = xin[r] ? xr[r] : 0.f;
+            if (SN && ep.in_alpha) v = xin[r] ? snake_beta(v, arev, inv) : 0.f;
+            xbuf[xrow * XS + xcol + r * kXLanes] = v;
         }
     };
-    // one chunk: start staging chunk c+1 into (Wn, Xn), MFMA work on chunk c
-    // from (Wc, Xc), store the input window, barrier
+    // one chunk: MFMA work on chunk c from (Wc, Xc) with the staging of the
+    // next chunk into (Wn, Xn) spread evenly over its k-steps; the last
+    // chunk re-stages itself into the free buffers (never read)
     auto step = [&](int c, const float* Wc, const float* Xc, float* Wn, float* Xn) {
-        if (c + 1 < nch) {
-            dma_w((c + 1) * KC, Wn);
-            gx((c + 1) * KC);
-        }
-        constexpr int kTapUnroll = BM >= 48 ? 4 : 1;
-#pragma unroll kTapUnroll
+        const int cn = (c + 1 < nch) ? c + 1 : c;
+        const float* wc = w + (size_t)cn * KC * KT;
+        const float* xrowp = xb + (size_t)(cn * KC + xrow) * T;
+        if (SN && ep.in_alpha) xa = ep.in_alpha[cn * KC + xrow];
+        constexpr int SLOTS = KT * (KC / 4);  // k-steps of the chunk
+        constexpr int ITEMS = NI + X_PT;      // staging loads per thread
+        // 3-tap chunks are short: their loads go into the first quarter
+        constexpr int kSpread = KT <= 3 ? 4 : 1;
+#pragma unroll
         for (int j = 0; j < KT; ++j) {
 #pragma unroll
             for (int kk = 0; kk < KC / 4; ++kk) {
@@ -625,6 +618,16 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void conv1d_dma_kernel(
                     for (int cc = 0; cc < NTL; ++cc)
                         part[a][cc] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a], bv[cc],
                                                                            part[a][cc], 0, 0, 0);
+                const int slot = j * (KC / 4) + kk;
+#pragma unroll
+                for (int it = 0; it < ITEMS; ++it)
+                    if ((it * SLOTS) / (kSpread * ITEMS) == slot) {
+                        if (it < NI) dma_one(wc, Wn, it);
+                        else gx_one(xrowp, it - NI);
+                        // pin the load here: only VALU, SALU (not MFMA) and LDS reads
+                        // may be scheduled across this point
+                        __builtin_amdgcn_sched_barrier(0x106);
+                    }
             }
         }
         if ((c + 1) % flush == 0 || c + 1 == nch) {
@@ -636,15 +639,20 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void conv1d_dma_kernel(
                     part[a][cc] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
         }
-        if (c + 1 < nch) sx(Xn);
-        // the barrier also waits for this wave's DMA of chunk c+1
+        sx(Xn);
         __syncthreads();
     };
 
-    dma_w(0, WsA);
-    gx(0);
-    sx(XsA);
-    __syncthreads();
+    {
+        const float* xrowp = xb + (size_t)xrow * T;
+        if (SN && ep.in_alpha) xa = ep.in_alpha[xrow];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) dma_one(w, WsA, i);
+#pragma unroll
+        for (int r = 0; r < X_PT; ++r) gx_one(xrowp, r);
+        sx(XsA);
+        __syncthreads();
+    }
     for (int c = 0; c < nch; c += 2) {
         step(c, WsA, XsA, WsB, XsB);
         if (c + 1 < nch) step(c + 1, WsB, XsB, WsA, XsA);
@@ -661,7 +669,9 @@ hipError_t run_conv1d_dma(const float* x, float* y, const float* w, int B, int C
     const int m_tiles = (Cout + BM - 1) / BM;
     const int n_tiles = (Tout + BN - 1) / BN;
     const long long nblk = (long long)m_tiles * n_tiles * B;
-    if (nblk > 0x7fffffffLL || Cin % KC != 0 || (long long)Cout * Cin * KT >= (1LL << 31))
+    // (T >= 1: the kernel clamps its input offsets into [0, T-1])
+    if (nblk > 0x7fffffffLL || T < 1 || Cin % KC != 0 ||
+        (long long)Cout * Cin * KT >= (1LL << 31))
         return hipErrorInvalidValue;
     const int flush = (24 / ((KC / 4) * KT)) > 0 ? 24 / ((KC / 4) * KT) : 1;
     static const std::string name = "conv1d_dma_kernel<" + std::to_string(BM) + "," +
