@@ -490,14 +490,14 @@ hipError_t run_conv1d_pipe(const float* x, float* y, const float* w, int B, int 
 // The staging loads of the next chunk are spread over the k-steps of the
 // current one, each pinned between two groups of MFMAs by a scheduling
 // barrier (left alone, the compiler sinks them all to the end of the chunk,
-// just before the barrier that waits for them); the loads are branch-free
-// (every lane of the last DMA instruction has an LDS slot, input offsets are
-// clamped and out-of-range samples zeroed when stored).
+// just before the barrier that waits for them); the loads take no lane masks
+// (every lane of a wave that issues the last DMA instruction has an LDS slot,
+// input offsets are clamped and out-of-range samples zeroed when stored).
 // Same GEMM, LDS layouts (padded weight rows), blocked accumulation and
-// epilogue as conv1d_pipe_kernel.  Cin must be a multiple of KC.
-// (Used for the 64-row tiles.  On the 96- and 48-row tiles it measured
-// slower than the register-prefetch kernel for 11 taps and within a few
-// percent either way otherwise, so those keep conv1d_pipe_kernel.)
+// epilogue as conv1d_pipe_kernel.  Cin must be a multiple of KC.  Used for
+// the 96-, 64- and 48-row tiles (measured equal or up to 5% faster than the
+// register-prefetch kernel on the 96- and 48-row ones); the 32- and 16-row
+// tiles keep conv1d_pipe_kernel.
 template <int BM, int BN, int WM, int WN, int KT, int KC, int DM, bool SN>
 __global__ __launch_bounds__(WM * WN * 64, 2) void conv1d_dma_kernel(
     const float* __restrict__ x, float* y, const float* __restrict__ w, int Cin, int Cout,
@@ -513,7 +513,9 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void conv1d_dma_kernel(
     constexpr int GR = WS / 4, GV = WROW / 4;              // 16-byte granules per row
     constexpr int NG = BM * GR;                            // granules per weight buffer
     constexpr int NI = (NG + NT - 1) / NT;                 // DMA instructions per thread
-    constexpr int WBUF = NI * NT * 4;                      // floats per weight buffer (every lane has a slot)
+    // floats per weight buffer: every lane of a wave that takes part in the
+    // last DMA instruction has a slot (waves wholly past the tile skip it)
+    constexpr int WBUF = (NG + 63) / 64 * 64 * 4;
     constexpr int XW_MAX = BN + (KT - 1) * DM;
     constexpr int XS = xs_stride_const(XW_MAX);
     constexpr int X_PT = (XW_MAX + kXLanes - 1) / kXLanes;
@@ -576,8 +578,9 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void conv1d_dma_kernel(
     float xa = 1.f;
 
     auto dma_one = [&](const float* wc, float* wbuf, int i) {
-        __builtin_amdgcn_global_load_lds((const void*)(wc + woff[i]),
-                                         (void*)(wbuf + (i * NT + wid * 64) * 4), 16, 0, 0);
+        if (NG % NT == 0 || i + 1 < NI || i * NT + wid * 64 < NG)  // wave-uniform
+            __builtin_amdgcn_global_load_lds((const void*)(wc + woff[i]),
+                                             (void*)(wbuf + (i * NT + wid * 64) * 4), 16, 0, 0);
     };
     auto gx_one = [&](const float* xrowp, int r) { xr[r] = xrowp[xoff[r]]; };
     auto sx = [&](float* xbuf) {
@@ -696,7 +699,7 @@ template <int BM, int BN, int WM, int WN>
 hipError_t dispatch_pipe(const float* x, float* y, const float* w, int B, int Cin, int Cout,
                          int T, int Tout, int K, int dil, int pad, const ConvEpilogue& ep,
                          hipStream_t stream) {
-    if constexpr (BM == 64) {
+    if constexpr (BM == 64 || BM == 96 || BM == 48) {
       if (Cin % (K <= 3 ? 16 : 8) == 0 && (long long)Cout * Cin * K < (1LL << 31)) {
         switch (K) {
             case 1: return run_conv1d_dma<BM, BN, WM, WN, 1>(x, y, w, B, Cin, Cout, T, Tout, dil, pad, ep, stream);
@@ -1349,10 +1352,15 @@ hipError_t launch_conv1d(const float* x, float* y, const float* w, int B, int Ci
         if (Cout == 48)
             return dispatch_pipe<48, 128, 1, 4>(x, y, w, B, Cin, Cout, T, Tout, K, dilation, pad, ep, stream);
         if (Cout > 32) {
-            // 64 x 128 tiles; 64 x 64 when that would leave fewer than ~2.5
-            // blocks per CU on 256 CUs.
+            // 64 x 128 tiles; when that would leave fewer than ~2.5 blocks per
+            // CU on 256 CUs, 64 x 96 if those make one resident round of at
+            // least 384 blocks (two 4-wave blocks per CU: 512 slots; e.g. 768
+            // channels x 2 x 2000 samples: 504 blocks, where 64 x 64 tiles
+            // make 768, a round and a half), else 64 x 64.
             if (blocks(64, 128) >= 640)
                 return dispatch_pipe<64, 128, 2, 2>(x, y, w, B, Cin, Cout, T, Tout, K, dilation, pad, ep, stream);
+            if (blocks(64, 96) >= 384 && blocks(64, 96) <= 512)
+                return dispatch_pipe<64, 96, 2, 2>(x, y, w, B, Cin, Cout, T, Tout, K, dilation, pad, ep, stream);
             return dispatch_pipe<64, 64, 2, 2>(x, y, w, B, Cin, Cout, T, Tout, K, dilation, pad, ep, stream);
         }
         if (Cout > 16)
