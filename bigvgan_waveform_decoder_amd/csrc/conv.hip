@@ -501,7 +501,7 @@ hipError_t run_conv1d_pipe(const float* x, float* y, const float* w, int B, int 
 template <int BM, int BN, int WM, int WN, int KT, int KC, int DM, bool SN>
 __global__ __launch_bounds__(WM * WN * 64, 2) void conv1d_dma_kernel(
     const float* __restrict__ x, float* y, const float* __restrict__ w, int Cin, int Cout,
-    int T, int Tout, int dil, int pad, int m_tiles, int n_tiles, int nblk, int flush,
+    int T, int Tout, int dil, int pad, int m_tiles, int n_tiles, int nblk, int flush, int mg,
     ConvEpilogue ep) {
     constexpr int NT = WM * WN * 64;
     static_assert(NT == 256, "256 threads");
@@ -527,9 +527,18 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void conv1d_dma_kernel(
     __shared__ __align__(16) float XsA[KC * XS];
     __shared__ __align__(16) float XsB[KC * XS];
 
+    // Logical tiles in groups of mg output-channel tiles that sweep all time
+    // tiles (channel tile fastest inside a group): an XCD's contiguous range
+    // then needs the weights of about mg channel tiles, sized on the host to
+    // stay in its L2, while neighbouring tiles still share the input window.
     const int lid = xcd_remap(blockIdx.x, nblk);
-    const int mt_i = lid % m_tiles;
-    const int rest = lid / m_tiles;
+    const int nn_tiles = nblk / m_tiles;  // time tiles x batch
+    const int grp = lid / (mg * nn_tiles);
+    const int m_lo = grp * mg;
+    const int mg_eff = min(mg, m_tiles - m_lo);
+    const int r_in = lid - m_lo * nn_tiles;
+    const int mt_i = m_lo + r_in % mg_eff;
+    const int rest = r_in / mg_eff;
     const int nt_i = rest % n_tiles;
     const int b = rest / n_tiles;
     const int o0 = mt_i * BM, t0 = nt_i * BN;
@@ -677,6 +686,9 @@ hipError_t run_conv1d_dma(const float* x, float* y, const float* w, int B, int C
         (long long)Cout * Cin * KT >= (1LL << 31))
         return hipErrorInvalidValue;
     const int flush = (24 / ((KC / 4) * KT)) > 0 ? 24 / ((KC / 4) * KT) : 1;
+    // channel tiles per group: their weights within ~2.5 MB (an XCD's L2 is 4 MB)
+    const long long wtile = (long long)BM * Cin * KT * 4;
+    const int mg = (int)std::max(1LL, std::min((long long)m_tiles, (5LL << 19) / wtile));
     static const std::string name = "conv1d_dma_kernel<" + std::to_string(BM) + "," +
                                     std::to_string(BN) + "," + std::to_string(WM) + "," +
                                     std::to_string(WN) + "," + std::to_string(KT) + "," +
@@ -686,7 +698,7 @@ hipError_t run_conv1d_dma(const float* x, float* y, const float* w, int B, int C
     prof_pre(stream);
     hipLaunchKernelGGL((conv1d_dma_kernel<BM, BN, WM, WN, KT, KC, DM, SN>), dim3((unsigned)nblk),
                        dim3(WM * WN * 64), 0, stream, x, y, w, Cin, Cout, T, Tout, dil, pad,
-                       m_tiles, n_tiles, (int)nblk, flush, ep);
+                       m_tiles, n_tiles, (int)nblk, flush, mg, ep);
     const hipError_t e = hipGetLastError();
     const double out_n = (double)B * Cout * Tout;
     prof_post(stream, name.c_str(), 2.0 * out_n * Cin * KT,

@@ -38,6 +38,9 @@ CONV_CASES = [
     (2, 48, 70, 300, 3, 2, None, True),     # LDS-DMA staging, Cout tail in a 64-row tile
     (1, 64, 100, 200, 7, 9, None, False),   # 7 taps at dilation 9 (wider staged halo)
     (1, 36, 64, 300, 11, 1, None, False),   # Cin not a multiple of 8: register staging
+    # output-channel tiles in groups of two (weights of a tile ~1 MB), the
+    # last group holding one tile
+    (1, 384, 320, 600, 11, 1, None, True),
     # 64 x 96 tiles (one resident round of 384 blocks; ragged last time tile)
     (2, 64, 128, 9200, 11, 5, None, True),
     (2, 64, 64, 18400, 3, 1, None, False),
