@@ -498,8 +498,17 @@ hipError_t run_conv1d_pipe(const float* x, float* y, const float* w, int B, int 
 // the 96-, 64- and 48-row tiles (measured equal or up to 5% faster than the
 // register-prefetch kernel on the 96- and 48-row ones); the 32- and 16-row
 // tiles keep conv1d_pipe_kernel.
+// Input channels per K chunk of conv1d_dma_kernel: 16 for up to 3 taps; 4 for
+// the 11-tap 128-column tiles (33 KB of LDS and 142 VGPRs: three blocks per CU,
+// which share the CUs better with the other AMP blocks' kernels running
+// beside them); 8 otherwise.
+template <int BN, int KT>
+constexpr int dma_kc() {
+    return KT <= 3 ? 16 : (KT == 11 && BN == 128) ? 4 : 8;
+}
+
 template <int BM, int BN, int WM, int WN, int KT, int KC, int DM, bool SN>
-__global__ __launch_bounds__(WM * WN * 64, 2) void conv1d_dma_kernel(
+__global__ __launch_bounds__(WM * WN * 64, (KT == 11 && KC == 4) ? 3 : 2) void conv1d_dma_kernel(
     const float* __restrict__ x, float* y, const float* __restrict__ w, int Cin, int Cout,
     int T, int Tout, int dil, int pad, int m_tiles, int n_tiles, int nblk, int flush, int mg,
     ConvEpilogue ep) {
@@ -677,7 +686,7 @@ template <int BM, int BN, int WM, int WN, int KT, int DM = kDilMax, bool SN = fa
 hipError_t run_conv1d_dma(const float* x, float* y, const float* w, int B, int Cin, int Cout,
                           int T, int Tout, int dil, int pad, const ConvEpilogue& ep,
                           hipStream_t stream) {
-    constexpr int KC = KT <= 3 ? 16 : 8;
+    constexpr int KC = dma_kc<BN, KT>();
     const int m_tiles = (Cout + BM - 1) / BM;
     const int n_tiles = (Tout + BN - 1) / BN;
     const long long nblk = (long long)m_tiles * n_tiles * B;
