@@ -499,12 +499,12 @@ hipError_t run_conv1d_pipe(const float* x, float* y, const float* w, int B, int 
 // register-prefetch kernel on the 96- and 48-row ones); the 32- and 16-row
 // tiles keep conv1d_pipe_kernel.
 // Input channels per K chunk of conv1d_dma_kernel: 16 for up to 3 taps; 4 for
-// the 11-tap 128-column tiles (33 KB of LDS and 142 VGPRs: three blocks per CU,
-// which share the CUs better with the other AMP blocks' kernels running
+// 11 taps (on the 64x128 tile 33 KB of LDS and 142 VGPRs: three blocks per
+// CU, which share the CUs better with the other AMP blocks' kernels running
 // beside them); 8 otherwise.
 template <int BN, int KT>
 constexpr int dma_kc() {
-    return KT <= 3 ? 16 : (KT == 11 && BN == 128) ? 4 : 8;
+    return KT <= 3 ? 16 : KT == 11 ? 4 : 8;
 }
 
 template <int BM, int BN, int WM, int WN, int KT, int KC, int DM, bool SN>
