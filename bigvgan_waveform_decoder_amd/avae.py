@@ -131,6 +131,8 @@ def lib() -> ctypes.CDLL:
     L.avae_decoder_set_concurrent.argtypes = [P, c_int]
     L.avae_probe_mfma.restype = c_int
     L.avae_probe_mfma.argtypes = [c_int, c_int, c_int, P, P]
+    L.avae_probe_copy.restype = c_int
+    L.avae_probe_copy.argtypes = [P, P, ctypes.c_longlong, P]
     L.avae_bigvgan_decode.restype = c_int
     L.avae_bigvgan_decode.argtypes = [P, P, c_int, c_int, P, P, c_size_t, P]
     L.avae_bigvgan_decode_traced.restype = c_int
@@ -519,6 +521,14 @@ def probe_mfma(chains: int, blocks: int, iters: int, sink, stream=None) -> None:
     times it.  flops = blocks * 4 * iters * chains * 2048."""
     _check(lib().avae_probe_mfma(chains, blocks, iters, _dev(sink, "sink", (blocks * 256,)),
                                  _stream(stream)))
+
+def probe_copy(x, out, stream=None) -> None:
+    """avae_probe_copy: out = x by a streaming float4 copy (measurement
+    aid); the caller times it.  bytes moved = 8 * x.numel()."""
+    n = x.numel()
+    _check(lib().avae_probe_copy(_dev(x, "x"), _dev(out, "out", tuple(x.shape)), n,
+                                 _stream(stream)))
+
 
 def snake(x, alpha, out=None, stream=None):
     """avae_snake: plain Snake with alpha as stored; out may be x."""

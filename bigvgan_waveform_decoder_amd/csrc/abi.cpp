@@ -919,6 +919,17 @@ extern "C" int avae_probe_mfma(int chains, int blocks, int iters, float* sink, v
     return AVAE_OK;
 }
 
+extern "C" int avae_probe_copy(const float* x, float* y, long long n, void* stream) {
+    if (!x || !y) return fail(AVAE_EINVAL, "avae_probe_copy: null pointer");
+    if (n < 4 || n % 4 != 0 || n / 4 > 0x7fffffffLL * 256)
+        return fail(AVAE_EINVAL, "avae_probe_copy: n must be a positive multiple of 4 (got %lld)", n);
+    if ((((uintptr_t)x) | ((uintptr_t)y)) & 15)
+        return fail(AVAE_EINVAL, "avae_probe_copy: x and y must be 16-byte aligned");
+    avae::prof_set_phase(avae::kPhaseNone);
+    AVAE_TRY(avae::launch_stream_copy(x, y, n / 4, (hipStream_t)stream), "avae_probe_copy launch");
+    return AVAE_OK;
+}
+
 extern "C" int avae_snake(const float* x, float* y, int B, int C, int T, const float* alpha,
                           void* stream) {
     if (!x || !y || !alpha) return fail(AVAE_EINVAL, "avae_snake: null pointer");

@@ -62,7 +62,10 @@ __device__ __forceinline__ void up_pair(const float* xq, const ActTaps& taps, fl
 // the elements it sees used, and the narrowed pieces (a 16-byte lane
 // stride) conflict 4 ways in the LDS banks; full ds_read_b128 do not
 // (measured: +10% Activation1d throughput).  The block waits for its own
-// reads before it ends, so no output register is written after it.
+// reads before it ends, so no output register is written after it, and its
+// outputs are early-clobber: a read's destination must not overlap the
+// address register, which a later read of the block may issue from after
+// the earlier one's data has landed.
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void load12(const float* p, float* w) {
     const unsigned addr = (unsigned)(uintptr_t)p;  // LDS byte offset of p
@@ -72,7 +75,7 @@ __device__ __forceinline__ void load12(const float* p, float* w) {
         "ds_read_b128 %1, %3 offset:16\n"
         "ds_read_b128 %2, %3 offset:32\n"
         "s_waitcnt lgkmcnt(0)"
-        : "=v"(a), "=v"(b), "=v"(c)
+        : "=&v"(a), "=&v"(b), "=&v"(c)
         : "v"(addr)
         : "memory");
     w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
@@ -103,17 +106,21 @@ __device__ __forceinline__ void act1d_interior_stage(float4 a, float4 b, float4 
     if (tid < 4) dst[tid + 2 * kThreads] = c;
 }
 
-// Interior tile compute (input already staged in xs): every output exists
-// and the row start is 16-byte aligned (T % 4 == 0).  Each thread owns two
+// Tile compute (input already staged in xs, replicate-padded on edge tiles)
+// for rows with T % 4 == 0 and 16-byte aligned starts.  Each thread owns two
 // runs of 4 consecutive outputs, t0 + 4*tid + 1024*r + (0..3), so every
 // global and LDS access is a float4 and the 64 lanes of a wave touch 1 KiB
 // contiguously.  A 12-value register window of x feeds a run's 4 polyphase
 // pairs; two 12-value windows of the phase arrays feed its 4 stride-2 FIR
-// outputs.
-__device__ __forceinline__ void act1d_interior_compute(float* __restrict__ yrow, int t0,
-                                                       float alpha_rev, float inv_beta,
-                                                       const ActTaps& taps, const float* xs,
-                                                       float* se, float* so) {
+// outputs.  Edge tiles (the first and last of a row) take the same path:
+// the doubled-rate samples before position 0 become s[0] and those past
+// 2T-1 become s[2T-1] (the halo pairs directly, the ones past the row end
+// in a fix-up pass), and only outputs t < T are stored (whole float4
+// groups, T % 4 == 0).
+__device__ __forceinline__ void act1d_vec_compute(float* __restrict__ yrow, int T, int t0,
+                                                  bool edge, float alpha_rev, float inv_beta,
+                                                  const ActTaps& taps, const float* xs,
+                                                  float* se, float* so) {
     constexpr int kHalf = kTile / 2;
     const int tid = threadIdx.x;
     // Phase 1: q = t0 + 4 tid + kHalf r + k  <->  j = 8 + 4 tid + kHalf r + k.
@@ -133,15 +140,31 @@ __device__ __forceinline__ void act1d_interior_compute(float* __restrict__ yrow,
         *reinterpret_cast<float4*>(se + j0) = make_float4(ev[0], ev[1], ev[2], ev[3]);
         *reinterpret_cast<float4*>(so + j0) = make_float4(ov[0], ov[1], ov[2], ov[3]);
     }
-    // halo: q = t0-3 .. t0-1 (j = 5, 6, 7) and q = t0+kTile .. +2 (j = kTile+8 .. +10)
+    // halo: q = t0-3 .. t0-1 (j = 5, 6, 7) and q = t0+kTile .. +2 (j = kTile+8 .. +10);
+    // outside the row, the pair at the clamped position with both phases
+    // set to s[0] (q < 0) or s[2T-1] (q > T-1)
     if (tid < 6) {
         const int j = tid < 3 ? 5 + tid : kTile + 5 + tid;
+        const int q = t0 - 8 + j;
+        const int qc = min(max(q, 0), T - 1);
         float e, o;
-        up_pair(xs + j, taps, e, o);
+        up_pair(xs + (qc - (t0 - 8)), taps, e, o);
+        if (q < 0) o = e;
+        if (q > T - 1) e = o;
         se[j] = snake_beta(e, alpha_rev, inv_beta);
         so[j] = snake_beta(o, alpha_rev, inv_beta);
     }
     __syncthreads();
+    if (edge && t0 + kTile > T) {
+        // pairs at q = T .. t0+kTile-1 take s[2T-1] = so at q = T-1
+        const int jT = T - 1 - (t0 - 8);
+        const float sl = so[jT];
+        for (int j = jT + 1 + tid; j < kTile + 8; j += kThreads) {
+            se[j] = sl;
+            so[j] = sl;
+        }
+        __syncthreads();
+    }
 
     // Phase 2: y[t] = sum_m down[2m] so[t+m-3] + down[2m+1] se[t+m-2] for
     // t = t0 + 4 tid + kHalf r + k; so index = j0 + k + m - 3, se index + 1.
@@ -162,14 +185,34 @@ __device__ __forceinline__ void act1d_interior_compute(float* __restrict__ yrow,
             }
             out[k] = acc;
         }
-        *reinterpret_cast<float4*>(yrow + t0 + 4 * tid + kHalf * r) =
-            make_float4(out[0], out[1], out[2], out[3]);
+        const int t = t0 + 4 * tid + kHalf * r;
+        if (!edge || t < T)
+            *reinterpret_cast<float4*>(yrow + t) = make_float4(out[0], out[1], out[2], out[3]);
     }
 }
 
-// Edge tile (first or last tile of a row, a row shorter than a tile, or
-// T % 4 != 0): same arrays and index conventions, scalar and strided over
-// the block, every index clamped to implement the replicate padding.
+// Edge tile staging for the vector path: x[clamp(t0 - 8 + i)], i < kX, into
+// xs (the replicate padding), all of a thread's loads before its first LDS
+// write.
+__device__ __forceinline__ void act1d_stage_clamped(const float* __restrict__ xrow, int T,
+                                                    int t0, float* xs) {
+    constexpr int kLoads = (kX + kThreads - 1) / kThreads;
+    float xv[kLoads];
+#pragma unroll
+    for (int r = 0; r < kLoads; ++r) {
+        const int i = threadIdx.x + r * kThreads;
+        xv[r] = (i < kX) ? xrow[min(max(t0 - 8 + i, 0), T - 1)] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < kLoads; ++r) {
+        const int i = threadIdx.x + r * kThreads;
+        if (i < kX) xs[i] = xv[r];
+    }
+}
+
+// Scalar tile (rows with T % 4 != 0 or unaligned tensors): same arrays and
+// index conventions, scalar and strided over the block, every index clamped
+// to implement the replicate padding.
 __device__ __forceinline__ void act1d_tile_edge(const float* __restrict__ xrow,
                                                 float* __restrict__ yrow, int T, int t0,
                                                 float alpha_rev, float inv_beta,
@@ -222,7 +265,8 @@ __device__ __forceinline__ void act1d_tile_edge(const float* __restrict__ xrow,
 // order.  The next interior tile's input is loaded into registers right
 // after the current tile is staged, so its HBM latency overlaps the current
 // tile's compute.
-__global__ __launch_bounds__(kThreads) void act1d_kernel(
+// (six waves per SIMD: at most 80 VGPRs, six blocks' LDS per CU)
+__global__ __launch_bounds__(kThreads, 6) void act1d_kernel(
     const float* __restrict__ x, float* __restrict__ y, int C, int T, int tiles, int total,
     int per_block, int vec_ok, const float* __restrict__ log_alpha,
     const float* __restrict__ log_beta, ActTaps taps) {
@@ -253,15 +297,17 @@ __global__ __launch_bounds__(kThreads) void act1d_kernel(
         }
         const size_t base = (size_t)row * (size_t)T;
         if (id > first) __syncthreads();  // previous tile done with xs, se, so
-        if (interior(t0)) {
-            act1d_interior_stage(pa, pb, pc, xs);
+        if (vec_ok) {
+            const bool inner = interior(t0);
+            if (inner) act1d_interior_stage(pa, pb, pc, xs);
+            else act1d_stage_clamped(x + base, T, t0, xs);
             if (id + 1 < last) {
                 const int nrow = (id + 1) / tiles;
                 const int nt0 = (id + 1 - nrow * tiles) * kTile;
                 if (interior(nt0)) act1d_interior_load(x + (size_t)nrow * T, nt0, pa, pb, pc);
             }
             __syncthreads();
-            act1d_interior_compute(y + base, t0, alpha_rev, inv_beta, taps, xs, se, so);
+            act1d_vec_compute(y + base, T, t0, !inner, alpha_rev, inv_beta, taps, xs, se, so);
         } else {
             if (id + 1 < last) {
                 const int nrow = (id + 1) / tiles;

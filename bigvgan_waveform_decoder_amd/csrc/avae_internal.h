@@ -110,6 +110,7 @@ hipError_t launch_sum_into(float* y, float* const* x, int n, size_t count, hipSt
 // threads, each wave running `chains` (8 or 16) independent FP32 MFMA
 // accumulator chains for `iters` iterations; sink gets blocks*256 floats.
 hipError_t launch_mfma_probe(int chains, int blocks, int iters, float* sink, hipStream_t s);
+hipError_t launch_stream_copy(const float* x, float* y, long long n4, hipStream_t s);
 
 // y[b,c,t] = x[b,c,t] * scale[c] + shift[c]
 hipError_t launch_channel_affine(const float* x, float* y, const float* scale,

@@ -1,5 +1,8 @@
-// Matrix-core throughput probe: a measurement aid for the convolution
-// kernels' roofline, not part of the decode path.  Every wave runs N
+// Measurement aids, not part of the decode path: a matrix-core throughput
+// probe for the convolution kernels' roofline and a streaming copy that
+// gives the HBM rate a plain read-and-write kernel reaches.
+//
+// Matrix-core probe:  Every wave runs N
 // independent v_mfma_f32_16x16x4_f32 accumulator chains (the instruction
 // the convolutions use) with no memory traffic inside the loop, so the
 // achieved rate is what the matrix cores deliver for that many independent
@@ -42,7 +45,26 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(float* __restrict__ sin
     sink[(size_t)blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// Streaming copy y = x of n4 float4: one float4 per thread, no loop, so every
+// load of a wave is in flight at once and the grid streams HBM both ways.
+__global__ __launch_bounds__(256) void stream_copy_kernel(const float4* __restrict__ x,
+                                                          float4* __restrict__ y, long long n4) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i < n4) y[i] = x[i];
+}
+
 }  // namespace
+
+hipError_t launch_stream_copy(const float* x, float* y, long long n4, hipStream_t s) {
+    const long long blocks = (n4 + 255) / 256;
+    if (blocks < 1 || blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    prof_pre(s);
+    hipLaunchKernelGGL(stream_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       reinterpret_cast<const float4*>(x), reinterpret_cast<float4*>(y), n4);
+    const hipError_t e = hipGetLastError();
+    prof_post(s, "stream_copy_kernel", 0.0, 32.0 * (double)n4);
+    return e;
+}
 
 hipError_t launch_mfma_probe(int chains, int blocks, int iters, float* sink, hipStream_t s) {
     prof_pre(s);

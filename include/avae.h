@@ -440,6 +440,16 @@ int avae_profile_phases(double* ms6);
  */
 int avae_probe_mfma(int chains, int blocks, int iters, float* sink, void* stream);
 
+/*
+ * Streaming-copy probe, a measurement aid for the HBM roofline of the
+ * memory-bound kernels (Activation1d): y[i] = x[i] for i < n, one float4 per
+ * thread, enqueued on `stream` (the caller times it: 8 n bytes moved).
+ * x and y are device buffers of n floats, 16-byte aligned, not overlapping.
+ * Errors: EINVAL (null pointer, n not a positive multiple of 4, misaligned
+ * buffers), EHIP.
+ */
+int avae_probe_copy(const float* x, float* y, long long n, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

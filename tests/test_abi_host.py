@@ -95,6 +95,9 @@ def test_decoder_create_rejects_bad_config():
     assert L.avae_probe_mfma(8, 1, 1, None, None) == -1
     assert L.avae_probe_mfma(7, 1, 1, fake, None) == -1
     assert L.avae_probe_mfma(16, 0, 1, fake, None) == -1
+    assert L.avae_probe_copy(None, fake, 16, None) == -1
+    assert L.avae_probe_copy(fake, fake, 6, None) == -1
+    assert L.avae_probe_copy(fake, ctypes.c_void_p(0x1004), 16, None) == -1
 
 
 def test_streaming_rejects_bad_arguments():

@@ -22,7 +22,10 @@ def _inputs(tag, B, C, T, scale=1.0):
 
 @pytest.mark.parametrize("B,C,T,scale", [
     (1, 1, 1, 1.0), (1, 3, 2, 1.0), (2, 3, 7, 3.0), (1, 2, 1023, 1.0), (1, 2, 1024, 1.0),
-    (2, 2, 1025, 1.0), (1, 4, 3000, 10.0), (1, 2, 5000, 1000.0), (3, 5, 2049, 0.01)])
+    (2, 2, 1025, 1.0), (1, 4, 3000, 10.0), (1, 2, 5000, 1000.0), (3, 5, 2049, 0.01),
+    # T % 4 == 0: edge tiles on the vector path (first, last, partial, single)
+    (1, 2, 4, 1.0), (2, 3, 8, 1.0), (1, 2, 12, 2.0), (1, 3, 2048, 1.0), (2, 2, 2052, 1.0),
+    (1, 2, 4096, 1.0), (1, 2, 4104, 1.0), (1, 1, 6148, 1.0)])
 def test_act1d_matches_oracle(B, C, T, scale):
     announce(f"act1d B={B} C={C} T={T} scale={scale}")
     x, la, lb = _inputs(f"{B}-{C}-{T}", B, C, T, scale)
@@ -100,3 +103,15 @@ def test_mfma_probe_runs_and_sums_are_finite():
         nz = np.abs(s10) > 1e-12
         assert nz.sum() > 0
         np.testing.assert_allclose(s11[nz], 1.1 * s10[nz], rtol=1e-4)
+
+
+def test_probe_copy_is_exact():
+    """The streaming-copy probe bench.py times copies every element, including
+    a last partial block."""
+    import torch
+    announce("stream copy probe")
+    for n in (4, 1024, 4 * 1000 + 8):
+        x = torch.from_numpy(W.normal(0, f"copy/{n}", [n])).to("cuda:0")
+        y = torch.full_like(x, float("nan"))
+        avae.probe_copy(x, y)
+        assert np.array_equal(host(y), host(x))
