@@ -39,6 +39,11 @@ constexpr int kTile = 8 * kThreads;        // outputs per block
 constexpr int kX = kTile + 16;             // staged input: x[t0-8 .. t0+kTile+8)
 constexpr int kQ = kTile + 16;             // phase arrays: index j <-> q = t0 - 8 + j
 
+// Source of the unconditional prefetch when the next tile is not interior
+// (its loads must stay in bounds; the values are never used).
+__device__ __align__(16) float g_zero_window[kX];
+
+
 // The doubled-rate pair (2q, 2q+1) from x[q-3 .. q+3], xq pointing at x[q].
 __device__ __forceinline__ void up_pair(const float* xq, const ActTaps& taps, float& e, float& o) {
     e = 0.f;
@@ -89,13 +94,17 @@ __device__ __forceinline__ void load12(const float* p, float* w) {
 // previous tile's compute.  (Plain register variables: passed as a struct
 // by reference, the window was kept in scratch memory and every prefetch
 // waited for its load.)
-__device__ __forceinline__ void act1d_interior_load(const float* __restrict__ xrow, int t0,
-                                                    float4& a, float4& b, float4& c) {
+// w points at the tile's first input (x + t0); the window starts 8 before.
+__device__ __forceinline__ void act1d_window_load(const float* __restrict__ w, float4& a,
+                                                  float4& b, float4& c) {
     const int tid = threadIdx.x;
-    const float4* src = reinterpret_cast<const float4*>(xrow + t0 - 8);
+    const float4* src = reinterpret_cast<const float4*>(w - 8);
     a = src[tid];
     b = src[tid + kThreads];
-    c = (tid < 4) ? src[tid + 2 * kThreads] : make_float4(0.f, 0.f, 0.f, 0.f);
+    // every lane loads (lanes >= 4 re-read one of the four tail float4 and
+    // drop it): a load under a lane mask cannot be counted by the compiler,
+    // which then waits for all memory operations, later stores included
+    c = src[2 * kThreads + (tid & 3)];
 }
 
 __device__ __forceinline__ void act1d_interior_stage(float4 a, float4 b, float4 c, float* xs) {
@@ -117,10 +126,12 @@ __device__ __forceinline__ void act1d_interior_stage(float4 a, float4 b, float4 
 // 2T-1 become s[2T-1] (the halo pairs directly, the ones past the row end
 // in a fix-up pass), and only outputs t < T are stored (whole float4
 // groups, T % 4 == 0).
-__device__ __forceinline__ void act1d_vec_compute(float* __restrict__ yrow, int T, int t0,
-                                                  bool edge, float alpha_rev, float inv_beta,
-                                                  const ActTaps& taps, const float* xs,
-                                                  float* se, float* so) {
+// The thread's two output groups come back in out[0..1] (t0 + 4 tid and
+// t0 + 4 tid + kTile/2); the caller stores them.
+__device__ __forceinline__ void act1d_vec_compute(int T, int t0, bool edge, float alpha_rev,
+                                                  float inv_beta, const ActTaps& taps,
+                                                  const float* xs, float* se, float* so,
+                                                  float4 (&res)[2]) {
     constexpr int kHalf = kTile / 2;
     const int tid = threadIdx.x;
     // Phase 1: q = t0 + 4 tid + kHalf r + k  <->  j = 8 + 4 tid + kHalf r + k.
@@ -185,9 +196,7 @@ __device__ __forceinline__ void act1d_vec_compute(float* __restrict__ yrow, int 
             }
             out[k] = acc;
         }
-        const int t = t0 + 4 * tid + kHalf * r;
-        if (!edge || t < T)
-            *reinterpret_cast<float4*>(yrow + t) = make_float4(out[0], out[1], out[2], out[3]);
+        res[r] = make_float4(out[0], out[1], out[2], out[3]);
     }
 }
 
@@ -278,42 +287,84 @@ __global__ __launch_bounds__(kThreads, 6) void act1d_kernel(
     const int last = min(first + per_block, total);
     auto interior = [&](int t0) { return vec_ok && t0 >= 8 && t0 + kTile + 8 <= T; };
 
-    float4 pa = make_float4(0.f, 0.f, 0.f, 0.f), pb = pa, pc = pa;
-    {
-        const int row = first / tiles;
-        const int t0 = (first - row * tiles) * kTile;
-        if (interior(t0)) act1d_interior_load(x + (size_t)row * T, t0, pa, pb, pc);
-    }
+    // The next tile's window is loaded every tile, unconditionally: from the
+    // row when the next tile is interior, else from a zero window that is
+    // never used.  (A conditional load made the window a two-way merge that
+    // the compiler resolved with register copies at the loop latch, each
+    // waiting for every outstanding memory operation, the tile's own stores
+    // included.)
+    auto window = [&](int id) -> const float* {
+        if (id < last) {
+            const int row = id / tiles;
+            const int t0 = (id - row * tiles) * kTile;
+            if (interior(t0)) return x + (size_t)row * T + t0;
+        }
+        return g_zero_window + 8;
+    };
     int cur_c = -1;
     float alpha_rev = 0.f, inv_beta = 0.f;
-    for (int id = first; id < last; ++id) {
-        const int row = id / tiles;
-        const int t0 = (id - row * tiles) * kTile;
+    auto set_channel = [&](int row) {
         const int c = row % C;
         if (c != cur_c) {
             cur_c = c;
             alpha_rev = snake_alpha_rev(log_alpha[c]);
             inv_beta = snake_inv_beta(log_beta[c]);
         }
-        const size_t base = (size_t)row * (size_t)T;
-        if (id > first) __syncthreads();  // previous tile done with xs, se, so
-        if (vec_ok) {
+    };
+    // (two loops: with the float4 / scalar choice inside one, the window
+    // registers were again a two-way merge)
+    if (vec_ok) {
+        // A tile's two output groups are stored a tile later, after the
+        // next window's loads are issued: loads and stores share one wait
+        // counter, and a wait for the window then never waits for stores
+        // issued just before it (they have a whole tile's compute to land).
+        float4 pa, pb, pc;
+        float4 res[2];
+        float* dst[2] = {nullptr, nullptr};
+        auto store = [&]() {
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+                if (dst[r]) *reinterpret_cast<float4*>(dst[r]) = res[r];
+        };
+        act1d_window_load(window(first), pa, pb, pc);
+        for (int id = first; id < last; ++id) {
+            const int row = id / tiles;
+            const int t0 = (id - row * tiles) * kTile;
+            set_channel(row);
+            const size_t base = (size_t)row * (size_t)T;
+            if (id > first) __syncthreads();  // previous tile done with xs, se, so
             const bool inner = interior(t0);
-            if (inner) act1d_interior_stage(pa, pb, pc, xs);
-            else act1d_stage_clamped(x + base, T, t0, xs);
-            if (id + 1 < last) {
-                const int nrow = (id + 1) / tiles;
-                const int nt0 = (id + 1 - nrow * tiles) * kTile;
-                if (interior(nt0)) act1d_interior_load(x + (size_t)nrow * T, nt0, pa, pb, pc);
+            if (inner) {
+                act1d_interior_stage(pa, pb, pc, xs);
+            } else {
+                // the window was loaded (from the zero window) but is not
+                // used: consume it here so that no load into these registers
+                // is pending on either path when the next window overwrites
+                // them (a pending one made the compiler wait for every memory
+                // operation there, the stores just issued included)
+                asm volatile("" ::"v"(pa.x), "v"(pa.y), "v"(pa.z), "v"(pa.w), "v"(pb.x),
+                             "v"(pb.y), "v"(pb.z), "v"(pb.w), "v"(pc.x), "v"(pc.y), "v"(pc.z),
+                             "v"(pc.w));
+                act1d_stage_clamped(x + base, T, t0, xs);
             }
+            act1d_window_load(window(id + 1), pa, pb, pc);
+            store();  // the previous tile's outputs, behind the next window's loads
             __syncthreads();
-            act1d_vec_compute(y + base, T, t0, !inner, alpha_rev, inv_beta, taps, xs, se, so);
-        } else {
-            if (id + 1 < last) {
-                const int nrow = (id + 1) / tiles;
-                const int nt0 = (id + 1 - nrow * tiles) * kTile;
-                if (interior(nt0)) act1d_interior_load(x + (size_t)nrow * T, nt0, pa, pb, pc);
+            act1d_vec_compute(T, t0, !inner, alpha_rev, inv_beta, taps, xs, se, so, res);
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int t = t0 + 4 * (int)threadIdx.x + (kTile / 2) * r;
+                dst[r] = (inner || t < T) ? y + base + t : nullptr;
             }
+        }
+        store();
+    } else {
+        for (int id = first; id < last; ++id) {
+            const int row = id / tiles;
+            const int t0 = (id - row * tiles) * kTile;
+            set_channel(row);
+            const size_t base = (size_t)row * (size_t)T;
+            if (id > first) __syncthreads();
             act1d_tile_edge(x + base, y + base, T, t0, alpha_rev, inv_beta, taps, xs, se, so);
         }
     }
