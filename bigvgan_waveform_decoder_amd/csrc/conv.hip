@@ -501,14 +501,15 @@ hipError_t run_conv1d_pipe(const float* x, float* y, const float* w, int B, int 
 // Input channels per K chunk of conv1d_dma_kernel: 16 for up to 3 taps; 4 for
 // 11 taps (on the 64x128 tile 33 KB of LDS and 142 VGPRs: three blocks per
 // CU, which share the CUs better with the other AMP blocks' kernels running
-// beside them); 8 otherwise.
+// beside them); 8 otherwise.  The 160-column tile (three blocks per CU,
+// 150-168 VGPRs) takes 8 for up to 3 taps and 4 otherwise.
 template <int BN, int KT>
 constexpr int dma_kc() {
-    return KT <= 3 ? 16 : KT == 11 ? 4 : 8;
+    return BN == 160 ? (KT <= 3 ? 8 : 4) : KT <= 3 ? 16 : KT == 11 ? 4 : 8;
 }
 
 template <int BM, int BN, int WM, int WN, int KT, int KC, int DM, bool SN>
-__global__ __launch_bounds__(WM * WN * 64, (KT == 11 && KC == 4) ? 3 : 2) void conv1d_dma_kernel(
+__global__ __launch_bounds__(WM * WN * 64, ((KT == 11 && KC == 4) || BN == 160) ? 3 : 2) void conv1d_dma_kernel(
     const float* __restrict__ x, float* y, const float* __restrict__ w, int Cin, int Cout,
     int T, int Tout, int dil, int pad, int m_tiles, int n_tiles, int nblk, int flush, int mg,
     ConvEpilogue ep) {
@@ -1378,14 +1379,17 @@ hipError_t launch_conv1d(const float* x, float* y, const float* w, int B, int Ci
             // least 384 blocks (two 4-wave blocks per CU: 512 slots; e.g. 768
             // channels x 2 x 2000 samples: 504 blocks, where 64 x 64 tiles
             // make 768, a round and a half), else 64 x 64.
-            // 11 taps (three blocks per CU: 768 slots): 64 x 160 tiles when
-            // they make one resident round where 64 x 128 would make more
-            // (384 channels x 2 x 10000 samples: 756 blocks instead of 948;
-            // 558 -> 516 us alone)
-            if (K == 11 && !snake && Cin % dma_kc<160, 11>() == 0 && dilation <= kDilMax &&
+            // 64 x 160 tiles (three blocks per CU: 768 slots) when they make
+            // one resident round where 64 x 128 would make more (384 channels
+            // x 2 x 10000 samples: 756 blocks instead of 948; a launch alone
+            // 558 -> 516 us at 11 taps, -6% at 7 and 3)
+            if ((K == 11 || K == 7 || K == 3) && !snake && Cin % 8 == 0 && dilation <= kDilMax &&
                 (long long)Cout * Cin * K < (1LL << 31) && blocks(64, 128) > 768 &&
-                blocks(64, 160) <= 768 && blocks(64, 160) >= 600)
-                return run_conv1d_dma<64, 160, 2, 2, 11>(x, y, w, B, Cin, Cout, T, Tout, dilation, pad, ep, stream);
+                blocks(64, 160) <= 768 && blocks(64, 160) >= 600) {
+                if (K == 11) return run_conv1d_dma<64, 160, 2, 2, 11>(x, y, w, B, Cin, Cout, T, Tout, dilation, pad, ep, stream);
+                if (K == 7) return run_conv1d_dma<64, 160, 2, 2, 7>(x, y, w, B, Cin, Cout, T, Tout, dilation, pad, ep, stream);
+                return run_conv1d_dma<64, 160, 2, 2, 3>(x, y, w, B, Cin, Cout, T, Tout, dilation, pad, ep, stream);
+            }
             if (blocks(64, 128) >= 640)
                 return dispatch_pipe<64, 128, 2, 2>(x, y, w, B, Cin, Cout, T, Tout, K, dilation, pad, ep, stream);
             if (blocks(64, 96) >= 384 && blocks(64, 96) <= 512)

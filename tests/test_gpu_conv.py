@@ -41,10 +41,12 @@ CONV_CASES = [
     # output-channel tiles in groups of two (weights of a tile ~1 MB), the
     # last group holding one tile
     (1, 384, 320, 600, 11, 1, None, True),
-    # 11-tap 64 x 160 tiles (one round of <= 768 blocks where 64 x 128 makes
-    # more; ragged last time tile, Cout tail)
+    # 64 x 160 tiles (one round of <= 768 blocks where 64 x 128 makes more;
+    # ragged last time tile, Cout tail)
     (2, 16, 64, 59999, 11, 3, None, True),
     (1, 8, 100, 52700, 11, 1, None, False),
+    (2, 16, 64, 59999, 7, 5, None, False),
+    (1, 16, 100, 52700, 3, 1, None, True),
     # 64 x 96 tiles (one resident round of 384 blocks; ragged last time tile)
     (2, 64, 128, 9200, 11, 5, None, True),
     (2, 64, 64, 18400, 3, 1, None, False),
