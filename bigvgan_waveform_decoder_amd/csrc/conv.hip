@@ -501,11 +501,13 @@ hipError_t run_conv1d_pipe(const float* x, float* y, const float* w, int B, int 
 // Input channels per K chunk of conv1d_dma_kernel: 16 for up to 3 taps; 4 for
 // 11 taps (on the 64x128 tile 33 KB of LDS and 142 VGPRs: three blocks per
 // CU, which share the CUs better with the other AMP blocks' kernels running
-// beside them); 8 otherwise.  The 160-column tile (three blocks per CU,
-// 150-168 VGPRs) takes 8 for up to 3 taps and 4 otherwise.
+// beside them), except on the 96-column tile, whose grids are one round of
+// two blocks per CU (8: fewer barriers); 8 otherwise.  The 160-column tile
+// (three blocks per CU, 150-168 VGPRs) takes 8 for up to 3 taps and 4
+// otherwise.
 template <int BN, int KT>
 constexpr int dma_kc() {
-    return BN == 160 ? (KT <= 3 ? 8 : 4) : KT <= 3 ? 16 : KT == 11 ? 4 : 8;
+    return BN == 160 ? (KT <= 3 ? 8 : 4) : KT <= 3 ? 16 : (KT == 11 && BN != 96) ? 4 : 8;
 }
 
 template <int BM, int BN, int WM, int WN, int KT, int KC, int DM, bool SN>
