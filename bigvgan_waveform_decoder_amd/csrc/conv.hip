@@ -1435,6 +1435,13 @@ hipError_t launch_convtr1d(const float* x, float* y, const float* w, const float
         return run_convtr1d_poly<2, 2, 2, 11, 5>(x, y, w, bias, in_alpha, B, Cin, Cout, Tin, Tout, pad, stream);
     if (vec && stride == 5 && K == 10)
         return run_convtr1d_poly<2, 2, 2, 10, 5>(x, y, w, bias, in_alpha, B, Cin, Cout, Tin, Tout, pad, stream);
+    // stride 2: 64-channel tiles of 64 positions, narrower and longer tiles
+    // for the narrow stages (Cout <= 32: 16 x 256, e.g. 24 -> 12 at 160000
+    // positions 80 -> 37 us; Cout 96: 32 x 128, 100 -> 87 us)
+    if (vec && stride == 2 && K == 4 && Cout <= 32)
+        return run_convtr1d_poly<1, 4, 4, 4, 2>(x, y, w, bias, in_alpha, B, Cin, Cout, Tin, Tout, pad, stream);
+    if (vec && stride == 2 && K == 4 && Cout % 32 == 0 && Cout % 64 != 0)
+        return run_convtr1d_poly<2, 2, 4, 4, 2>(x, y, w, bias, in_alpha, B, Cin, Cout, Tin, Tout, pad, stream);
     if (vec && stride == 2 && K == 4)
         return run_convtr1d_poly<4, 1, 4, 4, 2>(x, y, w, bias, in_alpha, B, Cin, Cout, Tin, Tout, pad, stream);
     if (vec && stride == 8 && K == 16)

@@ -121,6 +121,9 @@ CONVT_CASES = [
     (1, 32, 20, 50, 11, 5, -1),    # short input: 16-channel tiles, LDS-DMA, Cout tail
     (2, 48, 20, 77, 8, 4, -1),
     (1, 16, 33, 29, 11, 5, -1),    # Cout*K not a multiple of 4: generic kernel
+    (2, 48, 24, 300, 4, 2, -1),    # stride 2, Cout <= 32: 16 x 256 tiles (LDS DMA)
+    (1, 24, 12, 500, 4, 2, -1),    # the same with Cin not a multiple of 16 (register staging)
+    (2, 64, 96, 257, 4, 2, -1),    # stride 2, Cout 96: 32 x 128 tiles
 ]
 
 
