@@ -1370,9 +1370,17 @@ hipError_t launch_conv1d(const float* x, float* y, const float* w, int B, int Ci
             return (long long)((Cout + bm - 1) / bm) * ((Tout + bn - 1) / bn) * B;
         };
         // Cout tiles that divide the decoder's widths: 96 and 48 (H3's 96- and
-        // 48-channel stages) avoid padding a 64-row tile.
-        if (Cout % 96 == 0 && Cout % 64 != 0)
+        // 48-channel stages) avoid padding a 64-row tile.  Long grids (the
+        // DAV decoder's 96-channel stage over 441344 samples: 6896 blocks)
+        // take 96 x 128 tiles, whose rounds are many enough that only the
+        // halved input re-staging counts; short ones keep 96 x 64 (H3 at
+        // 40000 samples: 96 x 128 made 626 blocks, 1.2 rounds, 10% slower),
+        // and so do 11 taps, which spill at 96 x 128.
+        if (Cout % 96 == 0 && Cout % 64 != 0) {
+            if (K != 11 && blocks(96, 128) >= 2048)
+                return dispatch_pipe<96, 128, 2, 2>(x, y, w, B, Cin, Cout, T, Tout, K, dilation, pad, ep, stream);
             return dispatch_pipe<96, 64, 2, 2>(x, y, w, B, Cin, Cout, T, Tout, K, dilation, pad, ep, stream);
+        }
         if (Cout == 48)
             return dispatch_pipe<48, 128, 1, 4>(x, y, w, B, Cin, Cout, T, Tout, K, dilation, pad, ep, stream);
         if (Cout > 32) {

@@ -51,6 +51,10 @@ CONV_CASES = [
     (2, 64, 128, 9200, 11, 5, None, True),
     (2, 64, 64, 18400, 3, 1, None, False),
     (1, 128, 128, 18400, 7, 3, None, False),
+    # 96 x 128 tiles (96-row channel tiles over grids of >= 2048 blocks;
+    # ragged last time tile, three channel tiles)
+    (1, 16, 96, 262100, 7, 3, None, True),
+    (1, 16, 288, 90000, 3, 1, None, False),
 ]
 
 
