@@ -118,6 +118,11 @@ def lib() -> ctypes.CDLL:
     L.avae_amp_block.restype = c_int
     L.avae_amp_block.argtypes = [P, P, c_int, c_int, c_int, c_int, c_int, P, P, P, P, P, P, P,
                                  c_float, c_int, P, c_size_t, P]
+    L.avae_amp_block_static_max_bytes.restype = c_size_t
+    L.avae_amp_block_static_max_bytes.argtypes = []
+    L.avae_amp_block_static.restype = c_int
+    L.avae_amp_block_static.argtypes = [P, P, c_int, c_int, c_int, c_int, c_int, P, P, P, P, P,
+                                        P, P, c_float, c_int, P]
     L.avae_decoder_create.restype = c_int
     L.avae_decoder_create.argtypes = [ctypes.POINTER(avae_config), ctypes.POINTER(avae_weights),
                                       ctypes.POINTER(P)]
@@ -359,6 +364,41 @@ def amp_block(x, K: int, dil: Sequence[int], w1: List, b1: List, w2: List, b2: L
         ctypes.addressof(w1a), ctypes.addressof(b1a), ctypes.addressof(w2a),
         ctypes.addressof(b2a), ctypes.addressof(laa), ctypes.addressof(lba), float(out_scale),
         1 if accumulate else 0, workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return out
+
+
+def amp_block_static_max_bytes() -> int:
+    return int(lib().avae_amp_block_static_max_bytes())
+
+
+def amp_block_static(x, K: int, dil: Sequence[int], w1: List, b1: List, w2: List, b2: List,
+                     log_alpha: List, log_beta: List, out_scale: float = 1.0,
+                     accumulate: bool = False, out=None, stream=None):
+    """avae_amp_block_static: avae_amp_block with the library's static device
+    scratch instead of a workspace (nothing is allocated by the library;
+    `out` is allocated here only when the caller passes none)."""
+    torch = _torch()
+    B, C, T = x.shape
+    n = len(dil)
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs an existing out tensor")
+        out = torch.empty_like(x)
+    if len(w1) != n or len(w2) != n or len(log_alpha) != 2 * n or len(log_beta) != 2 * n:
+        raise ValueError("amp_block_static: per-dilation lists have the wrong length")
+    dil_a = (c_int * n)(*[int(d) for d in dil])
+    arr = lambda ts, nm, shape: (P * len(ts))(*[_opt(t, nm, shape) for t in ts])
+    w1a = arr(w1, "w1", (C, C, K))
+    b1a = arr(b1, "b1", (C,))
+    w2a = arr(w2, "w2", (C, C, K))
+    b2a = arr(b2, "b2", (C,))
+    laa = arr(log_alpha, "log_alpha", (C,))
+    lba = arr(log_beta, "log_beta", (C,))
+    _check(lib().avae_amp_block_static(
+        _dev(x, "x"), _dev(out, "out", (B, C, T)), B, C, T, K, n, ctypes.addressof(dil_a),
+        ctypes.addressof(w1a), ctypes.addressof(b1a), ctypes.addressof(w2a),
+        ctypes.addressof(b2a), ctypes.addressof(laa), ctypes.addressof(lba), float(out_scale),
+        1 if accumulate else 0, _stream(stream)))
     return out
 
 

@@ -226,39 +226,44 @@ extern "C" size_t avae_amp_block_workspace_bytes(int B, int C, int T) {
     return 3 * round_up((size_t)B * C * T * sizeof(float), 256) + amp_pack_reserve(C);
 }
 
-extern "C" int avae_amp_block(const float* x, float* y, int B, int C, int T, int K, int n_dil,
-                              const int* dil, const float* const* w1, const float* const* b1,
-                              const float* const* w2, const float* const* b2,
-                              const float* const* log_alpha, const float* const* log_beta,
-                              float out_scale, int accumulate, void* workspace, size_t ws_bytes,
-                              void* stream) {
+namespace {
+// Argument checks shared by avae_amp_block and avae_amp_block_static
+// (`who` names the entry point in the messages).
+int amp_block_check(const char* who, const float* x, const float* y, int B, int C, int T, int K,
+                    int n_dil, const int* dil, const float* const* w1, const float* const* w2,
+                    const float* const* log_alpha, const float* const* log_beta) {
     if (!x || !y || !dil || !w1 || !w2 || !log_alpha || !log_beta)
-        return fail(AVAE_EINVAL, "avae_amp_block: null pointer");
-    if (B < 1 || C < 1 || T < 1 || n_dil < 1)
-        return fail(AVAE_EINVAL, "avae_amp_block: bad size");
-    if (n_dil > AVAE_MAX_DIL) return fail(AVAE_ESHAPE, "avae_amp_block: n_dil > %d", AVAE_MAX_DIL);
+        return fail(AVAE_EINVAL, "%s: null pointer", who);
+    if (B < 1 || C < 1 || T < 1 || n_dil < 1) return fail(AVAE_EINVAL, "%s: bad size", who);
+    if (n_dil > AVAE_MAX_DIL) return fail(AVAE_ESHAPE, "%s: n_dil > %d", who, AVAE_MAX_DIL);
     if (K < 1 || K % 2 == 0 || K > AVAE_MAX_TAPS)
-        return fail(AVAE_ESHAPE, "avae_amp_block: K must be odd and <= %d", AVAE_MAX_TAPS);
-    if (x == y) return fail(AVAE_EINVAL, "avae_amp_block: x and y must not overlap");
-    static const float* const kNull[AVAE_MAX_DIL] = {nullptr, nullptr, nullptr, nullptr};
+        return fail(AVAE_ESHAPE, "%s: K must be odd and <= %d", who, AVAE_MAX_TAPS);
+    if (x == y) return fail(AVAE_EINVAL, "%s: x and y must not overlap", who);
     for (int q = 0; q < n_dil; ++q) {
-        if (dil[q] < 1) return fail(AVAE_EINVAL, "avae_amp_block: dilation < 1");
+        if (dil[q] < 1) return fail(AVAE_EINVAL, "%s: dilation < 1", who);
         if ((long long)(K - 1) * dil[q] > 4096)
-            return fail(AVAE_ESHAPE, "avae_amp_block: receptive field too large");
-        if (!w1[q] || !w2[q]) return fail(AVAE_EINVAL, "avae_amp_block: null weight");
+            return fail(AVAE_ESHAPE, "%s: receptive field too large", who);
+        if (!w1[q] || !w2[q]) return fail(AVAE_EINVAL, "%s: null weight", who);
         if (!log_alpha[2 * q] || !log_alpha[2 * q + 1] || !log_beta[2 * q] || !log_beta[2 * q + 1])
-            return fail(AVAE_EINVAL, "avae_amp_block: null activation parameter");
+            return fail(AVAE_EINVAL, "%s: null activation parameter", who);
     }
-    const size_t need = avae_amp_block_workspace_bytes(B, C, T);
-    if (!workspace || ws_bytes < need)
-        return fail(AVAE_EWORKSPACE, "avae_amp_block: workspace %zu bytes < %zu needed", ws_bytes,
-                    need);
+    return AVAE_OK;
+}
+
+// The AMP block on a checked call and a workspace of at least
+// avae_amp_block_workspace_bytes(B, C, T) bytes: three [B, C, T] slots (cur,
+// t1, t2), then the fused unit's packed weights.
+int amp_block_run(const float* x, float* y, int B, int C, int T, int K, int n_dil,
+                  const int* dil, const float* const* w1, const float* const* b1,
+                  const float* const* w2, const float* const* b2,
+                  const float* const* log_alpha, const float* const* log_beta, float out_scale,
+                  int accumulate, void* workspace, hipStream_t s) {
+    static const float* const kNull[AVAE_MAX_DIL] = {nullptr, nullptr, nullptr, nullptr};
     const size_t slot = round_up((size_t)B * C * T * sizeof(float), 256);
     char* ws = (char*)workspace;
     float* cur = (float*)ws;
     float* t1 = (float*)(ws + slot);
     float* t2 = (float*)(ws + 2 * slot);
-    hipStream_t s = (hipStream_t)stream;
     avae::prof_set_phase(avae::kPhaseNone);
     const float* pw1[AVAE_MAX_DIL] = {};
     const float* pw2[AVAE_MAX_DIL] = {};
@@ -279,6 +284,85 @@ extern "C" int avae_amp_block(const float* x, float* y, int B, int C, int T, int
     return run_amp(x, y, B, C, T, K, n_dil, dil, w1, b1 ? b1 : kNull, w2, b2 ? b2 : kNull,
                    log_alpha, log_beta, fused ? pw1 : nullptr, fused ? pw2 : nullptr, out_scale,
                    accumulate, cur, t1, t2, make_taps(nullptr, nullptr), s);
+}
+}  // namespace
+
+extern "C" int avae_amp_block(const float* x, float* y, int B, int C, int T, int K, int n_dil,
+                              const int* dil, const float* const* w1, const float* const* b1,
+                              const float* const* w2, const float* const* b2,
+                              const float* const* log_alpha, const float* const* log_beta,
+                              float out_scale, int accumulate, void* workspace, size_t ws_bytes,
+                              void* stream) {
+    int rc = amp_block_check("avae_amp_block", x, y, B, C, T, K, n_dil, dil, w1, w2, log_alpha,
+                             log_beta);
+    if (rc) return rc;
+    const size_t need = avae_amp_block_workspace_bytes(B, C, T);
+    if (!workspace || ws_bytes < need)
+        return fail(AVAE_EWORKSPACE, "avae_amp_block: workspace %zu bytes < %zu needed", ws_bytes,
+                    need);
+    return amp_block_run(x, y, B, C, T, K, n_dil, dil, w1, b1, w2, b2, log_alpha, log_beta,
+                         out_scale, accumulate, workspace, (hipStream_t)stream);
+}
+
+// -------------------------------------------------------------------------
+// AMP block without a workspace argument, for callers that cannot allocate.
+// Its scratch is one file-scope device array per GPU (loaded with the
+// library's code object and held until the process ends).  In host code the
+// array's name is only a host-side stand-in: its device address is looked
+// up once per device (hipGetSymbolAddress, with that device current) and
+// that address is what the kernels receive.
+// -------------------------------------------------------------------------
+
+namespace {
+constexpr size_t kStaticScratchBytes = (size_t)AVAE_AMP_STATIC_SCRATCH_MB << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device (looked up on the
+// first call there).
+int static_scratch(void** out) {
+    int dev = 0;
+    AVAE_TRY(hipGetDevice(&dev), "avae_amp_block_static: hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(AVAE_EINVAL, "avae_amp_block_static: device %d out of range", dev);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        AVAE_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)),
+                 "avae_amp_block_static: hipGetSymbolAddress(scratch)");
+        if (!p) return fail(AVAE_EHIP, "avae_amp_block_static: null scratch address");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return AVAE_OK;
+}
+}  // namespace
+
+extern "C" size_t avae_amp_block_static_max_bytes(void) { return kStaticScratchBytes; }
+
+extern "C" int avae_amp_block_static(const float* x, float* y, int B, int C, int T, int K,
+                                     int n_dil, const int* dil, const float* const* w1,
+                                     const float* const* b1, const float* const* w2,
+                                     const float* const* b2, const float* const* log_alpha,
+                                     const float* const* log_beta, float out_scale,
+                                     int accumulate, void* stream) {
+    int rc = amp_block_check("avae_amp_block_static", x, y, B, C, T, K, n_dil, dil, w1, w2,
+                             log_alpha, log_beta);
+    if (rc) return rc;
+    const size_t need = avae_amp_block_workspace_bytes(B, C, T);
+    if (need == 0 || need > kStaticScratchBytes)
+        return fail(AVAE_ESHAPE,
+                    "avae_amp_block_static: [%d, %d, %d] needs %zu bytes of scratch, more than "
+                    "the library's static %zu (use avae_amp_block with a workspace)",
+                    B, C, T, need, kStaticScratchBytes);
+    void* ws = nullptr;
+    rc = static_scratch(&ws);
+    if (rc) return rc;
+    return amp_block_run(x, y, B, C, T, K, n_dil, dil, w1, b1, w2, b2, log_alpha, log_beta,
+                         out_scale, accumulate, ws, (hipStream_t)stream);
 }
 
 // =========================================================================

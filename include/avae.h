@@ -145,6 +145,37 @@ int avae_amp_block(const float* x, float* y, int B, int C, int T, int K,
                    void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * avae_amp_block for callers that cannot allocate device memory (code under
+ * stream/graph capture, tight serving loops, hosts that forbid hipMalloc):
+ * the same computation, arguments and results as avae_amp_block, without
+ * the workspace arguments.  Its scratch (the three [B, C, T] slots and the
+ * packed weights of avae_amp_block's workspace) is a static device array
+ * of AVAE_AMP_STATIC_SCRATCH_MB MiB built into the library: each GPU the
+ * library runs on holds its own copy from the library's load until the
+ * process ends.  The call allocates nothing (no hipMalloc, no hipFree) and
+ * never synchronises; its device address is looked up on the first call on
+ * each device.
+ *   Limit: avae_amp_block_workspace_bytes(B, C, T) must not exceed
+ *   avae_amp_block_static_max_bytes() (ESHAPE otherwise), e.g. B*C*T up to
+ *   about 5.5 M samples at C > 24.
+ *   Concurrency: every call on one GPU shares that GPU's array, which keeps
+ *   the last call's contents; two calls that overlap on one GPU (on
+ *   different streams, or from different host threads without ordering
+ *   between their streams) race and give wrong results.  Calls ordered on
+ *   one stream are safe.
+ * Errors: as avae_amp_block, with ESHAPE for sizes over the limit instead
+ * of EWORKSPACE, and EHIP if the scratch address cannot be looked up.
+ */
+#define AVAE_AMP_STATIC_SCRATCH_MB 64
+size_t avae_amp_block_static_max_bytes(void);
+int avae_amp_block_static(const float* x, float* y, int B, int C, int T, int K,
+                          int n_dil, const int* dil,
+                          const float* const* w1, const float* const* b1,
+                          const float* const* w2, const float* const* b2,
+                          const float* const* log_alpha, const float* const* log_beta,
+                          float out_scale, int accumulate, void* stream);
+
+/*
  * Whole decoder ([H3] AudioVae::from_cmf/decode; [LTX] Vocoder::forward):
  *   [optional z*std + mean] -> [optional 1x1 dec_in conv] -> conv_pre
  *   (k_pre, "same") -> per stage i: ConvTranspose1d (rate rates[i], kernel

@@ -143,3 +143,30 @@ def test_kernel_names_in_the_profiler_are_stable():
     for name, e in d["kernels"].items():
         assert re.match(r"conv1d_(pipe|dma)_kernel<\d+,\d+,\d+,\d+,\d+,\d+>$", name), name
         assert os.path.exists(os.path.join(ROOT, e["source"]))
+
+
+def test_amp_block_static_checks_before_any_launch():
+    """The no-workspace AMP block rejects null pointers and sizes beyond its
+    static scratch on the host (no device call: this runs without a GPU)."""
+    L = avae.lib()
+    cap = L.avae_amp_block_static_max_bytes()
+    assert cap == 64 << 20
+    fake = ctypes.c_void_p(0x1000)
+    dil = (ctypes.c_int * 1)(1)
+    ptrs = (ctypes.c_void_p * 2)(0x3000, 0x3000)
+    C = 64
+    T = cap // (3 * 4 * C) + 1024
+    assert L.avae_amp_block_workspace_bytes(1, C, T) > cap
+    rc = L.avae_amp_block_static(fake, ctypes.c_void_p(0x2000), 1, C, T, 3, 1,
+                                 ctypes.addressof(dil), ctypes.addressof(ptrs),
+                                 ctypes.addressof(ptrs), ctypes.addressof(ptrs),
+                                 ctypes.addressof(ptrs), ctypes.addressof(ptrs),
+                                 ctypes.addressof(ptrs), ctypes.c_float(1.0), 0, None)
+    assert rc == -2
+    assert b"scratch" in L.avae_last_error()
+    rc = L.avae_amp_block_static(None, fake, 1, 4, 8, 3, 1, ctypes.addressof(dil),
+                                 ctypes.addressof(ptrs), ctypes.addressof(ptrs),
+                                 ctypes.addressof(ptrs), ctypes.addressof(ptrs),
+                                 ctypes.addressof(ptrs), ctypes.addressof(ptrs),
+                                 ctypes.c_float(1.0), 0, None)
+    assert rc == -1
