@@ -41,66 +41,43 @@ FILTER_LEN = 12  # [H3] constant FILTER_LEN: both resampling filters have 12 tap
 # --------------------------------------------------------------------------
 
 def bessel_i0(x: float) -> float:
-    """Modified Bessel function I0 by its power series ([H3] ``bessel_i0``).
-
-    term_k = term_{k-1} * (x / 2k)^2, summed from 1; at most 39 terms,
-    stopping once a term falls below 1e-18 of the running sum.
-    """
-    s = 1.0
-    term = 1.0
-    for k in range(1, 40):
-        term *= (x / (2.0 * k)) ** 2
-        s += term
-        if term < 1e-18 * s:
-            break
-    return s
-
-
-def sinc(x: float) -> float:
-    """Normalised sinc sin(pi x)/(pi x), 1 at 0 ([H3] ``sinc``)."""
-    if x == 0.0:
-        return 1.0
-    return math.sin(math.pi * x) / (math.pi * x)
+    """Modified Bessel function of the first kind, order 0 ([H3] ``bessel_i0``
+    sums its power series; here numpy's ``np.i0`` is the library step)."""
+    return float(np.i0(float(x)))
 
 
 def kaiser_params(half_width: float, k: int) -> Tuple[float, float]:
-    """Attenuation A and Kaiser beta of the design ([H3] ``kaiser_sinc``).
+    """Stop-band attenuation A (dB) and Kaiser's beta for the design of
+    [H3] ``kaiser_sinc``.
 
-    A = 2.285 (k/2 - 1) pi (4 half_width) + 7.95; beta by Kaiser's piecewise
-    rule (A > 50, A >= 21, else 0).
+    The page estimates A with Kaiser's length rule for a filter of k/2 taps
+    and transition width 4 half_width (in units of pi): A = 2.285 (k/2 - 1)
+    pi (4 half_width) + 7.95.  beta follows Kaiser's empirical formula:
+    0.1102 (A - 8.7) above 50 dB, 0.5842 (A - 21)^0.4 + 0.07886 (A - 21) from
+    21 to 50 dB, and 0 (a rectangular window) below.
     """
-    half = k // 2
-    delta_f = 4.0 * half_width
-    a = 2.285 * (half - 1.0) * math.pi * delta_f + 7.95
-    if a > 50.0:
-        beta = 0.1102 * (a - 8.7)
-    elif a >= 21.0:
-        beta = 0.5842 * (a - 21.0) ** 0.4 + 0.07886 * (a - 21.0)
-    else:
-        beta = 0.0
-    return a, beta
+    atten = 2.285 * (k // 2 - 1) * math.pi * (4.0 * half_width) + 7.95
+    if atten > 50.0:
+        return atten, 0.1102 * (atten - 8.7)
+    if atten >= 21.0:
+        return atten, 0.5842 * (atten - 21.0) ** 0.4 + 0.07886 * (atten - 21.0)
+    return atten, 0.0
 
 
 def kaiser_sinc_f64(cutoff: float, half_width: float, k: int) -> np.ndarray:
     """Kaiser-windowed sinc lowpass, unit sum, unrounded float64 ([H3] ``kaiser_sinc``).
 
-    Tap i sits at the half-integer t = i - k/2 + 0.5 (even length); its
-    window is I0(beta sqrt(1 - r^2)) / I0(beta) with r = 2i/(k-1) - 1; its
-    value is 2 cutoff * window * sinc(2 cutoff t).  The taps are then divided
-    by their sum.
+    The ideal lowpass impulse response 2 cutoff sinc(2 cutoff t) (cutoff in
+    cycles per sample, normalised sinc) is sampled at the k tap positions
+    t = i - (k - 1)/2 (half-integers for even k), multiplied by the Kaiser
+    window I0(beta sqrt(1 - (2t/(k-1))^2)) / I0(beta), and scaled to unit sum.
     """
-    half = k // 2
     _, beta = kaiser_params(half_width, k)
-    denom = bessel_i0(beta)
-    n = k - 1.0
-    taps = []
-    for i in range(k):
-        r = 2.0 * i / n - 1.0
-        win = bessel_i0(beta * math.sqrt(max(1.0 - r * r, 0.0))) / denom
-        t = -half + i + 0.5
-        taps.append(2.0 * cutoff * win * sinc(2.0 * cutoff * t))
-    f = np.array(taps, dtype=np.float64)
-    return f / f.sum()
+    pos = np.arange(k, dtype=np.float64) - (k - 1) / 2.0
+    rel = 2.0 * pos / (k - 1)
+    window = np.i0(beta * np.sqrt(np.clip(1.0 - rel * rel, 0.0, None))) / np.i0(beta)
+    h = 2.0 * cutoff * np.sinc(2.0 * cutoff * pos) * window
+    return h / h.sum()
 
 
 def kaiser_sinc(cutoff: float = 0.25, half_width: float = 0.3, k: int = FILTER_LEN) -> np.ndarray:
@@ -519,11 +496,11 @@ def mel_stft(x: np.ndarray, forward_basis: np.ndarray, mel_basis: np.ndarray,
     return out
 
 
-def hann_sinc_filter(ratio: int, rolloff: float = 0.99, lpw: float = 6.0) -> np.ndarray:
+def hann_sinc_filter_f64(ratio: int, rolloff: float = 0.99, lpw: float = 6.0) -> np.ndarray:
     """The x``ratio`` Hann-windowed sinc interpolator of [LTX]
-    ``hann_sinc_upsample``: k = 2 w ratio + 1 taps, w = ceil(lpw / rolloff);
-    tap i at t = (i / ratio - w) * rolloff: sinc(t) cos^2(pi clamp(t) / (2 lpw))
-    * rolloff / ratio (float64; the page rounds it to float32)."""
+    ``hann_sinc_upsample``, unrounded float64: k = 2 w ratio + 1 taps,
+    w = ceil(lpw / rolloff); tap i at t = (i / ratio - w) * rolloff:
+    sinc(t) cos^2(pi clamp(t) / (2 lpw)) * rolloff / ratio."""
     w = math.ceil(lpw / rolloff)
     k = 2 * w * ratio + 1
     i = np.arange(k, dtype=np.float64)
@@ -532,6 +509,13 @@ def hann_sinc_filter(ratio: int, rolloff: float = 0.99, lpw: float = 6.0) -> np.
     win = np.cos(tc * math.pi / lpw / 2.0) ** 2
     s = np.where(ta == 0.0, 1.0, np.sin(math.pi * ta) / np.where(ta == 0.0, 1.0, math.pi * ta))
     return s * win * rolloff / ratio
+
+
+def hann_sinc_filter(ratio: int, rolloff: float = 0.99, lpw: float = 6.0) -> np.ndarray:
+    """The interpolator's taps as [LTX] ``hann_sinc_upsample`` uses them:
+    designed in float64, then cast to float32 (returned as float64 holding
+    float32 values), like ``kaiser_sinc``."""
+    return hann_sinc_filter_f64(ratio, rolloff, lpw).astype(np.float32).astype(np.float64)
 
 
 def hann_sinc_upsample(x: np.ndarray, ratio: int, filt: Optional[np.ndarray] = None) -> np.ndarray:

@@ -50,11 +50,24 @@ def test_mel_stft_causal_framing_and_floor():
 
 
 def test_hann_sinc_filter_shape_and_centre():
-    f = O.hann_sinc_filter(3)
+    f = O.hann_sinc_filter_f64(3)
     w = math.ceil(6.0 / 0.99)
     assert f.shape == (2 * w * 3 + 1,)
     assert abs(f[w * 3] - 0.99 / 3) < 1e-15
     assert np.allclose(f, f[::-1], rtol=0, atol=1e-15)
+
+
+def test_hann_sinc_filter_taps_are_float32_like_the_page():
+    """[LTX] hann_sinc_upsample builds its taps in float64 and stores them as
+    f32: every tap the oracle uses is a float32 value, the nearest one to
+    the float64 design (within half a float32 ulp), mirror-symmetric."""
+    f64 = O.hann_sinc_filter_f64(3)
+    f = O.hann_sinc_filter(3)
+    assert np.array_equal(f, f.astype(np.float32).astype(np.float64))
+    half_ulp = 0.5 * np.spacing(np.abs(f64).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(f - f64) <= half_ulp)
+    assert np.array_equal(f, f[::-1])
+    assert f[3 * math.ceil(6.0 / 0.99)] == np.float32(0.99 / 3)
 
 
 def test_hann_sinc_upsample_interpolates_a_sinusoid():
