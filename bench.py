@@ -45,6 +45,13 @@ def parse():
     ap.add_argument("--serial-mrf", action="store_true",
                     help="run each stage's AMP blocks one after the other on one stream "
                          "(default: overlapped on the decoder's side streams)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the figures of configs 1-3 (AMP blocks and one upsample stage)")
+    ap.add_argument("--no-parity", action="store_true",
+                    help="skip the oracle parity figures (sampled windows) in the JSON line")
+    ap.add_argument("--only", choices=("act1d", "configs"),
+                    help="run one figure alone and print it (for counter profiles): "
+                         "act1d = avae_act1d on [2,512,65536]; configs = configs 1-3")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="also run one plain 256 MiB device-to-device copy, whose "
                          "FETCH_SIZE / WRITE_SIZE counters calibrate the traffic figures")
@@ -57,20 +64,37 @@ def cpu_baseline(spec, z, t, frames):
     import numpy as np
     from oracle import avae_oracle as O
     from tests.helpers import decoder_params
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
     p = decoder_params(spec, t)
     zs = np.ascontiguousarray(z[:1, :, :frames])
     t0 = time.perf_counter()
+    c0 = time.process_time()
     y = O.decode(zs, p)
     dt = time.perf_counter() - t0
+    cpu = time.process_time() - c0
     samples = y.shape[-1]
-    return {"value": samples / dt, "unit": "samples/s", "cores": int(cores), "kind": "oracle",
+    return {"value": samples / dt, "unit": "samples/s", "cores": blas_threads(),
+            "kind": "oracle",
             "sample": f"one mono pass of the first {frames} latent frames "
-                      f"({samples} output samples) in {dt:.1f} s"}
+                      f"({samples} output samples) in {dt:.1f} s",
+            "nproc": nproc(), "cpu_seconds": cpu, "mean_busy_threads": cpu / dt}
+
+
+def nproc():
+    """Host cores this process may run on."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def blas_threads():
+    """Threads the oracle's library matrix products run on (its only
+    multi-threaded step; the rest of the oracle is single-threaded numpy)."""
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] + [1]))
+    except Exception:
+        return 1
 
 
 def roofline(kernels, steps):
@@ -200,7 +224,8 @@ def roofline_sum(kernels, steps):
 
 
 def cpu_amp_block_one_core(W):
-    """The oracle on workload 1 (one AMP block, [1, 32, 4096]) on one core."""
+    """The oracle on one core: workload 1 (one AMP block, [1, 32, 4096])
+    whole, and bounded samples of workload 2."""
     import numpy as np
     from oracle import avae_oracle as O
     from tests.helpers import amp_params
@@ -209,9 +234,9 @@ def cpu_amp_block_one_core(W):
     xs = np.asarray(x, np.float64)
     try:
         from threadpoolctl import threadpool_limits
-        ctx = threadpool_limits(1)
     except Exception:
-        ctx = None
+        threadpool_limits = None
+    ctx = threadpool_limits(1) if threadpool_limits else None
     t0 = time.perf_counter()
     if ctx is not None:
         with ctx:
@@ -219,8 +244,261 @@ def cpu_amp_block_one_core(W):
     else:
         O.amp_block(xs, p)
     dt = time.perf_counter() - t0
-    return {"workload": "one AMP block, [1,32,4096], k=3, d=(1,3,5)", "seconds": dt,
-            "samples_per_s": x.shape[-1] / dt, "cores": 1}
+    res = {"workload": "one AMP block, [1,32,4096], k=3, d=(1,3,5)", "seconds": dt,
+           "samples_per_s": x.shape[-1] / dt, "cores": 1}
+    # workload 2 on one core, on a bounded sample: one pass (B = 1) of the
+    # 512-channel block and of the standalone Activation1d over the first
+    # 2048 samples (the full [2, 512, 65536] block is 1.24 TFLOP of float64
+    # work); samples/s scale linearly with the length at this size
+    x2, la, lb, t2 = W.workload2()
+    xs = np.asarray(x2[:1, :, :2048], np.float64)
+    p2 = amp_params(t2, "block", 3, (1, 3, 5))
+    ctx = threadpool_limits(1) if threadpool_limits else None
+    t0 = time.perf_counter()
+    if ctx is not None:
+        with ctx:
+            O.amp_block(xs, p2)
+    else:
+        O.amp_block(xs, p2)
+    dt2 = time.perf_counter() - t0
+    h = O.kaiser_sinc()
+    t0 = time.perf_counter()
+    O.act1d(xs[0], np.asarray(la, np.float64), np.asarray(lb, np.float64), h, h)
+    dt3 = time.perf_counter() - t0
+    res["workload2_amp_block_sample"] = {
+        "sample": "one pass, [1, 512, 2048] of workload 2, k=3, d=(1,3,5)", "seconds": dt2,
+        "samples_per_s": 2048 / dt2, "cores": 1,
+        "full_config_estimate_s": dt2 * (2 * 65536) / 2048}
+    res["workload2_act1d_sample"] = {
+        "sample": "one pass, [512, 2048] of workload 2", "seconds": dt3,
+        "elements_per_s": 512 * 2048 / dt3, "GBps": 8.0 * 512 * 2048 / dt3 / 1e9, "cores": 1}
+    return res
+
+
+def _timed(torch, fn, n):
+    """Average ms of fn() over n calls, timed with events on the current
+    stream (the library launches on it); two warm-up calls first."""
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(n):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def _profiled(avae, fn, n, per_call):
+    """Per-kernel event figures of n calls of fn() from the library's
+    launch profiler (each launch bracketed by events on its own stream)."""
+    avae.profile_begin(n * per_call + 64)
+    for _ in range(n):
+        fn()
+    kernels, _ = avae.profile_end()
+    return kernels
+
+
+def _kernel_rows(kernels, n):
+    """Per kernel name: launches and ms per call, algorithmic rate and its
+    fraction of the MI355X peak (FP32 matrix for the convolutions, HBM for
+    the activations)."""
+    rows = {}
+    for name, k in sorted(kernels.items(), key=lambda kv: -kv[1]["total_ms"]):
+        sec = k["total_ms"] / 1e3
+        row = {"launches_per_call": k["launches"] / n, "ms_per_call": k["total_ms"] / n,
+               "avg_launch_us": 1e6 * sec / max(k["launches"], 1)}
+        if name.startswith(("act1d", "snake", "channel_affine", "sum_into", "bwe_combine")):
+            row["GBps"] = k["bytes"] / sec / 1e9
+            row["frac_of_hbm_peak"] = row["GBps"] / HBM_PEAK_GBPS
+        else:
+            row["TFLOPs"] = k["flops"] / sec / 1e12
+            row["frac_of_fp32_mfma_peak"] = row["TFLOPs"] / FP32_MFMA_PEAK_TFLOPS
+        rows[name] = row
+    return rows
+
+
+def _amp_lists(td, prefix, n):
+    return ([td[f"{prefix}.convs1.{q}.weight"] for q in range(n)],
+            [td[f"{prefix}.convs1.{q}.bias"] for q in range(n)],
+            [td[f"{prefix}.convs2.{q}.weight"] for q in range(n)],
+            [td[f"{prefix}.convs2.{q}.bias"] for q in range(n)],
+            [td[f"{prefix}.activations.{q}.act.alpha"] for q in range(2 * n)],
+            [td[f"{prefix}.activations.{q}.act.beta"] for q in range(2 * n)])
+
+
+def _rel_err(got, ref):
+    import numpy as np
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    return float(np.max(np.abs(got - ref))) / rms
+
+
+def amp_configs(torch, avae, W, steps, parity):
+    """Configs 1-3 of the workload table, each timed as a whole (events on
+    the stream) and per kernel (the library's launch profiler), with the
+    roofline sum of its kernels and, with `parity`, max|err|/RMS against
+    the float64 oracle (whole output for config 1; windows recomputed from
+    crops wider than the block's reach for configs 2 and 3)."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    out = {}
+    dil = (1, 3, 5)
+    n = max(steps // 2, 5)
+
+    def finish(key, ms, kernels, flops_call, extra):
+        fig = {"ms": ms, "kernels": _kernel_rows(kernels, n)}
+        t_roof = roofline_sum(kernels, n)
+        fig["roofline_sum_ms"] = t_roof
+        fig["frac_of_roofline_sum"] = t_roof / ms
+        fig["TFLOPs_overall"] = flops_call / (ms / 1e3) / 1e12
+        fig.update(extra)
+        out[key] = fig
+
+    # config 1: one AMP block [1, 32, 4096], k=3
+    x, t = W.workload1()
+    td = {k: torch.from_numpy(v).to(dev) for k, v in t.items()}
+    xd = torch.from_numpy(x).to(dev)
+    yd = torch.empty_like(xd)
+    ws = torch.empty(avae.amp_block_workspace_bytes(*x.shape), dtype=torch.uint8, device=dev)
+    lists = _amp_lists(td, "block", 3)
+    call = lambda: avae.amp_block(xd, 3, dil, *lists, out=yd, workspace=ws)
+    ms = _timed(torch, call, n)
+    kernels = _profiled(avae, call, n, 16)
+    B, C, T = x.shape
+    extra = {"workload": "one AMP block, [1,32,4096], k=3, d=(1,3,5)",
+             "samples_per_s": B * T / (ms / 1e3)}
+    if parity:
+        from oracle import avae_oracle as O
+        from tests.helpers import amp_params
+        call()
+        torch.cuda.synchronize()
+        extra["parity_max_err_over_rms"] = _rel_err(yd.cpu().numpy(),
+                                                    O.amp_block(x, amp_params(t, "block", 3, dil)))
+        extra["parity_scope"] = "whole output"
+    finish("config1_amp_block", ms, kernels, 6 * 2.0 * C * C * 3 * T * B, extra)
+    del td, xd, yd, ws
+
+    # config 2: one AMP block [2, 512, 65536], k=3 (the 3-tap 512-channel convs)
+    x, _, _, t = W.workload2()
+    td = {k: torch.from_numpy(v).to(dev) for k, v in t.items()}
+    xd = torch.from_numpy(x).to(dev)
+    yd = torch.empty_like(xd)
+    ws = torch.empty(avae.amp_block_workspace_bytes(*x.shape), dtype=torch.uint8, device=dev)
+    lists = _amp_lists(td, "block", 3)
+    call = lambda: avae.amp_block(xd, 3, dil, *lists, out=yd, workspace=ws)
+    ms = _timed(torch, call, n)
+    kernels = _profiled(avae, call, n, 16)
+    B, C, T = x.shape
+    convs = {k: v for k, v in kernels.items() if k.startswith("conv1d")}
+    cf = sum(v["flops"] for v in convs.values())
+    ct = sum(v["total_ms"] for v in convs.values()) / 1e3
+    extra = {"workload": "one AMP block, [2,512,65536], k=3, d=(1,3,5)",
+             "samples_per_s": B * T / (ms / 1e3),
+             "conv_TFLOPs": cf / ct / 1e12,
+             "conv_frac_of_fp32_mfma_peak": cf / ct / 1e12 / FP32_MFMA_PEAK_TFLOPS,
+             "conv_ms_per_call": ct * 1e3 / n}
+    if parity:
+        from oracle import avae_oracle as O
+        from tests.helpers import amp_params, amp_reach
+        call()
+        torch.cuda.synchronize()
+        y = yd.cpu().numpy()
+        p = amp_params(t, "block", 3, dil)
+        m = amp_reach(3, dil) + 8
+        errs = []
+        for a0 in (0, 30000, T - 256):
+            lo, hi = max(a0 - m, 0), min(a0 + 256 + m, T)
+            ref = O.amp_block(x[..., lo:hi], p)[..., a0 - lo:a0 - lo + 256]
+            errs.append(_rel_err(y[..., a0:a0 + 256], ref))
+        extra["parity_max_err_over_rms"] = max(errs)
+        extra["parity_scope"] = "all 512 channels of both passes, time windows [0,256), " \
+                                "[30000,30256), [65280,65536)"
+    finish("config2_amp_block", ms, kernels, 6 * 2.0 * C * C * 3 * T * B, extra)
+    del td, xd, yd, ws
+    torch.cuda.empty_cache()
+
+    # config 3: ConvTranspose1d 1024 -> 512 (k=10, s=5) on [2,1024,8000], then
+    # the MRF of blocks k=(3,7,11) accumulated into one output
+    x, t = W.workload3()
+    td = {k: torch.from_numpy(v).to(dev) for k, v in t.items()}
+    xd = torch.from_numpy(x).to(dev)
+    up = avae.convtr1d(xd, td["ups.0.weight"], td["ups.0.bias"], stride=5)
+    yd = torch.empty_like(up)
+    ws = torch.empty(avae.amp_block_workspace_bytes(*up.shape), dtype=torch.uint8, device=dev)
+    blists = [_amp_lists(td, f"resblocks.{j}", 3) for j in range(3)]
+
+    def stage():
+        avae.convtr1d(xd, td["ups.0.weight"], td["ups.0.bias"], stride=5, out=up)
+        for j, k in enumerate((3, 7, 11)):
+            avae.amp_block(up, k, dil, *blists[j], out_scale=1.0 / 3.0, accumulate=j > 0,
+                           out=yd, workspace=ws)
+    ms = _timed(torch, stage, n)
+    kernels = _profiled(avae, stage, n, 48)
+    B, Cin, Tin = x.shape
+    _, C, T = up.shape
+    flops = 2.0 * Cin * C * 10 * Tin * B + sum(6 * 2.0 * C * C * k * T * B for k in (3, 7, 11))
+    extra = {"workload": "ConvTranspose1d 1024->512 k=10 s=5 on [2,1024,8000], then the MRF "
+                         "(3,7,11)x(1,3,5) -> [2,512,40001]",
+             "samples_per_s": B * T / (ms / 1e3)}
+    if parity:
+        from oracle import avae_oracle as O
+        from tests.helpers import amp_params, amp_reach
+        stage()
+        torch.cuda.synchronize()
+        y = yd.cpu().numpy()
+        xo = O.convtr1d(x, t["ups.0.weight"], t["ups.0.bias"], stride=5)
+        e_up = _rel_err(up.cpu().numpy(), xo)
+        blocks = [amp_params(t, f"resblocks.{j}", k, dil) for j, k in enumerate((3, 7, 11))]
+        m = max(amp_reach(k, dil) for k in (3, 7, 11)) + 8
+        errs = []
+        for a0 in (0, T - 200):
+            lo, hi = max(a0 - m, 0), min(a0 + 200 + m, T)
+            ref = O.mrf(xo[..., lo:hi], blocks)[..., a0 - lo:a0 - lo + 200]
+            errs.append(_rel_err(y[..., a0:a0 + 200], ref))
+        extra["parity_max_err_over_rms"] = max(errs)
+        extra["parity_convtr1d_max_err_over_rms"] = e_up
+        extra["parity_scope"] = "ConvTranspose1d output whole; MRF output on all 512 channels " \
+                                "of both passes, time windows [0,200) and [39801,40001)"
+    finish("config3_upsample_stage", ms, kernels, flops, extra)
+    del td, xd, up, yd, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def decode_parity(torch, dec, spec, z, t, B, F):
+    """max|err|/RMS of the full-size decode against the float64 oracle on a
+    4-frame window in the middle of the last pass, the oracle decoding a
+    latent crop whose margin exceeds the receptive-field bound: on the
+    conv_post output before the final nonlinearity (the decode's bar) and on
+    the waveform."""
+    import numpy as np
+    from oracle import avae_oracle as O
+    from tests.helpers import decoder_params, decoder_reach_frames
+    wave, stages = dec.decode(torch.from_numpy(z).to("cuda:0"), trace=True)
+    torch.cuda.synchronize()
+    pre = stages[-1][B - 1].cpu().numpy()
+    w = wave[B - 1].cpu().numpy()
+    R = decoder_reach_frames(spec)
+    a = F // 2
+    lo, hi = max(a - R, 0), min(a + 4 + R, F)
+    p = decoder_params(spec, t)
+    t0 = time.perf_counter()
+    wref = O.decode(z[B - 1:B, :, lo:hi], p, record=True)[0]
+    dt = time.perf_counter() - t0
+    hop = spec.hop
+    off = (a - lo) * hop
+    pre_ref = p.stages[-1][0, 0, off:off + 4 * hop]
+    return {"workload": f"{spec.name}, pass {B - 1}, latent frames [{a}, {a + 4}) "
+                        f"from a crop [{lo}, {hi})",
+            "pre_final_max_err_over_rms": _rel_err(pre[a * hop:(a + 4) * hop], pre_ref),
+            "wave_max_abs_err": float(np.max(np.abs(w[a * hop:(a + 4) * hop] -
+                                                    wref[off:off + 4 * hop]))),
+            "bar": 1e-3, "oracle_seconds": dt}
 
 
 def other_decoder(torch, avae, W, which, steps):
@@ -248,10 +526,22 @@ def other_decoder(torch, avae, W, which, steps):
     e1.record(s)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    return {"workload": f"{spec.name} decode, latent [{B},{spec.c_in},{F}] -> wave [{B},{L}] "
-                        f"at {spec.sample_rate} Hz",
-            "ms": ms, "samples_per_s": B * L / (ms / 1e3),
-            "x_realtime": (L / spec.sample_rate) / (ms / 1e3)}
+    res = {"workload": f"{spec.name} decode, latent [{B},{spec.c_in},{F}] -> wave [{B},{L}] "
+                       f"at {spec.sample_rate} Hz",
+           "ms": ms, "samples_per_s": B * L / (ms / 1e3),
+           "x_realtime": (L / spec.sample_rate) / (ms / 1e3)}
+    # roofline sum over its kernels, each launch alone on the GPU (blocks
+    # serialized for the profiled pass), against the timed step
+    dec.set_concurrent(False)
+    n = max(steps // 2, 3)
+    kernels = _profiled(avae, lambda: dec.decode(zd, out=out, workspace=ws), n, 400)
+    dec.set_concurrent(True)
+    t_roof = roofline_sum(kernels, n)
+    res["roofline_sum_ms"] = t_roof
+    res["frac_of_roofline_sum"] = t_roof / ms
+    top = sorted(kernels.items(), key=lambda kv: -kv[1]["total_ms"])[:8]
+    res["kernels"] = _kernel_rows(dict(top), n)
+    return res
 
 
 def streaming(torch, dec, zd, out, tile, steps):
@@ -315,11 +605,13 @@ def dav_figure(torch, avae, W, steps):
         dav.decode(zd, out=out, workspace=ws)
     kernels, _ = avae.profile_end()
     top = sorted(kernels.items(), key=lambda kv: -kv[1]["total_ms"])[:6]
+    t_roof = roofline_sum(kernels, n)
     return {"workload": f"music3-dav decode, latent [{B},128,{F}] -> [{B},{2 * L}] "
                         f"interleaved stereo at {W.DAV.sample_rate} Hz",
             "ms": ms, "samples_per_s": out.numel() / (ms / 1e3),
             "x_realtime": (L / W.DAV.sample_rate) / (ms / 1e3),
-            "kernels_ms": {k: v["total_ms"] / n for k, v in top}}
+            "roofline_sum_ms": t_roof, "frac_of_roofline_sum": t_roof / ms,
+            "kernels": _kernel_rows(dict(top), n)}
 
 
 def bwe_figure(torch, avae, W, steps):
@@ -350,12 +642,24 @@ def bwe_figure(torch, avae, W, steps):
         dec.decode(ld, out=out, workspace=ws)
     kernels, _ = avae.profile_end()
     top = sorted(kernels.items(), key=lambda kv: -kv[1]["total_ms"])[:6]
+    t_roof = roofline_sum(kernels, n)
     return {"workload": f"ltx bandwidth extension, [{B},{T}] at 16 kHz -> [{B},{3 * T}] at 48 kHz",
             "ms": ms, "samples_per_s": out.numel() / (ms / 1e3),
             "x_realtime": (T / 16000.0) / (ms / 1e3),
-            "kernels_ms": {k: v["total_ms"] / n for k, v in top},
+            "roofline_sum_ms": t_roof, "frac_of_roofline_sum": t_roof / ms,
+            "kernels": _kernel_rows(dict(top), n),
             "mel_stft_ms": kernels.get("mel_stft_kernel", {}).get("total_ms", 0.0) / n,
             "combine_ms": kernels.get("bwe_combine_kernel", {}).get("total_ms", 0.0) / n}
+
+
+def pmc_calibration_copy(torch, res):
+    """One plain 256 MiB device-to-device copy: its FETCH_SIZE / WRITE_SIZE
+    counters (known bytes) calibrate the traffic figures of a counter run."""
+    src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    res["pmc_calibration_copy_bytes"] = src.numel() * 4
 
 
 def main():
@@ -369,6 +673,16 @@ def main():
     from bigvgan_waveform_decoder_amd import workloads as W
 
     dev = torch.device("cuda:0")
+    if args.only:
+        res = {"only": args.only}
+        if args.only == "act1d":
+            res["act1d_workload2"] = act1d_standalone(torch, avae, W, args.steps)
+        else:
+            res["configs"] = amp_configs(torch, avae, W, args.steps, not args.no_parity)
+        if args.pmc_calibration:
+            pmc_calibration_copy(torch, res)
+        print(json.dumps(res), flush=True)
+        return
     if args.workload == 4:
         z, t = W.workload4()
         spec = W.H3
@@ -492,12 +806,16 @@ def main():
                                              args.steps)
     if args.stream_tile > 0:
         res["streaming"] = streaming(torch, dec, zd, out, args.stream_tile, args.steps)
+    if not args.no_configs:
+        res["configs"] = amp_configs(torch, avae, W, args.steps, not args.no_parity)
+    if not args.no_parity:
+        res["parity"] = decode_parity(torch, dec, spec, z, t, B, F)
+    res["seeds"] = {"generator": "numpy PCG64, one stream per tensor, seed = master ^ "
+                                 "FNV-1a-64(tensor name); normals drawn in float64, rounded "
+                                 "to float32",
+                    "master": {f"workload{i}": hex(W.master_seed(i)) for i in range(1, 8)}}
     if args.pmc_calibration:
-        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        res["pmc_calibration_copy_bytes"] = src.numel() * 4
+        pmc_calibration_copy(torch, res)
     # the same step with the latent coming from pinned host memory and the
     # waveform going back to it (PCIe both ways), for context
     zh = torch.from_numpy(z).pin_memory()

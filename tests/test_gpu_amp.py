@@ -81,6 +81,31 @@ def test_fused_amp_unit_shapes(C, T, K, dil):
     assert rel_err(y, ref) <= TOL_BLOCK
 
 
+# One dilation step of the fused unit is one launch doing four operations
+# (activation, dilated conv, activation, conv + residual).  It is held to the
+# per-kernel bar, 1e-5, like any single launch: measured on MI355X, the
+# worst case below is 4.1e-6 (C = 24, K = 11, d = 5), the C = 12 cases stay
+# under 2.8e-6.  Every width the decoders run fused (12 and 24 in H3, 16 in
+# LTX) at every tap count and dilation of their AMP blocks, on [2, C, 40037]
+# (about sixty time tiles, a ragged last one), and at the decoders' full row
+# lengths for the widest halo (K = 11, d = 5).
+TOL_UNIT = 1e-5
+UNIT = [(C, 40037, K, d) for C in (12, 16, 24) for K in (3, 7, 11) for d in (1, 3, 5)]
+UNIT += [(12, 320000, 11, 5), (16, 320000, 11, 5), (24, 160000, 11, 5)]
+
+
+@pytest.mark.parametrize("C,T,K,d", UNIT, ids=[f"C{c}-T{t}-K{k}-d{d}" for c, t, k, d in UNIT])
+def test_fused_amp_unit_one_launch(C, T, K, d):
+    announce(f"fused amp unit (one launch) C={C} T={T} K={K} d={d}")
+    x = W.normal(0, f"unit/{C}/{T}/x", [2, C, T])
+    t = W.amp_tensors(0, f"unit{C}", C, K, (d,), weight_var=2.0 / (C * K))
+    y = host(_amp_call(cuda(x), cuda_dict(t), f"unit{C}", K, (d,)))
+    ref = O.amp_block(x, amp_params(t, f"unit{C}", K, (d,)))
+    e = rel_err(y, ref)
+    print(f"fused unit C={C} T={T} K={K} d={d}: max|err|/RMS = {e:.3e}", flush=True)
+    assert e <= TOL_UNIT
+
+
 def test_fused_amp_unit_accumulate_epilogue():
     """out <- out + 0.37 * AMP(x) through the fused path's epilogue."""
     announce("fused amp accumulate")

@@ -85,12 +85,23 @@ def test_decode_batched_equals_single_and_deterministic():
     assert np.max(np.abs(a[0] - a[1])) > 0
 
 
+# max|concurrent - serial| / RMS(serial) per traced output (conv_pre, the
+# seven stages, conv_post before tanh) of the decode below, measured on
+# MI355X: 0, 4.35e-7, 2.88e-6, 5.36e-6, 1.33e-5, 1.91e-5, 3.85e-5, 1.25e-4,
+# 2.15e-4.  The two schedules round the MRF sum differently (block j > 0
+# accumulates in its convolution's epilogue, or writes its own scaled buffer
+# that one kernel adds afterwards), about one float32 rounding of the stage
+# output; each later stage carries that difference forward with the
+# network's gain (x3-8 per stage with these random weights).  The kernels
+# are deterministic, so the figures repeat exactly; the bar is twice each.
+CONC_VS_SERIAL = [0.0, 8.7e-7, 5.8e-6, 1.1e-5, 2.7e-5, 3.9e-5, 7.7e-5, 2.5e-4, 4.3e-4]
+
+
 def test_decode_concurrent_blocks_match_serial():
     """A stage's AMP blocks overlapped on the decoder's side streams and the
     single-stream schedule both match the oracle at every stage boundary (the
-    decode bar); they differ only in the rounding of the block sum, which the
-    later stages' gain carries forward (~1e-4 at the last boundary of this
-    spec).  The overlapped decode repeats bit for bit."""
+    decode bar), and each other within twice their measured divergence.  The
+    overlapped decode repeats bit for bit."""
     announce("decode concurrent vs serial AMP blocks")
     spec = W.scaled_spec(W.H3, 128)
     zn = W.normal(4, "latent", [2, spec.c_in, 6])
@@ -104,12 +115,15 @@ def test_decode_concurrent_blocks_match_serial():
     dec.set_concurrent(False)
     _, ss = dec.decode(z, trace=True)
     last = len(p.stages) - 1
+    assert len(sc) == len(CONC_VS_SERIAL)
     for i, (a, b, r) in enumerate(zip(sc, ss, p.stages)):
         r = r[:, 0, :] if i == last else r
         a, b = host(a), host(b)
         assert rel_err(a, r) <= TOL, ("concurrent", i)
         assert rel_err(b, r) <= TOL, ("serial", i)
-        assert rel_err(a, b) <= TOL, ("concurrent vs serial", i)
+        e = rel_err(a, b)
+        print(f"concurrent vs serial, output {i}: {e:.3e}", flush=True)
+        assert e <= CONC_VS_SERIAL[i], ("concurrent vs serial", i, e)
     dec.set_concurrent(True)
     np.testing.assert_array_equal(host(dec.decode(z)), host(wc))
 

@@ -30,8 +30,10 @@ def test_streaming_equals_whole_decode(name, spec, frames, tile):
     whole = host(dec.decode(zd))
     tiled = host(dec.decode_streaming(zd, tile))
     assert tiled.shape == whole.shape == (2, frames * spec.hop)
-    # same arithmetic up to float32 summation order (tile shapes follow T)
-    assert rel_err(tiled, whole) <= 1e-4
+    # At these widths every tile's crop selects the same kernel tilings as the
+    # whole sequence, so the kept samples are bit-identical (measured on
+    # MI355X for all three cases).
+    np.testing.assert_array_equal(tiled, whole)
     # and the oracle, on a window in the middle of a tile boundary
     R = decoder_reach_frames(spec)
     a = tile - 2
@@ -51,7 +53,7 @@ def test_streaming_halo_matters():
     zd = cuda(z)
     whole = host(dec.decode(zd))
     assert rel_err(host(dec.decode_streaming(zd, 10, halo_frames=0)), whole) > 1e-3
-    assert rel_err(host(dec.decode_streaming(zd, 10)), whole) <= 1e-4
+    np.testing.assert_array_equal(host(dec.decode_streaming(zd, 10)), whole)
 
 
 def test_streaming_workload4_full_size():
@@ -66,10 +68,14 @@ def test_streaming_workload4_full_size():
     whole = host(dec.decode(zd))
     tiled = host(dec.decode_streaming(zd, 100))
     assert tiled.shape == (2, 370 * spec.hop)
-    # both are float32 decodes of the same arithmetic whose tile shapes (and so
-    # summation orders) follow the sequence length; at full width the growth
-    # over seven stages makes that ~1e-4, inside the decode's 1e-3 bar
-    assert rel_err(tiled, whole) <= 1e-3
+    # At full width the crops (100 + 35 or 100 + 70 frames) and the whole
+    # sequence (370 frames) select different tilings in some stages, so the
+    # float32 summation orders differ by about one rounding there and the
+    # later stages' gain carries it forward: measured on MI355X 1.36e-4
+    # (1.27e-4 on an earlier kernel set); the bar is twice that, rounded up.
+    e = rel_err(tiled, whole)
+    print(f"tiled vs whole at full width: {e:.3e}", flush=True)
+    assert e <= 3e-4
 
 
 def test_streaming_rejects_bad_tiles():
