@@ -14,7 +14,9 @@ from typing import Dict, List, Optional, Sequence
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libavae.so")
+# AVAE_LIB_PATH selects another build of the same library (the host-sanitized
+# check build); a missing file raises like a missing default.
+LIB_PATH = os.environ.get("AVAE_LIB_PATH") or os.path.join(_HERE, "libavae.so")
 
 AVAE_FILTER_LEN = 12
 AVAE_MAX_STAGES = 8

@@ -15,6 +15,7 @@
 
 #include "avae.h"
 #include "avae_internal.h"
+#include "plan.h"
 
 using avae::ActTaps;
 using avae::ConvEpilogue;
@@ -66,7 +67,7 @@ ActTaps make_taps(const float* up, const float* down) {
     return t;
 }
 
-size_t round_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
+using avae::plan::round_up;
 
 int conv_out_len(int T, int K, int dil, int pad) { return T + 2 * pad - dil * (K - 1); }
 
@@ -223,7 +224,8 @@ size_t amp_pack_reserve(int C) {
 
 extern "C" size_t avae_amp_block_workspace_bytes(int B, int C, int T) {
     if (B < 1 || C < 1 || T < 1) return 0;
-    return 3 * round_up((size_t)B * C * T * sizeof(float), 256) + amp_pack_reserve(C);
+    const size_t slot = avae::plan::tensor_bytes(B, C, T);
+    return slot ? 3 * slot + amp_pack_reserve(C) : 0;
 }
 
 namespace {
@@ -259,7 +261,7 @@ int amp_block_run(const float* x, float* y, int B, int C, int T, int K, int n_di
                   const float* const* log_alpha, const float* const* log_beta, float out_scale,
                   int accumulate, void* workspace, hipStream_t s) {
     static const float* const kNull[AVAE_MAX_DIL] = {nullptr, nullptr, nullptr, nullptr};
-    const size_t slot = round_up((size_t)B * C * T * sizeof(float), 256);
+    const size_t slot = avae::plan::tensor_bytes(B, C, T);
     char* ws = (char*)workspace;
     float* cur = (float*)ws;
     float* t1 = (float*)(ws + slot);
@@ -297,6 +299,7 @@ extern "C" int avae_amp_block(const float* x, float* y, int B, int C, int T, int
                              log_beta);
     if (rc) return rc;
     const size_t need = avae_amp_block_workspace_bytes(B, C, T);
+    if (need == 0) return fail(AVAE_ESHAPE, "avae_amp_block: workspace size overflows");
     if (!workspace || ws_bytes < need)
         return fail(AVAE_EWORKSPACE, "avae_amp_block: workspace %zu bytes < %zu needed", ws_bytes,
                     need);
@@ -430,30 +433,8 @@ int check_config(const avae_config* c) {
     return AVAE_OK;
 }
 
-// Per-stage lengths for `frames` frames: T[0] = frames, T[i+1] after stage i.
-int stage_lengths(const avae_config& c, int frames, long long* T) {
-    T[0] = frames;
-    for (int i = 0; i < c.n_stages; ++i) {
-        const int p = (c.up_k[i] - c.rates[i]) / 2;
-        T[i + 1] = (T[i] - 1) * c.rates[i] + c.up_k[i] - 2LL * p;
-        if (T[i + 1] < 1 || T[i + 1] > 0x7fffffffLL) return -1;
-    }
-    return 0;
-}
-
-// Bytes of each of the five decode buffers (largest activation).
-size_t decode_slot_bytes(const avae_config& c, int B, const long long* T) {
-    size_t m = 0;
-    auto upd = [&](long long ch, long long t) {
-        size_t v = (size_t)B * (size_t)ch * (size_t)t * sizeof(float);
-        if (v > m) m = v;
-    };
-    upd(c.c_in, T[0]);
-    if (c.dec_in_ch) upd(c.dec_in_ch, T[0]);
-    upd(c.ch[0], T[0]);
-    for (int i = 0; i < c.n_stages; ++i) upd(c.ch[i + 1], T[i + 1]);
-    return round_up(m, 256);
-}
+using avae::plan::decode_slot_bytes;
+using avae::plan::stage_lengths;
 
 struct BlobPlan {
     std::vector<std::pair<const float**, std::pair<const float*, size_t>>> items;
@@ -681,6 +662,7 @@ int decode_impl(const avae_decoder* dec, const float* latent, int B, int frames,
     if (stage_lengths(c, frames, T))
         return fail(AVAE_ESHAPE, "avae_bigvgan_decode: length overflow");
     const size_t slot = decode_slot_bytes(c, B, T);
+    if (slot == 0) return fail(AVAE_ESHAPE, "avae_bigvgan_decode: workspace size overflows");
     const size_t need = decode_slots(dec) * slot;
     if (!workspace || ws_bytes < need)
         return fail(AVAE_EWORKSPACE, "avae_bigvgan_decode: workspace %zu bytes < %zu needed",
@@ -812,57 +794,12 @@ extern "C" int avae_bigvgan_decode_traced(const avae_decoder* dec, const float* 
 
 namespace {
 
-// Receptive-field reach in latent frames (per layer, in that layer's input
-// samples: Activation1d +-5, a "same" conv (k-1)d/2, a ConvTranspose1d
-// ceil(k/s)+1; each divided by the upsampling already applied), rounded up,
-// plus one frame of slack.
-int reach_frames(const avae_config& c) {
-    double reach = (c.k_pre - 1) / 2.0;
-    double rate = 1.0;
-    for (int i = 0; i < c.n_stages; ++i) {
-        reach += ((c.up_k[i] + c.rates[i] - 1) / c.rates[i] + 1) / rate;
-        rate *= c.rates[i];
-        double mrf = 0.0;
-        for (int j = 0; j < c.n_kernels; ++j) {
-            double r = 0.0;
-            for (int q = 0; q < c.n_dil; ++q)
-                r += 5.0 + (c.rb_k[j] - 1) * c.rb_d[j][q] / 2.0 + 5.0 + (c.rb_k[j] - 1) / 2.0;
-            mrf = r > mrf ? r : mrf;
-        }
-        reach += mrf / rate;
-    }
-    reach += (5.0 + (c.k_post - 1) / 2.0) / rate;
-    return (int)std::ceil(reach) + 1;
-}
+using avae::plan::hop_of;
+using avae::plan::reach_frames;
 
-long long hop_of(const avae_config& c) {
-    long long h = 1;
-    for (int i = 0; i < c.n_stages; ++i) h *= c.rates[i];
-    return h;
-}
-
-// The streaming workspace: latent crop, tile waveform, decode workspace.
-// Tiles decoded together in one batched pass (their crops stacked along the
-// batch axis): the workspace covers this many tiles.
-constexpr int kTileBatch = 4;
-
-struct StreamPlan {
-    size_t crop_bytes, wave_bytes, dec_bytes;
-    size_t total() const { return crop_bytes + wave_bytes + dec_bytes; }
-};
-
-bool stream_plan(const avae_decoder* dec, int B, int tile_frames, int halo, StreamPlan* p) {
-    const avae_config& c = dec->cfg;
-    const long long cf = (long long)tile_frames + 2LL * halo;
-    if (cf > 0x3fffffffLL) return false;
-    if ((long long)B * kTileBatch > 0x7fffffffLL / 2) return false;
-    const int rows = B * kTileBatch;
-    long long T[AVAE_MAX_STAGES + 1];
-    if (stage_lengths(c, (int)cf, T)) return false;
-    p->crop_bytes = round_up((size_t)rows * c.c_in * cf * sizeof(float), 256);
-    p->wave_bytes = round_up((size_t)rows * T[c.n_stages] * sizeof(float), 256);
-    p->dec_bytes = decode_slots(dec) * decode_slot_bytes(c, rows, T);
-    return true;
+bool stream_plan(const avae_decoder* dec, int B, int tile_frames, int halo,
+                 avae::plan::StreamBytes* p) {
+    return avae::plan::stream_bytes(dec->cfg, decode_slots(dec), B, tile_frames, halo, p);
 }
 
 }  // namespace
@@ -877,7 +814,7 @@ extern "C" size_t avae_decoder_streaming_workspace_bytes(const avae_decoder* dec
                                                          int tile_frames, int halo_frames) {
     if (!dec || B < 1 || tile_frames < 1) return 0;
     const int halo = halo_frames < 0 ? reach_frames(dec->cfg) : halo_frames;
-    StreamPlan p;
+    avae::plan::StreamBytes p;
     if (!stream_plan(dec, B, tile_frames, halo, &p)) return 0;
     return p.total();
 }
@@ -898,9 +835,9 @@ extern "C" int avae_bigvgan_decode_streaming(const avae_decoder* dec, const floa
         return fail(AVAE_ESHAPE,
                     "avae_bigvgan_decode_streaming: output length is not frames x hop for this config");
     const int halo = halo_frames < 0 ? reach_frames(c) : halo_frames;
-    const int tf = tile_frames < frames ? tile_frames : frames;
-    StreamPlan plan;
-    if (!stream_plan(dec, B, tf, halo, &plan))
+    const avae::plan::TileGrid g = avae::plan::tile_grid(frames, tile_frames, halo);
+    avae::plan::StreamBytes plan;
+    if (!stream_plan(dec, B, g.tf, halo, &plan))
         return fail(AVAE_ESHAPE, "avae_bigvgan_decode_streaming: tile too long");
     if (!workspace || ws_bytes < plan.total())
         return fail(AVAE_EWORKSPACE, "avae_bigvgan_decode_streaming: workspace %zu bytes < %zu",
@@ -911,81 +848,32 @@ extern "C" int avae_bigvgan_decode_streaming(const avae_decoder* dec, const floa
     float* twave = (float*)(ws + plan.crop_bytes);
     void* dws = ws + plan.crop_bytes + plan.wave_bytes;
     const size_t rows = (size_t)B * c.c_in;
-    // Tile i keeps frames [i tf, min((i+1) tf, frames)).  Its crop: the
-    // first tile [0, tf + halo), the last tile the final tf + halo frames,
-    // an inner tile tf + 2 halo frames centred on it (slid inward when the
-    // halo reaches past an end), every length clipped to the sequence; each
-    // kept frame has at least `halo` frames of context on every side that is
-    // not a true end.  So there are at most two crop lengths, and tiles of
-    // one length stack along the batch axis, up to kTileBatch per pass.
-    const int ntiles = (frames + tf - 1) / tf;
-    const int len_edge = (int)std::min<long long>((long long)tf + halo, frames);
-    const int len_mid = (int)std::min<long long>((long long)tf + 2LL * halo, frames);
-    auto crop_of = [&](int i, int* c0, int* len) {
-        if (ntiles == 1) {
-            *c0 = 0;
-            *len = frames;
-        } else if (i == 0) {
-            *c0 = 0;
-            *len = len_edge;
-        } else if (i == ntiles - 1) {
-            *c0 = frames - len_edge;
-            *len = len_edge;
-        } else {
-            *c0 = std::max(0, std::min(i * tf - halo, frames - len_mid));
-            *len = len_mid;
-        }
-    };
-    for (int pass = 0; pass < 2; ++pass) {
-        // pass 0: the end tiles (and a single whole-sequence tile), pass 1: inner tiles
-        int group[kTileBatch];
-        int ng = 0, glen = 0;
-        auto flush = [&]() -> int {
-            if (ng == 0) return AVAE_OK;
-            for (int g = 0; g < ng; ++g) {
-                int c0, len;
-                crop_of(group[g], &c0, &len);
-                AVAE_TRY(hipMemcpy2DAsync(crop + (size_t)g * rows * len, (size_t)len * sizeof(float),
-                                          latent + c0, (size_t)frames * sizeof(float),
-                                          (size_t)len * sizeof(float), rows,
-                                          hipMemcpyDeviceToDevice, s),
-                         "streaming crop copy");
-            }
-            int rc = decode_impl(dec, crop, B * ng, glen, twave, dws, plan.dec_bytes, nullptr, s);
-            if (rc) return rc;
-            const size_t lcrop = (size_t)glen * hop;
-            for (int g = 0; g < ng; ++g) {
-                int c0, len;
-                crop_of(group[g], &c0, &len);
-                const int f0 = group[g] * tf;
-                const int f1 = std::min(f0 + tf, frames);
-                AVAE_TRY(hipMemcpy2DAsync(wave + (size_t)f0 * hop,
-                                          (size_t)frames * hop * sizeof(float),
-                                          twave + (size_t)g * B * lcrop + (size_t)(f0 - c0) * hop,
-                                          lcrop * sizeof(float),
-                                          (size_t)(f1 - f0) * hop * sizeof(float), (size_t)B,
-                                          hipMemcpyDeviceToDevice, s),
-                         "streaming tile copy");
-            }
-            ng = 0;
-            return AVAE_OK;
-        };
-        for (int i = 0; i < ntiles; ++i) {
-            const bool end_tile = (i == 0 || i == ntiles - 1);
-            if (end_tile != (pass == 0)) continue;
+    // One batched decode per group of tiles with equal crop lengths.
+    return avae::plan::for_each_tile_group(g, [&](const int* group, int ng, int glen) -> int {
+        for (int k = 0; k < ng; ++k) {
             int c0, len;
-            crop_of(i, &c0, &len);
-            if (ng == kTileBatch || (ng > 0 && len != glen)) {
-                int rc = flush();
-                if (rc) return rc;
-            }
-            glen = len;
-            group[ng++] = i;
+            g.crop(group[k], &c0, &len);
+            AVAE_TRY(hipMemcpy2DAsync(crop + (size_t)k * rows * len, (size_t)len * sizeof(float),
+                                      latent + c0, (size_t)frames * sizeof(float),
+                                      (size_t)len * sizeof(float), rows, hipMemcpyDeviceToDevice,
+                                      s),
+                     "streaming crop copy");
         }
-        int rc = flush();
+        int rc = decode_impl(dec, crop, B * ng, glen, twave, dws, plan.dec_bytes, nullptr, s);
         if (rc) return rc;
-    }
-    return AVAE_OK;
+        const size_t lcrop = (size_t)glen * hop;
+        for (int k = 0; k < ng; ++k) {
+            int c0, len, f0, f1;
+            g.crop(group[k], &c0, &len);
+            g.kept(group[k], &f0, &f1);
+            AVAE_TRY(hipMemcpy2DAsync(wave + (size_t)f0 * hop, (size_t)frames * hop * sizeof(float),
+                                      twave + (size_t)k * B * lcrop + (size_t)(f0 - c0) * hop,
+                                      lcrop * sizeof(float), (size_t)(f1 - f0) * hop * sizeof(float),
+                                      (size_t)B, hipMemcpyDeviceToDevice, s),
+                     "streaming tile copy");
+        }
+        return AVAE_OK;
+    });
 }
 
 // =========================================================================
@@ -1069,14 +957,18 @@ int dav_lengths(const avae_dav_config& c, int frames, long long* T) {
 }
 
 // One workspace slot: the largest [2B, C, T] activation of the decode.
+// Largest activation of the 2 B side passes (0 if its size overflows).
 size_t dav_slot_bytes(const avae_dav_config& c, int B, const long long* T) {
-    const size_t B2 = 2 * (size_t)B;
-    size_t m = B2 * (size_t)std::max(c.dec_in_ch, c.ch[0]) * (size_t)T[0];
+    const long long B2 = 2LL * B;
+    size_t m = avae::plan::tensor_bytes(B2, std::max(c.dec_in_ch, c.ch[0]), T[0]);
+    bool over = m == 0;
     for (int i = 0; i < c.n_stages; ++i) {
-        m = std::max(m, B2 * (size_t)c.ch[i] * (size_t)T[i]);
-        m = std::max(m, B2 * (size_t)c.ch[i + 1] * (size_t)T[i + 1]);
+        const size_t a = avae::plan::tensor_bytes(B2, c.ch[i], T[i]);
+        const size_t b = avae::plan::tensor_bytes(B2, c.ch[i + 1], T[i + 1]);
+        over = over || a == 0 || b == 0;
+        m = std::max(m, std::max(a, b));
     }
-    return round_up(m * sizeof(float), 256);
+    return over ? 0 : m;
 }
 
 int dav_decode_impl(const avae_dav* dav, const float* latent, int B, int frames, float* wave,
@@ -1090,6 +982,7 @@ int dav_decode_impl(const avae_dav* dav, const float* latent, int B, int frames,
     if ((long long)2 * B * T[c.n_stages] > 0x7fffffffLL)
         return fail(AVAE_ESHAPE, "avae_dav_decode: output too long");
     const size_t slot = dav_slot_bytes(c, B, T);
+    if (slot == 0) return fail(AVAE_ESHAPE, "avae_dav_decode: workspace size overflows");
     if (!workspace || ws_bytes < 3 * slot)
         return fail(AVAE_EWORKSPACE, "avae_dav_decode: workspace %zu bytes < %zu needed", ws_bytes,
                     3 * slot);

@@ -1,0 +1,131 @@
+// Host-only check of the C-ABI's planning arithmetic (csrc/plan.h): decoder
+// stage lengths and workspace sizes, the receptive-field reach and the tile
+// grid of the streaming decode.  Built and run by tests/test_host_sanitized.py
+// with the address and undefined-behaviour sanitizers; prints "plan_check ok"
+// and exits 0 when every check holds.
+#include <cstdio>
+#include <cstdlib>
+#include <set>
+#include <vector>
+
+#include "plan.h"
+
+using namespace avae::plan;
+
+static int g_fail = 0;
+#define CHECK(cond, ...)                                   \
+    do {                                                   \
+        if (!(cond)) {                                     \
+            std::fprintf(stderr, "FAIL %s:%d: ", __FILE__, __LINE__); \
+            std::fprintf(stderr, __VA_ARGS__);             \
+            std::fprintf(stderr, "\n");                    \
+            if (++g_fail > 20) std::exit(1);               \
+        }                                                  \
+    } while (0)
+
+static avae_config bigvgan(int c_in, int c0, std::vector<int> rates, std::vector<int> up_k) {
+    avae_config c{};
+    c.c_in = c_in;
+    c.k_pre = c.k_post = 7;
+    c.n_stages = (int)rates.size();
+    c.ch[0] = c0;
+    for (int i = 0; i < c.n_stages; ++i) {
+        c.rates[i] = rates[i];
+        c.up_k[i] = up_k[i];
+        c.ch[i + 1] = c.ch[i] / 2;
+    }
+    c.n_kernels = 3;
+    const int ks[3] = {3, 7, 11};
+    c.n_dil = 3;
+    for (int j = 0; j < 3; ++j) {
+        c.rb_k[j] = ks[j];
+        c.rb_d[j][0] = 1;
+        c.rb_d[j][1] = 3;
+        c.rb_d[j][2] = 5;
+    }
+    return c;
+}
+
+// Every frame kept exactly once, kept frames inside their crop, crops inside
+// the sequence with enough context, at most two crop lengths, every tile in
+// exactly one batched group of equal crop lengths and at most kTileBatch.
+static void check_grid(int frames, int tile, int halo) {
+    const TileGrid g = tile_grid(frames, tile, halo);
+    CHECK(g.tf >= 1 && g.tf <= frames, "tf %d frames %d", g.tf, frames);
+    std::vector<int> kept(frames, 0);
+    std::set<int> lens;
+    for (int i = 0; i < g.ntiles; ++i) {
+        int c0, len, f0, f1;
+        g.crop(i, &c0, &len);
+        g.kept(i, &f0, &f1);
+        CHECK(f0 < f1, "empty tile %d", i);
+        CHECK(c0 >= 0 && len >= 1 && c0 + len <= frames, "crop [%d,+%d) of %d", c0, len, frames);
+        CHECK(c0 <= f0 && f1 <= c0 + len, "tile [%d,%d) outside crop [%d,+%d)", f0, f1, c0, len);
+        const int left = f0 - c0, right = c0 + len - f1;
+        CHECK(left >= halo || c0 == 0, "left context %d < halo %d", left, halo);
+        CHECK(right >= halo || c0 + len == frames, "right context %d < halo %d", right, halo);
+        for (int f = f0; f < f1; ++f) kept[f]++;
+        lens.insert(len);
+    }
+    for (int f = 0; f < frames; ++f) CHECK(kept[f] == 1, "frame %d kept %d times", f, kept[f]);
+    CHECK(lens.size() <= 2, "%zu crop lengths", lens.size());
+    std::vector<int> seen(g.ntiles, 0);
+    const int rc = for_each_tile_group(g, [&](const int* t, int n, int len) -> int {
+        CHECK(n >= 1 && n <= kTileBatch, "group of %d", n);
+        for (int k = 0; k < n; ++k) {
+            CHECK(t[k] >= 0 && t[k] < g.ntiles, "tile index %d", t[k]);
+            int c0, l;
+            g.crop(t[k], &c0, &l);
+            CHECK(l == len, "group length %d vs crop %d", len, l);
+            seen[t[k]]++;
+        }
+        return 0;
+    });
+    CHECK(rc == 0, "rc %d", rc);
+    for (int i = 0; i < g.ntiles; ++i) CHECK(seen[i] == 1, "tile %d decoded %d times", i, seen[i]);
+}
+
+int main() {
+    // H3-shaped and LTX-shaped decoders: frames x hop output, the reach.
+    const avae_config h3 = bigvgan(32, 1536, {5, 5, 2, 2, 2, 2, 2}, {11, 11, 4, 4, 4, 4, 4});
+    const avae_config ltx = bigvgan(64, 1024, {5, 2, 2, 2, 2, 2}, {11, 4, 4, 4, 4, 4});
+    long long T[AVAE_MAX_STAGES + 1];
+    for (int f : {1, 2, 7, 400, 2000, 100000}) {
+        CHECK(stage_lengths(h3, f, T) == 0 && T[7] == 800LL * f, "h3 %d -> %lld", f, T[7]);
+        CHECK(stage_lengths(ltx, f, T) == 0 && T[6] == 160LL * f, "ltx %d -> %lld", f, T[6]);
+    }
+    CHECK(hop_of(h3) == 800 && hop_of(ltx) == 160, "hops");
+    CHECK(reach_frames(h3) == 35, "h3 reach %d", reach_frames(h3));
+    CHECK(reach_frames(ltx) == 45, "ltx reach %d", reach_frames(ltx));
+    // lengths past 2^31 are rejected, not wrapped
+    CHECK(stage_lengths(h3, 3000000, T) != 0, "h3 overflow accepted");
+    CHECK(stage_lengths(h3, 0, T) != 0, "zero frames accepted");
+    // workspace slots: workload 4 = 30.72 MB ([2, 12, 320000] and [2, 768, 2000] ...)
+    CHECK(stage_lengths(h3, 400, T) == 0, "h3 400");
+    CHECK(decode_slot_bytes(h3, 2, T) == round_up(2ULL * 24 * 160000 * 4, 256),
+          "h3 slot %zu", decode_slot_bytes(h3, 2, T));
+    // sizes that would wrap a 64-bit product give 0
+    CHECK(tensor_bytes(0x7fffffff, 0x7fffffff, 0x7fffffff) == 0, "tensor_bytes wrap");
+    CHECK(tensor_bytes(1, 1, 1) == 256, "tensor_bytes small");
+    CHECK(tensor_bytes(-1, 1, 1) == 0, "tensor_bytes negative");
+    CHECK(decode_slot_bytes(h3, 0x7fffffff, T) == 0 || decode_slot_bytes(h3, 0x7fffffff, T) >
+          (size_t)0x7fffffff, "huge batch");
+    StreamBytes sb;
+    CHECK(stream_bytes(h3, 13, 2, 100, 35, &sb) && sb.total() > 0, "h3 streaming bytes");
+    CHECK(!stream_bytes(h3, 13, 2, 0x3fffffff, 35, &sb), "huge tile accepted");
+    CHECK(!stream_bytes(h3, 13, 0x7fffffff, 100, 35, &sb), "huge batch accepted");
+    CHECK(!stream_bytes(h3, 13, 2, 100, -1, &sb), "negative halo accepted");
+    // the tile grid, exhaustively over small sizes, then a few long ones
+    for (int frames = 1; frames <= 160; ++frames)
+        for (int tile = 1; tile <= frames + 3; ++tile)
+            for (int halo : {0, 1, 2, 5, 17, 35, 45, 200}) check_grid(frames, tile, halo);
+    for (int frames : {400, 1999, 2000, 100003})
+        for (int tile : {1, 25, 100, 399, 4096})
+            for (int halo : {0, 35, 45}) check_grid(frames, tile, halo);
+    if (g_fail) {
+        std::fprintf(stderr, "plan_check: %d failures\n", g_fail);
+        return 1;
+    }
+    std::printf("plan_check ok\n");
+    return 0;
+}
