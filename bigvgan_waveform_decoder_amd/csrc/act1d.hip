@@ -270,6 +270,18 @@ __device__ __forceinline__ void act1d_tile_edge(const float* __restrict__ xrow,
     }
 }
 
+// A y tile's float4 store, non-temporal (the line is not kept in the caches
+// on the way to HBM): a read-once / write-once stream of this size then
+// reaches 97% of a plain copy's rate (measured on MI355X, [2, 512, 65536]:
+// 102.3 -> 89.8 us; inside the H3-shaped decode, where the next convolution
+// reads y, Activation1d 1.58 -> 1.45 ms per decode and the convolutions
+// unchanged).  Non-temporal loads of x were slower.
+__device__ __forceinline__ void store4_stream(float* p, float4 v) {
+    typedef float nt4 __attribute__((ext_vector_type(4)));
+    const nt4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<nt4*>(p));
+}
+
 // A block walks `per_block` consecutive tiles of the flattened (row, tile)
 // order.  The next interior tile's input is loaded into registers right
 // after the current tile is staged, so its HBM latency overlaps the current
@@ -324,7 +336,7 @@ __global__ __launch_bounds__(kThreads, 6) void act1d_kernel(
         auto store = [&]() {
 #pragma unroll
             for (int r = 0; r < 2; ++r)
-                if (dst[r]) *reinterpret_cast<float4*>(dst[r]) = res[r];
+                if (dst[r]) store4_stream(dst[r], res[r]);
         };
         act1d_window_load(window(first), pa, pb, pc);
         for (int id = first; id < last; ++id) {

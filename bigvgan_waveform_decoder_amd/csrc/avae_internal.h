@@ -47,6 +47,7 @@ void design_kaiser_sinc(double cutoff, double half_width, int taps, double* out)
 // (out may be null to query it).
 int design_hann_sinc(int ratio, double rolloff, double lpw, double* out);
 
+// y is written with non-temporal stores (not kept in the caches).
 hipError_t launch_act1d(const float* x, float* y, int B, int C, int T,
                         const float* log_alpha, const float* log_beta,
                         const ActTaps& taps, hipStream_t stream);
