@@ -76,10 +76,17 @@ int conv_out_len(int T, int K, int dil, int pad) { return T + 2 * pad - dil * (K
 // True if every dilation step of an AMP block of width C and K taps runs as
 // one fused launch (amp_unit.hip).  The kernel takes C <= 32; it is used up
 // to C = 24, the widths where it measured faster than the four separate
-// launches (at 32 channels the separate launches are a few percent faster).
+// launches on the decoders' long rows (at 32 channels the separate launches
+// are a few percent faster there), and at 32 channels for short inputs
+// (B T <= kFuseSmallBT samples per channel: one launch per step instead of
+// four, each of which fills only part of the GPU).
 constexpr int kFuseMaxC = 24;
+constexpr long long kFuseSmallBT = 65536;
+bool fuse_width(int B, int C, int T) {
+    return C <= kFuseMaxC || (C <= 32 && (long long)B * T <= kFuseSmallBT);
+}
 bool amp_fusable(int C, int K, int n_dil, const int* dil) {
-    if (C > kFuseMaxC) return false;
+    if (C > 32) return false;
     for (int q = 0; q < n_dil; ++q)
         if (!avae::amp_unit_supported(C, K, dil[q])) return false;
     return true;
@@ -215,8 +222,8 @@ extern "C" int avae_convtr1d(const float* x, float* y, int B, int Cin, int Cout,
 namespace {
 // Packed-weight reserve of the standalone AMP block: room for every
 // dilation step's two packed convolutions at the largest K.
-size_t amp_pack_reserve(int C) {
-    if (C > kFuseMaxC) return 0;
+size_t amp_pack_reserve(int B, int C, int T) {
+    if (!fuse_width(B, C, T)) return 0;
     const size_t per = avae::amp_unit_packed_floats(C, AVAE_MAX_TAPS);
     return per ? 2 * AVAE_MAX_DIL * round_up(per * sizeof(float), 256) : 0;
 }
@@ -225,7 +232,7 @@ size_t amp_pack_reserve(int C) {
 extern "C" size_t avae_amp_block_workspace_bytes(int B, int C, int T) {
     if (B < 1 || C < 1 || T < 1) return 0;
     const size_t slot = avae::plan::tensor_bytes(B, C, T);
-    return slot ? 3 * slot + amp_pack_reserve(C) : 0;
+    return slot ? 3 * slot + amp_pack_reserve(B, C, T) : 0;
 }
 
 namespace {
@@ -269,19 +276,24 @@ int amp_block_run(const float* x, float* y, int B, int C, int T, int K, int n_di
     avae::prof_set_phase(avae::kPhaseNone);
     const float* pw1[AVAE_MAX_DIL] = {};
     const float* pw2[AVAE_MAX_DIL] = {};
-    const bool fused = amp_pack_reserve(C) > 0 && amp_fusable(C, K, n_dil, dil);
+    const bool fused = amp_pack_reserve(B, C, T) > 0 && amp_fusable(C, K, n_dil, dil);
     if (fused) {
         // pack this call's weights into the reserve (amp_unit.hip layout)
         char* pk = ws + 3 * slot;
         const size_t per = round_up(avae::amp_unit_packed_floats(C, K) * sizeof(float), 256);
+        const float* src[2 * AVAE_MAX_DIL];
+        float* dst[2 * AVAE_MAX_DIL];
         for (int q = 0; q < n_dil; ++q) {
             float* p1 = (float*)(pk + (2 * q) * per);
             float* p2 = (float*)(pk + (2 * q + 1) * per);
-            AVAE_TRY(avae::launch_pack_unit_weights(w1[q], p1, C, K, s), "weight packing");
-            AVAE_TRY(avae::launch_pack_unit_weights(w2[q], p2, C, K, s), "weight packing");
+            src[2 * q] = w1[q];
+            src[2 * q + 1] = w2[q];
+            dst[2 * q] = p1;
+            dst[2 * q + 1] = p2;
             pw1[q] = p1;
             pw2[q] = p2;
         }
+        AVAE_TRY(avae::launch_pack_unit_weights_n(src, dst, 2 * n_dil, C, K, s), "weight packing");
     }
     return run_amp(x, y, B, C, T, K, n_dil, dil, w1, b1 ? b1 : kNull, w2, b2 ? b2 : kNull,
                    log_alpha, log_beta, fused ? pw1 : nullptr, fused ? pw2 : nullptr, out_scale,
@@ -548,7 +560,7 @@ extern "C" int avae_decoder_create(const avae_config* cfg, const avae_weights* w
     size_t pbytes = 0;
     for (int i = 0; i < c.n_stages; ++i)
         for (int j = 0; j < c.n_kernels; ++j)
-            if (amp_fusable(c.ch[i + 1], c.rb_k[j], c.n_dil, c.rb_d[j]))
+            if (c.ch[i + 1] <= kFuseMaxC && amp_fusable(c.ch[i + 1], c.rb_k[j], c.n_dil, c.rb_d[j]))
                 pbytes += 2 * c.n_dil *
                           round_up(avae::amp_unit_packed_floats(c.ch[i + 1], c.rb_k[j]) *
                                        sizeof(float), 256);
@@ -564,7 +576,7 @@ extern "C" int avae_decoder_create(const avae_config* cfg, const avae_weights* w
         for (int i = 0; i < c.n_stages && e == hipSuccess; ++i)
             for (int j = 0; j < c.n_kernels && e == hipSuccess; ++j) {
                 const int co = c.ch[i + 1], K = c.rb_k[j];
-                if (!amp_fusable(co, K, c.n_dil, c.rb_d[j])) continue;
+                if (co > kFuseMaxC || !amp_fusable(co, K, c.n_dil, c.rb_d[j])) continue;
                 const size_t per = round_up(avae::amp_unit_packed_floats(co, K) * sizeof(float), 256);
                 for (int q = 0; q < c.n_dil && e == hipSuccess; ++q) {
                     float* p1 = (float*)pp;

@@ -53,8 +53,8 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kUT = 256;              // threads per block (4 waves)
-constexpr int kRun = 16;              // activation outputs per thread run (default)
-constexpr int kRunMax = 24;           // longest run length act_stage picks
+// longest run length act_stage picks: 20 with MT = 1, 28 with MT = 2
+constexpr int run_max(int MT) { return MT == 1 ? 20 : 28; }
 constexpr int kLdsBudget = 80 * 1024; // two blocks per CU
 // Three blocks per CU for C <= 16: smaller time tiles (more halo work) but a
 // third co-resident block to overlap the phases; measured -20% at C = 16
@@ -209,6 +209,12 @@ __device__ __forceinline__ void act_pass(const float* __restrict__ src, int ss,
 // take ceil(C * ceil(Nd / R) / 256) passes; a range just over a multiple of
 // 256 runs of 16 would leave most threads idle in its last pass, so runs of
 // 20 or 24 are taken when they need fewer pass-pairs.
+// Run lengths are 12, 20 or 28 floats: the 64 lanes of a wave read windows
+// R floats apart with 16-byte LDS loads, and for R = 4 (mod 8) every 8
+// consecutive lanes (one LDS cycle of 16-byte reads) land in distinct bank
+// groups; R = 16 put 4 lanes, R = 24 two lanes, on one group.  28 needs
+// the register room of the two-blocks-per-CU kernels (kLong).
+template <bool kLong>
 __device__ __forceinline__ void act_stage(const float* __restrict__ src, int ss,
                                           float* __restrict__ dst, int ds, int C, int Nd, int og,
                                           int T, bool edge, const float* arev, const float* ibeta,
@@ -217,13 +223,13 @@ __device__ __forceinline__ void act_stage(const float* __restrict__ src, int ss,
         const int items = C * ((Nd + R - 1) / R);
         return ((items + kUT - 1) / kUT) * (R + 5);
     };
-    const int c16 = cost(16), c20 = cost(20), c24 = cost(24);
-    if (c20 < c16 && c20 <= c24)
+    const int c12 = cost(12), c20 = cost(20), c28 = kLong ? cost(28) : 1 << 30;
+    if (c28 < c20 && c28 < c12)
+        act_pass<kLong ? 28 : 20>(src, ss, dst, ds, C, Nd, og, T, edge, arev, ibeta, taps);
+    else if (c20 <= c12)
         act_pass<20>(src, ss, dst, ds, C, Nd, og, T, edge, arev, ibeta, taps);
-    else if (c24 < c16)
-        act_pass<24>(src, ss, dst, ds, C, Nd, og, T, edge, arev, ibeta, taps);
     else
-        act_pass<16>(src, ss, dst, ds, C, Nd, og, T, edge, arev, ibeta, taps);
+        act_pass<12>(src, ss, dst, ds, C, Nd, og, T, edge, arev, ibeta, taps);
 }
 
 typedef const float __attribute__((address_space(1))) gfloat;
@@ -387,7 +393,7 @@ __global__ __launch_bounds__(kUT, 2) void amp_unit_kernel(UnitArgs a, ActTaps ta
             }
 
     // 2. act1: P -> Q over [t0 - H + 5, +NA1)
-    act_stage(P, SP, Q, SQ, C, NA1, t0 - H + 5, T, edge, prm, prm + C, taps);
+    act_stage<MT == 2>(P, SP, Q, SQ, C, NA1, t0 - H + 5, T, edge, prm, prm + C, taps);
     __syncthreads();
 
     f32x4 acc[MT][NTW];
@@ -420,7 +426,7 @@ __global__ __launch_bounds__(kUT, 2) void amp_unit_kernel(UnitArgs a, ActTaps ta
     }
 
     // 5. act2: P -> Q over [t0 - h2, +N2)
-    act_stage(P, SP, Q, SQ, C, N2, t0 - h2, T, edge, prm + 2 * C, prm + 3 * C, taps);
+    act_stage<MT == 2>(P, SP, Q, SQ, C, N2, t0 - h2, T, edge, prm + 2 * C, prm + 3 * C, taps);
     __syncthreads();
 
     // 6. conv2: Q -> y over [t0, t0 + TT), plus bias, residual x, epilogue
@@ -452,10 +458,9 @@ __global__ __launch_bounds__(kUT, 2) void amp_unit_kernel(UnitArgs a, ActTaps ta
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int o = m * 16 + 4 * g4 + r;
-                    if (o < C) {
-                        const size_t idx = (size_t)o * T + t;
-                        yb[idx] = fmaf(acc[m][s][r], a.out_scale, res[m][s][r]);
-                    }
+                    if (o < C)
+                        __builtin_nontemporal_store(fmaf(acc[m][s][r], a.out_scale, res[m][s][r]),
+                                                    yb + (size_t)o * T + t);
                 }
             }
         }
@@ -464,6 +469,28 @@ __global__ __launch_bounds__(kUT, 2) void amp_unit_kernel(UnitArgs a, ActTaps ta
 // wt[(j*C + i)*CP + o] = w[o][i][j]; zero for o >= C and for padding rows.
 __global__ void pack_unit_weights_kernel(const float* __restrict__ w, float* __restrict__ wt,
                                          int C, int K, int CP, int rows) {
+    const int n = rows * CP;
+    for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += gridDim.x * blockDim.x) {
+        const int o = idx % CP;
+        const int row = idx / CP;
+        float v = 0.f;
+        if (o < C && row < K * C) {
+            const int j = row / C;
+            const int i = row - j * C;
+            v = w[((size_t)o * C + i) * K + j];
+        }
+        wt[idx] = v;
+    }
+}
+
+// Several weights packed in one launch (blockIdx.y selects the pair).
+struct PackList {
+    const float* w[2 * 4];
+    float* wt[2 * 4];
+};
+__global__ void pack_unit_weights_multi_kernel(PackList l, int C, int K, int CP, int rows) {
+    const float* __restrict__ w = l.w[blockIdx.y];
+    float* __restrict__ wt = l.wt[blockIdx.y];
     const int n = rows * CP;
     for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += gridDim.x * blockDim.x) {
         const int o = idx % CP;
@@ -500,7 +527,12 @@ struct UnitPlan {
 // Largest time tile whose LDS fits two blocks per CU (three for C <= 16),
 // with the per-wave tile count NTW chosen so that conv1's time tiles fill
 // the four waves exactly.
-bool plan_unit(int C, int K, int d, UnitPlan* p) {
+// The largest time tile that fits, unless the grid of B rows of T samples
+// would then be less than one resident round of blocks (two, or three for
+// C <= 16, per CU): then the largest tile that still fills one round, or the
+// smallest one (short rows, such as a single [1, 32, 4096] block).  B = 0:
+// the largest tile (the support check).
+bool plan_unit(int C, int K, int d, int B, int T, UnitPlan* p) {
     if (C < 4 || C > 32 || C % 4 != 0 || K < 1 || K % 2 == 0 || d < 1) return false;
     if ((long long)(K - 1) * d > 4096) return false;
     const int MT = (C + 15) / 16;
@@ -509,21 +541,24 @@ bool plan_unit(int C, int K, int d, UnitPlan* p) {
     static const int kNtw2[] = {6, 5, 4, 3, 2};
     const int* list = MT == 1 ? kNtw1 : kNtw2;
     const int n = MT == 1 ? 7 : 5;
+    const long long slots = 256LL * (C <= 16 ? 3 : 2);
+    bool found = false;
     for (int i = 0; i < n; ++i) {
         const int NTW = list[i];
         const int N1r = 64 * NTW;
         const int TT = (N1r - 2 * h2 - 10) / 16 * 16;
         if (TT < 32) continue;
         const int NX = TT + 2 * H;
-        const int SP = stride16(std::max(NX + kRunMax + 4, N1r));
+        const int SP = stride16(std::max(NX + run_max(MT) + 4, N1r));
         const int SQ = stride16(N1r + 2 * h1);
         const size_t lds = ((size_t)C * (SP + SQ) + 4 * (size_t)C) * sizeof(float);
         if (lds > (size_t)(C <= 16 ? kLdsBudget3 : kLdsBudget)) continue;
         if ((C * NX + kUT - 1) / kUT > kXR) continue;
         *p = UnitPlan{MT, NTW, TT, SP, SQ, lds};
-        return true;
+        found = true;
+        if (B <= 0 || (long long)B * ((T + TT - 1) / TT) >= slots) return true;
     }
-    return false;
+    return found;
 }
 
 template <int MT, int NTW>
@@ -550,7 +585,7 @@ hipError_t launch_unit_t(const UnitArgs& a, size_t lds, const ActTaps& taps, hip
 
 bool amp_unit_supported(int C, int K, int dilation) {
     UnitPlan p;
-    return plan_unit(C, K, dilation, &p);
+    return plan_unit(C, K, dilation, 0, 0, &p);
 }
 
 size_t amp_unit_packed_floats(int C, int K) {
@@ -567,13 +602,29 @@ hipError_t launch_pack_unit_weights(const float* w, float* wt, int C, int K, hip
     return hipGetLastError();
 }
 
+hipError_t launch_pack_unit_weights_n(const float* const* w, float* const* wt, int n, int C,
+                                      int K, hipStream_t s) {
+    if (n < 1 || n > 8) return hipErrorInvalidValue;
+    PackList l{};
+    for (int i = 0; i < n; ++i) {
+        l.w[i] = w[i];
+        l.wt[i] = wt[i];
+    }
+    const int CP = 16 * ((C + 15) / 16);
+    const int rows = packed_rows(C, K);
+    const int blocks = (rows * CP + 255) / 256;
+    hipLaunchKernelGGL(pack_unit_weights_multi_kernel, dim3(blocks < 1 ? 1 : blocks, n), dim3(256),
+                       0, s, l, C, K, CP, rows);
+    return hipGetLastError();
+}
+
 hipError_t launch_amp_unit(const float* x, float* y, const float* wt1, const float* b1,
                            const float* wt2, const float* b2, const float* la1, const float* lb1,
                            const float* la2, const float* lb2, int B, int C, int T, int K,
                            int dilation, float out_scale, int accumulate, const ActTaps& taps,
                            hipStream_t stream) {
     UnitPlan p;
-    if (!plan_unit(C, K, dilation, &p)) return hipErrorInvalidValue;
+    if (!plan_unit(C, K, dilation, B, T, &p)) return hipErrorInvalidValue;
     const int tiles = (T + p.TT - 1) / p.TT;
     const long long nblk = (long long)B * tiles;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;

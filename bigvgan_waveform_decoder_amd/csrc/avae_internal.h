@@ -84,6 +84,9 @@ hipError_t launch_snake(const float* x, float* y, int B, int C, int T, const flo
 bool amp_unit_supported(int C, int K, int dilation);
 size_t amp_unit_packed_floats(int C, int K);
 hipError_t launch_pack_unit_weights(const float* w, float* wt, int C, int K, hipStream_t s);
+// n <= 8 weights of one (C, K) packed in one launch.
+hipError_t launch_pack_unit_weights_n(const float* const* w, float* const* wt, int n, int C,
+                                      int K, hipStream_t s);
 hipError_t launch_amp_unit(const float* x, float* y, const float* wt1, const float* b1,
                            const float* wt2, const float* b2, const float* la1, const float* lb1,
                            const float* la2, const float* lb2, int B, int C, int T, int K,

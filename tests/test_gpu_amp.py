@@ -51,12 +51,13 @@ def test_amp_block_odd_shapes(C, T, K):
     assert rel_err(y, ref) <= TOL_BLOCK
 
 
-# Widths up to 24 (multiples of 4) run each dilation step as one fused launch
-# (activation, dilated conv, activation, conv, residual).  These cover the
-# tile shapes it picks (1 or 2 channel tiles; 5..11 time tiles per wave),
-# rows shorter than the unit's halo, one-sample rows, and several tiles with
-# a ragged last one; widths 28 and 32 check the separate-launch path at the
-# same sizes.
+# Widths up to 24 (multiples of 4), and up to 32 for short inputs (B T <=
+# 65536), run each dilation step as one fused launch (activation, dilated
+# conv, activation, conv, residual).  These cover the tile shapes it picks
+# (1 or 2 channel tiles; 2..11 time tiles per wave, the small ones for
+# grids under one resident round), rows shorter than the unit's halo,
+# one-sample rows, and several tiles with a ragged last one; the last case
+# (32 channels, B T > 65536) checks the separate-launch path.
 FUSED = [
     (4, 5, 3, (1,)),
     (12, 1, 11, (1, 3, 5)),
@@ -68,6 +69,7 @@ FUSED = [
     (28, 97, 11, (3,)),
     (32, 700, 7, (1, 3, 5)),
     (32, 1000, 3, (1, 3, 5)),
+    (32, 33000, 7, (1, 3, 5)),
 ]
 
 
