@@ -46,11 +46,19 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(float* __restrict__ sin
 }
 
 // Streaming copy y = x of n4 float4: one float4 per thread, no loop, so every
-// load of a wave is in flight at once and the grid streams HBM both ways.
+// load of a wave is in flight at once and the grid streams HBM both ways;
+// non-temporal stores (measured on MI355X, 512 MiB of random data: 7.4 TB/s
+// against 6.0 with ordinary stores; two or four float4 per thread and
+// non-temporal loads were slower).
 __global__ __launch_bounds__(256) void stream_copy_kernel(const float4* __restrict__ x,
                                                           float4* __restrict__ y, long long n4) {
+    typedef float nt4 __attribute__((ext_vector_type(4)));
     const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-    if (i < n4) y[i] = x[i];
+    if (i < n4) {
+        const float4 v = x[i];
+        const nt4 w = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(w, reinterpret_cast<nt4*>(y) + i);
+    }
 }
 
 }  // namespace

@@ -32,7 +32,8 @@ __global__ __launch_bounds__(kSnakeThreads) void snake_kernel(const float* __res
                 snake_plain(v.x, a), snake_plain(v.y, a), snake_plain(v.z, a), snake_plain(v.w, a));
         }
     } else {
-        for (int t = t0 + threadIdx.x; t < t1; t += kSnakeThreads) yr[t] = snake_plain(xr[t], a);
+        for (int t = t0 + threadIdx.x; t < t1; t += kSnakeThreads)
+            __builtin_nontemporal_store(snake_plain(xr[t], a), yr + t);
     }
 }
 
