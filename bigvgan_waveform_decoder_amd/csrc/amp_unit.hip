@@ -14,9 +14,11 @@
 // and four writes of [B, C, T] through HBM, and each convolution alone has
 // too few flops per byte to keep the matrix cores busy.  Here one block owns
 // a time tile of TT outputs of every channel of one batch row: it stages x
-// over the tile plus the unit's halo (H = 10 + (K-1)(d+1)/2 per side) in LDS,
-// runs act1, conv1, act2 and conv2 out of LDS, and writes y once.  HBM
-// traffic is one read of x (plus halo) and one write of y.
+// over the tile plus the unit's halo (H = 10 + (K-1)(d+1)/2 per side) in LDS
+// by LDS DMA (no register round trip), runs act1, conv1, act2 and conv2 out
+// of LDS, and writes y once.  HBM traffic is one read of x (plus halo) and
+// one write of y; the residual x is read again from L2 for the epilogue
+// rather than held in registers through the activations.
 //
 // LDS holds two buffers of C rows.  P holds x, then conv1's output; Q holds
 // act1's output, then act2's.  Ranges (global sample index):
@@ -31,7 +33,8 @@
 // is replicate-padded in LDS before act2 (the activation's own padding);
 // doubled-rate samples outside [0, 2T) take the boundary sample (the
 // down-sampler's replicate padding); activation outputs outside [0, T) are
-// 0 (the convolutions' zero padding).  Interior tiles skip all of this.
+// 0 (the convolutions' zero padding).  Interior tiles run a separate copy of
+// the activation without any of this.
 //
 // Convolutions: implicit GEMM on v_mfma_f32_16x16x4_f32 with M = output
 // channel (MT tiles of 16), N = time (16-wide tiles, NTW per wave, every
@@ -60,7 +63,6 @@ constexpr int kLdsBudget = 80 * 1024; // two blocks per CU
 // third co-resident block to overlap the phases; measured -20% at C = 16
 // and -5% at C = 12, slower at C = 24 (whose tiles would shrink to 160).
 constexpr int kLdsBudget3 = 53 * 1024;
-constexpr int kXR = 48;               // staged x values per thread (bound)
 
 struct UnitArgs {
     const float* x;
@@ -84,23 +86,24 @@ struct UnitArgs {
 // R + 10 inputs: the doubled-rate pairs e[u] = s(2(g-2+u)) and
 // o[u] = s(2(g-3+u)+1) both read the inputs u .. u+5 of the window, and
 // output r is sum_k down[2k] o[r+k] + down[2k+1] e[r+k] (g = og + m0).
-// Runs start at multiples of R floats of 16-float-aligned rows, so the
-// window is read with 16-byte LDS loads and a full run is written with them.
-template <int R>
+// Runs start at multiples of R floats of 16-float-aligned rows, so an
+// interior run reads its window with 16-byte LDS loads and writes a full run
+// with them; an edge run (kEdge) reads every input at its clamped position.
+template <int R, bool kEdge>
 __device__ __forceinline__ void act_run(const float* __restrict__ src, int ss,
                                         float* __restrict__ dst, int ds, int c, int m0, int Nd,
-                                        int og, int T, bool edge, const float* arev,
-                                        const float* ibeta, const ActTaps& taps) {
+                                        int og, int T, const float* arev, const float* ibeta,
+                                        const ActTaps& taps) {
     constexpr int W = R + 12;  // window read (R + 10 used)
     const int g = og + m0;
     float out[R];
-    if (edge && (g + R <= 0 || g >= T)) {
+    if (kEdge && (g + R <= 0 || g >= T)) {
 #pragma unroll
         for (int r = 0; r < R; ++r) out[r] = 0.f;
     } else {
         const float* srow = src + c * ss;
         float xw[W];
-        if (!edge) {
+        if (!kEdge) {
             const float4* s4 = reinterpret_cast<const float4*>(srow + m0);
 #pragma unroll
             for (int i = 0; i < W / 4; ++i) {
@@ -128,7 +131,7 @@ __device__ __forceinline__ void act_run(const float* __restrict__ src, int ss,
             e[u] = snake_beta(ev, ar, ib);
             o[u] = snake_beta(ov, ar, ib);
         }
-        if (edge) {
+        if (kEdge) {
             const int base = 5 - og;  // src index of global position 0
             if (g < 3) {
                 // s(0): the even sample at q = 0 from x[clamp(2 - k)]
@@ -165,7 +168,7 @@ __device__ __forceinline__ void act_run(const float* __restrict__ src, int ss,
                 acc = fmaf(taps.down[2 * k], o[r + k], acc);
                 acc = fmaf(taps.down[2 * k + 1], e[r + k], acc);
             }
-            out[r] = (edge && (g + r < 0 || g + r >= T)) ? 0.f : acc;
+            out[r] = (kEdge && (g + r < 0 || g + r >= T)) ? 0.f : acc;
         }
     }
     float* drow = dst + c * ds + m0;
@@ -183,10 +186,10 @@ __device__ __forceinline__ void act_run(const float* __restrict__ src, int ss,
 
 // The activation over all C rows of a range: runs of R outputs, one per
 // thread per pass.
-template <int R>
+template <int R, bool kEdge>
 __device__ __forceinline__ void act_pass(const float* __restrict__ src, int ss,
                                          float* __restrict__ dst, int ds, int C, int Nd, int og,
-                                         int T, bool edge, const float* arev, const float* ibeta,
+                                         int T, const float* arev, const float* ibeta,
                                          const ActTaps& taps) {
     const int runs = (Nd + R - 1) / R;
     const int items = C * runs;
@@ -194,7 +197,7 @@ __device__ __forceinline__ void act_pass(const float* __restrict__ src, int ss,
     const int add_c = kUT / runs, add_r = kUT - add_c * runs;
     int c = threadIdx.x / runs, run = threadIdx.x - c * runs;
     for (int it = threadIdx.x; it < items; it += kUT) {
-        act_run<R>(src, ss, dst, ds, c, run * R, Nd, og, T, edge, arev, ibeta, taps);
+        act_run<R, kEdge>(src, ss, dst, ds, c, run * R, Nd, og, T, arev, ibeta, taps);
         c += add_c;
         run += add_r;
         if (run >= runs) {
@@ -204,32 +207,39 @@ __device__ __forceinline__ void act_pass(const float* __restrict__ src, int ss,
     }
 }
 
-// The run length is chosen per range: a pass over the block costs about one
-// run (R outputs from R + 5 doubled-rate pairs), and C * ceil(Nd / R) runs
-// take ceil(C * ceil(Nd / R) / 256) passes; a range just over a multiple of
-// 256 runs of 16 would leave most threads idle in its last pass, so runs of
-// 20 or 24 are taken when they need fewer pass-pairs.
-// Run lengths are 12, 20 or 28 floats: the 64 lanes of a wave read windows
-// R floats apart with 16-byte LDS loads, and for R = 4 (mod 8) every 8
-// consecutive lanes (one LDS cycle of 16-byte reads) land in distinct bank
-// groups; R = 16 put 4 lanes, R = 24 two lanes, on one group.  28 needs
-// the register room of the two-blocks-per-CU kernels (kLong).
+// The run length of an interior range: a pass over the block costs about
+// one run (R outputs from R + 5 doubled-rate pairs), and C * ceil(Nd / R)
+// runs take ceil(C * ceil(Nd / R) / 256) passes; a range just over a
+// multiple of 256 runs of 16 would leave most threads idle in its last pass,
+// so the length with the fewest pass-pairs wins.  Run lengths are 12, 20 or
+// 28 floats: the 64 lanes of a wave read windows R floats apart with 16-byte
+// LDS loads, and for R = 4 (mod 8) every 8 consecutive lanes (one LDS cycle
+// of 16-byte reads) land in distinct bank groups; R = 16 put 4 lanes, R = 24
+// two lanes, on one group.  28 needs the register room of the
+// two-blocks-per-CU kernels (kLong).  Edge tiles (two per row) run a
+// separate copy with runs of 12: kept apart, the interior copy's window
+// loads stay 16-byte vector loads (merged with the edge path's clamped
+// reads, the compiler turns them all into 4-byte loads).
 template <bool kLong>
 __device__ __forceinline__ void act_stage(const float* __restrict__ src, int ss,
                                           float* __restrict__ dst, int ds, int C, int Nd, int og,
                                           int T, bool edge, const float* arev, const float* ibeta,
                                           const ActTaps& taps) {
+    if (edge) {
+        act_pass<12, true>(src, ss, dst, ds, C, Nd, og, T, arev, ibeta, taps);
+        return;
+    }
     auto cost = [&](int R) {
         const int items = C * ((Nd + R - 1) / R);
         return ((items + kUT - 1) / kUT) * (R + 5);
     };
     const int c12 = cost(12), c20 = cost(20), c28 = kLong ? cost(28) : 1 << 30;
     if (c28 < c20 && c28 < c12)
-        act_pass<kLong ? 28 : 20>(src, ss, dst, ds, C, Nd, og, T, edge, arev, ibeta, taps);
+        act_pass<kLong ? 28 : 20, false>(src, ss, dst, ds, C, Nd, og, T, arev, ibeta, taps);
     else if (c20 <= c12)
-        act_pass<20>(src, ss, dst, ds, C, Nd, og, T, edge, arev, ibeta, taps);
+        act_pass<20, false>(src, ss, dst, ds, C, Nd, og, T, arev, ibeta, taps);
     else
-        act_pass<12>(src, ss, dst, ds, C, Nd, og, T, edge, arev, ibeta, taps);
+        act_pass<12, false>(src, ss, dst, ds, C, Nd, og, T, arev, ibeta, taps);
 }
 
 typedef const float __attribute__((address_space(1))) gfloat;
@@ -305,8 +315,35 @@ __device__ __forceinline__ void conv_tiles(const float* __restrict__ Bs, int sb,
     }
 }
 
+// x[clamp(t0 - H + u)] for u in [0, NX) of every channel into P by LDS DMA
+// (global_load_lds_dword: lane l's sample goes straight to LDS at the chunk
+// start + l, no registers): each DMA instruction of a wave fills a chunk of
+// 64 samples of one row.  A row's last chunk starts at NX - 64 and rewrites
+// the overlap with the chunk before it with the same values, so no chunk
+// crosses into the next row; a row shorter than 64 (NX >= 36) takes one
+// chunk whose tail lands in the row's padding (SP >= 64 NTW >= 128).  The
+// caller waits for the loads (vmcnt) before the barrier that publishes P.
+__device__ __forceinline__ void stage_x(const float* __restrict__ xb, float* P, int SP, int C,
+                                        int T, int t0, int H, int NX, int wid, int lane) {
+    const int nch = (NX + 63) / 64;
+    for (int k = wid; k < C * nch; k += kUT / 64) {
+        const int c = k / nch, j = k - c * nch;
+        const int u0 = (NX > 64 && j == nch - 1) ? NX - 64 : 64 * j;
+        const int t = min(max(t0 - H + u0 + lane, 0), T - 1);
+        __builtin_amdgcn_global_load_lds((const void*)(xb + (size_t)c * T + t),
+                                         (void*)(P + c * SP + u0), 4, 0, 0);
+    }
+}
+
+// Waits for this wave's outstanding vector memory operations (the LDS DMA
+// of stage_x; also its stores).
+__device__ __forceinline__ void wait_vmem() {
+    // s_waitcnt vmcnt(0), expcnt and lgkmcnt left at their maxima
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
 template <int MT, int NTW>
-__global__ __launch_bounds__(kUT, 2) void amp_unit_kernel(UnitArgs a, ActTaps taps) {
+__global__ __launch_bounds__(kUT, (MT == 1 && NTW <= 8) ? 3 : 2) void amp_unit_kernel(UnitArgs a, ActTaps taps) {
     extern __shared__ __align__(16) float lds[];
     const int C = a.C, T = a.T, K = a.K, d = a.d, TT = a.TT, SP = a.SP, SQ = a.SQ;
     const int h1 = (K - 1) * d / 2, h2 = (K - 1) / 2, H = h1 + h2 + 10;
@@ -337,60 +374,17 @@ __global__ __launch_bounds__(kUT, 2) void amp_unit_kernel(UnitArgs a, ActTaps ta
             bias2[m][r] = (a.b2 && o < C) ? a.b2[o] : 0.f;
         }
 
-    // 1. x[clamp(t0 - H + u)] for u in [0, NX): every load of the thread is
-    //    issued before the first LDS write (one HBM latency per tile); the
-    //    activation constants.
-    {
-        const int total = C * NX;
-        const int nload = (total + kUT - 1) / kUT;  // <= kXR by the plan
-        const int add_c = kUT / NX, add_u = kUT - add_c * NX;
-        const int c0 = tid / NX, u0 = tid - c0 * NX;
-        float v[kXR];
-        int c = c0, u = u0;
-#pragma unroll
-        for (int r = 0; r < kXR; ++r) {
-            if (r < nload && c < C) v[r] = xb[(size_t)c * T + min(max(t0 - H + u, 0), T - 1)];
-            c += add_c;
-            u += add_u;
-            if (u >= NX) {
-                u -= NX;
-                ++c;
-            }
-        }
-        c = c0;
-        u = u0;
-#pragma unroll
-        for (int r = 0; r < kXR; ++r) {
-            if (r < nload && c < C) P[c * SP + u] = v[r];
-            c += add_c;
-            u += add_u;
-            if (u >= NX) {
-                u -= NX;
-                ++c;
-            }
-        }
-        if (tid < C) {
-            prm[tid] = snake_alpha_rev(a.la1[tid]);
-            prm[C + tid] = snake_inv_beta(a.lb1[tid]);
-            prm[2 * C + tid] = snake_alpha_rev(a.la2[tid]);
-            prm[3 * C + tid] = snake_inv_beta(a.lb2[tid]);
-        }
+    // 1. x[clamp(t0 - H + u)] for u in [0, NX) by LDS DMA; the activation
+    //    constants.
+    stage_x(xb, P, SP, C, T, t0, H, NX, wid, lane);
+    if (tid < C) {
+        prm[tid] = snake_alpha_rev(a.la1[tid]);
+        prm[C + tid] = snake_inv_beta(a.lb1[tid]);
+        prm[2 * C + tid] = snake_alpha_rev(a.la2[tid]);
+        prm[3 * C + tid] = snake_inv_beta(a.lb2[tid]);
     }
+    wait_vmem();
     __syncthreads();
-
-    // x + b2 at this lane's outputs, kept in registers (P is reused); the
-    // epilogue adds conv2's sum to it.
-    float res[MT][NTW][4];
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int s = 0; s < NTW; ++s)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int o = m * 16 + 4 * g4 + r;
-                const int n = (wid + 4 * s) * 16 + l16;
-                res[m][s][r] = ((o < C && n < TT) ? P[o * SP + n + H] : 0.f) + bias2[m][r];
-            }
 
     // 2. act1: P -> Q over [t0 - H + 5, +NA1)
     act_stage<MT == 2>(P, SP, Q, SQ, C, NA1, t0 - H + 5, T, edge, prm, prm + C, taps);
@@ -431,8 +425,11 @@ __global__ __launch_bounds__(kUT, 2) void amp_unit_kernel(UnitArgs a, ActTaps ta
 
     // 6. conv2: Q -> y over [t0, t0 + TT), plus bias, residual x, epilogue
     // out = (conv2 + b2 + x) * out_scale (+ out): fold everything but the
-    // sum into res, reading the old output before the matrix loop.
+    // sum into res before the matrix loop, x read again (from L2: this
+    // block staged it) rather than kept in registers through the
+    // activations, the old output read if accumulating.
     float* __restrict__ yb = a.y + row0;
+    float res[MT][NTW][4];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -442,9 +439,11 @@ __global__ __launch_bounds__(kUT, 2) void amp_unit_kernel(UnitArgs a, ActTaps ta
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int o = m * 16 + 4 * g4 + r;
-                const float old =
-                    (a.accumulate && nt < NT2 && t < T && o < C) ? yb[(size_t)o * T + t] : 0.f;
-                res[m][s][r] = fmaf(res[m][s][r], a.out_scale, old);
+                const bool in = nt < NT2 && t < T && o < C;
+                const size_t idx = (size_t)o * T + t;
+                const float xv = in ? xb[idx] : 0.f;
+                const float old = (a.accumulate && in) ? yb[idx] : 0.f;
+                res[m][s][r] = fmaf(xv + bias2[m][r], a.out_scale, old);
             }
         }
     conv_tiles<MT, NTW>(Q, SQ, 1, a.wt2, C, K, acc);
@@ -553,7 +552,6 @@ bool plan_unit(int C, int K, int d, int B, int T, UnitPlan* p) {
         const int SQ = stride16(N1r + 2 * h1);
         const size_t lds = ((size_t)C * (SP + SQ) + 4 * (size_t)C) * sizeof(float);
         if (lds > (size_t)(C <= 16 ? kLdsBudget3 : kLdsBudget)) continue;
-        if ((C * NX + kUT - 1) / kUT > kXR) continue;
         *p = UnitPlan{MT, NTW, TT, SP, SQ, lds};
         found = true;
         if (B <= 0 || (long long)B * ((T + TT - 1) / TT) >= slots) return true;

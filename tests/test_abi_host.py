@@ -137,11 +137,14 @@ def test_dav_bwe_and_tail_ops_reject_bad_arguments():
 
 
 def test_kernel_names_in_the_profiler_are_stable():
-    """bench.py's traffic lookup keys on the library's kernel names."""
+    """bench.py's traffic lookup keys on the names the library's launch
+    profiler gives its kernels (conv.hip, act1d.hip, amp_unit.hip)."""
     import json
     d = json.load(open(os.path.join(ROOT, "profiles", "pmc_traffic.json")))
+    pat = (r"(conv1d_(pipe|dma)_kernel<\d+,\d+,\d+,\d+,\d+,\d+>"
+           r"|act1d_kernel|amp_unit_kernel<\d+,\d+>)$")
     for name, e in d["kernels"].items():
-        assert re.match(r"conv1d_(pipe|dma)_kernel<\d+,\d+,\d+,\d+,\d+,\d+>$", name), name
+        assert re.match(pat, name), name
         assert os.path.exists(os.path.join(ROOT, e["source"]))
 
 
