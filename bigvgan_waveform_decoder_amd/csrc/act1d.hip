@@ -22,12 +22,11 @@
 // then runs the stride-2 FIR from LDS and writes the outputs once.  HBM
 // traffic is one read and one write of the row (8 bytes per element).
 //
-// SnakeBeta's sine: sin(alpha v) = sin(2 pi r) with r = v * (alpha / 2 pi);
-// r is reduced to [0, 1) by v_fract_f32 (exact) and v_sin_f32 evaluates
-// sin(2 pi r) directly in revolutions.  Against the reduced argument the
-// hardware sine is within ~1.3e-7 (measured on MI355X over [0, 1)); the only
-// other error is the float32 rounding of r itself, relative ~1e-7 of the
-// phase, the same order as rounding alpha*v before any float32 sine.
+// SnakeBeta's sine: sin(alpha v) = sin(2 pi r) with r = v * (alpha / 2 pi),
+// evaluated by v_sin_f32 in revolutions, which reduces the argument itself:
+// within ~1.3e-7 of sin(2 pi frac(r)) (measured on MI355X up to |r| = 1e5);
+// the only other error is the float32 rounding of r itself, relative ~1e-7
+// of the phase, the same order as rounding alpha*v before any float32 sine.
 #include "act_math.h"
 #include "avae_internal.h"
 
