@@ -1230,23 +1230,61 @@ __global__ __launch_bounds__(WM * WN * 64) void convtr1d_dma_kernel(
             dma_w((c + 1) * kKCT, Wn);
             gx((c + 1) * kKCT);
         }
-#pragma unroll
-        for (int m = 0; m < NTAP; ++m) {
-#pragma unroll 1
-            for (int kk = 0; kk < kKCT / 4; ++kk) {
-                float bv[NTL];
+        // One time tile per wave (the first stage's 16-channel tile): the
+        // substeps (tap m, channels kk*4 .. kk*4+3), m outer, fully unrolled,
+        // each substep's operands read from LDS before the previous
+        // substep's MFMAs (two register sets, pinned by a scheduling
+        // barrier), so the matrix work does not wait on its own reads.  The
+        // wider tiles would need 240-280 VGPRs that way and keep the rolled
+        // loop.
+        if constexpr (NTL == 1) {
+            constexpr int NSUB = NTAP * (kKCT / 4);
+            float avb[2][S], bvb[2][NTL];
+            auto ldo = [&](int sub, int buf) {
+                const int m = sub / (kKCT / 4), kk = sub - m * (kKCT / 4);
 #pragma unroll
                 for (int cc = 0; cc < NTL; ++cc)
-                    bv[cc] = Xc[(kk * 4 + g) * XS + wn0 + cc * 16 + l16 + (NTAP - 1 - m)];
+                    bvb[buf][cc] = Xc[(kk * 4 + g) * XS + wn0 + cc * 16 + l16 + (NTAP - 1 - m)];
 #pragma unroll
-                for (int r = 0; r < S; ++r) {
+                for (int r = 0; r < S; ++r)
+                    if (r + S * m < KT)
+                        avb[buf][r] = Wc[(kk * 4 + g) * RS + (wm * 16 + l16) * KT + r + S * m];
+            };
+            ldo(0, 0);
+#pragma unroll
+            for (int sub = 0; sub < NSUB; ++sub) {
+                const int m = sub / (kKCT / 4);
+                const int cb = sub & 1;
+                if (sub + 1 < NSUB) ldo(sub + 1, cb ^ 1);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int r = 0; r < S; ++r)
                     if (r + S * m < KT) {
-                        const float av =
-                            Wc[(kk * 4 + g) * RS + (wm * 16 + l16) * KT + r + S * m];
 #pragma unroll
                         for (int cc = 0; cc < NTL; ++cc)
                             part[r][cc] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                                av, bv[cc], part[r][cc], 0, 0, 0);
+                                avb[cb][r], bvb[cb][cc], part[r][cc], 0, 0, 0);
+                    }
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < NTAP; ++m) {
+#pragma unroll 1
+                for (int kk = 0; kk < kKCT / 4; ++kk) {
+                    float bv[NTL];
+#pragma unroll
+                    for (int cc = 0; cc < NTL; ++cc)
+                        bv[cc] = Xc[(kk * 4 + g) * XS + wn0 + cc * 16 + l16 + (NTAP - 1 - m)];
+#pragma unroll
+                    for (int r = 0; r < S; ++r) {
+                        if (r + S * m < KT) {
+                            const float av =
+                                Wc[(kk * 4 + g) * RS + (wm * 16 + l16) * KT + r + S * m];
+#pragma unroll
+                            for (int cc = 0; cc < NTL; ++cc)
+                                part[r][cc] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                    av, bv[cc], part[r][cc], 0, 0, 0);
+                        }
                     }
                 }
             }
