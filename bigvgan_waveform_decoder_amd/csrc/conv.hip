@@ -1520,12 +1520,12 @@ hipError_t launch_convtr1d(const float* x, float* y, const float* w, const float
                            hipStream_t stream, const float* in_alpha) {
     // float4 weight slices need Cout*K % 4 == 0 and a 16-byte aligned base
     const bool vec = ((long long)Cout * K) % 4 == 0 && ((uintptr_t)w & 15) == 0;
-    // short inputs (the first stage: 400 positions) get 16-channel tiles, twice
-    // the blocks of the 32-channel ones (measured 333 -> 272 us at 1536 -> 768)
-    if (vec && stride == 5 && K == 11 && Tin <= 1000)
-        return run_convtr1d_poly<1, 4, 1, 11, 5>(x, y, w, bias, in_alpha, B, Cin, Cout, Tin, Tout, pad, stream);
+    // 16-channel tiles of 64 positions (twice the blocks of the 32 x 128
+    // ones, and the unrolled substep loop with operands read one substep
+    // ahead): 1536 -> 768 at 400 positions 333 -> 248 us, 768 -> 384 at 2000
+    // positions 279 -> 247 us against 32-channel tiles of 128 positions
     if (vec && stride == 5 && K == 11)
-        return run_convtr1d_poly<2, 2, 2, 11, 5>(x, y, w, bias, in_alpha, B, Cin, Cout, Tin, Tout, pad, stream);
+        return run_convtr1d_poly<1, 4, 1, 11, 5>(x, y, w, bias, in_alpha, B, Cin, Cout, Tin, Tout, pad, stream);
     if (vec && stride == 5 && K == 10)
         return run_convtr1d_poly<2, 2, 2, 10, 5>(x, y, w, bias, in_alpha, B, Cin, Cout, Tin, Tout, pad, stream);
     // stride 2: 64-channel tiles of 64 positions, narrower and longer tiles
