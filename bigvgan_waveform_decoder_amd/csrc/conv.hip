@@ -1230,14 +1230,18 @@ __global__ __launch_bounds__(WM * WN * 64) void convtr1d_dma_kernel(
             dma_w((c + 1) * kKCT, Wn);
             gx((c + 1) * kKCT);
         }
-        // One time tile per wave (the first stage's 16-channel tile): the
-        // substeps (tap m, channels kk*4 .. kk*4+3), m outer, fully unrolled,
-        // each substep's operands read from LDS before the previous
+        // The substeps (tap m, channels kk*4 .. kk*4+3), m outer, fully
+        // unrolled, each substep's operands read from LDS before the previous
         // substep's MFMAs (two register sets, pinned by a scheduling
-        // barrier), so the matrix work does not wait on its own reads.  The
-        // wider tiles would need 240-280 VGPRs that way and keep the rolled
-        // loop.
-        if constexpr (NTL == 1) {
+        // barrier), so the matrix work does not wait on its own reads: for
+        // the tiles where that keeps the occupancy (one time tile per wave:
+        // 168 VGPRs, three blocks per CU; the stride-2 tiles of two or four
+        // channel tiles: 232-248, two blocks per CU as before).  Measured on
+        // MI355X: k=11 s=5 16 x 64 tiles 272 -> 248 us at 1536 -> 768
+        // channels; stride 2, 64 x 64 tiles 104 -> 95 us, 32 x 128 tiles 87
+        // -> 75 us.  The others would drop to one block per CU (280 VGPRs)
+        // and keep the rolled loop.
+        if constexpr (NTL == 1 || (S == 2 && WM >= 2)) {
             constexpr int NSUB = NTAP * (kKCT / 4);
             float avb[2][S], bvb[2][NTL];
             auto ldo = [&](int sub, int buf) {
