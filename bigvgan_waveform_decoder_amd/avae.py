@@ -113,6 +113,15 @@ def lib() -> ctypes.CDLL:
     L.avae_act1d.argtypes = [P, P, c_int, c_int, c_int, P, P, P, P, P]
     L.avae_conv1d.restype = c_int
     L.avae_conv1d.argtypes = [P, P, c_int, c_int, c_int, c_int, P, P, c_int, c_int, c_int, P, P]
+    L.avae_conv1d_fft_weight_floats.restype = c_size_t
+    L.avae_conv1d_fft_weight_floats.argtypes = [c_int, c_int]
+    L.avae_conv1d_fft_pack.restype = c_int
+    L.avae_conv1d_fft_pack.argtypes = [P, P, c_int, c_int, c_int, c_int, P]
+    L.avae_conv1d_fft_workspace_bytes.restype = c_size_t
+    L.avae_conv1d_fft_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int]
+    L.avae_conv1d_fft.restype = c_int
+    L.avae_conv1d_fft.argtypes = [P, P, c_int, c_int, c_int, c_int, P, P, c_int, c_int, P, P,
+                                  c_size_t, P]
     L.avae_convtr1d.restype = c_int
     L.avae_convtr1d.argtypes = [P, P, c_int, c_int, c_int, c_int, P, P, c_int, c_int, c_int, P]
     L.avae_amp_block_workspace_bytes.restype = c_size_t
@@ -311,6 +320,43 @@ def conv1d(x, w, bias=None, dilation: int = 1, pad: Optional[int] = None, residu
     _check(lib().avae_conv1d(_dev(x, "x"), _dev(out, "out", (B, Cout, Tout)), B, Cin, Cout, T,
                              _dev(w, "w"), _opt(bias, "bias", (Cout,)), K, dilation, pad,
                              _opt(residual, "residual", (B, Cout, Tout)), _stream(stream)))
+    return out
+
+
+def conv1d_fft_pack(w, dilation: int = 1, out=None, stream=None):
+    """avae_conv1d_fft_pack: w [Cout, Cin, K] -> packed frequency-domain weights."""
+    torch = _torch()
+    Cout, Cin, K = w.shape
+    n = int(lib().avae_conv1d_fft_weight_floats(Cin, Cout))
+    if out is None:
+        out = torch.empty((n,), device=w.device, dtype=torch.float32)
+    _check(lib().avae_conv1d_fft_pack(_dev(w, "w"), _dev(out, "out", (n,)), Cin, Cout, K,
+                                      dilation, _stream(stream)))
+    return out
+
+
+def conv1d_fft_workspace_bytes(B: int, Cin: int, Cout: int, T: int, K: int,
+                               dilation: int = 1) -> int:
+    return int(lib().avae_conv1d_fft_workspace_bytes(B, Cin, Cout, T, K, dilation))
+
+
+def conv1d_fft(x, wp, Cout: int, K: int, bias=None, dilation: int = 1, residual=None, out=None,
+               workspace=None, stream=None):
+    """avae_conv1d_fft: 'same'-padded Conv1d with weights packed by conv1d_fft_pack."""
+    torch = _torch()
+    B, Cin, T = x.shape
+    if out is None:
+        out = torch.empty((B, Cout, T), device=x.device, dtype=torch.float32)
+    need = conv1d_fft_workspace_bytes(B, Cin, Cout, T, K, dilation)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), device=x.device, dtype=torch.uint8)
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda:
+        raise ValueError("workspace must be a uint8 device tensor")
+    _check(lib().avae_conv1d_fft(_dev(x, "x"), _dev(out, "out", (B, Cout, T)), B, Cin, Cout, T,
+                                 _dev(wp, "wp"), _opt(bias, "bias", (Cout,)), K, dilation,
+                                 _opt(residual, "residual", (B, Cout, T)),
+                                 workspace.data_ptr(), workspace.numel(),
+                                 _stream(stream)))
     return out
 
 

@@ -97,11 +97,16 @@ bool amp_fusable(int C, int K, int n_dil, const int* dil) {
 // through the MRF epilogue (y = cur * out_scale, + y if accumulate).
 // pw1/pw2 (packed weights, or null) select the fused one-launch-per-step
 // path; otherwise each step is act1d, conv1d, act1d, conv1d launches.
+// fw1/fw2 (per dilation step; null, or null entries, for the direct
+// kernels) are frequency-domain weights from launch_fft_pack: that
+// convolution then runs as launch_conv1d_fft, its two spectra in t1 and t2
+// (slots of at least plan::fft_spectrum_bytes each).
 int run_amp(const float* x, float* y, int B, int C, int T, int K, int n_dil, const int* dil,
             const float* const* w1, const float* const* b1, const float* const* w2,
             const float* const* b2, const float* const* la, const float* const* lb,
-            const float* const* pw1, const float* const* pw2, float out_scale, int accumulate,
-            float* cur, float* t1, float* t2, const ActTaps& taps, hipStream_t s) {
+            const float* const* pw1, const float* const* pw2, const float* const* fw1,
+            const float* const* fw2, float out_scale, int accumulate, float* cur, float* t1,
+            float* t2, const ActTaps& taps, hipStream_t s) {
     if (pw1 && pw2) {
         float* bufs[2] = {t1, t2};
         for (int q = 0; q < n_dil; ++q) {
@@ -121,15 +126,28 @@ int run_amp(const float* x, float* y, int B, int C, int T, int K, int n_dil, con
         const int d = dil[q];
         AVAE_TRY(avae::launch_act1d(src, t1, B, C, T, la[2 * q], lb[2 * q], taps, s), "act1d");
         ConvEpilogue e1{b1[q], nullptr, 1.0f, 0};
-        AVAE_TRY(avae::launch_conv1d(t1, t2, w1[q], B, C, C, T, T, K, d, (K * d - d) / 2, e1, s),
-                 "conv1d (convs1)");
+        if (fw1 && fw1[q]) {
+            // t1 -> spectrum in t2 -> product in t1 -> output in t2
+            AVAE_TRY(avae::launch_conv1d_fft(t1, t2, fw1[q], B, C, C, T, K, d, e1, t2, t1, s),
+                     "conv1d_fft (convs1)");
+        } else {
+            AVAE_TRY(avae::launch_conv1d(t1, t2, w1[q], B, C, C, T, T, K, d, (K * d - d) / 2, e1,
+                                         s),
+                     "conv1d (convs1)");
+        }
         AVAE_TRY(avae::launch_act1d(t2, t1, B, C, T, la[2 * q + 1], lb[2 * q + 1], taps, s),
                  "act1d");
         const bool last = (q == n_dil - 1);
         ConvEpilogue e2{b2[q], src, last ? out_scale : 1.0f, last ? accumulate : 0};
-        AVAE_TRY(avae::launch_conv1d(t1, last ? y : cur, w2[q], B, C, C, T, T, K, 1, (K - 1) / 2,
-                                     e2, s),
-                 "conv1d (convs2)");
+        float* dst = last ? y : cur;
+        if (fw2 && fw2[q]) {
+            // t1 -> spectrum in t2 -> product in t1 -> dst (+ residual src)
+            AVAE_TRY(avae::launch_conv1d_fft(t1, dst, fw2[q], B, C, C, T, K, 1, e2, t2, t1, s),
+                     "conv1d_fft (convs2)");
+        } else {
+            AVAE_TRY(avae::launch_conv1d(t1, dst, w2[q], B, C, C, T, T, K, 1, (K - 1) / 2, e2, s),
+                     "conv1d (convs2)");
+        }
     }
     return AVAE_OK;
 }
@@ -191,6 +209,63 @@ extern "C" int avae_conv1d(const float* x, float* y, int B, int Cin, int Cout, i
     if (e == hipErrorInvalidValue)
         return fail(AVAE_ESHAPE, "avae_conv1d: shape exceeds the kernel's LDS or grid limits");
     if (e != hipSuccess) return hip_fail(e, "avae_conv1d launch");
+    return AVAE_OK;
+}
+
+extern "C" size_t avae_conv1d_fft_weight_floats(int Cin, int Cout) {
+    if (Cin < 1 || Cout < 1) return 0;
+    return avae::fft_conv_weight_floats(Cin, Cout);
+}
+
+extern "C" int avae_conv1d_fft_pack(const float* w, float* wp, int Cin, int Cout, int K,
+                                    int dilation, void* stream) {
+    if (!w || !wp) return fail(AVAE_EINVAL, "avae_conv1d_fft_pack: null pointer");
+    if (Cin < 1 || Cout < 1 || K < 1 || dilation < 1)
+        return fail(AVAE_EINVAL, "avae_conv1d_fft_pack: bad size (Cin=%d Cout=%d K=%d d=%d)", Cin,
+                    Cout, K, dilation);
+    if (!avae::plan::fft_supported(Cin, Cout, K, dilation))
+        return fail(AVAE_ESHAPE,
+                    "avae_conv1d_fft_pack: needs Cin %% 16 == 0, Cout %% 64 == 0, odd K, "
+                    "(K-1)*d <= 128 (Cin=%d Cout=%d K=%d d=%d)",
+                    Cin, Cout, K, dilation);
+    AVAE_TRY(avae::launch_fft_pack(w, wp, Cin, Cout, K, dilation, (hipStream_t)stream),
+             "avae_conv1d_fft_pack launch");
+    return AVAE_OK;
+}
+
+extern "C" size_t avae_conv1d_fft_workspace_bytes(int B, int Cin, int Cout, int T, int K,
+                                                  int dilation) {
+    if (B < 1 || T < 1 || !avae::plan::fft_supported(Cin, Cout, K, dilation)) return 0;
+    const size_t a = avae::plan::fft_spectrum_bytes(B, Cin, T, K, dilation);
+    const size_t b = avae::plan::fft_spectrum_bytes(B, Cout, T, K, dilation);
+    return (a == 0 || b == 0) ? 0 : a + b;
+}
+
+extern "C" int avae_conv1d_fft(const float* x, float* y, int B, int Cin, int Cout, int T,
+                               const float* wp, const float* bias, int K, int dilation,
+                               const float* residual, void* workspace, size_t ws_bytes,
+                               void* stream) {
+    if (!x || !y || !wp) return fail(AVAE_EINVAL, "avae_conv1d_fft: null tensor pointer");
+    if (B < 1 || Cin < 1 || Cout < 1 || T < 1 || K < 1 || dilation < 1)
+        return fail(AVAE_EINVAL, "avae_conv1d_fft: bad size (B=%d Cin=%d Cout=%d T=%d K=%d d=%d)",
+                    B, Cin, Cout, T, K, dilation);
+    if (x == y) return fail(AVAE_EINVAL, "avae_conv1d_fft: x and y must not overlap");
+    if (!avae::plan::fft_supported(Cin, Cout, K, dilation))
+        return fail(AVAE_ESHAPE,
+                    "avae_conv1d_fft: needs Cin %% 16 == 0, Cout %% 64 == 0, odd K, "
+                    "(K-1)*d <= 128 (Cin=%d Cout=%d K=%d d=%d)",
+                    Cin, Cout, K, dilation);
+    const size_t need = avae_conv1d_fft_workspace_bytes(B, Cin, Cout, T, K, dilation);
+    if (!workspace || ws_bytes < need)
+        return fail(AVAE_EWORKSPACE, "avae_conv1d_fft: workspace %zu bytes < %zu needed", ws_bytes,
+                    need);
+    float* xs = (float*)workspace;
+    float* ys = (float*)((char*)workspace + avae::plan::fft_spectrum_bytes(B, Cin, T, K, dilation));
+    ConvEpilogue ep{bias, residual, 1.0f, 0, nullptr, nullptr};
+    avae::prof_set_phase(avae::kPhaseNone);
+    AVAE_TRY(avae::launch_conv1d_fft(x, y, wp, B, Cin, Cout, T, K, dilation, ep, xs, ys,
+                                     (hipStream_t)stream),
+             "avae_conv1d_fft launch");
     return AVAE_OK;
 }
 
@@ -296,8 +371,8 @@ int amp_block_run(const float* x, float* y, int B, int C, int T, int K, int n_di
         AVAE_TRY(avae::launch_pack_unit_weights_n(src, dst, 2 * n_dil, C, K, s), "weight packing");
     }
     return run_amp(x, y, B, C, T, K, n_dil, dil, w1, b1 ? b1 : kNull, w2, b2 ? b2 : kNull,
-                   log_alpha, log_beta, fused ? pw1 : nullptr, fused ? pw2 : nullptr, out_scale,
-                   accumulate, cur, t1, t2, make_taps(nullptr, nullptr), s);
+                   log_alpha, log_beta, fused ? pw1 : nullptr, fused ? pw2 : nullptr, nullptr,
+                   nullptr, out_scale, accumulate, cur, t1, t2, make_taps(nullptr, nullptr), s);
 }
 }  // namespace
 
@@ -393,6 +468,11 @@ struct avae_decoder {
     const float* pw1[AVAE_MAX_STAGES][AVAE_MAX_KERNELS][AVAE_MAX_DIL] = {};
     const float* pw2[AVAE_MAX_STAGES][AVAE_MAX_KERNELS][AVAE_MAX_DIL] = {};
     void* pblob = nullptr;
+    // frequency-domain weights of the AMP convolutions that plan::fft_amp_conv
+    // selects (else null)
+    const float* fw1[AVAE_MAX_STAGES][AVAE_MAX_KERNELS][AVAE_MAX_DIL] = {};
+    const float* fw2[AVAE_MAX_STAGES][AVAE_MAX_KERNELS][AVAE_MAX_DIL] = {};
+    void* fblob = nullptr;
     // The AMP blocks of a stage are independent (they all read the ConvT
     // output): blocks 1.. run on side streams forked from and joined back to
     // the caller's stream with events, so one block's last partial wave of
@@ -597,6 +677,57 @@ extern "C" int avae_decoder_create(const avae_config* cfg, const avae_weights* w
             return hip_fail(e, "avae_decoder_create: weight packing");
         }
     }
+    // Frequency-domain copies of the wide AMP convolutions.
+    size_t fbytes = 0;
+    for (int i = 0; i < c.n_stages; ++i)
+        for (int j = 0; j < c.n_kernels; ++j) {
+            const int co = c.ch[i + 1], K = c.rb_k[j];
+            const size_t per = round_up(avae::fft_conv_weight_floats(co, co) * sizeof(float), 256);
+            for (int q = 0; q < c.n_dil; ++q) {
+                if (avae::plan::fft_amp_conv(co, K, c.rb_d[j][q])) fbytes += per;
+                if (avae::plan::fft_amp_conv(co, K, 1)) fbytes += per;
+            }
+        }
+    if (fbytes) {
+        e = hipMalloc(&d->fblob, fbytes);
+        if (e != hipSuccess) {
+            if (d->pblob) (void)hipFree(d->pblob);
+            (void)hipFree(d->blob);
+            delete d;
+            return fail(AVAE_ENOMEM, "avae_decoder_create: hipMalloc(%zu): %s", fbytes,
+                        hipGetErrorString(e));
+        }
+        char* fp = (char*)d->fblob;
+        for (int i = 0; i < c.n_stages && e == hipSuccess; ++i)
+            for (int j = 0; j < c.n_kernels && e == hipSuccess; ++j) {
+                const int co = c.ch[i + 1], K = c.rb_k[j];
+                const size_t per =
+                    round_up(avae::fft_conv_weight_floats(co, co) * sizeof(float), 256);
+                for (int q = 0; q < c.n_dil && e == hipSuccess; ++q) {
+                    const int dq = c.rb_d[j][q];
+                    if (avae::plan::fft_amp_conv(co, K, dq)) {
+                        e = avae::launch_fft_pack(d->w.w1[i][j][q], (float*)fp, co, co, K, dq,
+                                                  nullptr);
+                        d->fw1[i][j][q] = (const float*)fp;
+                        fp += per;
+                    }
+                    if (e == hipSuccess && avae::plan::fft_amp_conv(co, K, 1)) {
+                        e = avae::launch_fft_pack(d->w.w2[i][j][q], (float*)fp, co, co, K, 1,
+                                                  nullptr);
+                        d->fw2[i][j][q] = (const float*)fp;
+                        fp += per;
+                    }
+                }
+            }
+        if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
+        if (e != hipSuccess) {
+            (void)hipFree(d->fblob);
+            if (d->pblob) (void)hipFree(d->pblob);
+            (void)hipFree(d->blob);
+            delete d;
+            return hip_fail(e, "avae_decoder_create: frequency-domain weights");
+        }
+    }
     // side streams and events for the concurrent MRF blocks (non-blocking:
     // no implicit ordering with the null stream; default priority)
     if (c.n_kernels > 1) {
@@ -622,6 +753,7 @@ extern "C" void avae_decoder_destroy(avae_decoder* dec) {
     if (dec->fork) (void)hipEventDestroy(dec->fork);
     if (dec->blob) (void)hipFree(dec->blob);
     if (dec->pblob) (void)hipFree(dec->pblob);
+    if (dec->fblob) (void)hipFree(dec->fblob);
     (void)hipSetDevice(cur);
     delete dec;
 }
@@ -742,8 +874,8 @@ int decode_impl(const avae_decoder* dec, const float* latent, int B, int frames,
                 int rc = run_amp(X, outs[k], B, co, To, c.rb_k[k], c.n_dil, c.rb_d[k], w.w1[i][k],
                                  w.b1[i][k], w.w2[i][k], w.b2[i][k], w.act_la[i][k],
                                  w.act_lb[i][k], fused ? dec->pw1[i][k] : nullptr,
-                                 fused ? dec->pw2[i][k] : nullptr, inv_nk, 0, sc, s1, s2,
-                                 dec->taps, sk);
+                                 fused ? dec->pw2[i][k] : nullptr, dec->fw1[i][k],
+                                 dec->fw2[i][k], inv_nk, 0, sc, s1, s2, dec->taps, sk);
                 if (rc) return rc;
             }
             // join, then M = block 0 + the others (each already scaled by 1/nk)
@@ -759,8 +891,9 @@ int decode_impl(const avae_decoder* dec, const float* latent, int B, int frames,
                 int rc = run_amp(X, M, B, co, To, c.rb_k[j], c.n_dil, c.rb_d[j], w.w1[i][j],
                                  w.b1[i][j], w.w2[i][j], w.b2[i][j], w.act_la[i][j],
                                  w.act_lb[i][j], fused ? dec->pw1[i][j] : nullptr,
-                                 fused ? dec->pw2[i][j] : nullptr, inv_nk, j > 0 ? 1 : 0, cur,
-                                 t1, t2, dec->taps, s);
+                                 fused ? dec->pw2[i][j] : nullptr, dec->fw1[i][j],
+                                 dec->fw2[i][j], inv_nk, j > 0 ? 1 : 0, cur, t1, t2, dec->taps,
+                                 s);
                 if (rc) return rc;
             }
         }

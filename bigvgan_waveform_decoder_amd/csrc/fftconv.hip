@@ -1,0 +1,453 @@
+// Conv1d in the frequency domain (overlap-save, 256-point transforms) for
+// gfx950: the same operation as the direct kernels in conv.hip, evaluated
+// through the convolution theorem, so that the matrix cores do ~2 real
+// multiply-adds per output and channel pair instead of K.
+//
+// Operation ([H3] = docs.rs page of cortiq_engine/audiovae.rs, Conv1d::apply
+// and the dilated convolutions of AmpBlock::apply): "same" padding, odd K,
+//   y[b,o,t] = bias[o] + sum_c sum_j w[o,c,j] x[b,c,t + j d - P],  P = (K-1)d/2,
+// with x zero outside [0, T), then the epilogue of the direct kernels
+// (+ residual, * out_scale, + previous y).
+//
+// Framing.  With span S = (K-1)d and L = N - S, output block n of a row,
+// t in [nL, nL + L), only reads s_n[u] = x[nL - P + u], u in [0, N):
+//   y[nL + v] = sum_j w_j s_n[v + j d],  v < L,
+// a circular cross-correlation of s_n with g (g[j d] = w_j, else 0) that
+// never wraps.  In the DFT domain (X_k = sum_u s[u] e^{-2 pi i k u / N}):
+//   Y_k = sum_c conj(G_oc,k) X_c,k,   conj(G_k) = sum_j w_j e^{+2 pi i k j d / N},
+// one complex matrix product per frequency, over the channels.  Real signals
+// keep bins 0..N/2; bins 0 and N/2 are real and share slot 0 (re = bin 0,
+// im = bin N/2), so there are N/2 = 128 slots, the other 127 holding bins
+// 1..127.
+//
+// Three launches: fft_fwd_kernel (blocks of x -> X[slot][c][column]),
+// fft_gemm_kernel (Y[slot] = W[slot] X[slot] on the matrix cores,
+// v_mfma_f32_16x16x4_f32), fft_inv_kernel (Y -> y, epilogue).  A column is
+// one (batch, block) pair, column = b nb + n.  The packed weights W come from
+// fft_pack_kernel (double-precision sums, rounded once).
+//
+// The transforms are radix-4 Stockham FFTs (self-sorting: every stage reads
+// a[j + r N/4] and writes b[4(j - k) + k + q Ns], k = j mod Ns), one wave per
+// transform, lane j owning butterfly j of each of the four stages.  The
+// first stage's inputs are lane j's own loads and the last stage's outputs
+// are bins j + 64 q in lane j's registers, so only the three inner exchanges
+// go through LDS.
+#include <cstdio>
+
+#include "avae_internal.h"
+#include "plan.h"
+
+namespace avae {
+namespace {
+
+constexpr int kN = 256;           // transform length
+constexpr int kSlots = kN / 2;    // frequency slots (bins 0 and N/2 share slot 0)
+constexpr int kCols = 16;         // transforms (columns) per transform workgroup
+constexpr int kThreads = 256;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float2 cmul(float2 a, float2 b) {
+    return make_float2(fmaf(a.x, b.x, -a.y * b.y), fmaf(a.x, b.y, a.y * b.x));
+}
+__device__ __forceinline__ float2 cadd(float2 a, float2 b) { return make_float2(a.x + b.x, a.y + b.y); }
+__device__ __forceinline__ float2 csub(float2 a, float2 b) { return make_float2(a.x - b.x, a.y - b.y); }
+
+// tw[m] = exp(-2 pi i m / N), from a double-precision sine and cosine.
+__device__ void init_twiddles(float2* tw) {
+    for (int m = threadIdx.x; m < kN; m += blockDim.x) {
+        double s, c;
+        sincospi(-2.0 * (double)m / (double)kN, &s, &c);
+        tw[m] = make_float2((float)c, (float)s);
+    }
+}
+
+// One radix-4 Stockham stage for butterfly j (sub-transform size Ns = 4^p):
+// v[r] = a[j + 64 r] on entry, the four outputs (positions
+// 4(j - k) + k + q Ns, k = j mod Ns) on exit.
+__device__ __forceinline__ void radix4(float2 (&v)[4], int j, int Ns, const float2* tw) {
+    const int k = j & (Ns - 1);
+    if (Ns > 1) {
+        const int step = kN / (4 * Ns);
+        v[1] = cmul(v[1], tw[k * step]);
+        v[2] = cmul(v[2], tw[2 * k * step]);
+        v[3] = cmul(v[3], tw[3 * k * step]);
+    }
+    const float2 s0 = cadd(v[0], v[2]), s1 = csub(v[0], v[2]);
+    const float2 s2 = cadd(v[1], v[3]), s3 = csub(v[1], v[3]);
+    v[0] = cadd(s0, s2);
+    v[2] = csub(s0, s2);
+    v[1] = make_float2(s1.x + s3.y, s1.y - s3.x);  // s1 - i s3
+    v[3] = make_float2(s1.x - s3.y, s1.y + s3.x);  // s1 + i s3
+}
+
+// Forward 256-point DFT by one wave.  Entry: lane j holds a[j + 64 r] in
+// v[r]; exit: lane j holds A[j + 64 q] in v[q].  buf is this wave's own N
+// complex of LDS.  LDS operations of one wave complete in issue order and
+// every write depends on the reads before it, so the exchanges need no
+// barrier; wave_barrier only keeps the compiler from moving them.
+__device__ __forceinline__ void fft256(float2 (&v)[4], int j, float2* buf, const float2* tw) {
+#pragma unroll
+    for (int Ns = 1; Ns < kN / 4; Ns *= 4) {
+        radix4(v, j, Ns, tw);
+        const int k = j & (Ns - 1);
+        const int dst = 4 * (j - k) + k;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) buf[dst + q * Ns] = v[q];
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = buf[j + 64 * r];
+        __builtin_amdgcn_wave_barrier();
+    }
+    radix4(v, j, kN / 4, tw);  // k = j: outputs j + 64 q stay in place
+}
+
+// ---------------------------------------------------------------------------
+// Forward transforms.  grid (ceil(nb / kCols), C, B): workgroup = kCols
+// consecutive blocks of row (b, c), four waves taking one block each in turn.
+// Writes X[slot][c][b nb + n] (complex, NP columns per row).
+__global__ __launch_bounds__(kThreads) void fft_fwd_kernel(const float* __restrict__ x,
+                                                           float2* __restrict__ xf, int C, int T,
+                                                           int L, int P, int nb, int NP) {
+    __shared__ float2 tw[kN];
+    __shared__ float2 buf[kThreads / 64][kN];
+    __shared__ float2 res[kSlots][kCols + 1];
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int b = blockIdx.z, c = blockIdx.y, n0 = blockIdx.x * kCols;
+    init_twiddles(tw);
+    __syncthreads();
+    const float* xr = x + ((size_t)b * C + c) * (size_t)T;
+    for (int g = wid; g < kCols; g += kThreads / 64) {
+        const int n = n0 + g;
+        if (n >= nb) break;  // wave-uniform; no workgroup barrier until after the loop
+        float2 v[4];
+        const int u0 = n * L - P + lane;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = u0 + 64 * r;
+            v[r] = make_float2((t >= 0 && t < T) ? xr[t] : 0.f, 0.f);
+        }
+        fft256(v, lane, buf[wid], tw);
+        // lane j: bins j, j + 64, j + 128, j + 192; keep 0..128
+        if (lane == 0) {
+            res[0][g] = make_float2(v[0].x, v[2].x);  // bin 0 and bin N/2 (both real)
+            res[64][g] = v[1];
+        } else {
+            res[lane][g] = v[0];
+            res[lane + 64][g] = v[1];
+        }
+    }
+    __syncthreads();
+    const int ncol = min(kCols, nb - n0);
+    float2* dst = xf + (size_t)c * NP + (size_t)b * nb + n0;
+    const size_t plane = (size_t)C * NP;
+    for (int i = threadIdx.x; i < kSlots * kCols; i += kThreads) {
+        const int f = i / kCols, g = i - f * kCols;
+        if (g < ncol) dst[f * plane + g] = res[f][g];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Inverse transforms and the epilogue.  grid (ceil(nb / kCols), Cout, B).
+// y = IDFT(Y) = conj(DFT(conj(Y))) / N over the Hermitian spectrum; for a
+// real result only the real part is formed.
+__global__ __launch_bounds__(kThreads) void fft_inv_kernel(const float2* __restrict__ yf,
+                                                           float* y, int Cout, int T, int L, int nb,
+                                                           int NP, const float* __restrict__ bias,
+                                                           const float* residual, float out_scale,
+                                                           int accumulate) {
+    __shared__ float2 tw[kN];
+    __shared__ float2 buf[kThreads / 64][kN];
+    __shared__ float2 res[kSlots][kCols + 1];
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int b = blockIdx.z, o = blockIdx.y, n0 = blockIdx.x * kCols;
+    init_twiddles(tw);
+    const int ncol = min(kCols, nb - n0);
+    const float2* src = yf + (size_t)o * NP + (size_t)b * nb + n0;
+    const size_t plane = (size_t)Cout * NP;
+    for (int i = threadIdx.x; i < kSlots * kCols; i += kThreads) {
+        const int f = i / kCols, g = i - f * kCols;
+        res[f][g] = (g < ncol) ? src[f * plane + g] : make_float2(0.f, 0.f);
+    }
+    __syncthreads();
+    const float bo = bias ? bias[o] : 0.f;
+    const size_t row = ((size_t)b * Cout + o) * (size_t)T;
+    constexpr float inv_n = 1.0f / (float)kN;  // exact (power of two)
+    for (int g = wid; g < kCols; g += kThreads / 64) {
+        const int n = n0 + g;
+        if (n >= nb) break;
+        // Z = conj(Y) on bins 0..N/2, Z_k = Y_{N-k} above
+        const float2 s0 = res[0][g];
+        float2 v[4];
+        if (lane == 0) {
+            v[0] = make_float2(s0.x, 0.f);
+            v[2] = make_float2(s0.y, 0.f);
+        } else {
+            const float2 a = res[lane][g];
+            v[0] = make_float2(a.x, -a.y);
+            v[2] = res[128 - lane][g];
+        }
+        const float2 a1 = res[lane + 64][g];
+        v[1] = make_float2(a1.x, -a1.y);
+        v[3] = res[64 - lane][g];
+        fft256(v, lane, buf[wid], tw);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int u = lane + 64 * q;
+            const int t = n * L + u;
+            if (u < L && t < T) {
+                const size_t idx = row + t;
+                float val = fmaf(v[q].x, inv_n, bo);
+                if (residual) val += residual[idx];
+                val *= out_scale;
+                if (accumulate) val += y[idx];
+                y[idx] = val;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Y[slot] = W[slot] X[slot]: per slot a complex [Cout x Cin] x [Cin x NP]
+// product on the matrix cores.  Workgroup: one slot, 64 output rows (16 per
+// wave), NT = 16 NJ columns.  A operands (W) come pre-packed in MFMA
+// fragment order, wp[slot][o/16][c/16][re,im][lane][4] (4 consecutive
+// k-steps per lane per 16-byte load), read straight from memory one
+// 16-channel chunk ahead; B operands (X) are staged in LDS, 16 channels per
+// chunk, double-buffered.  Slot 0 holds two real bins (re: bin 0, im: bin
+// N/2), multiplied separately.  The blockIdx -> tile map keeps each XCD on a
+// contiguous range of slots, so a slot's X is fetched into one L2.
+template <int NJ>
+__global__ __launch_bounds__(kThreads) void fft_gemm_kernel(const float* __restrict__ wp,
+                                                            const float2* __restrict__ xf,
+                                                            float2* __restrict__ yf, int Cin,
+                                                            int Cout, int NP, int ntiles) {
+    constexpr int NT = 16 * NJ;
+    constexpr int KC = 16;
+    constexpr int RS = NT + 2;                 // LDS row stride (float2)
+    constexpr int kF4 = KC * NT / 2;           // float4 per staged chunk
+    constexpr int kPer = (kF4 + kThreads - 1) / kThreads;
+    __shared__ __align__(16) float2 bs[2][KC][RS];
+
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    // XCD-contiguous tile order: workgroups are dealt to the 8 XCDs round robin
+    const int mt = Cout / 64;
+    const int G = ntiles * mt * kSlots;
+    const int id = blockIdx.x;
+    const int lid = (id & 7) * (G >> 3) + (id >> 3);
+    const int nt = lid % ntiles;
+    const int om = (lid / ntiles) % mt;
+    const int f = lid / (ntiles * mt);
+    const int ot = om * 4 + wid;
+    const int n0 = nt * NT;
+    const int S4 = Cin / 16;
+
+    const f32x4* ap = reinterpret_cast<const f32x4*>(wp) +
+                      ((size_t)(f * (Cout / 16) + ot) * S4) * 128 + lane;
+    const float2* xb = xf + (size_t)f * Cin * NP + n0;
+
+    f32x4 stg[kPer];
+    auto load_chunk = [&](int s4) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int q = threadIdx.x + kThreads * i;
+            if (q < kF4) {
+                const int kk = q / (NT / 2), c2 = q - kk * (NT / 2);
+                stg[i] = *reinterpret_cast<const f32x4*>(xb + (size_t)(16 * s4 + kk) * NP + 2 * c2);
+            }
+        }
+    };
+    auto store_chunk = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int q = threadIdx.x + kThreads * i;
+            if (q < kF4) {
+                const int kk = q / (NT / 2), c2 = q - kk * (NT / 2);
+                *reinterpret_cast<f32x4*>(&bs[buf][kk][2 * c2]) = stg[i];
+            }
+        }
+    };
+
+    f32x4 accR[NJ], accI[NJ];
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt) {
+        accR[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        accI[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    f32x4 ar = ap[0], ai = ap[64];
+    load_chunk(0);
+    store_chunk(0);
+    __syncthreads();
+    const bool dc = (f == 0);
+    const int brow = lane >> 4, bcol = lane & 15;
+    for (int s4 = 0; s4 < S4; ++s4) {
+        const int cb = s4 & 1;
+        f32x4 nar = ar, nai = ai;
+        if (s4 + 1 < S4) {
+            load_chunk(s4 + 1);
+            nar = ap[(size_t)(s4 + 1) * 128];
+            nai = ap[(size_t)(s4 + 1) * 128 + 64];
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const float a_r = ar[ks], a_i = ai[ks], a_n = -ai[ks];
+            float2 bv[NJ];
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt) bv[jt] = bs[cb][4 * ks + brow][16 * jt + bcol];
+            if (dc) {
+#pragma unroll
+                for (int jt = 0; jt < NJ; ++jt)
+                    accR[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_r, bv[jt].x, accR[jt], 0, 0, 0);
+#pragma unroll
+                for (int jt = 0; jt < NJ; ++jt)
+                    accI[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_i, bv[jt].y, accI[jt], 0, 0, 0);
+            } else {
+#pragma unroll
+                for (int jt = 0; jt < NJ; ++jt)
+                    accR[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_r, bv[jt].x, accR[jt], 0, 0, 0);
+#pragma unroll
+                for (int jt = 0; jt < NJ; ++jt)
+                    accI[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_i, bv[jt].x, accI[jt], 0, 0, 0);
+#pragma unroll
+                for (int jt = 0; jt < NJ; ++jt)
+                    accR[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_n, bv[jt].y, accR[jt], 0, 0, 0);
+#pragma unroll
+                for (int jt = 0; jt < NJ; ++jt)
+                    accI[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_r, bv[jt].y, accI[jt], 0, 0, 0);
+            }
+        }
+        if (s4 + 1 < S4) {
+            store_chunk(cb ^ 1);
+            ar = nar;
+            ai = nai;
+        }
+        __syncthreads();
+    }
+    // D layout: lane l holds rows 4 (l / 16) + i, column l % 16 of each tile
+    float2* yo = yf + ((size_t)f * Cout + 16 * ot + 4 * brow) * NP + n0 + bcol;
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            yo[(size_t)i * NP + 16 * jt] = make_float2(accR[jt][i], accI[jt][i]);
+}
+
+// ---------------------------------------------------------------------------
+// Packed frequency-domain weights: for slot f >= 1
+//   W = sum_j w[o,c,j] e^{+2 pi i f j d / N},
+// slot 0 = (sum_j w_j, sum_j (-1)^{j d} w_j) (bins 0 and N/2), summed in
+// double and rounded once, stored in fft_gemm_kernel's fragment order.
+__global__ __launch_bounds__(256) void fft_pack_kernel(const float* __restrict__ w,
+                                                       float* __restrict__ wp, int Cin, int Cout,
+                                                       int K, int d) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long total = (long long)kSlots * Cout * Cin;
+    if (i >= total) return;
+    const int c = (int)(i % Cin);
+    const int o = (int)((i / Cin) % Cout);
+    const int f = (int)(i / ((long long)Cin * Cout));
+    const float* wr = w + ((size_t)o * Cin + c) * K;
+    double re = 0.0, im = 0.0;
+    for (int j = 0; j < K; ++j) {
+        const double wj = (double)wr[j];
+        if (f == 0) {
+            re += wj;
+            im += ((j * d) & 1) ? -wj : wj;
+        } else {
+            const int m = (int)(((long long)f * j * d) % kN);
+            double s, cs;
+            sincospi(2.0 * (double)m / (double)kN, &s, &cs);
+            re += wj * cs;
+            im += wj * s;
+        }
+    }
+    const int ot = o >> 4, s4 = c >> 4;
+    const int ln = (o & 15) + 16 * (c & 3), e = (c & 15) >> 2;
+    const size_t base = ((((size_t)f * (Cout / 16) + ot) * (Cin / 16) + s4) * 2) * 256 + ln * 4 + e;
+    wp[base] = (float)re;
+    wp[base + 256] = (float)im;
+}
+
+template <int NJ>
+void gemm_launch(const float* wp, const float2* xf, float2* yf, int Cin, int Cout, int NP,
+                 int ntiles, hipStream_t s) {
+    const int G = ntiles * (Cout / 64) * kSlots;
+    hipLaunchKernelGGL(fft_gemm_kernel<NJ>, dim3((unsigned)G), dim3(kThreads), 0, s, wp, xf, yf,
+                       Cin, Cout, NP, ntiles);
+}
+
+}  // namespace
+
+size_t fft_conv_weight_floats(int Cin, int Cout) {
+    return (size_t)kSlots * (size_t)Cout * (size_t)Cin * 2;
+}
+
+hipError_t launch_fft_pack(const float* w, float* wp, int Cin, int Cout, int K, int dilation,
+                           hipStream_t s) {
+    if (!plan::fft_supported(Cin, Cout, K, dilation)) return hipErrorInvalidValue;
+    const long long total = (long long)kSlots * Cout * Cin;
+    hipLaunchKernelGGL(fft_pack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, w,
+                       wp, Cin, Cout, K, dilation);
+    return hipGetLastError();
+}
+
+hipError_t launch_conv1d_fft(const float* x, float* y, const float* wp, int B, int Cin, int Cout,
+                             int T, int K, int dilation, const ConvEpilogue& ep, float* xspec,
+                             float* yspec, hipStream_t s) {
+    if (!plan::fft_supported(Cin, Cout, K, dilation) || ep.snake_alpha || ep.in_alpha)
+        return hipErrorInvalidValue;
+    const plan::FftShape sh = plan::fft_shape(B, T, K, dilation);
+    if (sh.ntiles < 1 || sh.NJ < 1 || sh.NJ > 8) return hipErrorInvalidValue;
+    const int P = (K - 1) * dilation / 2;
+    float2* xf = reinterpret_cast<float2*>(xspec);
+    float2* yf = reinterpret_cast<float2*>(yspec);
+    const dim3 tg((unsigned)((sh.nb + kCols - 1) / kCols), 1, (unsigned)B);
+    const double blocks = (double)sh.NB;
+
+    prof_pre(s);
+    hipLaunchKernelGGL(fft_fwd_kernel, dim3(tg.x, (unsigned)Cin, tg.z), dim3(kThreads), 0, s, x,
+                       xf, Cin, T, sh.L, P, sh.nb, sh.NP);
+    hipError_t e = hipGetLastError();
+    // algorithmic: x read once (4 B per sample), the spectrum written once
+    prof_post(s, "fft_fwd_kernel", 0.0, 4.0 * B * Cin * (double)T + 8.0 * kSlots * Cin * blocks);
+    if (e != hipSuccess) return e;
+
+    prof_pre(s);
+    switch (sh.NJ) {
+        case 1: gemm_launch<1>(wp, xf, yf, Cin, Cout, sh.NP, sh.ntiles, s); break;
+        case 2: gemm_launch<2>(wp, xf, yf, Cin, Cout, sh.NP, sh.ntiles, s); break;
+        case 3: gemm_launch<3>(wp, xf, yf, Cin, Cout, sh.NP, sh.ntiles, s); break;
+        case 4: gemm_launch<4>(wp, xf, yf, Cin, Cout, sh.NP, sh.ntiles, s); break;
+        case 5: gemm_launch<5>(wp, xf, yf, Cin, Cout, sh.NP, sh.ntiles, s); break;
+        case 6: gemm_launch<6>(wp, xf, yf, Cin, Cout, sh.NP, sh.ntiles, s); break;
+        case 7: gemm_launch<7>(wp, xf, yf, Cin, Cout, sh.NP, sh.ntiles, s); break;
+        default: gemm_launch<8>(wp, xf, yf, Cin, Cout, sh.NP, sh.ntiles, s); break;
+    }
+    e = hipGetLastError();
+    {
+        // algorithmic: 127 complex slots (4 real products each) + slot 0 (2),
+        // one multiply-add = 2 flops, over the real columns
+        static const char* names[8] = {"fft_gemm_kernel<1>", "fft_gemm_kernel<2>",
+                                       "fft_gemm_kernel<3>", "fft_gemm_kernel<4>",
+                                       "fft_gemm_kernel<5>", "fft_gemm_kernel<6>",
+                                       "fft_gemm_kernel<7>", "fft_gemm_kernel<8>"};
+        const double macs = (127.0 * 4.0 + 2.0) * Cout * (double)Cin * blocks;
+        const double bytes = 8.0 * kSlots * (double)Cout * Cin +
+                             8.0 * kSlots * (double)(Cin + Cout) * blocks;
+        prof_post(s, names[sh.NJ - 1], 2.0 * macs, bytes);
+    }
+    if (e != hipSuccess) return e;
+
+    prof_pre(s);
+    hipLaunchKernelGGL(fft_inv_kernel, dim3(tg.x, (unsigned)Cout, tg.z), dim3(kThreads), 0, s, yf,
+                       y, Cout, T, sh.L, sh.nb, sh.NP, ep.bias, ep.residual, ep.out_scale,
+                       ep.accumulate);
+    e = hipGetLastError();
+    const double n = (double)B * Cout * T;
+    prof_post(s, "fft_inv_kernel", 0.0,
+              8.0 * kSlots * Cout * blocks + 4.0 * n * (1 + (ep.residual != nullptr) +
+                                                        (ep.accumulate != 0)));
+    return e;
+}
+
+}  // namespace avae

@@ -38,20 +38,78 @@ inline int stage_lengths(const avae_config& c, int frames, long long* T) {
     return 0;
 }
 
+// Overlap-save Conv1d (fftconv.hip): 256-point transforms, 128 frequency
+// slots.  A row of T outputs is cut into nb blocks of L = 256 - (K-1) d; the
+// B nb columns are split into ntiles tiles of 16 NJ columns (NJ <= 8), NP
+// columns in all.
+constexpr int kFftN = 256;
+constexpr int kFftSlots = 128;
+
+struct FftShape {
+    int L = 0, nb = 0, NB = 0, NJ = 0, ntiles = 0, NP = 0;
+};
+
+inline bool fft_supported(int Cin, int Cout, int K, int d) {
+    return Cin >= 16 && Cin % 16 == 0 && Cout >= 64 && Cout % 64 == 0 && K >= 1 && K % 2 == 1 &&
+           d >= 1 && (long long)(K - 1) * d <= kFftN / 2;
+}
+
+// B, T >= 1 and a supported (K, d); ntiles = 0 if B nb overflows an int.
+inline FftShape fft_shape(int B, int T, int K, int d) {
+    FftShape s;
+    s.L = kFftN - (K - 1) * d;
+    s.nb = (int)(((long long)T + s.L - 1) / s.L);
+    const long long nbt = (long long)B * s.nb;
+    if (nbt > 0x3fffffffLL) return s;
+    s.NB = (int)nbt;
+    s.ntiles = (s.NB + 127) / 128;
+    const int per = (s.NB + s.ntiles - 1) / s.ntiles;
+    s.NJ = (per + 15) / 16;
+    s.NP = s.ntiles * 16 * s.NJ;
+    return s;
+}
+
+// Bytes of one spectrum (128 slots x C rows x NP complex float columns),
+// rounded up to 256; 0 on overflow.
+inline size_t fft_spectrum_bytes(int B, int C, int T, int K, int d) {
+    const FftShape s = fft_shape(B, T, K, d);
+    if (s.ntiles == 0) return 0;
+    return tensor_bytes((long long)kFftSlots * 2, C, s.NP);
+}
+
+// The decoders' AMP convolutions that run in the frequency domain: wide
+// channel counts (the transforms' cost per sample is then small against the
+// channel mixing) and 7 or more taps (where the transform form needs fewer
+// multiply-adds than the direct one: ~2 per output and channel pair, against K).
+inline bool fft_amp_conv(int C, int K, int d) {
+    return C >= 128 && K >= 7 && fft_supported(C, C, K, d);
+}
+
 // Bytes of one decode workspace slot: the largest activation of the decode
-// (B passes), rounded up to 256 bytes; 0 if it does not fit a size_t.
+// (B passes) and the largest spectrum of a frequency-domain AMP convolution,
+// rounded up to 256 bytes; 0 if it does not fit a size_t.
 inline size_t decode_slot_bytes(const avae_config& c, int B, const long long* T) {
     size_t m = 0;
     bool over = false;
-    auto upd = [&](long long ch, long long t) {
-        const size_t b = tensor_bytes(B, ch, t);
+    auto keep = [&](size_t b) {
         if (b == 0) over = true;
         if (b > m) m = b;
     };
+    auto upd = [&](long long ch, long long t) { keep(tensor_bytes(B, ch, t)); };
     upd(c.c_in, T[0]);
     if (c.dec_in_ch) upd(c.dec_in_ch, T[0]);
     upd(c.ch[0], T[0]);
-    for (int i = 0; i < c.n_stages; ++i) upd(c.ch[i + 1], T[i + 1]);
+    for (int i = 0; i < c.n_stages; ++i) {
+        const int co = c.ch[i + 1];
+        upd(co, T[i + 1]);
+        for (int j = 0; j < c.n_kernels; ++j) {
+            const int K = c.rb_k[j];
+            if (fft_amp_conv(co, K, 1)) keep(fft_spectrum_bytes(B, co, (int)T[i + 1], K, 1));
+            for (int q = 0; q < c.n_dil; ++q)
+                if (fft_amp_conv(co, K, c.rb_d[j][q]))
+                    keep(fft_spectrum_bytes(B, co, (int)T[i + 1], K, c.rb_d[j][q]));
+        }
+    }
     return over ? 0 : m;
 }
 

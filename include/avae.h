@@ -102,6 +102,38 @@ int avae_conv1d(const float* x, float* y, int B, int Cin, int Cout, int T,
                 const float* residual, void* stream);
 
 /*
+ * The same "same"-padded Conv1d (pad = (K-1)*dilation/2, Tout = T) through
+ * the convolution theorem ([H3] Conv1d::apply; overlap-save framing):
+ * each row is cut into blocks of L = 256 - (K-1)*dilation outputs, every
+ * block's 256-sample input window is transformed, the channels are mixed
+ * by one complex matrix product per frequency on the FP32 matrix cores,
+ * and the L valid samples of each block's inverse transform are kept.
+ * Same result as avae_conv1d up to float32 rounding (a few 1e-6 of the
+ * output's RMS).  Takes Cin % 16 == 0, Cout % 64 == 0, odd K and
+ * (K-1)*dilation <= 128.
+ *
+ * avae_conv1d_fft_weight_floats: floats of the packed weights for (Cin, Cout).
+ * avae_conv1d_fft_pack: w [Cout, Cin, K] (device) -> wp (device, that many
+ *   floats, caller-owned): the frequency responses of every (o, i) filter at
+ *   the given dilation, summed in double and rounded to float32, in the
+ *   matrix kernel's operand order.  Pack once per weight tensor and dilation.
+ * avae_conv1d_fft_workspace_bytes: device workspace avae_conv1d_fft needs
+ *   (the two spectra); 0 if the shape is not supported.
+ * avae_conv1d_fft: x [B, Cin, T], y [B, Cout, T] (must not overlap x or the
+ *   workspace), wp from avae_conv1d_fft_pack with the same K and dilation,
+ *   bias [Cout] or NULL, residual [B, Cout, T] or NULL (may be y).
+ * Errors: EINVAL (null pointers, sizes < 1, x == y); ESHAPE (unsupported
+ *   Cin, Cout, K or dilation); EWORKSPACE (workspace too small).
+ */
+size_t avae_conv1d_fft_weight_floats(int Cin, int Cout);
+int avae_conv1d_fft_pack(const float* w, float* wp, int Cin, int Cout, int K, int dilation,
+                         void* stream);
+size_t avae_conv1d_fft_workspace_bytes(int B, int Cin, int Cout, int T, int K, int dilation);
+int avae_conv1d_fft(const float* x, float* y, int B, int Cin, int Cout, int T, const float* wp,
+                    const float* bias, int K, int dilation, const float* residual,
+                    void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * ConvTranspose1d ([H3] ConvT1d::apply/load; [LTX] ConvT1d):
  *   y[b, o, t*stride + j - pad] += x[b,i,t] * w[i,o,j], plus bias[o];
  *   Tout = (Tin - 1)*stride + K - 2*pad.

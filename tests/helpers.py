@@ -125,3 +125,19 @@ def dav_reach_frames(spec) -> int:
         reach += sum((spec.unit_k - 1) * d / 2.0 for d in spec.unit_dil) / rate
     reach += (spec.k_post - 1) / 2.0 / rate
     return int(math.ceil(reach)) + 1
+
+
+def runs_fft_convs(spec) -> bool:
+    """Whether the library runs some of this decoder's AMP convolutions in the
+    frequency domain (overlap-save, 256-point transforms): widths of at least
+    128 channels, a multiple of 64, with 7 or more taps and (K-1) d <= 128.
+    The block framing then follows the sequence start, so decodes of crops
+    (streaming tiles) round differently from the whole sequence there."""
+    chans = [spec.c0 // (2 ** (i + 1)) for i in range(len(spec.rates))]
+    for c in chans:
+        if c < 128 or c % 64:
+            continue
+        for k, dil in zip(spec.rb_k, spec.rb_d):
+            if k >= 7 and any((k - 1) * d <= 128 for d in tuple(dil) + (1,)):
+                return True
+    return False

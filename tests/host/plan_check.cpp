@@ -100,10 +100,39 @@ int main() {
     // lengths past 2^31 are rejected, not wrapped
     CHECK(stage_lengths(h3, 3000000, T) != 0, "h3 overflow accepted");
     CHECK(stage_lengths(h3, 0, T) != 0, "zero frames accepted");
-    // workspace slots: workload 4 = 30.72 MB ([2, 12, 320000] and [2, 768, 2000] ...)
+    // workspace slots, workload 4: the largest activation is 30.72 MB ([2, 24,
+    // 160000] and its equals), the largest spectrum 44.04 MB: the 384-channel
+    // stage at 11 taps, dilation 5 (blocks of 206 outputs: 49 per row, 98
+    // columns padded to 112) and the 192-channel stage (98 per row, 196
+    // columns in two tiles of 112), 128 slots of complex floats.
     CHECK(stage_lengths(h3, 400, T) == 0, "h3 400");
-    CHECK(decode_slot_bytes(h3, 2, T) == round_up(2ULL * 24 * 160000 * 4, 256),
+    CHECK(decode_slot_bytes(h3, 2, T) == 128ULL * 2 * 384 * 112 * 4,
           "h3 slot %zu", decode_slot_bytes(h3, 2, T));
+    {
+        const FftShape a = fft_shape(2, 10000, 11, 5), b = fft_shape(2, 20000, 11, 5);
+        CHECK(a.L == 206 && a.nb == 49 && a.NB == 98 && a.ntiles == 1 && a.NJ == 7 && a.NP == 112,
+              "fft shape 384");
+        CHECK(b.nb == 98 && b.NB == 196 && b.ntiles == 2 && b.NJ == 7 && b.NP == 224,
+              "fft shape 192");
+        CHECK(fft_amp_conv(384, 11, 5) && fft_amp_conv(192, 7, 1) && !fft_amp_conv(96, 11, 5) &&
+                  !fft_amp_conv(384, 3, 1) && !fft_amp_conv(336, 7, 1),
+              "fft selection");
+    }
+    // the column plan over many sizes: every column covered, at most 8 MFMA
+    // tiles of 16 per workgroup, fewer than 16 padding columns per tile
+    for (int B : {1, 2, 3, 8})
+        for (int T = 1; T <= 70000; T = T * 3 + 1)
+            for (int K : {3, 7, 11})
+                for (int d : {1, 3, 5, 12}) {
+                    if (!fft_supported(16, 64, K, d)) continue;
+                    const FftShape f = fft_shape(B, T, K, d);
+                    CHECK(f.ntiles >= 1 && f.NJ >= 1 && f.NJ <= 8 && f.NP >= f.NB &&
+                              (long long)f.nb * f.L >= T && (long long)(f.nb - 1) * f.L < T &&
+                              f.NP - f.NB < 16 * f.ntiles,
+                          "fft shape B=%d T=%d K=%d d=%d", B, T, K, d);
+                    CHECK(fft_spectrum_bytes(B, 64, T, K, d) == 128ULL * 2 * 64 * f.NP * 4,
+                          "fft spectrum bytes");
+                }
     // sizes that would wrap a 64-bit product give 0
     CHECK(tensor_bytes(0x7fffffff, 0x7fffffff, 0x7fffffff) == 0, "tensor_bytes wrap");
     CHECK(tensor_bytes(1, 1, 1) == 256, "tensor_bytes small");

@@ -1,0 +1,93 @@
+"""Parity of the frequency-domain Conv1d (avae_conv1d_fft: 256-point
+overlap-save transforms, complex channel mixing on the matrix cores) with the
+float64 oracle's direct convolution: max|err| / RMS(ref) <= 1e-5 per call."""
+import numpy as np
+import pytest
+
+from bigvgan_waveform_decoder_amd import avae
+from bigvgan_waveform_decoder_amd import workloads as W
+from oracle import avae_oracle as O
+from tests.gpu_util import announce, cuda, host
+from tests.helpers import rel_err
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+
+
+def _inputs(tag, B, Cin, Cout, T, K):
+    x = W.normal(0, f"fft/{tag}/x", [B, Cin, T])
+    w = W.normal(0, f"fft/{tag}/w", [Cout, Cin, K], 0.0, 2.0 / (Cin * K))
+    b = W.normal(0, f"fft/{tag}/b", [Cout], 0.0, 0.01)
+    return x, w, b
+
+
+def _oracle_window(x, w, b, d, a, n, residual=None):
+    """The oracle's 'same' convolution on outputs [a, a + n) only."""
+    K = w.shape[2]
+    P = (K - 1) * d // 2
+    xp = np.pad(x, ((0, 0), (0, 0), (P, P)))
+    ref = O.conv1d(xp[:, :, a:a + n + 2 * P], w, b, dilation=d, pad=0)
+    if residual is not None:
+        ref = ref + residual[:, :, a:a + n]
+    return ref
+
+
+FFT_CASES = [
+    # B, Cin, Cout, T, K, d, residual
+    (1, 16, 64, 300, 3, 1, False),       # one column tile of 16, ragged last block
+    (2, 64, 64, 1000, 7, 3, True),
+    (1, 32, 128, 1, 11, 5, False),       # T = 1: one block, every tap but the centre outside
+    (1, 16, 64, 206, 11, 5, False),      # T = L exactly (one full block)
+    (2, 128, 192, 2000, 11, 5, False),   # 20 columns (two 16-column tiles)
+    (1, 48, 64, 5000, 5, 32, True),      # span (K-1) d = 128, the largest taken
+    (2, 384, 384, 3001, 11, 1, True),
+    (2, 256, 128, 20000, 7, 5, False),   # 178 columns: two column tiles
+    (1, 64, 64, 31000, 3, 3, False),     # 122 columns: one tile of 8 x 16
+]
+
+
+@pytest.mark.parametrize("B,Cin,Cout,T,K,d,res", FFT_CASES)
+def test_conv1d_fft_matches_oracle(B, Cin, Cout, T, K, d, res):
+    announce(f"conv1d_fft B={B} Cin={Cin} Cout={Cout} T={T} K={K} d={d} res={res}")
+    x, w, b = _inputs(f"{B}-{Cin}-{Cout}-{T}-{K}-{d}", B, Cin, Cout, T, K)
+    r = W.normal(0, f"fft/{Cin}-{Cout}-{T}/res", [B, Cout, T]) if res else None
+    wp = avae.conv1d_fft_pack(cuda(w), dilation=d)
+    y = host(avae.conv1d_fft(cuda(x), wp, Cout, K, bias=cuda(b), dilation=d,
+                             residual=cuda(r) if res else None))
+    ref = O.conv1d(x, w, b, dilation=d, pad=(K - 1) * d // 2, residual=r)
+    err = rel_err(y, ref)
+    print(f"max|err|/rms = {err:.3e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("C,T,K,d", [(768, 2000, 11, 5), (384, 10000, 11, 5),
+                                     (384, 10000, 7, 3), (192, 20000, 11, 1)])
+def test_conv1d_fft_decoder_widths(C, T, K, d):
+    """The H3 decoder's wide stages at full size, B = 2, in-place residual:
+    oracle windows at both row ends and across block seams."""
+    announce(f"conv1d_fft decoder width C={C} T={T} K={K} d={d}")
+    B = 2
+    x, w, b = _inputs(f"dec-{C}-{T}-{K}-{d}", B, C, C, T, K)
+    cur = W.normal(0, f"fft/dec-{C}-{T}/cur", [B, C, T])
+    wp = avae.conv1d_fft_pack(cuda(w), dilation=d)
+    out = cuda(cur)
+    avae.conv1d_fft(cuda(x), wp, C, K, bias=cuda(b), dilation=d, residual=out, out=out)
+    y = host(out)
+    L = 256 - (K - 1) * d
+    for a in (0, 3 * L - 40, T // 2, T - 300):
+        ref = _oracle_window(x, w, b, d, a, 300, residual=cur)
+        err = rel_err(y[:, :, a:a + 300], ref)
+        print(f"window {a}: max|err|/rms = {err:.3e}")
+        assert err <= TOL, a
+
+
+def test_conv1d_fft_same_as_direct_kernel_shape_checks():
+    """Shapes the frequency-domain kernel does not take are refused."""
+    announce("conv1d_fft shape checks")
+    assert avae.conv1d_fft_workspace_bytes(1, 12, 64, 100, 3, 1) == 0   # Cin % 16
+    assert avae.conv1d_fft_workspace_bytes(1, 16, 48, 100, 3, 1) == 0   # Cout % 64
+    assert avae.conv1d_fft_workspace_bytes(1, 16, 64, 100, 4, 1) == 0   # even K
+    assert avae.conv1d_fft_workspace_bytes(1, 16, 64, 100, 11, 13) == 0  # span 130 > 128
+    w = cuda(W.normal(0, "fft/bad/w", [48, 16, 3]))
+    with pytest.raises(avae.AvaeError):
+        avae.conv1d_fft_pack(w, dilation=1)

@@ -8,9 +8,13 @@ from bigvgan_waveform_decoder_amd import avae
 from bigvgan_waveform_decoder_amd import workloads as W
 from oracle import avae_oracle as O
 from tests.gpu_util import announce, cuda, cuda_dict, host
-from tests.helpers import decoder_params, decoder_reach_frames, rel_err
+from tests.helpers import decoder_params, decoder_reach_frames, rel_err, runs_fft_convs
 
 pytestmark = pytest.mark.gpu
+# Tiled vs whole where frequency-domain convolutions run (the 256-point block
+# framing follows the crop): measured on MI355X 1.79e-4 (h3-c256, 90 frames in
+# 17-frame tiles); the bar is twice that, rounded up.
+TILE_FFT_BAR = 4e-4
 
 
 @pytest.mark.parametrize("name,spec,frames,tile", [
@@ -30,17 +34,24 @@ def test_streaming_equals_whole_decode(name, spec, frames, tile):
     whole = host(dec.decode(zd))
     tiled = host(dec.decode_streaming(zd, tile))
     assert tiled.shape == whole.shape == (2, frames * spec.hop)
-    # At these widths every tile's crop selects the same kernel tilings as the
-    # whole sequence, so the kept samples are bit-identical (measured on
-    # MI355X for all three cases).
-    np.testing.assert_array_equal(tiled, whole)
-    # and the oracle, on a window in the middle of a tile boundary
+    e = rel_err(tiled, whole)
+    print(f"tiled vs whole: {e:.3e}", flush=True)
+    if not runs_fft_convs(spec):
+        # every tile's crop selects the same kernel tilings as the whole
+        # sequence, so the kept samples are bit-identical (measured on MI355X)
+        np.testing.assert_array_equal(tiled, whole)
+    else:
+        # the frequency-domain stages frame their 256-point blocks from the
+        # crop's start, so the rounding differs from the whole sequence's
+        assert e <= TILE_FFT_BAR
+    # both against the oracle, on a window in the middle of a tile boundary
     R = decoder_reach_frames(spec)
     a = tile - 2
     lo, hi = max(a - R, 0), min(a + 4 + R, frames)
     ref = O.decode(z[:1, :, lo:hi], decoder_params(spec, t))[0]
     off = (a - lo) * spec.hop
-    assert rel_err(tiled[0, a * spec.hop:(a + 4) * spec.hop], ref[off:off + 4 * spec.hop]) <= 1e-3
+    for got in (tiled, whole):
+        assert rel_err(got[0, a * spec.hop:(a + 4) * spec.hop], ref[off:off + 4 * spec.hop]) <= 1e-3
 
 
 def test_streaming_halo_matters():
@@ -69,13 +80,14 @@ def test_streaming_workload4_full_size():
     tiled = host(dec.decode_streaming(zd, 100))
     assert tiled.shape == (2, 370 * spec.hop)
     # At full width the crops (100 + 35 or 100 + 70 frames) and the whole
-    # sequence (370 frames) select different tilings in some stages, so the
-    # float32 summation orders differ by about one rounding there and the
-    # later stages' gain carries it forward: measured on MI355X 1.36e-4
-    # (1.27e-4 on an earlier kernel set); the bar is twice that, rounded up.
+    # sequence (370 frames) round differently: the frequency-domain stages
+    # frame their 256-point blocks from the crop's start, and some direct
+    # stages select other tilings.  The later stages' gain carries it forward:
+    # measured on MI355X 4.47e-4 (1.36e-4 with direct convolutions only); the
+    # bar is twice that, rounded up.
     e = rel_err(tiled, whole)
     print(f"tiled vs whole at full width: {e:.3e}", flush=True)
-    assert e <= 3e-4
+    assert e <= 1e-3
 
 
 def test_streaming_rejects_bad_tiles():
