@@ -117,16 +117,26 @@ __global__ __launch_bounds__(kThreads) void fft_fwd_kernel(const float* __restri
     init_twiddles(tw);
     __syncthreads();
     const float* xr = x + ((size_t)b * C + c) * (size_t)T;
-    for (int g = wid; g < kCols; g += kThreads / 64) {
-        const int n = n0 + g;
-        if (n >= nb) break;  // wave-uniform; no workgroup barrier until after the loop
-        float2 v[4];
-        const int u0 = n * L - P + lane;
+    // every input of this wave's kCols / 4 transforms is loaded up front (the
+    // loads of one transform alone leave HBM latency exposed)
+    constexpr int kPerWave = kCols / (kThreads / 64);
+    float xin[kPerWave][4];
+#pragma unroll
+    for (int it = 0; it < kPerWave; ++it) {
+        const int u0 = (n0 + wid + (kThreads / 64) * it) * L - P + lane;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = u0 + 64 * r;
-            v[r] = make_float2((t >= 0 && t < T) ? xr[t] : 0.f, 0.f);
+            xin[it][r] = (t >= 0 && t < T) ? xr[t] : 0.f;
         }
+    }
+#pragma unroll
+    for (int it = 0; it < kPerWave; ++it) {
+        const int g = wid + (kThreads / 64) * it;
+        if (n0 + g >= nb) break;  // wave-uniform; no workgroup barrier until after the loop
+        float2 v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = make_float2(xin[it][r], 0.f);
         fft256(v, lane, buf[wid], tw);
         // lane j: bins j, j + 64, j + 128, j + 192; keep 0..128
         if (lane == 0) {
@@ -165,17 +175,47 @@ __global__ __launch_bounds__(kThreads) void fft_inv_kernel(const float2* __restr
     const int ncol = min(kCols, nb - n0);
     const float2* src = yf + (size_t)o * NP + (size_t)b * nb + n0;
     const size_t plane = (size_t)Cout * NP;
-    for (int i = threadIdx.x; i < kSlots * kCols; i += kThreads) {
-        const int f = i / kCols, g = i - f * kCols;
-        res[f][g] = (g < ncol) ? src[f * plane + g] : make_float2(0.f, 0.f);
+    {
+        // all loads first, then the LDS writes
+        constexpr int kLd = kSlots * kCols / kThreads;
+        float2 ld[kLd];
+#pragma unroll
+        for (int k = 0; k < kLd; ++k) {
+            const int i = threadIdx.x + kThreads * k;
+            const int f = i / kCols, g = i - f * kCols;
+            ld[k] = (g < ncol) ? src[f * plane + g] : make_float2(0.f, 0.f);
+        }
+#pragma unroll
+        for (int k = 0; k < kLd; ++k) {
+            const int i = threadIdx.x + kThreads * k;
+            res[i / kCols][i % kCols] = ld[k];
+        }
     }
     __syncthreads();
     const float bo = bias ? bias[o] : 0.f;
     const size_t row = ((size_t)b * Cout + o) * (size_t)T;
     constexpr float inv_n = 1.0f / (float)kN;  // exact (power of two)
-    for (int g = wid; g < kCols; g += kThreads / 64) {
+    // the residual and previous-output values of this wave's outputs are read
+    // before any transform (each read otherwise waits out its own latency)
+    constexpr int kPerWave = kCols / (kThreads / 64);
+    float rv[kPerWave][4], ov[kPerWave][4];
+#pragma unroll
+    for (int it = 0; it < kPerWave; ++it) {
+        const int n = n0 + wid + (kThreads / 64) * it;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int u = lane + 64 * q;
+            const int t = n * L + u;
+            const bool ok = n < nb && u < L && t < T;
+            rv[it][q] = (ok && residual) ? residual[row + t] : 0.f;
+            ov[it][q] = (ok && accumulate) ? y[row + t] : 0.f;
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < kPerWave; ++it) {
+        const int g = wid + (kThreads / 64) * it;
         const int n = n0 + g;
-        if (n >= nb) break;
+        if (n >= nb) break;  // wave-uniform
         // Z = conj(Y) on bins 0..N/2, Z_k = Y_{N-k} above
         const float2 s0 = res[0][g];
         float2 v[4];
@@ -195,14 +235,8 @@ __global__ __launch_bounds__(kThreads) void fft_inv_kernel(const float2* __restr
         for (int q = 0; q < 4; ++q) {
             const int u = lane + 64 * q;
             const int t = n * L + u;
-            if (u < L && t < T) {
-                const size_t idx = row + t;
-                float val = fmaf(v[q].x, inv_n, bo);
-                if (residual) val += residual[idx];
-                val *= out_scale;
-                if (accumulate) val += y[idx];
-                y[idx] = val;
-            }
+            if (u < L && t < T)
+                y[row + t] = fmaf(fmaf(v[q].x, inv_n, bo) + rv[it][q], out_scale, ov[it][q]);
         }
     }
 }
@@ -213,21 +247,31 @@ __global__ __launch_bounds__(kThreads) void fft_inv_kernel(const float2* __restr
 // wave), NT = 16 NJ columns.  A operands (W) come pre-packed in MFMA
 // fragment order, wp[slot][o/16][c/16][re,im][lane][4] (4 consecutive
 // k-steps per lane per 16-byte load), read straight from memory one
-// 16-channel chunk ahead; B operands (X) are staged in LDS, 16 channels per
-// chunk, double-buffered.  Slot 0 holds two real bins (re: bin 0, im: bin
-// N/2), multiplied separately.  The blockIdx -> tile map keeps each XCD on a
-// contiguous range of slots, so a slot's X is fetched into one L2.
+// 16-channel chunk ahead.  B operands (X) go to LDS by LDS DMA
+// (global_load_lds_dwordx4: no register round trip), 16 channels per chunk,
+// double-buffered, rows of NT complex back to back; each wave reads its B
+// fragments one k-step ahead of the matrix instructions that use them.
+// Slot 0 holds two real bins (re: bin 0, im: bin N/2): its operands are
+// chosen so that the same four products give W0 X0 and W128 X128.  The
+// blockIdx -> tile map keeps each XCD on a contiguous range of slots, so a
+// slot's X is fetched into one L2.
+__device__ __forceinline__ void wait_vmem_all() {
+    // s_waitcnt vmcnt(0), expcnt and lgkmcnt left at their maxima
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
 template <int NJ>
-__global__ __launch_bounds__(kThreads) void fft_gemm_kernel(const float* __restrict__ wp,
-                                                            const float2* __restrict__ xf,
-                                                            float2* __restrict__ yf, int Cin,
-                                                            int Cout, int NP, int ntiles) {
+__global__ __launch_bounds__(kThreads, 2) void fft_gemm_kernel(const float* __restrict__ wp,
+                                                               const float2* __restrict__ xf,
+                                                               float2* __restrict__ yf, int Cin,
+                                                               int Cout, int NP, int ntiles) {
     constexpr int NT = 16 * NJ;
     constexpr int KC = 16;
-    constexpr int RS = NT + 2;                 // LDS row stride (float2)
-    constexpr int kF4 = KC * NT / 2;           // float4 per staged chunk
-    constexpr int kPer = (kF4 + kThreads - 1) / kThreads;
-    __shared__ __align__(16) float2 bs[2][KC][RS];
+    constexpr int kDma = KC * NT / 128;  // 1 KB wave instructions per chunk (2 NJ)
+    // two buffers as two objects, so that the compiler sees the DMA into one
+    // and the fragment reads from the other as independent
+    __shared__ __align__(16) float2 bsA[KC * NT];
+    __shared__ __align__(16) float2 bsB[KC * NT];
 
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     // XCD-contiguous tile order: workgroups are dealt to the 8 XCDs round robin
@@ -246,25 +290,14 @@ __global__ __launch_bounds__(kThreads) void fft_gemm_kernel(const float* __restr
                       ((size_t)(f * (Cout / 16) + ot) * S4) * 128 + lane;
     const float2* xb = xf + (size_t)f * Cin * NP + n0;
 
-    f32x4 stg[kPer];
-    auto load_chunk = [&](int s4) {
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int q = threadIdx.x + kThreads * i;
-            if (q < kF4) {
-                const int kk = q / (NT / 2), c2 = q - kk * (NT / 2);
-                stg[i] = *reinterpret_cast<const f32x4*>(xb + (size_t)(16 * s4 + kk) * NP + 2 * c2);
-            }
-        }
-    };
-    auto store_chunk = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int q = threadIdx.x + kThreads * i;
-            if (q < kF4) {
-                const int kk = q / (NT / 2), c2 = q - kk * (NT / 2);
-                *reinterpret_cast<f32x4*>(&bs[buf][kk][2 * c2]) = stg[i];
-            }
+    // chunk s4 -> buf: float4 q = 64 i + lane of the chunk image
+    auto issue_chunk = [&](int s4, float2* buf) {
+        for (int i = wid; i < kDma; i += kThreads / 64) {
+            const int q = 64 * i + lane;
+            const int kk = q / (NT / 2), c2 = q - kk * (NT / 2);
+            __builtin_amdgcn_global_load_lds(
+                (const void*)(xb + (size_t)(16 * s4 + kk) * NP + 2 * c2), (void*)(buf + 128 * i),
+                16, 0, 0);
         }
     };
 
@@ -274,54 +307,63 @@ __global__ __launch_bounds__(kThreads) void fft_gemm_kernel(const float* __restr
         accR[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
         accI[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    f32x4 ar = ap[0], ai = ap[64];
-    load_chunk(0);
-    store_chunk(0);
-    __syncthreads();
-    const bool dc = (f == 0);
+    // operand selection: general slots (Wr, Wi, -Wi, Wr), slot 0 (W0, 0, 0, W128)
+    const float sel = (f == 0) ? 0.f : 1.f;
     const int brow = lane >> 4, bcol = lane & 15;
-    for (int s4 = 0; s4 < S4; ++s4) {
-        const int cb = s4 & 1;
+    f32x4 ar, ai;
+    // one chunk: matrix work on s4 from Bc while chunk s4 + 1 lands in Bn
+    auto step = [&](int s4, const float2* Bc, float2* Bn) {
+        const bool more = s4 + 1 < S4;
         f32x4 nar = ar, nai = ai;
-        if (s4 + 1 < S4) {
-            load_chunk(s4 + 1);
+        if (more) {
+            issue_chunk(s4 + 1, Bn);
             nar = ap[(size_t)(s4 + 1) * 128];
             nai = ap[(size_t)(s4 + 1) * 128 + 64];
         }
+        const float2* bb = Bc + brow * NT + bcol;
+        float2 bv[2][NJ];
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) bv[0][jt] = bb[16 * jt];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const float a_r = ar[ks], a_i = ai[ks], a_n = -ai[ks];
-            float2 bv[NJ];
+            const int c = ks & 1;
+            if (ks < 3) {
 #pragma unroll
-            for (int jt = 0; jt < NJ; ++jt) bv[jt] = bs[cb][4 * ks + brow][16 * jt + bcol];
-            if (dc) {
-#pragma unroll
-                for (int jt = 0; jt < NJ; ++jt)
-                    accR[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_r, bv[jt].x, accR[jt], 0, 0, 0);
-#pragma unroll
-                for (int jt = 0; jt < NJ; ++jt)
-                    accI[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_i, bv[jt].y, accI[jt], 0, 0, 0);
-            } else {
-#pragma unroll
-                for (int jt = 0; jt < NJ; ++jt)
-                    accR[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_r, bv[jt].x, accR[jt], 0, 0, 0);
-#pragma unroll
-                for (int jt = 0; jt < NJ; ++jt)
-                    accI[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_i, bv[jt].x, accI[jt], 0, 0, 0);
-#pragma unroll
-                for (int jt = 0; jt < NJ; ++jt)
-                    accR[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_n, bv[jt].y, accR[jt], 0, 0, 0);
-#pragma unroll
-                for (int jt = 0; jt < NJ; ++jt)
-                    accI[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_r, bv[jt].y, accI[jt], 0, 0, 0);
+                for (int jt = 0; jt < NJ; ++jt) bv[c ^ 1][jt] = bb[(4 * (ks + 1)) * NT + 16 * jt];
             }
+            __builtin_amdgcn_sched_barrier(0);
+            const float p1 = ar[ks];
+            const float p2 = sel * ai[ks];
+            const float p3 = -p2;
+            const float p4 = (f == 0) ? ai[ks] : ar[ks];
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt)
+                accR[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(p1, bv[c][jt].x, accR[jt], 0, 0, 0);
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt)
+                accI[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(p2, bv[c][jt].x, accI[jt], 0, 0, 0);
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt)
+                accR[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(p3, bv[c][jt].y, accR[jt], 0, 0, 0);
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt)
+                accI[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(p4, bv[c][jt].y, accI[jt], 0, 0, 0);
         }
-        if (s4 + 1 < S4) {
-            store_chunk(cb ^ 1);
-            ar = nar;
-            ai = nai;
-        }
+        // the next chunk's DMA and A operands have landed; every wave is done
+        // with Bc before it is refilled
+        wait_vmem_all();
         __syncthreads();
+        ar = nar;
+        ai = nai;
+    };
+    issue_chunk(0, bsA);
+    ar = ap[0];
+    ai = ap[64];
+    wait_vmem_all();
+    __syncthreads();
+    for (int s4 = 0; s4 < S4; s4 += 2) {
+        step(s4, bsA, bsB);
+        if (s4 + 1 < S4) step(s4 + 1, bsB, bsA);
     }
     // D layout: lane l holds rows 4 (l / 16) + i, column l % 16 of each tile
     float2* yo = yf + ((size_t)f * Cout + 16 * ot + 4 * brow) * NP + n0 + bcol;
