@@ -122,6 +122,9 @@ def lib() -> ctypes.CDLL:
     L.avae_conv1d_fft.restype = c_int
     L.avae_conv1d_fft.argtypes = [P, P, c_int, c_int, c_int, c_int, P, P, c_int, c_int, P, P,
                                   c_size_t, P]
+    L.avae_act_conv1d_fft.restype = c_int
+    L.avae_act_conv1d_fft.argtypes = [P, P, c_int, c_int, c_int, c_int, P, P, P, P, c_int, c_int,
+                                      P, P, c_size_t, P]
     L.avae_convtr1d.restype = c_int
     L.avae_convtr1d.argtypes = [P, P, c_int, c_int, c_int, c_int, P, P, c_int, c_int, c_int, P]
     L.avae_amp_block_workspace_bytes.restype = c_size_t
@@ -357,6 +360,26 @@ def conv1d_fft(x, wp, Cout: int, K: int, bias=None, dilation: int = 1, residual=
                                  _opt(residual, "residual", (B, Cout, T)),
                                  workspace.data_ptr(), workspace.numel(),
                                  _stream(stream)))
+    return out
+
+
+def act_conv1d_fft(x, log_alpha, log_beta, wp, Cout: int, K: int, bias=None, dilation: int = 1,
+                   residual=None, out=None, workspace=None, stream=None):
+    """avae_act_conv1d_fft: conv1d_fft of act1d(x) (designed taps), one pass."""
+    torch = _torch()
+    B, Cin, T = x.shape
+    if out is None:
+        out = torch.empty((B, Cout, T), device=x.device, dtype=torch.float32)
+    need = conv1d_fft_workspace_bytes(B, Cin, Cout, T, K, dilation)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), device=x.device, dtype=torch.uint8)
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda:
+        raise ValueError("workspace must be a uint8 device tensor")
+    _check(lib().avae_act_conv1d_fft(
+        _dev(x, "x"), _dev(out, "out", (B, Cout, T)), B, Cin, Cout, T,
+        _dev(log_alpha, "log_alpha", (Cin,)), _dev(log_beta, "log_beta", (Cin,)), _dev(wp, "wp"),
+        _opt(bias, "bias", (Cout,)), K, dilation, _opt(residual, "residual", (B, Cout, T)),
+        workspace.data_ptr(), workspace.numel(), _stream(stream)))
     return out
 
 

@@ -99,8 +99,9 @@ bool amp_fusable(int C, int K, int n_dil, const int* dil) {
 // path; otherwise each step is act1d, conv1d, act1d, conv1d launches.
 // fw1/fw2 (per dilation step; null, or null entries, for the direct
 // kernels) are frequency-domain weights from launch_fft_pack: that
-// convolution then runs as launch_conv1d_fft, its two spectra in t1 and t2
-// (slots of at least plan::fft_spectrum_bytes each).
+// activation + convolution then runs as launch_conv1d_fft with the
+// activation inside its forward transforms, the spectra in t1 and t2 (slots
+// of at least plan::fft_spectrum_bytes each).
 int run_amp(const float* x, float* y, int B, int C, int T, int K, int n_dil, const int* dil,
             const float* const* w1, const float* const* b1, const float* const* w2,
             const float* const* b2, const float* const* la, const float* const* lb,
@@ -124,28 +125,36 @@ int run_amp(const float* x, float* y, int B, int C, int T, int K, int n_dil, con
     for (int q = 0; q < n_dil; ++q) {
         const float* src = (q == 0) ? x : cur;
         const int d = dil[q];
-        AVAE_TRY(avae::launch_act1d(src, t1, B, C, T, la[2 * q], lb[2 * q], taps, s), "act1d");
         ConvEpilogue e1{b1[q], nullptr, 1.0f, 0};
+        // h = conv1(act(src)) lands in t2 either way
         if (fw1 && fw1[q]) {
-            // t1 -> spectrum in t2 -> product in t1 -> output in t2
-            AVAE_TRY(avae::launch_conv1d_fft(t1, t2, fw1[q], B, C, C, T, K, d, e1, t2, t1, s),
-                     "conv1d_fft (convs1)");
+            // act(src) inside the transforms: spectrum in t1, product in t2,
+            // output in t1, moved to t2 by the next step's choice below
+            AVAE_TRY(avae::launch_conv1d_fft(src, t1, fw1[q], B, C, C, T, K, d, e1, t1, t2, s,
+                                             la[2 * q], lb[2 * q], &taps),
+                     "act + conv1d_fft (convs1)");
         } else {
+            AVAE_TRY(avae::launch_act1d(src, t1, B, C, T, la[2 * q], lb[2 * q], taps, s),
+                     "act1d");
             AVAE_TRY(avae::launch_conv1d(t1, t2, w1[q], B, C, C, T, T, K, d, (K * d - d) / 2, e1,
                                          s),
                      "conv1d (convs1)");
         }
-        AVAE_TRY(avae::launch_act1d(t2, t1, B, C, T, la[2 * q + 1], lb[2 * q + 1], taps, s),
-                 "act1d");
+        float* h = (fw1 && fw1[q]) ? t1 : t2;   // conv1's output
+        float* fr = (fw1 && fw1[q]) ? t2 : t1;  // the other scratch slot
         const bool last = (q == n_dil - 1);
         ConvEpilogue e2{b2[q], src, last ? out_scale : 1.0f, last ? accumulate : 0};
         float* dst = last ? y : cur;
         if (fw2 && fw2[q]) {
-            // t1 -> spectrum in t2 -> product in t1 -> dst (+ residual src)
-            AVAE_TRY(avae::launch_conv1d_fft(t1, dst, fw2[q], B, C, C, T, K, 1, e2, t2, t1, s),
-                     "conv1d_fft (convs2)");
+            // act(h) inside the transforms: spectrum in fr, product in h,
+            // then dst (+ residual src)
+            AVAE_TRY(avae::launch_conv1d_fft(h, dst, fw2[q], B, C, C, T, K, 1, e2, fr, h, s,
+                                             la[2 * q + 1], lb[2 * q + 1], &taps),
+                     "act + conv1d_fft (convs2)");
         } else {
-            AVAE_TRY(avae::launch_conv1d(t1, dst, w2[q], B, C, C, T, T, K, 1, (K - 1) / 2, e2, s),
+            AVAE_TRY(avae::launch_act1d(h, fr, B, C, T, la[2 * q + 1], lb[2 * q + 1], taps, s),
+                     "act1d");
+            AVAE_TRY(avae::launch_conv1d(fr, dst, w2[q], B, C, C, T, T, K, 1, (K - 1) / 2, e2, s),
                      "conv1d (convs2)");
         }
     }
@@ -266,6 +275,38 @@ extern "C" int avae_conv1d_fft(const float* x, float* y, int B, int Cin, int Cou
     AVAE_TRY(avae::launch_conv1d_fft(x, y, wp, B, Cin, Cout, T, K, dilation, ep, xs, ys,
                                      (hipStream_t)stream),
              "avae_conv1d_fft launch");
+    return AVAE_OK;
+}
+
+extern "C" int avae_act_conv1d_fft(const float* x, float* y, int B, int Cin, int Cout, int T,
+                                   const float* log_alpha, const float* log_beta,
+                                   const float* wp, const float* bias, int K, int dilation,
+                                   const float* residual, void* workspace, size_t ws_bytes,
+                                   void* stream) {
+    if (!x || !y || !wp || !log_alpha || !log_beta)
+        return fail(AVAE_EINVAL, "avae_act_conv1d_fft: null tensor pointer");
+    if (B < 1 || Cin < 1 || Cout < 1 || T < 1 || K < 1 || dilation < 1)
+        return fail(AVAE_EINVAL,
+                    "avae_act_conv1d_fft: bad size (B=%d Cin=%d Cout=%d T=%d K=%d d=%d)", B, Cin,
+                    Cout, T, K, dilation);
+    if (x == y) return fail(AVAE_EINVAL, "avae_act_conv1d_fft: x and y must not overlap");
+    if (!avae::plan::fft_supported(Cin, Cout, K, dilation))
+        return fail(AVAE_ESHAPE,
+                    "avae_act_conv1d_fft: needs Cin %% 16 == 0, Cout %% 64 == 0, odd K, "
+                    "(K-1)*d <= 128 (Cin=%d Cout=%d K=%d d=%d)",
+                    Cin, Cout, K, dilation);
+    const size_t need = avae_conv1d_fft_workspace_bytes(B, Cin, Cout, T, K, dilation);
+    if (!workspace || ws_bytes < need)
+        return fail(AVAE_EWORKSPACE, "avae_act_conv1d_fft: workspace %zu bytes < %zu needed",
+                    ws_bytes, need);
+    float* xs = (float*)workspace;
+    float* ys = (float*)((char*)workspace + avae::plan::fft_spectrum_bytes(B, Cin, T, K, dilation));
+    ConvEpilogue ep{bias, residual, 1.0f, 0, nullptr, nullptr};
+    const ActTaps taps = make_taps(nullptr, nullptr);
+    avae::prof_set_phase(avae::kPhaseNone);
+    AVAE_TRY(avae::launch_conv1d_fft(x, y, wp, B, Cin, Cout, T, K, dilation, ep, xs, ys,
+                                     (hipStream_t)stream, log_alpha, log_beta, &taps),
+             "avae_act_conv1d_fft launch");
     return AVAE_OK;
 }
 

@@ -66,13 +66,17 @@ hipError_t launch_convtr1d(const float* x, float* y, const float* w, const float
 // padding, shapes that plan::fft_supported takes.  wp holds
 // fft_conv_weight_floats(Cin, Cout) floats from launch_fft_pack; xspec and
 // yspec plan::fft_spectrum_bytes(B, Cin | Cout, T, K, d) bytes each.  The
-// epilogue's Snake fields must be null.
+// epilogue's Snake fields must be null.  With act_log_alpha, act_log_beta
+// and act_taps all given, the convolution's input is Activation1d(x) (as
+// launch_act1d computes it), evaluated inside the forward transforms.
 size_t fft_conv_weight_floats(int Cin, int Cout);
 hipError_t launch_fft_pack(const float* w, float* wp, int Cin, int Cout, int K, int dilation,
                            hipStream_t s);
 hipError_t launch_conv1d_fft(const float* x, float* y, const float* wp, int B, int Cin, int Cout,
                              int T, int K, int dilation, const ConvEpilogue& ep, float* xspec,
-                             float* yspec, hipStream_t s);
+                             float* yspec, hipStream_t s, const float* act_log_alpha = nullptr,
+                             const float* act_log_beta = nullptr,
+                             const ActTaps* act_taps = nullptr);
 
 // Conv1d to a single output channel ("same" padding, odd K) followed by the
 // final nonlinearity (0 none, 1 tanh, 2 clamp to [-1,1]).  pre_final, if not

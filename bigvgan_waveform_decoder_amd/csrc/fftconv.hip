@@ -34,6 +34,7 @@
 // go through LDS.
 #include <cstdio>
 
+#include "act_math.h"
 #include "avae_internal.h"
 #include "plan.h"
 
@@ -106,45 +107,135 @@ __device__ __forceinline__ void fft256(float2 (&v)[4], int j, float2* buf, const
 // Forward transforms.  grid (ceil(nb / kCols), C, B): workgroup = kCols
 // consecutive blocks of row (b, c), four waves taking one block each in turn.
 // Writes X[slot][c][b nb + n] (complex, NP columns per row).
+//
+// With ACT the transformed signal is Activation1d(x) ([H3] Activation1d::
+// apply, SnakeBeta, fir_pad), evaluated on the block's window as it is
+// loaded, in the polyphase form of act1d.hip: the doubled-rate pair at q is
+//   e(q) = sum_k up2[2k+1] x[clamp(q+2-k)],  o(q) = sum_k up2[2k] x[clamp(q+3-k)],
+// both through SnakeBeta (for q < 0 both phases are s[0] = e(0), for q > T-1
+// both are s[2T-1] = o(T-1): the down-sampler's replicate padding), and
+//   a(p) = sum_m down[2m] so(p+m-3) + down[2m+1] se(p+m-2).
+// A window of 256 outputs p0 .. p0+255 needs q in [p0-3, p0+259) and x in
+// [p0-6, p0+262).  The convolution's zero padding then applies to a.
+constexpr int kActX = kN + 12;   // x window per transform
+constexpr int kActQ = kN + 6;    // phase pairs per transform
+
+struct ActIn {
+    const float* log_alpha;  // [C]
+    const float* log_beta;   // [C]
+    ActTaps taps;
+};
+
+template <bool ACT>
 __global__ __launch_bounds__(kThreads) void fft_fwd_kernel(const float* __restrict__ x,
                                                            float2* __restrict__ xf, int C, int T,
-                                                           int L, int P, int nb, int NP) {
+                                                           int L, int P, int nb, int NP,
+                                                           ActIn act) {
     __shared__ float2 tw[kN];
     __shared__ float2 buf[kThreads / 64][kN];
     __shared__ float2 res[kSlots][kCols + 1];
+    __shared__ float aw[ACT ? kThreads / 64 : 1][ACT ? kActX + 2 * kActQ : 1];
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int b = blockIdx.z, c = blockIdx.y, n0 = blockIdx.x * kCols;
     init_twiddles(tw);
     __syncthreads();
     const float* xr = x + ((size_t)b * C + c) * (size_t)T;
-    // every input of this wave's kCols / 4 transforms is loaded up front (the
-    // loads of one transform alone leave HBM latency exposed)
     constexpr int kPerWave = kCols / (kThreads / 64);
-    float xin[kPerWave][4];
+    if constexpr (!ACT) {
+        // every input of this wave's kCols / 4 transforms is loaded up front
+        // (the loads of one transform alone leave HBM latency exposed)
+        float xin[kPerWave][4];
 #pragma unroll
-    for (int it = 0; it < kPerWave; ++it) {
-        const int u0 = (n0 + wid + (kThreads / 64) * it) * L - P + lane;
+        for (int it = 0; it < kPerWave; ++it) {
+            const int u0 = (n0 + wid + (kThreads / 64) * it) * L - P + lane;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = u0 + 64 * r;
-            xin[it][r] = (t >= 0 && t < T) ? xr[t] : 0.f;
+            for (int r = 0; r < 4; ++r) {
+                const int t = u0 + 64 * r;
+                xin[it][r] = (t >= 0 && t < T) ? xr[t] : 0.f;
+            }
         }
-    }
 #pragma unroll
-    for (int it = 0; it < kPerWave; ++it) {
-        const int g = wid + (kThreads / 64) * it;
-        if (n0 + g >= nb) break;  // wave-uniform; no workgroup barrier until after the loop
-        float2 v[4];
+        for (int it = 0; it < kPerWave; ++it) {
+            const int g = wid + (kThreads / 64) * it;
+            if (n0 + g >= nb) break;  // wave-uniform; no workgroup barrier until after the loop
+            float2 v[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = make_float2(xin[it][r], 0.f);
-        fft256(v, lane, buf[wid], tw);
-        // lane j: bins j, j + 64, j + 128, j + 192; keep 0..128
-        if (lane == 0) {
-            res[0][g] = make_float2(v[0].x, v[2].x);  // bin 0 and bin N/2 (both real)
-            res[64][g] = v[1];
-        } else {
-            res[lane][g] = v[0];
-            res[lane + 64][g] = v[1];
+            for (int r = 0; r < 4; ++r) v[r] = make_float2(xin[it][r], 0.f);
+            fft256(v, lane, buf[wid], tw);
+            if (lane == 0) {
+                res[0][g] = make_float2(v[0].x, v[2].x);  // bin 0 and bin N/2 (both real)
+                res[64][g] = v[1];
+            } else {
+                res[lane][g] = v[0];
+                res[lane + 64][g] = v[1];
+            }
+        }
+    } else {
+        const float alpha_rev = snake_alpha_rev(act.log_alpha[c]);
+        const float inv_beta = snake_inv_beta(act.log_beta[c]);
+        float* xw = aw[wid];             // x[clamp(p0 - 6 + i)]
+        float* se = xw + kActX;          // snake(e(q)), q = p0 - 3 + j
+        float* so = se + kActQ;          // snake(o(q))
+        constexpr int kXr = (kActX + 63) / 64;
+        float xin[kPerWave][kXr];
+#pragma unroll
+        for (int it = 0; it < kPerWave; ++it) {
+            const int p0 = (n0 + wid + (kThreads / 64) * it) * L - P;
+#pragma unroll
+            for (int r = 0; r < kXr; ++r)
+                xin[it][r] = xr[min(max(p0 - 6 + lane + 64 * r, 0), T - 1)];
+        }
+#pragma unroll
+        for (int it = 0; it < kPerWave; ++it) {
+            const int g = wid + (kThreads / 64) * it;
+            if (n0 + g >= nb) break;  // wave-uniform
+            const int p0 = (n0 + g) * L - P;
+#pragma unroll
+            for (int r = 0; r < kXr; ++r)
+                if (lane + 64 * r < kActX) xw[lane + 64 * r] = xin[it][r];
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int r = 0; r < (kActQ + 63) / 64; ++r) {
+                const int j = lane + 64 * r;
+                if (j < kActQ) {
+                    const int q = p0 - 3 + j;
+                    const int qc = min(max(q, 0), T - 1);
+                    const float* xq = xw + (qc - p0 + 6);
+                    float e = 0.f, o = 0.f;
+#pragma unroll
+                    for (int k = 0; k < 6; ++k) {
+                        e = fmaf(act.taps.up2[2 * k + 1], xq[2 - k], e);
+                        o = fmaf(act.taps.up2[2 * k], xq[3 - k], o);
+                    }
+                    if (q < 0) o = e;
+                    if (q > T - 1) e = o;
+                    se[j] = snake_beta(e, alpha_rev, inv_beta);
+                    so[j] = snake_beta(o, alpha_rev, inv_beta);
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+            float2 v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int u = lane + 64 * r;
+                float acc = 0.f;
+#pragma unroll
+                for (int m = 0; m < 6; ++m) {
+                    acc = fmaf(act.taps.down[2 * m], so[u + m], acc);
+                    acc = fmaf(act.taps.down[2 * m + 1], se[u + m + 1], acc);
+                }
+                const int p = p0 + u;
+                v[r] = make_float2((p >= 0 && p < T) ? acc : 0.f, 0.f);
+            }
+            __builtin_amdgcn_wave_barrier();
+            fft256(v, lane, buf[wid], tw);
+            if (lane == 0) {
+                res[0][g] = make_float2(v[0].x, v[2].x);
+                res[64][g] = v[1];
+            } else {
+                res[lane][g] = v[0];
+                res[lane + 64][g] = v[1];
+            }
         }
     }
     __syncthreads();
@@ -435,7 +526,8 @@ hipError_t launch_fft_pack(const float* w, float* wp, int Cin, int Cout, int K, 
 
 hipError_t launch_conv1d_fft(const float* x, float* y, const float* wp, int B, int Cin, int Cout,
                              int T, int K, int dilation, const ConvEpilogue& ep, float* xspec,
-                             float* yspec, hipStream_t s) {
+                             float* yspec, hipStream_t s, const float* act_log_alpha,
+                             const float* act_log_beta, const ActTaps* act_taps) {
     if (!plan::fft_supported(Cin, Cout, K, dilation) || ep.snake_alpha || ep.in_alpha)
         return hipErrorInvalidValue;
     const plan::FftShape sh = plan::fft_shape(B, T, K, dilation);
@@ -446,12 +538,21 @@ hipError_t launch_conv1d_fft(const float* x, float* y, const float* wp, int B, i
     const dim3 tg((unsigned)((sh.nb + kCols - 1) / kCols), 1, (unsigned)B);
     const double blocks = (double)sh.NB;
 
+    const bool act = act_log_alpha && act_log_beta && act_taps;
+    ActIn ai{act_log_alpha, act_log_beta, {}};
+    if (act) ai.taps = *act_taps;
     prof_pre(s);
-    hipLaunchKernelGGL(fft_fwd_kernel, dim3(tg.x, (unsigned)Cin, tg.z), dim3(kThreads), 0, s, x,
-                       xf, Cin, T, sh.L, P, sh.nb, sh.NP);
+    if (act)
+        hipLaunchKernelGGL(fft_fwd_kernel<true>, dim3(tg.x, (unsigned)Cin, tg.z), dim3(kThreads),
+                           0, s, x, xf, Cin, T, sh.L, P, sh.nb, sh.NP, ai);
+    else
+        hipLaunchKernelGGL(fft_fwd_kernel<false>, dim3(tg.x, (unsigned)Cin, tg.z), dim3(kThreads),
+                           0, s, x, xf, Cin, T, sh.L, P, sh.nb, sh.NP, ai);
     hipError_t e = hipGetLastError();
     // algorithmic: x read once (4 B per sample), the spectrum written once
-    prof_post(s, "fft_fwd_kernel", 0.0, 4.0 * B * Cin * (double)T + 8.0 * kSlots * Cin * blocks);
+    prof_post(s, act ? "fft_fwd_kernel<act>" : "fft_fwd_kernel",
+              act ? 52.0 * B * Cin * (double)T : 0.0,
+              4.0 * B * Cin * (double)T + 8.0 * kSlots * Cin * blocks);
     if (e != hipSuccess) return e;
 
     prof_pre(s);

@@ -134,6 +134,20 @@ int avae_conv1d_fft(const float* x, float* y, int B, int Cin, int Cout, int T, c
                     void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * avae_conv1d_fft of Activation1d(x): the activation of an AMP block's
+ * act -> conv pair ([H3] AmpBlock::apply, Activation1d::apply) with the
+ * designed avae_kaiser_sinc(0.25, 0.3, 12) taps, evaluated on each block's
+ * window inside the forward transforms (the activation never goes to
+ * memory).  Arguments as avae_conv1d_fft, plus log_alpha, log_beta [Cin]
+ * (device) as in avae_act1d.  Same result as avae_act1d followed by
+ * avae_conv1d_fft up to float32 rounding.
+ */
+int avae_act_conv1d_fft(const float* x, float* y, int B, int Cin, int Cout, int T,
+                        const float* log_alpha, const float* log_beta, const float* wp,
+                        const float* bias, int K, int dilation, const float* residual,
+                        void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * ConvTranspose1d ([H3] ConvT1d::apply/load; [LTX] ConvT1d):
  *   y[b, o, t*stride + j - pad] += x[b,i,t] * w[i,o,j], plus bias[o];
  *   Tout = (Tin - 1)*stride + K - 2*pad.

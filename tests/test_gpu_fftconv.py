@@ -81,7 +81,7 @@ def test_conv1d_fft_decoder_widths(C, T, K, d):
         assert err <= TOL, a
 
 
-def test_conv1d_fft_same_as_direct_kernel_shape_checks():
+def test_conv1d_fft_shape_checks():
     """Shapes the frequency-domain kernel does not take are refused."""
     announce("conv1d_fft shape checks")
     assert avae.conv1d_fft_workspace_bytes(1, 12, 64, 100, 3, 1) == 0   # Cin % 16
@@ -91,3 +91,32 @@ def test_conv1d_fft_same_as_direct_kernel_shape_checks():
     w = cuda(W.normal(0, "fft/bad/w", [48, 16, 3]))
     with pytest.raises(avae.AvaeError):
         avae.conv1d_fft_pack(w, dilation=1)
+
+
+ACT_CASES = [
+    # B, Cin, Cout, T, K, d, residual, input scale
+    (1, 16, 64, 300, 7, 1, False, 1.0),      # both row ends inside one block
+    (2, 64, 128, 1000, 11, 5, True, 3.0),
+    (1, 32, 64, 5, 11, 3, False, 1.0),       # T < the activation's reach: every index clamped
+    (2, 128, 128, 4000, 7, 3, False, 20.0),  # large inputs (many sine periods)
+    (1, 48, 64, 7001, 5, 32, True, 1.0),     # span 128
+]
+
+
+@pytest.mark.parametrize("B,Cin,Cout,T,K,d,res,scale", ACT_CASES)
+def test_act_conv1d_fft_matches_oracle(B, Cin, Cout, T, K, d, res, scale):
+    """avae_act_conv1d_fft: the activation evaluated inside the forward
+    transforms against the oracle's act1d followed by its direct conv1d."""
+    announce(f"act_conv1d_fft B={B} Cin={Cin} Cout={Cout} T={T} K={K} d={d} res={res} x{scale}")
+    x, w, b = _inputs(f"act-{B}-{Cin}-{Cout}-{T}-{K}-{d}", B, Cin, Cout, T, K)
+    x = x * scale
+    la = W.normal(0, f"fft/act-{Cin}/la", [Cin], 0.0, 0.01)
+    lb = W.normal(0, f"fft/act-{Cin}/lb", [Cin], 0.0, 0.01)
+    r = W.normal(0, f"fft/act-{Cin}-{Cout}-{T}/res", [B, Cout, T]) if res else None
+    wp = avae.conv1d_fft_pack(cuda(w), dilation=d)
+    y = host(avae.act_conv1d_fft(cuda(x), cuda(la), cuda(lb), wp, Cout, K, bias=cuda(b),
+                                 dilation=d, residual=cuda(r) if res else None))
+    ref = O.conv1d(O.act1d(x, la, lb), w, b, dilation=d, pad=(K - 1) * d // 2, residual=r)
+    err = rel_err(y, ref)
+    print(f"max|err|/rms = {err:.3e}")
+    assert err <= TOL
