@@ -117,7 +117,7 @@ def roofline(kernels, steps, name=None):
         name = dominant_kernel(kernels)
     k = kernels[name]
     avg_s = k["total_ms"] / 1e3 / k["launches"]
-    if name.startswith("act1d") or name.startswith("channel_affine"):
+    if _hbm_bound(name, k):
         achieved = k["bytes"] / k["launches"] / avg_s / 1e9
         peak, unit, bound = HBM_PEAK_GBPS, "GB/s", "hbm"
     else:
@@ -127,6 +127,13 @@ def roofline(kernels, steps, name=None):
             "frac": achieved / peak, "traffic": traffic_for(name),
             "launches_per_step": k["launches"] / steps, "avg_launch_us": avg_s * 1e6,
             "algorithmic_per_launch": (k["bytes"] if bound == "hbm" else k["flops"]) / k["launches"]}
+
+
+def _hbm_bound(name, k):
+    """Whether a kernel's algorithmic bound is HBM bandwidth: its bytes at the
+    HBM peak take longer than its flops at the FP32 matrix peak (the
+    activations, the FFT convolution's transforms, the MRF sum)."""
+    return k["bytes"] / (HBM_PEAK_GBPS * 1e9) > k["flops"] / (FP32_MFMA_PEAK_TFLOPS * 1e12)
 
 
 def traffic_for(name):
@@ -234,6 +241,24 @@ def mfma_probe(torch, avae):
     return out
 
 
+def direct_form_flops(spec, B, frames):
+    """The decode's convolution flops counted in the direct form (2 Cout Cin K
+    per output sample for every Conv1d, 2 Cin Cout K per input sample for
+    every ConvTranspose1d): the algorithmic count of the pages' layers,
+    whatever form a kernel evaluates them in."""
+    w = spec.widths()
+    T = frames
+    f = 2.0 * spec.c_in * w[0] * spec.k_pre * T * B
+    for i, r in enumerate(spec.rates):
+        f += 2.0 * w[i] * w[i + 1] * spec.up_k[i] * T * B
+        T *= r
+        c = w[i + 1]
+        for k, dil in zip(spec.rb_k, spec.rb_d):
+            f += len(dil) * 2 * (2.0 * c * c * k * T * B)
+    f += 2.0 * w[-1] * spec.k_post * T * B
+    return f
+
+
 def roofline_sum(kernels, steps):
     """Sum over the decode's kernels of max(flops / MFMA peak, bytes / HBM
     peak), per step (aggregated per kernel name; every launch of a name has
@@ -332,7 +357,7 @@ def _kernel_rows(kernels, n):
         sec = k["total_ms"] / 1e3
         row = {"launches_per_call": k["launches"] / n, "ms_per_call": k["total_ms"] / n,
                "avg_launch_us": 1e6 * sec / max(k["launches"], 1)}
-        if name.startswith(("act1d", "snake", "channel_affine", "sum_into", "bwe_combine")):
+        if _hbm_bound(name, k):
             row["GBps"] = k["bytes"] / sec / 1e9
             row["frac_of_hbm_peak"] = row["GBps"] / HBM_PEAK_GBPS
         else:
@@ -817,8 +842,12 @@ def main():
     single_ms = ms if args.serial_mrf else res["single_stream"]["ms_per_step"]
     res["decode_roofline_sum"] = {"ms": t_roof, "frac_of_timed": t_roof / ms,
                                   "frac_of_single_stream": t_roof / single_ms}
-    # the whole step's matrix rate (the convolutions are ~97% of its flops)
+    # the whole step's rate of executed flops (the frequency-domain
+    # convolutions count their complex products, not the direct form's taps)
     res["decode_TFLOPs"] = sum(k["flops"] for k in iso.values()) / args.steps / (ms / 1e3) / 1e12
+    # the same step against the direct form's flop count: above the matrix
+    # peak where the transforms save more multiply-adds than they cost
+    res["decode_direct_form_TFLOPs"] = (direct_form_flops(spec, B, F) / (ms / 1e3) / 1e12)
     acts = [v for k, v in iso.items() if k.startswith("act1d")]
     if acts:
         ab = sum(v["bytes"] for v in acts)

@@ -234,7 +234,7 @@ extern "C" int avae_conv1d_fft_pack(const float* w, float* wp, int Cin, int Cout
                     Cout, K, dilation);
     if (!avae::plan::fft_supported(Cin, Cout, K, dilation))
         return fail(AVAE_ESHAPE,
-                    "avae_conv1d_fft_pack: needs Cin %% 16 == 0, Cout %% 64 == 0, odd K, "
+                    "avae_conv1d_fft_pack: needs Cin and Cout multiples of 16, odd K, "
                     "(K-1)*d <= 128 (Cin=%d Cout=%d K=%d d=%d)",
                     Cin, Cout, K, dilation);
     AVAE_TRY(avae::launch_fft_pack(w, wp, Cin, Cout, K, dilation, (hipStream_t)stream),
@@ -261,7 +261,7 @@ extern "C" int avae_conv1d_fft(const float* x, float* y, int B, int Cin, int Cou
     if (x == y) return fail(AVAE_EINVAL, "avae_conv1d_fft: x and y must not overlap");
     if (!avae::plan::fft_supported(Cin, Cout, K, dilation))
         return fail(AVAE_ESHAPE,
-                    "avae_conv1d_fft: needs Cin %% 16 == 0, Cout %% 64 == 0, odd K, "
+                    "avae_conv1d_fft: needs Cin and Cout multiples of 16, odd K, "
                     "(K-1)*d <= 128 (Cin=%d Cout=%d K=%d d=%d)",
                     Cin, Cout, K, dilation);
     const size_t need = avae_conv1d_fft_workspace_bytes(B, Cin, Cout, T, K, dilation);
@@ -292,7 +292,7 @@ extern "C" int avae_act_conv1d_fft(const float* x, float* y, int B, int Cin, int
     if (x == y) return fail(AVAE_EINVAL, "avae_act_conv1d_fft: x and y must not overlap");
     if (!avae::plan::fft_supported(Cin, Cout, K, dilation))
         return fail(AVAE_ESHAPE,
-                    "avae_act_conv1d_fft: needs Cin %% 16 == 0, Cout %% 64 == 0, odd K, "
+                    "avae_act_conv1d_fft: needs Cin and Cout multiples of 16, odd K, "
                     "(K-1)*d <= 128 (Cin=%d Cout=%d K=%d d=%d)",
                     Cin, Cout, K, dilation);
     const size_t need = avae_conv1d_fft_workspace_bytes(B, Cin, Cout, T, K, dilation);

@@ -63,16 +63,34 @@ __device__ void init_twiddles(float2* tw) {
     }
 }
 
-// One radix-4 Stockham stage for butterfly j (sub-transform size Ns = 4^p):
-// v[r] = a[j + 64 r] on entry, the four outputs (positions
-// 4(j - k) + k + q Ns, k = j mod Ns) on exit.
-__device__ __forceinline__ void radix4(float2 (&v)[4], int j, int Ns, const float2* tw) {
-    const int k = j & (Ns - 1);
-    if (Ns > 1) {
+// Lane j's twiddles for the three stages that have them (Ns = 4, 16, 64):
+// w[s][r-1] = tw[r k step], k = j mod Ns, step = N / (4 Ns).  Read once per
+// wave from the LDS table and reused for every transform of the wave.
+struct LaneTwiddles {
+    float2 w[3][3];
+};
+
+__device__ __forceinline__ LaneTwiddles lane_twiddles(int j, const float2* tw) {
+    LaneTwiddles t;
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+        const int Ns = 4 << (2 * s);
+        const int k = j & (Ns - 1);
         const int step = kN / (4 * Ns);
-        v[1] = cmul(v[1], tw[k * step]);
-        v[2] = cmul(v[2], tw[2 * k * step]);
-        v[3] = cmul(v[3], tw[3 * k * step]);
+#pragma unroll
+        for (int r = 1; r < 4; ++r) t.w[s][r - 1] = tw[r * k * step];
+    }
+    return t;
+}
+
+// One radix-4 Stockham stage for butterfly j (sub-transform size Ns = 4^p,
+// stage p; p = 0 has unit twiddles): v[r] = a[j + 64 r] on entry, the four
+// outputs (positions 4(j - k) + k + q Ns, k = j mod Ns) on exit.
+__device__ __forceinline__ void radix4(float2 (&v)[4], int p, const LaneTwiddles& lt) {
+    if (p > 0) {
+        v[1] = cmul(v[1], lt.w[p - 1][0]);
+        v[2] = cmul(v[2], lt.w[p - 1][1]);
+        v[3] = cmul(v[3], lt.w[p - 1][2]);
     }
     const float2 s0 = cadd(v[0], v[2]), s1 = csub(v[0], v[2]);
     const float2 s2 = cadd(v[1], v[3]), s3 = csub(v[1], v[3]);
@@ -87,10 +105,11 @@ __device__ __forceinline__ void radix4(float2 (&v)[4], int j, int Ns, const floa
 // complex of LDS.  LDS operations of one wave complete in issue order and
 // every write depends on the reads before it, so the exchanges need no
 // barrier; wave_barrier only keeps the compiler from moving them.
-__device__ __forceinline__ void fft256(float2 (&v)[4], int j, float2* buf, const float2* tw) {
+__device__ __forceinline__ void fft256(float2 (&v)[4], int j, float2* buf, const LaneTwiddles& lt) {
 #pragma unroll
-    for (int Ns = 1; Ns < kN / 4; Ns *= 4) {
-        radix4(v, j, Ns, tw);
+    for (int p = 0; p < 3; ++p) {
+        const int Ns = 1 << (2 * p);
+        radix4(v, p, lt);
         const int k = j & (Ns - 1);
         const int dst = 4 * (j - k) + k;
 #pragma unroll
@@ -100,7 +119,7 @@ __device__ __forceinline__ void fft256(float2 (&v)[4], int j, float2* buf, const
         for (int r = 0; r < 4; ++r) v[r] = buf[j + 64 * r];
         __builtin_amdgcn_wave_barrier();
     }
-    radix4(v, j, kN / 4, tw);  // k = j: outputs j + 64 q stay in place
+    radix4(v, 3, lt);  // Ns = 64, k = j: outputs j + 64 q stay in place
 }
 
 // ---------------------------------------------------------------------------
@@ -117,8 +136,8 @@ __device__ __forceinline__ void fft256(float2 (&v)[4], int j, float2* buf, const
 //   a(p) = sum_m down[2m] so(p+m-3) + down[2m+1] se(p+m-2).
 // A window of 256 outputs p0 .. p0+255 needs q in [p0-3, p0+259) and x in
 // [p0-6, p0+262).  The convolution's zero padding then applies to a.
-constexpr int kActX = kN + 12;   // x window per transform
-constexpr int kActQ = kN + 6;    // phase pairs per transform
+constexpr int kActX = kN + 12;   // x window per transform (a multiple of 4)
+constexpr int kActQ = kN + 8;    // phase pairs per transform (kN + 6, padded to 16 bytes)
 
 struct ActIn {
     const float* log_alpha;  // [C]
@@ -134,11 +153,12 @@ __global__ __launch_bounds__(kThreads) void fft_fwd_kernel(const float* __restri
     __shared__ float2 tw[kN];
     __shared__ float2 buf[kThreads / 64][kN];
     __shared__ float2 res[kSlots][kCols + 1];
-    __shared__ float aw[ACT ? kThreads / 64 : 1][ACT ? kActX + 2 * kActQ : 1];
+    __shared__ __align__(16) float aw[ACT ? kThreads / 64 : 1][ACT ? kActX + 2 * kActQ : 1];
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int b = blockIdx.z, c = blockIdx.y, n0 = blockIdx.x * kCols;
     init_twiddles(tw);
     __syncthreads();
+    const LaneTwiddles lt = lane_twiddles(lane, tw);
     const float* xr = x + ((size_t)b * C + c) * (size_t)T;
     constexpr int kPerWave = kCols / (kThreads / 64);
     if constexpr (!ACT) {
@@ -161,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void fft_fwd_kernel(const float* __restri
             float2 v[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = make_float2(xin[it][r], 0.f);
-            fft256(v, lane, buf[wid], tw);
+            fft256(v, lane, buf[wid], lt);
             if (lane == 0) {
                 res[0][g] = make_float2(v[0].x, v[2].x);  // bin 0 and bin N/2 (both real)
                 res[64][g] = v[1];
@@ -194,10 +214,80 @@ __global__ __launch_bounds__(kThreads) void fft_fwd_kernel(const float* __restri
             for (int r = 0; r < kXr; ++r)
                 if (lane + 64 * r < kActX) xw[lane + 64 * r] = xin[it][r];
             __builtin_amdgcn_wave_barrier();
+            float2 v[4];
+            if (p0 >= 6 && p0 + kActX - 6 <= T) {
+                // interior window: no index is clamped.  Lane l evaluates the
+                // pairs j = 4l .. 4l + 3 from xw[4l .. 4l + 9] and the outputs
+                // u = 4l .. 4l + 3 from so[4l .. 4l + 8], se[4l + 1 .. 4l + 9]
+                // (16-byte LDS windows), then one LDS transposition gives the
+                // FFT its a[j + 64 r] order.
+                const int j0 = 4 * lane;
+                {
+                    const float4* xp = reinterpret_cast<const float4*>(xw + j0);
+                    const float4 w0 = xp[0], w1 = xp[1], w2 = xp[2];
+                    const float xwin[12] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y,
+                                            w1.z, w1.w, w2.x, w2.y, w2.z, w2.w};
+                    float ev[4], ov[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        float e = 0.f, o = 0.f;
+#pragma unroll
+                        for (int m = 0; m < 6; ++m) {
+                            e = fmaf(act.taps.up2[2 * m + 1], xwin[k + 5 - m], e);
+                            o = fmaf(act.taps.up2[2 * m], xwin[k + 6 - m], o);
+                        }
+                        ev[k] = snake_beta(e, alpha_rev, inv_beta);
+                        ov[k] = snake_beta(o, alpha_rev, inv_beta);
+                    }
+                    *reinterpret_cast<float4*>(se + j0) = make_float4(ev[0], ev[1], ev[2], ev[3]);
+                    *reinterpret_cast<float4*>(so + j0) = make_float4(ov[0], ov[1], ov[2], ov[3]);
+                    if (lane < kActQ - 2 - kN) {  // j = 256 .. 261
+                        const int j = kN + lane;
+                        const float* xq = xw + j + 3;
+                        float e = 0.f, o = 0.f;
+#pragma unroll
+                        for (int m = 0; m < 6; ++m) {
+                            e = fmaf(act.taps.up2[2 * m + 1], xq[2 - m], e);
+                            o = fmaf(act.taps.up2[2 * m], xq[3 - m], o);
+                        }
+                        se[j] = snake_beta(e, alpha_rev, inv_beta);
+                        so[j] = snake_beta(o, alpha_rev, inv_beta);
+                    }
+                }
+                __builtin_amdgcn_wave_barrier();
+                {
+                    const float4* op = reinterpret_cast<const float4*>(so + j0);
+                    const float4* ep = reinterpret_cast<const float4*>(se + j0);
+                    const float4 o0 = op[0], o1 = op[1], o2 = op[2];
+                    const float4 e0 = ep[0], e1 = ep[1], e2 = ep[2];
+                    const float sw[12] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y,
+                                          o1.z, o1.w, o2.x, o2.y, o2.z, o2.w};
+                    const float ew[12] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y,
+                                          e1.z, e1.w, e2.x, e2.y, e2.z, e2.w};
+                    float out[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        float acc = 0.f;
+#pragma unroll
+                        for (int m = 0; m < 6; ++m) {
+                            acc = fmaf(act.taps.down[2 * m], sw[k + m], acc);
+                            acc = fmaf(act.taps.down[2 * m + 1], ew[k + m + 1], acc);
+                        }
+                        out[k] = acc;
+                    }
+                    // xw is free: the transposition goes through it
+                    *reinterpret_cast<float4*>(xw + j0) =
+                        make_float4(out[0], out[1], out[2], out[3]);
+                }
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = make_float2(xw[lane + 64 * r], 0.f);
+            } else {
+                // a window at a row end: clamped indices, the boundary pairs
 #pragma unroll
             for (int r = 0; r < (kActQ + 63) / 64; ++r) {
                 const int j = lane + 64 * r;
-                if (j < kActQ) {
+                if (j < kActQ - 2) {
                     const int q = p0 - 3 + j;
                     const int qc = min(max(q, 0), T - 1);
                     const float* xq = xw + (qc - p0 + 6);
@@ -214,7 +304,6 @@ __global__ __launch_bounds__(kThreads) void fft_fwd_kernel(const float* __restri
                 }
             }
             __builtin_amdgcn_wave_barrier();
-            float2 v[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int u = lane + 64 * r;
@@ -227,8 +316,9 @@ __global__ __launch_bounds__(kThreads) void fft_fwd_kernel(const float* __restri
                 const int p = p0 + u;
                 v[r] = make_float2((p >= 0 && p < T) ? acc : 0.f, 0.f);
             }
+            }
             __builtin_amdgcn_wave_barrier();
-            fft256(v, lane, buf[wid], tw);
+            fft256(v, lane, buf[wid], lt);
             if (lane == 0) {
                 res[0][g] = make_float2(v[0].x, v[2].x);
                 res[64][g] = v[1];
@@ -283,6 +373,7 @@ __global__ __launch_bounds__(kThreads) void fft_inv_kernel(const float2* __restr
         }
     }
     __syncthreads();
+    const LaneTwiddles lt = lane_twiddles(lane, tw);
     const float bo = bias ? bias[o] : 0.f;
     const size_t row = ((size_t)b * Cout + o) * (size_t)T;
     constexpr float inv_n = 1.0f / (float)kN;  // exact (power of two)
@@ -321,7 +412,7 @@ __global__ __launch_bounds__(kThreads) void fft_inv_kernel(const float2* __restr
         const float2 a1 = res[lane + 64][g];
         v[1] = make_float2(a1.x, -a1.y);
         v[3] = res[64 - lane][g];
-        fft256(v, lane, buf[wid], tw);
+        fft256(v, lane, buf[wid], lt);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int u = lane + 64 * q;
@@ -335,7 +426,7 @@ __global__ __launch_bounds__(kThreads) void fft_inv_kernel(const float2* __restr
 // ---------------------------------------------------------------------------
 // Y[slot] = W[slot] X[slot]: per slot a complex [Cout x Cin] x [Cin x NP]
 // product on the matrix cores.  Workgroup: one slot, 64 output rows (16 per
-// wave), NT = 16 NJ columns.  A operands (W) come pre-packed in MFMA
+// wave; Cout a multiple of 16), NT = 16 NJ columns.  A operands (W) come pre-packed in MFMA
 // fragment order, wp[slot][o/16][c/16][re,im][lane][4] (4 consecutive
 // k-steps per lane per 16-byte load), read straight from memory one
 // 16-channel chunk ahead.  B operands (X) go to LDS by LDS DMA
@@ -357,7 +448,7 @@ __global__ __launch_bounds__(kThreads, 2) void fft_gemm_kernel(const float* __re
                                                                float2* __restrict__ yf, int Cin,
                                                                int Cout, int NP, int ntiles) {
     constexpr int NT = 16 * NJ;
-    constexpr int KC = 16;
+    constexpr int KC = 16;               // channels per chunk (4 k-steps)
     constexpr int kDma = KC * NT / 128;  // 1 KB wave instructions per chunk (2 NJ)
     // two buffers as two objects, so that the compiler sees the DMA into one
     // and the fragment reads from the other as independent
@@ -366,28 +457,33 @@ __global__ __launch_bounds__(kThreads, 2) void fft_gemm_kernel(const float* __re
 
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     // XCD-contiguous tile order: workgroups are dealt to the 8 XCDs round robin
-    const int mt = Cout / 64;
+    const int mt = (Cout + 63) / 64;
     const int G = ntiles * mt * kSlots;
     const int id = blockIdx.x;
     const int lid = (id & 7) * (G >> 3) + (id >> 3);
     const int nt = lid % ntiles;
     const int om = (lid / ntiles) % mt;
     const int f = lid / (ntiles * mt);
+    // a wave past the last 16-row tile (Cout % 64 != 0) computes on the last
+    // tile's weights and stores nothing
+    const int OT = Cout / 16;
     const int ot = om * 4 + wid;
+    const bool rows_ok = ot < OT;
     const int n0 = nt * NT;
     const int S4 = Cin / 16;
+    const int nchunk = Cin / KC;
 
     const f32x4* ap = reinterpret_cast<const f32x4*>(wp) +
-                      ((size_t)(f * (Cout / 16) + ot) * S4) * 128 + lane;
+                      ((size_t)(f * OT + min(ot, OT - 1)) * S4) * 128 + lane;
     const float2* xb = xf + (size_t)f * Cin * NP + n0;
 
-    // chunk s4 -> buf: float4 q = 64 i + lane of the chunk image
-    auto issue_chunk = [&](int s4, float2* buf) {
+    // chunk ch -> buf: float4 q = 64 i + lane of the chunk image
+    auto issue_chunk = [&](int ch, float2* buf) {
         for (int i = wid; i < kDma; i += kThreads / 64) {
             const int q = 64 * i + lane;
             const int kk = q / (NT / 2), c2 = q - kk * (NT / 2);
             __builtin_amdgcn_global_load_lds(
-                (const void*)(xb + (size_t)(16 * s4 + kk) * NP + 2 * c2), (void*)(buf + 128 * i),
+                (const void*)(xb + (size_t)(KC * ch + kk) * NP + 2 * c2), (void*)(buf + 128 * i),
                 16, 0, 0);
         }
     };
@@ -402,14 +498,14 @@ __global__ __launch_bounds__(kThreads, 2) void fft_gemm_kernel(const float* __re
     const float sel = (f == 0) ? 0.f : 1.f;
     const int brow = lane >> 4, bcol = lane & 15;
     f32x4 ar, ai;
-    // one chunk: matrix work on s4 from Bc while chunk s4 + 1 lands in Bn
-    auto step = [&](int s4, const float2* Bc, float2* Bn) {
-        const bool more = s4 + 1 < S4;
+    // one chunk: matrix work on chunk ch from Bc while chunk ch + 1 lands in Bn
+    auto step = [&](int ch, const float2* Bc, float2* Bn) {
+        const bool more = ch + 1 < nchunk;
         f32x4 nar = ar, nai = ai;
         if (more) {
-            issue_chunk(s4 + 1, Bn);
-            nar = ap[(size_t)(s4 + 1) * 128];
-            nai = ap[(size_t)(s4 + 1) * 128 + 64];
+            issue_chunk(ch + 1, Bn);
+            nar = ap[(size_t)(ch + 1) * 128];
+            nai = ap[(size_t)(ch + 1) * 128 + 64];
         }
         const float2* bb = Bc + brow * NT + bcol;
         float2 bv[2][NJ];
@@ -426,7 +522,7 @@ __global__ __launch_bounds__(kThreads, 2) void fft_gemm_kernel(const float* __re
             const float p1 = ar[ks];
             const float p2 = sel * ai[ks];
             const float p3 = -p2;
-            const float p4 = (f == 0) ? ai[ks] : ar[ks];
+            const float p4 = (f == 0) ? ai[ks] : p1;
 #pragma unroll
             for (int jt = 0; jt < NJ; ++jt)
                 accR[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(p1, bv[c][jt].x, accR[jt], 0, 0, 0);
@@ -452,11 +548,12 @@ __global__ __launch_bounds__(kThreads, 2) void fft_gemm_kernel(const float* __re
     ai = ap[64];
     wait_vmem_all();
     __syncthreads();
-    for (int s4 = 0; s4 < S4; s4 += 2) {
-        step(s4, bsA, bsB);
-        if (s4 + 1 < S4) step(s4 + 1, bsB, bsA);
+    for (int ch = 0; ch < nchunk; ch += 2) {
+        step(ch, bsA, bsB);
+        if (ch + 1 < nchunk) step(ch + 1, bsB, bsA);
     }
     // D layout: lane l holds rows 4 (l / 16) + i, column l % 16 of each tile
+    if (!rows_ok) return;
     float2* yo = yf + ((size_t)f * Cout + 16 * ot + 4 * brow) * NP + n0 + bcol;
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt)
@@ -504,7 +601,7 @@ __global__ __launch_bounds__(256) void fft_pack_kernel(const float* __restrict__
 template <int NJ>
 void gemm_launch(const float* wp, const float2* xf, float2* yf, int Cin, int Cout, int NP,
                  int ntiles, hipStream_t s) {
-    const int G = ntiles * (Cout / 64) * kSlots;
+    const int G = ntiles * ((Cout + 63) / 64) * kSlots;
     hipLaunchKernelGGL(fft_gemm_kernel<NJ>, dim3((unsigned)G), dim3(kThreads), 0, s, wp, xf, yf,
                        Cin, Cout, NP, ntiles);
 }

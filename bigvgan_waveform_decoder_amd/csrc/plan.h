@@ -50,7 +50,7 @@ struct FftShape {
 };
 
 inline bool fft_supported(int Cin, int Cout, int K, int d) {
-    return Cin >= 16 && Cin % 16 == 0 && Cout >= 64 && Cout % 64 == 0 && K >= 1 && K % 2 == 1 &&
+    return Cin >= 16 && Cin % 16 == 0 && Cout >= 16 && Cout % 16 == 0 && K >= 1 && K % 2 == 1 &&
            d >= 1 && (long long)(K - 1) * d <= kFftN / 2;
 }
 
@@ -77,12 +77,12 @@ inline size_t fft_spectrum_bytes(int B, int C, int T, int K, int d) {
     return tensor_bytes((long long)kFftSlots * 2, C, s.NP);
 }
 
-// The decoders' AMP convolutions that run in the frequency domain: wide
-// channel counts (the transforms' cost per sample is then small against the
+// The decoders' AMP convolutions that run in the frequency domain: 96 or
+// more channels (the transforms' cost per sample is then small against the
 // channel mixing) and 7 or more taps (where the transform form needs fewer
 // multiply-adds than the direct one: ~2 per output and channel pair, against K).
 inline bool fft_amp_conv(int C, int K, int d) {
-    return C >= 128 && K >= 7 && fft_supported(C, C, K, d);
+    return C >= 96 && K >= 7 && fft_supported(C, C, K, d);
 }
 
 // Bytes of one decode workspace slot: the largest activation of the decode

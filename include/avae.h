@@ -109,7 +109,7 @@ int avae_conv1d(const float* x, float* y, int B, int Cin, int Cout, int T,
  * by one complex matrix product per frequency on the FP32 matrix cores,
  * and the L valid samples of each block's inverse transform are kept.
  * Same result as avae_conv1d up to float32 rounding (a few 1e-6 of the
- * output's RMS).  Takes Cin % 16 == 0, Cout % 64 == 0, odd K and
+ * output's RMS).  Takes Cin and Cout multiples of 16, odd K and
  * (K-1)*dilation <= 128.
  *
  * avae_conv1d_fft_weight_floats: floats of the packed weights for (Cin, Cout).

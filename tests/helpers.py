@@ -130,12 +130,12 @@ def dav_reach_frames(spec) -> int:
 def runs_fft_convs(spec) -> bool:
     """Whether the library runs some of this decoder's AMP convolutions in the
     frequency domain (overlap-save, 256-point transforms): widths of at least
-    128 channels, a multiple of 64, with 7 or more taps and (K-1) d <= 128.
+    96 channels, a multiple of 16, with 7 or more taps and (K-1) d <= 128.
     The block framing then follows the sequence start, so decodes of crops
     (streaming tiles) round differently from the whole sequence there."""
     chans = [spec.c0 // (2 ** (i + 1)) for i in range(len(spec.rates))]
     for c in chans:
-        if c < 128 or c % 64:
+        if c < 96 or c % 16:
             continue
         for k, dil in zip(spec.rb_k, spec.rb_d):
             if k >= 7 and any((k - 1) * d <= 128 for d in tuple(dil) + (1,)):

@@ -114,8 +114,9 @@ int main() {
               "fft shape 384");
         CHECK(b.nb == 98 && b.NB == 196 && b.ntiles == 2 && b.NJ == 7 && b.NP == 224,
               "fft shape 192");
-        CHECK(fft_amp_conv(384, 11, 5) && fft_amp_conv(192, 7, 1) && !fft_amp_conv(96, 11, 5) &&
-                  !fft_amp_conv(384, 3, 1) && !fft_amp_conv(336, 7, 1),
+        CHECK(fft_amp_conv(384, 11, 5) && fft_amp_conv(192, 7, 1) && fft_amp_conv(96, 11, 5) &&
+                  !fft_amp_conv(48, 11, 5) && !fft_amp_conv(384, 3, 1) &&
+                  !fft_amp_conv(100, 7, 1) && !fft_amp_conv(384, 11, 13),
               "fft selection");
     }
     // the column plan over many sizes: every column covered, at most 8 MFMA

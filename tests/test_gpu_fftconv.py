@@ -43,6 +43,8 @@ FFT_CASES = [
     (2, 384, 384, 3001, 11, 1, True),
     (2, 256, 128, 20000, 7, 5, False),   # 178 columns: two column tiles
     (1, 64, 64, 31000, 3, 3, False),     # 122 columns: one tile of 8 x 16
+    (2, 32, 48, 700, 7, 3, True),        # Cout 48: one 64-row tile, its last wave idle
+    (1, 96, 96, 9000, 11, 5, False),     # Cout 96: the second tile half full
 ]
 
 
@@ -61,7 +63,8 @@ def test_conv1d_fft_matches_oracle(B, Cin, Cout, T, K, d, res):
 
 
 @pytest.mark.parametrize("C,T,K,d", [(768, 2000, 11, 5), (384, 10000, 11, 5),
-                                     (384, 10000, 7, 3), (192, 20000, 11, 1)])
+                                     (384, 10000, 7, 3), (192, 20000, 11, 1),
+                                     (96, 40000, 11, 5), (96, 40000, 7, 1)])
 def test_conv1d_fft_decoder_widths(C, T, K, d):
     """The H3 decoder's wide stages at full size, B = 2, in-place residual:
     oracle windows at both row ends and across block seams."""
@@ -85,10 +88,10 @@ def test_conv1d_fft_shape_checks():
     """Shapes the frequency-domain kernel does not take are refused."""
     announce("conv1d_fft shape checks")
     assert avae.conv1d_fft_workspace_bytes(1, 12, 64, 100, 3, 1) == 0   # Cin % 16
-    assert avae.conv1d_fft_workspace_bytes(1, 16, 48, 100, 3, 1) == 0   # Cout % 64
+    assert avae.conv1d_fft_workspace_bytes(1, 16, 40, 100, 3, 1) == 0   # Cout % 16
     assert avae.conv1d_fft_workspace_bytes(1, 16, 64, 100, 4, 1) == 0   # even K
     assert avae.conv1d_fft_workspace_bytes(1, 16, 64, 100, 11, 13) == 0  # span 130 > 128
-    w = cuda(W.normal(0, "fft/bad/w", [48, 16, 3]))
+    w = cuda(W.normal(0, "fft/bad/w", [40, 16, 3]))
     with pytest.raises(avae.AvaeError):
         avae.conv1d_fft_pack(w, dilation=1)
 
