@@ -161,6 +161,34 @@ __global__ __launch_bounds__(kThreads) void fft_fwd_kernel(const float* __restri
     const LaneTwiddles lt = lane_twiddles(lane, tw);
     const float* xr = x + ((size_t)b * C + c) * (size_t)T;
     constexpr int kPerWave = kCols / (kThreads / 64);
+    // Two real blocks per complex transform: z = s1 + i s2, then
+    // S1[k] = (Z[k] + conj(Z[N-k])) / 2, S2[k] = -i (Z[k] - conj(Z[N-k])) / 2.
+    // Lane j holds Z[j + 64 q]; Z[N - j] and Z[N - 64 - j] are lane (64 - j)'s
+    // q = 3 and q = 2 values (lane 0: its own), exchanged through its buffer.
+    auto store_pair = [&](const float2 (&v)[4], int g1, int g2) {
+        float2* bw = buf[wid];
+        bw[lane] = v[2];
+        bw[64 + lane] = v[3];
+        __builtin_amdgcn_wave_barrier();
+        const int pj = (64 - lane) & 63;
+        const float2 w2 = bw[pj], w3 = bw[64 + pj];
+        __builtin_amdgcn_wave_barrier();
+        auto split = [&](float2 zk, float2 zm, int k) {
+            // zm = Z[N - k]
+            const float2 d = make_float2(zk.x - zm.x, zk.y + zm.y);  // Z[k] - conj(Z[N-k])
+            res[k][g1] = make_float2(0.5f * (zk.x + zm.x), 0.5f * (zk.y - zm.y));
+            res[k][g2] = make_float2(0.5f * d.y, -0.5f * d.x);
+        };
+        if (lane == 0) {
+            // bins 0 and N/2 of both blocks are real: slot 0 = (bin 0, bin N/2)
+            res[0][g1] = make_float2(v[0].x, v[2].x);
+            res[0][g2] = make_float2(v[0].y, v[2].y);
+            split(v[1], w3, 64);
+        } else {
+            split(v[0], w3, lane);
+            split(v[1], w2, lane + 64);
+        }
+    };
     if constexpr (!ACT) {
         // every input of this wave's kCols / 4 transforms is loaded up front
         // (the loads of one transform alone leave HBM latency exposed)
@@ -175,20 +203,14 @@ __global__ __launch_bounds__(kThreads) void fft_fwd_kernel(const float* __restri
             }
         }
 #pragma unroll
-        for (int it = 0; it < kPerWave; ++it) {
-            const int g = wid + (kThreads / 64) * it;
-            if (n0 + g >= nb) break;  // wave-uniform; no workgroup barrier until after the loop
+        for (int pr = 0; pr < kPerWave / 2; ++pr) {
+            const int g1 = wid + (kThreads / 64) * (2 * pr), g2 = g1 + kThreads / 64;
+            if (n0 + g1 >= nb) break;  // wave-uniform; no workgroup barrier until after the loop
             float2 v[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = make_float2(xin[it][r], 0.f);
+            for (int r = 0; r < 4; ++r) v[r] = make_float2(xin[2 * pr][r], xin[2 * pr + 1][r]);
             fft256(v, lane, buf[wid], lt);
-            if (lane == 0) {
-                res[0][g] = make_float2(v[0].x, v[2].x);  // bin 0 and bin N/2 (both real)
-                res[64][g] = v[1];
-            } else {
-                res[lane][g] = v[0];
-                res[lane + 64][g] = v[1];
-            }
+            store_pair(v, g1, g2);
         }
     } else {
         const float alpha_rev = snake_alpha_rev(act.log_alpha[c]);
@@ -205,16 +227,13 @@ __global__ __launch_bounds__(kThreads) void fft_fwd_kernel(const float* __restri
             for (int r = 0; r < kXr; ++r)
                 xin[it][r] = xr[min(max(p0 - 6 + lane + 64 * r, 0), T - 1)];
         }
-#pragma unroll
-        for (int it = 0; it < kPerWave; ++it) {
-            const int g = wid + (kThreads / 64) * it;
-            if (n0 + g >= nb) break;  // wave-uniform
-            const int p0 = (n0 + g) * L - P;
+        // the activated window of column it: av[r] = a(p0 + lane + 64 r)
+        auto act_col = [&](int it, float (&av)[4]) {
+            const int p0 = (n0 + wid + (kThreads / 64) * it) * L - P;
 #pragma unroll
             for (int r = 0; r < kXr; ++r)
                 if (lane + 64 * r < kActX) xw[lane + 64 * r] = xin[it][r];
             __builtin_amdgcn_wave_barrier();
-            float2 v[4];
             if (p0 >= 6 && p0 + kActX - 6 <= T) {
                 // interior window: no index is clamped.  Lane l evaluates the
                 // pairs j = 4l .. 4l + 3 from xw[4l .. 4l + 9] and the outputs
@@ -281,51 +300,56 @@ __global__ __launch_bounds__(kThreads) void fft_fwd_kernel(const float* __restri
                 }
                 __builtin_amdgcn_wave_barrier();
 #pragma unroll
-                for (int r = 0; r < 4; ++r) v[r] = make_float2(xw[lane + 64 * r], 0.f);
+                for (int r = 0; r < 4; ++r) av[r] = xw[lane + 64 * r];
             } else {
                 // a window at a row end: clamped indices, the boundary pairs
 #pragma unroll
-            for (int r = 0; r < (kActQ + 63) / 64; ++r) {
-                const int j = lane + 64 * r;
-                if (j < kActQ - 2) {
-                    const int q = p0 - 3 + j;
-                    const int qc = min(max(q, 0), T - 1);
-                    const float* xq = xw + (qc - p0 + 6);
-                    float e = 0.f, o = 0.f;
+                for (int r = 0; r < (kActQ + 63) / 64; ++r) {
+                    const int j = lane + 64 * r;
+                    if (j < kActQ - 2) {
+                        const int q = p0 - 3 + j;
+                        const int qc = min(max(q, 0), T - 1);
+                        const float* xq = xw + (qc - p0 + 6);
+                        float e = 0.f, o = 0.f;
 #pragma unroll
-                    for (int k = 0; k < 6; ++k) {
-                        e = fmaf(act.taps.up2[2 * k + 1], xq[2 - k], e);
-                        o = fmaf(act.taps.up2[2 * k], xq[3 - k], o);
+                        for (int k = 0; k < 6; ++k) {
+                            e = fmaf(act.taps.up2[2 * k + 1], xq[2 - k], e);
+                            o = fmaf(act.taps.up2[2 * k], xq[3 - k], o);
+                        }
+                        if (q < 0) o = e;
+                        if (q > T - 1) e = o;
+                        se[j] = snake_beta(e, alpha_rev, inv_beta);
+                        so[j] = snake_beta(o, alpha_rev, inv_beta);
                     }
-                    if (q < 0) o = e;
-                    if (q > T - 1) e = o;
-                    se[j] = snake_beta(e, alpha_rev, inv_beta);
-                    so[j] = snake_beta(o, alpha_rev, inv_beta);
+                }
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int u = lane + 64 * r;
+                    float acc = 0.f;
+#pragma unroll
+                    for (int m = 0; m < 6; ++m) {
+                        acc = fmaf(act.taps.down[2 * m], so[u + m], acc);
+                        acc = fmaf(act.taps.down[2 * m + 1], se[u + m + 1], acc);
+                    }
+                    const int p = p0 + u;
+                    av[r] = (p >= 0 && p < T) ? acc : 0.f;
                 }
             }
             __builtin_amdgcn_wave_barrier();
+        };
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int u = lane + 64 * r;
-                float acc = 0.f;
+        for (int pr = 0; pr < kPerWave / 2; ++pr) {
+            const int g1 = wid + (kThreads / 64) * (2 * pr), g2 = g1 + kThreads / 64;
+            if (n0 + g1 >= nb) break;  // wave-uniform
+            float a1[4], a2[4] = {0.f, 0.f, 0.f, 0.f};
+            act_col(2 * pr, a1);
+            if (n0 + g2 < nb) act_col(2 * pr + 1, a2);
+            float2 v[4];
 #pragma unroll
-                for (int m = 0; m < 6; ++m) {
-                    acc = fmaf(act.taps.down[2 * m], so[u + m], acc);
-                    acc = fmaf(act.taps.down[2 * m + 1], se[u + m + 1], acc);
-                }
-                const int p = p0 + u;
-                v[r] = make_float2((p >= 0 && p < T) ? acc : 0.f, 0.f);
-            }
-            }
-            __builtin_amdgcn_wave_barrier();
+            for (int r = 0; r < 4; ++r) v[r] = make_float2(a1[r], a2[r]);
             fft256(v, lane, buf[wid], lt);
-            if (lane == 0) {
-                res[0][g] = make_float2(v[0].x, v[2].x);
-                res[64][g] = v[1];
-            } else {
-                res[lane][g] = v[0];
-                res[lane + 64][g] = v[1];
-            }
+            store_pair(v, g1, g2);
         }
     }
     __syncthreads();
@@ -393,32 +417,46 @@ __global__ __launch_bounds__(kThreads) void fft_inv_kernel(const float2* __restr
             ov[it][q] = (ok && accumulate) ? y[row + t] : 0.f;
         }
     }
-#pragma unroll
-    for (int it = 0; it < kPerWave; ++it) {
-        const int g = wid + (kThreads / 64) * it;
-        const int n = n0 + g;
-        if (n >= nb) break;  // wave-uniform
-        // Z = conj(Y) on bins 0..N/2, Z_k = Y_{N-k} above
+    // Z = conj(Y) on bins 0..N/2, Z_k = Y_{N-k} above, for column g in lane
+    // j's order (k = j + 64 q)
+    auto spectrum = [&](int g, float2 (&z)[4]) {
         const float2 s0 = res[0][g];
-        float2 v[4];
         if (lane == 0) {
-            v[0] = make_float2(s0.x, 0.f);
-            v[2] = make_float2(s0.y, 0.f);
+            z[0] = make_float2(s0.x, 0.f);
+            z[2] = make_float2(s0.y, 0.f);
         } else {
             const float2 a = res[lane][g];
-            v[0] = make_float2(a.x, -a.y);
-            v[2] = res[128 - lane][g];
+            z[0] = make_float2(a.x, -a.y);
+            z[2] = res[128 - lane][g];
         }
         const float2 a1 = res[lane + 64][g];
-        v[1] = make_float2(a1.x, -a1.y);
-        v[3] = res[64 - lane][g];
+        z[1] = make_float2(a1.x, -a1.y);
+        z[3] = res[64 - lane][g];
+    };
+    auto store = [&](int it, int n, int q, float val) {
+        const int u = lane + 64 * q;
+        const int t = n * L + u;
+        if (u < L && t < T)
+            y[row + t] = fmaf(fmaf(val, inv_n, bo) + rv[it][q], out_scale, ov[it][q]);
+    };
+    // two blocks per transform: both results are real, so the transform of
+    // Z1 + i Z2 carries block 1 in its real part and block 2 in its imaginary
+    // part
+#pragma unroll
+    for (int pr = 0; pr < kPerWave / 2; ++pr) {
+        const int g1 = wid + (kThreads / 64) * (2 * pr), g2 = g1 + kThreads / 64;
+        const int n1 = n0 + g1, n2 = n0 + g2;
+        if (n1 >= nb) break;  // wave-uniform
+        float2 z1[4], z2[4], v[4];
+        spectrum(g1, z1);
+        spectrum(g2, z2);  // zeros past the row's last block
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = make_float2(z1[q].x - z2[q].y, z1[q].y + z2[q].x);
         fft256(v, lane, buf[wid], lt);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int u = lane + 64 * q;
-            const int t = n * L + u;
-            if (u < L && t < T)
-                y[row + t] = fmaf(fmaf(v[q].x, inv_n, bo) + rv[it][q], out_scale, ov[it][q]);
+            store(2 * pr, n1, q, v[q].x);
+            if (n2 < nb) store(2 * pr + 1, n2, q, v[q].y);
         }
     }
 }
