@@ -98,7 +98,8 @@ bool amp_fusable(int C, int K, int n_dil, const int* dil) {
 // pw1/pw2 (packed weights, or null) select the fused one-launch-per-step
 // path; otherwise each step is act1d, conv1d, act1d, conv1d launches.
 // fw1/fw2 (per dilation step; null, or null entries, for the direct
-// kernels) are frequency-domain weights from launch_fft_pack: that
+// kernels) are frequency-domain weights from launch_fft_pack: where
+// plan::fft_amp_use takes the shape, that
 // activation + convolution then runs as launch_conv1d_fft with the
 // activation inside its forward transforms, the spectra in t1 and t2 (slots
 // of at least plan::fft_spectrum_bytes each).
@@ -127,9 +128,11 @@ int run_amp(const float* x, float* y, int B, int C, int T, int K, int n_dil, con
         const int d = dil[q];
         ConvEpilogue e1{b1[q], nullptr, 1.0f, 0};
         // h = conv1(act(src)) lands in t2 either way
-        if (fw1 && fw1[q]) {
+        const bool f1 = fw1 && fw1[q] && avae::plan::fft_amp_use(B, C, T, K, d);
+        const bool f2 = fw2 && fw2[q] && avae::plan::fft_amp_use(B, C, T, K, 1);
+        if (f1) {
             // act(src) inside the transforms: spectrum in t1, product in t2,
-            // output in t1, moved to t2 by the next step's choice below
+            // output in t1
             AVAE_TRY(avae::launch_conv1d_fft(src, t1, fw1[q], B, C, C, T, K, d, e1, t1, t2, s,
                                              la[2 * q], lb[2 * q], &taps),
                      "act + conv1d_fft (convs1)");
@@ -140,12 +143,12 @@ int run_amp(const float* x, float* y, int B, int C, int T, int K, int n_dil, con
                                          s),
                      "conv1d (convs1)");
         }
-        float* h = (fw1 && fw1[q]) ? t1 : t2;   // conv1's output
-        float* fr = (fw1 && fw1[q]) ? t2 : t1;  // the other scratch slot
+        float* h = f1 ? t1 : t2;   // conv1's output
+        float* fr = f1 ? t2 : t1;  // the other scratch slot
         const bool last = (q == n_dil - 1);
         ConvEpilogue e2{b2[q], src, last ? out_scale : 1.0f, last ? accumulate : 0};
         float* dst = last ? y : cur;
-        if (fw2 && fw2[q]) {
+        if (f2) {
             // act(h) inside the transforms: spectrum in fr, product in h,
             // then dst (+ residual src)
             AVAE_TRY(avae::launch_conv1d_fft(h, dst, fw2[q], B, C, C, T, K, 1, e2, fr, h, s,
@@ -509,7 +512,7 @@ struct avae_decoder {
     const float* pw1[AVAE_MAX_STAGES][AVAE_MAX_KERNELS][AVAE_MAX_DIL] = {};
     const float* pw2[AVAE_MAX_STAGES][AVAE_MAX_KERNELS][AVAE_MAX_DIL] = {};
     void* pblob = nullptr;
-    // frequency-domain weights of the AMP convolutions that plan::fft_amp_conv
+    // frequency-domain weights of the AMP convolutions that plan::fft_amp_pack
     // selects (else null)
     const float* fw1[AVAE_MAX_STAGES][AVAE_MAX_KERNELS][AVAE_MAX_DIL] = {};
     const float* fw2[AVAE_MAX_STAGES][AVAE_MAX_KERNELS][AVAE_MAX_DIL] = {};
@@ -725,8 +728,8 @@ extern "C" int avae_decoder_create(const avae_config* cfg, const avae_weights* w
             const int co = c.ch[i + 1], K = c.rb_k[j];
             const size_t per = round_up(avae::fft_conv_weight_floats(co, co) * sizeof(float), 256);
             for (int q = 0; q < c.n_dil; ++q) {
-                if (avae::plan::fft_amp_conv(co, K, c.rb_d[j][q])) fbytes += per;
-                if (avae::plan::fft_amp_conv(co, K, 1)) fbytes += per;
+                if (avae::plan::fft_amp_pack(co, K, c.rb_d[j][q])) fbytes += per;
+                if (avae::plan::fft_amp_pack(co, K, 1)) fbytes += per;
             }
         }
     if (fbytes) {
@@ -746,13 +749,13 @@ extern "C" int avae_decoder_create(const avae_config* cfg, const avae_weights* w
                     round_up(avae::fft_conv_weight_floats(co, co) * sizeof(float), 256);
                 for (int q = 0; q < c.n_dil && e == hipSuccess; ++q) {
                     const int dq = c.rb_d[j][q];
-                    if (avae::plan::fft_amp_conv(co, K, dq)) {
+                    if (avae::plan::fft_amp_pack(co, K, dq)) {
                         e = avae::launch_fft_pack(d->w.w1[i][j][q], (float*)fp, co, co, K, dq,
                                                   nullptr);
                         d->fw1[i][j][q] = (const float*)fp;
                         fp += per;
                     }
-                    if (e == hipSuccess && avae::plan::fft_amp_conv(co, K, 1)) {
+                    if (e == hipSuccess && avae::plan::fft_amp_pack(co, K, 1)) {
                         e = avae::launch_fft_pack(d->w.w2[i][j][q], (float*)fp, co, co, K, 1,
                                                   nullptr);
                         d->fw2[i][j][q] = (const float*)fp;

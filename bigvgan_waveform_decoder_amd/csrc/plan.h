@@ -77,12 +77,27 @@ inline size_t fft_spectrum_bytes(int B, int C, int T, int K, int d) {
     return tensor_bytes((long long)kFftSlots * 2, C, s.NP);
 }
 
-// The decoders' AMP convolutions that run in the frequency domain: 96 or
-// more channels (the transforms' cost per sample is then small against the
-// channel mixing) and 7 or more taps (where the transform form needs fewer
-// multiply-adds than the direct one: ~2 per output and channel pair, against K).
-inline bool fft_amp_conv(int C, int K, int d) {
-    return C >= 96 && K >= 7 && fft_supported(C, C, K, d);
+// The decoders' AMP convolutions whose frequency-domain weights are kept:
+// 7 or more taps from 96 channels up (the transform form needs ~2
+// multiply-adds per output and channel pair against K, and the transforms'
+// cost per sample is small against the channel mixing), and 3 taps from 192
+// to 512 channels (there the saving is 3 against 2 and the fused
+// activation's; wider, the frequency-domain weights of one convolution pass
+// 270 MB).
+inline bool fft_amp_pack(int C, int K, int d) {
+    if (!fft_supported(C, C, K, d)) return false;
+    return K >= 7 ? C >= 96 : (K >= 3 && C >= 192 && C <= 512);
+}
+
+// Whether a kept convolution runs in the frequency domain for B rows of T
+// samples: always with 7 or more taps; with 3 only when there are at least
+// 64 columns (blocks x rows), below which the product streams its weights
+// faster than it can use them and the direct form wins.
+inline bool fft_amp_use(int B, int C, int T, int K, int d) {
+    if (!fft_amp_pack(C, K, d)) return false;
+    if (K >= 7) return true;
+    const FftShape s = fft_shape(B, T, K, d);
+    return s.ntiles > 0 && s.NB >= 64;
 }
 
 // Bytes of one decode workspace slot: the largest activation of the decode
@@ -104,10 +119,11 @@ inline size_t decode_slot_bytes(const avae_config& c, int B, const long long* T)
         upd(co, T[i + 1]);
         for (int j = 0; j < c.n_kernels; ++j) {
             const int K = c.rb_k[j];
-            if (fft_amp_conv(co, K, 1)) keep(fft_spectrum_bytes(B, co, (int)T[i + 1], K, 1));
+            const int t = (int)T[i + 1];
+            if (fft_amp_use(B, co, t, K, 1)) keep(fft_spectrum_bytes(B, co, t, K, 1));
             for (int q = 0; q < c.n_dil; ++q)
-                if (fft_amp_conv(co, K, c.rb_d[j][q]))
-                    keep(fft_spectrum_bytes(B, co, (int)T[i + 1], K, c.rb_d[j][q]));
+                if (fft_amp_use(B, co, t, K, c.rb_d[j][q]))
+                    keep(fft_spectrum_bytes(B, co, t, K, c.rb_d[j][q]));
         }
     }
     return over ? 0 : m;

@@ -114,10 +114,15 @@ int main() {
               "fft shape 384");
         CHECK(b.nb == 98 && b.NB == 196 && b.ntiles == 2 && b.NJ == 7 && b.NP == 224,
               "fft shape 192");
-        CHECK(fft_amp_conv(384, 11, 5) && fft_amp_conv(192, 7, 1) && fft_amp_conv(96, 11, 5) &&
-                  !fft_amp_conv(48, 11, 5) && !fft_amp_conv(384, 3, 1) &&
-                  !fft_amp_conv(100, 7, 1) && !fft_amp_conv(384, 11, 13),
+        CHECK(fft_amp_pack(384, 11, 5) && fft_amp_pack(192, 7, 1) && fft_amp_pack(96, 11, 5) &&
+                  !fft_amp_pack(48, 11, 5) && fft_amp_pack(384, 3, 1) && !fft_amp_pack(768, 3, 1) &&
+                  !fft_amp_pack(96, 3, 1) && !fft_amp_pack(100, 7, 1) &&
+                  !fft_amp_pack(384, 11, 13),
               "fft selection");
+        // 3 taps: the 384-channel stage (2 x 40 columns) yes, 2 x 8 columns no
+        CHECK(fft_amp_use(2, 384, 10000, 3, 1) && !fft_amp_use(2, 384, 2000, 3, 1) &&
+                  fft_amp_use(2, 384, 2000, 11, 5),
+              "fft use");
     }
     // the column plan over many sizes: every column covered, at most 8 MFMA
     // tiles of 16 per workgroup, fewer than 16 padding columns per tile
