@@ -138,14 +138,24 @@ def test_dav_bwe_and_tail_ops_reject_bad_arguments():
 
 def test_kernel_names_in_the_profiler_are_stable():
     """bench.py's traffic lookup keys on the names the library's launch
-    profiler gives its kernels (conv.hip, act1d.hip, amp_unit.hip)."""
+    profiler gives its kernels, each with the source file it is built from."""
     import json
     d = json.load(open(os.path.join(ROOT, "profiles", "pmc_traffic.json")))
-    pat = (r"(conv1d_(pipe|dma)_kernel<\d+,\d+,\d+,\d+,\d+,\d+>"
-           r"|act1d_kernel|amp_unit_kernel<\d+,\d+>)$")
+    src = {
+        "conv.hip": (r"(conv1d_(pipe|dma|mfma)_kernel<\d+(,\d+)*(,d\d+)?(,snake)?>"
+                     r"|convtr1d_(dma|poly|mfma)_kernel<\d+(,\d+)*>|conv_out1_kernel"
+                     r"|sum_into_kernel)$"),
+        "fftconv.hip": r"(fft_fwd_kernel(<act>)?|fft_inv_kernel|fft_pack_kernel|fft_gemm_kernel<\d>)$",
+        "act1d.hip": r"act1d_kernel$",
+        "amp_unit.hip": r"(amp_unit_kernel<\d+,\d+>|pack_unit_weights_kernel)$",
+    }
     for name, e in d["kernels"].items():
-        assert re.match(pat, name), name
+        f = os.path.basename(e["source"])
+        assert f in src, (name, f)
+        assert re.match(src[f], name), (name, f)
         assert os.path.exists(os.path.join(ROOT, e["source"]))
+        text = open(os.path.join(ROOT, e["source"])).read()
+        assert name.split("<")[0] in text, name
 
 
 def test_amp_block_static_checks_before_any_launch():
