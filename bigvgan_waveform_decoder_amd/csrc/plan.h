@@ -78,15 +78,15 @@ inline size_t fft_spectrum_bytes(int B, int C, int T, int K, int d) {
 }
 
 // The decoders' AMP convolutions whose frequency-domain weights are kept:
-// 7 or more taps from 96 channels up (the transform form needs ~2
-// multiply-adds per output and channel pair against K, and the transforms'
-// cost per sample is small against the channel mixing), and 3 taps from 192
-// to 512 channels (there the saving is 3 against 2 and the fused
-// activation's; wider, the frequency-domain weights of one convolution pass
-// 270 MB).
+// 7 or more taps from 48 channels up (the transform form needs ~2
+// multiply-adds per output and channel pair against K, and with the
+// activation inside the forward transforms it also saves the activation's
+// own pass), and 3 taps from 192 to 512 channels (there the saving is 3
+// against 2 and the fused activation's; wider, the frequency-domain weights
+// of one convolution pass 270 MB).
 inline bool fft_amp_pack(int C, int K, int d) {
     if (!fft_supported(C, C, K, d)) return false;
-    return K >= 7 ? C >= 96 : (K >= 3 && C >= 192 && C <= 512);
+    return K >= 7 ? C >= 48 : (K >= 3 && C >= 192 && C <= 512);
 }
 
 // Whether a kept convolution runs in the frequency domain for B rows of T

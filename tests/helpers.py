@@ -130,7 +130,7 @@ def dav_reach_frames(spec) -> int:
 def runs_fft_convs(spec) -> bool:
     """Whether the library may run some of this decoder's AMP convolutions in
     the frequency domain (overlap-save, 256-point transforms): widths a
-    multiple of 16 with (K-1) d <= 128, from 96 channels with 7 or more taps,
+    multiple of 16 with (K-1) d <= 128, from 48 channels with 7 or more taps,
     from 192 to 512 channels with 3 (those only on long enough rows).  The
     block framing then follows the sequence start, so decodes of crops
     (streaming tiles) round differently from the whole sequence there."""
@@ -141,6 +141,6 @@ def runs_fft_convs(spec) -> bool:
         for k, dil in zip(spec.rb_k, spec.rb_d):
             if not any((k - 1) * d <= 128 for d in tuple(dil) + (1,)):
                 continue
-            if (k >= 7 and c >= 96) or (k >= 3 and 192 <= c <= 512):
+            if (k >= 7 and c >= 48) or (k >= 3 and 192 <= c <= 512):
                 return True
     return False

@@ -115,7 +115,8 @@ int main() {
         CHECK(b.nb == 98 && b.NB == 196 && b.ntiles == 2 && b.NJ == 7 && b.NP == 224,
               "fft shape 192");
         CHECK(fft_amp_pack(384, 11, 5) && fft_amp_pack(192, 7, 1) && fft_amp_pack(96, 11, 5) &&
-                  !fft_amp_pack(48, 11, 5) && fft_amp_pack(384, 3, 1) && !fft_amp_pack(768, 3, 1) &&
+                  fft_amp_pack(48, 11, 5) && !fft_amp_pack(32, 11, 5) &&
+                  fft_amp_pack(384, 3, 1) && !fft_amp_pack(768, 3, 1) &&
                   !fft_amp_pack(96, 3, 1) && !fft_amp_pack(100, 7, 1) &&
                   !fft_amp_pack(384, 11, 13),
               "fft selection");

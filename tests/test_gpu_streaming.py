@@ -12,9 +12,10 @@ from tests.helpers import decoder_params, decoder_reach_frames, rel_err, runs_ff
 
 pytestmark = pytest.mark.gpu
 # Tiled vs whole where frequency-domain convolutions run (the 256-point block
-# framing follows the crop): measured on MI355X 1.79e-4 (h3-c256, 90 frames in
-# 17-frame tiles); the bar is twice that, rounded up.
-TILE_FFT_BAR = 4e-4
+# framing follows the crop): measured on MI355X 1.94e-4 (h3-c256, 90 frames in
+# 17-frame tiles), 2.71e-4 (ltx-c128, 140 in 40), 4.22e-4 (h3-c128, 160 in 11);
+# the bar is twice the largest, rounded up.
+TILE_FFT_BAR = 9e-4
 
 
 @pytest.mark.parametrize("name,spec,frames,tile", [
@@ -64,7 +65,11 @@ def test_streaming_halo_matters():
     zd = cuda(z)
     whole = host(dec.decode(zd))
     assert rel_err(host(dec.decode_streaming(zd, 10, halo_frames=0)), whole) > 1e-3
-    np.testing.assert_array_equal(host(dec.decode_streaming(zd, 10)), whole)
+    tiled = host(dec.decode_streaming(zd, 10))
+    if runs_fft_convs(spec):
+        assert rel_err(tiled, whole) <= TILE_FFT_BAR
+    else:
+        np.testing.assert_array_equal(tiled, whole)
 
 
 def test_streaming_workload4_full_size():
@@ -83,8 +88,8 @@ def test_streaming_workload4_full_size():
     # sequence (370 frames) round differently: the frequency-domain stages
     # frame their 256-point blocks from the crop's start, and some direct
     # stages select other tilings.  The later stages' gain carries it forward:
-    # measured on MI355X 4.47e-4 (1.36e-4 with direct convolutions only); the
-    # bar is twice that, rounded up.
+    # measured on MI355X 4.5-4.9e-4 (1.36e-4 with direct convolutions only);
+    # the bar is twice that, rounded up.
     e = rel_err(tiled, whole)
     print(f"tiled vs whole at full width: {e:.3e}", flush=True)
     assert e <= 1e-3
