@@ -464,15 +464,15 @@ __global__ __launch_bounds__(kThreads) void fft_inv_kernel(const float2* __restr
 // ---------------------------------------------------------------------------
 // Y[slot] = W[slot] X[slot]: per slot a complex [Cout x Cin] x [Cin x NP]
 // product on the matrix cores.  Workgroup: one slot, 64 output rows (16 per
-// wave; Cout a multiple of 16), NT = 16 NJ columns.  A operands (W) come pre-packed in MFMA
-// fragment order, wp[slot][o/16][c/16][re,im][lane][4] (4 consecutive
+// wave; Cout a multiple of 16), NT = 16 NJ columns.  A operands (W) come
+// pre-packed in MFMA fragment order, wp[slot][o/16][c/16][re,im][lane][4] (4 consecutive
 // k-steps per lane per 16-byte load), read straight from memory one
 // 16-channel chunk ahead.  B operands (X) go to LDS by LDS DMA
 // (global_load_lds_dwordx4: no register round trip), 16 channels per chunk,
 // double-buffered, rows of NT complex back to back; each wave reads its B
 // fragments one k-step ahead of the matrix instructions that use them.
-// Slot 0 holds two real bins (re: bin 0, im: bin N/2): its operands are
-// chosen so that the same four products give W0 X0 and W128 X128.  The
+// Three real products per complex multiply-add (Gauss); slot 0 holds two
+// real bins (re: bin 0, im: bin N/2), whose products are the first two.  The
 // blockIdx -> tile map keeps each XCD on a contiguous range of slots, so a
 // slot's X is fetched into one L2.
 __device__ __forceinline__ void wait_vmem_all() {
@@ -526,14 +526,18 @@ __global__ __launch_bounds__(kThreads, 2) void fft_gemm_kernel(const float* __re
         }
     };
 
-    f32x4 accR[NJ], accI[NJ];
+    // Gauss's three real products per complex multiply-add:
+    //   P1 = Wr Xr, P2 = Wi Xi, P3 = (Wr + Wi)(Xr + Xi);
+    //   Re Y = P1 - P2, Im Y = P3 - P1 - P2
+    // (the sums formed in registers, one add per operand).  Slot 0's two
+    // real bins are P1 (bin 0) and P2 (bin N/2).
+    f32x4 p1a[NJ], p2a[NJ], p3a[NJ];
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt) {
-        accR[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        accI[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        p1a[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        p2a[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        p3a[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // operand selection: general slots (Wr, Wi, -Wi, Wr), slot 0 (W0, 0, 0, W128)
-    const float sel = (f == 0) ? 0.f : 1.f;
     const int brow = lane >> 4, bcol = lane & 15;
     f32x4 ar, ai;
     // one chunk: matrix work on chunk ch from Bc while chunk ch + 1 lands in Bn
@@ -557,22 +561,17 @@ __global__ __launch_bounds__(kThreads, 2) void fft_gemm_kernel(const float* __re
                 for (int jt = 0; jt < NJ; ++jt) bv[c ^ 1][jt] = bb[(4 * (ks + 1)) * NT + 16 * jt];
             }
             __builtin_amdgcn_sched_barrier(0);
-            const float p1 = ar[ks];
-            const float p2 = sel * ai[ks];
-            const float p3 = -p2;
-            const float p4 = (f == 0) ? ai[ks] : p1;
+            const float wr = ar[ks], wi = ai[ks], ws = wr + wi;
 #pragma unroll
             for (int jt = 0; jt < NJ; ++jt)
-                accR[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(p1, bv[c][jt].x, accR[jt], 0, 0, 0);
+                p1a[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(wr, bv[c][jt].x, p1a[jt], 0, 0, 0);
 #pragma unroll
             for (int jt = 0; jt < NJ; ++jt)
-                accI[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(p2, bv[c][jt].x, accI[jt], 0, 0, 0);
+                p2a[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(wi, bv[c][jt].y, p2a[jt], 0, 0, 0);
 #pragma unroll
             for (int jt = 0; jt < NJ; ++jt)
-                accR[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(p3, bv[c][jt].y, accR[jt], 0, 0, 0);
-#pragma unroll
-            for (int jt = 0; jt < NJ; ++jt)
-                accI[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(p4, bv[c][jt].y, accI[jt], 0, 0, 0);
+                p3a[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ws, bv[c][jt].x + bv[c][jt].y,
+                                                               p3a[jt], 0, 0, 0);
         }
         // the next chunk's DMA and A operands have landed; every wave is done
         // with Bc before it is refilled
@@ -593,11 +592,15 @@ __global__ __launch_bounds__(kThreads, 2) void fft_gemm_kernel(const float* __re
     // D layout: lane l holds rows 4 (l / 16) + i, column l % 16 of each tile
     if (!rows_ok) return;
     float2* yo = yf + ((size_t)f * Cout + 16 * ot + 4 * brow) * NP + n0 + bcol;
+    const bool dc = (f == 0);
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            yo[(size_t)i * NP + 16 * jt] = make_float2(accR[jt][i], accI[jt][i]);
+        for (int i = 0; i < 4; ++i) {
+            const float a = p1a[jt][i], b = p2a[jt][i];
+            yo[(size_t)i * NP + 16 * jt] =
+                dc ? make_float2(a, b) : make_float2(a - b, p3a[jt][i] - (a + b));
+        }
 }
 
 // ---------------------------------------------------------------------------
@@ -703,13 +706,13 @@ hipError_t launch_conv1d_fft(const float* x, float* y, const float* wp, int B, i
     }
     e = hipGetLastError();
     {
-        // algorithmic: 127 complex slots (4 real products each) + slot 0 (2),
-        // one multiply-add = 2 flops, over the real columns
+        // algorithmic: 127 complex slots (3 real products each, Gauss) + slot
+        // 0 (2), one multiply-add = 2 flops, over the real columns
         static const char* names[8] = {"fft_gemm_kernel<1>", "fft_gemm_kernel<2>",
                                        "fft_gemm_kernel<3>", "fft_gemm_kernel<4>",
                                        "fft_gemm_kernel<5>", "fft_gemm_kernel<6>",
                                        "fft_gemm_kernel<7>", "fft_gemm_kernel<8>"};
-        const double macs = (127.0 * 4.0 + 2.0) * Cout * (double)Cin * blocks;
+        const double macs = (127.0 * 3.0 + 2.0) * Cout * (double)Cin * blocks;
         const double bytes = 8.0 * kSlots * (double)Cout * Cin +
                              8.0 * kSlots * (double)(Cin + Cout) * blocks;
         prof_post(s, names[sh.NJ - 1], 2.0 * macs, bytes);
