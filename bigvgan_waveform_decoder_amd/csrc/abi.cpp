@@ -1105,6 +1105,10 @@ struct avae_dav {
     avae_dav_config cfg;
     avae_dav_weights w;  // pointers into `blob`
     void* blob = nullptr;
+    // frequency-domain weights of the units' first (dilated) convolutions
+    // that plan::fft_amp_pack selects (else null)
+    const float* fw1[AVAE_MAX_STAGES][AVAE_MAX_DIL] = {};
+    void* fblob = nullptr;
     int device = 0;
 };
 
@@ -1145,17 +1149,27 @@ int dav_lengths(const avae_dav_config& c, int frames, long long* T) {
     return 0;
 }
 
-// One workspace slot: the largest [2B, C, T] activation of the decode.
-// Largest activation of the 2 B side passes (0 if its size overflows).
+// One workspace slot: the largest [2B, C, T] activation of the 2 B side
+// passes, or the largest spectrum of a unit convolution run in the
+// frequency domain (0 if a size overflows).
 size_t dav_slot_bytes(const avae_dav_config& c, int B, const long long* T) {
     const long long B2 = 2LL * B;
     size_t m = avae::plan::tensor_bytes(B2, std::max(c.dec_in_ch, c.ch[0]), T[0]);
-    bool over = m == 0;
-    for (int i = 0; i < c.n_stages; ++i) {
+    bool over = m == 0 || B2 > 0x3fffffffLL;
+    for (int i = 0; i < c.n_stages && !over; ++i) {
         const size_t a = avae::plan::tensor_bytes(B2, c.ch[i], T[i]);
         const size_t b = avae::plan::tensor_bytes(B2, c.ch[i + 1], T[i + 1]);
         over = over || a == 0 || b == 0;
         m = std::max(m, std::max(a, b));
+        for (int u = 0; u < c.n_units; ++u)
+            if (avae::plan::fft_amp_use((int)B2, c.ch[i + 1], (int)T[i + 1], c.unit_k,
+                                        c.unit_dil[u])) {
+                const size_t f = avae::plan::fft_spectrum_bytes((int)B2, c.ch[i + 1],
+                                                                (int)T[i + 1], c.unit_k,
+                                                                c.unit_dil[u]);
+                over = over || f == 0;
+                m = std::max(m, f);
+            }
     }
     return over ? 0 : m;
 }
@@ -1212,14 +1226,23 @@ int dav_decode_impl(const avae_dav* dav, const float* latent, int B, int frames,
         avae::prof_set_phase(avae::kPhaseResblocks);
         for (int u = 0; u < c.n_units; ++u) {
             const int d = c.unit_dil[u];
-            // c1: the first Snake on its staged input, the second in its epilogue
+            // c1: the first Snake on its input, the second in its epilogue
             ConvEpilogue e1{w.b1[i][u], nullptr, 1.0f, 0, w.a2[i][u], w.a1[i][u]};
-            AVAE_TRY(avae::launch_conv1d(P0, P2, w.w1[i][u], B2, co, co, To, To, c.unit_k, d,
-                                         (c.unit_k - 1) / 2 * d, e1, s),
-                     "dav unit conv");
+            float* h = P2;  // c1's output
+            if (dav->fw1[i][u] && avae::plan::fft_amp_use(B2, co, To, c.unit_k, d)) {
+                // frequency domain: spectrum in P1, product in P2, output in P1
+                AVAE_TRY(avae::launch_conv1d_fft(P0, P1, dav->fw1[i][u], B2, co, co, To,
+                                                 c.unit_k, d, e1, P1, P2, s),
+                         "dav unit conv_fft");
+                h = P1;
+            } else {
+                AVAE_TRY(avae::launch_conv1d(P0, P2, w.w1[i][u], B2, co, co, To, To, c.unit_k, d,
+                                             (c.unit_k - 1) / 2 * d, e1, s),
+                         "dav unit conv");
+            }
             // c2 (one tap) plus the residual, in place on the running activation
             ConvEpilogue e2{w.b2[i][u], P0, 1.0f, 0, nullptr, nullptr};
-            AVAE_TRY(avae::launch_conv1d(P2, P0, w.w2[i][u], B2, co, co, To, To, 1, 1, 0, e2, s),
+            AVAE_TRY(avae::launch_conv1d(h, P0, w.w2[i][u], B2, co, co, To, To, 1, 1, 0, e2, s),
                      "dav unit 1-tap conv");
         }
         if (trace && trace[1 + i])
@@ -1307,17 +1330,51 @@ extern "C" int avae_dav_create(const avae_dav_config* cfg, const avae_dav_weight
         *it.first = (const float*)p;
         p += round_up(n * sizeof(float), 256);
     }
+    // frequency-domain copies of the units' dilated convolutions
+    size_t fbytes = 0;
+    for (int i = 0; i < c.n_stages; ++i)
+        for (int u = 0; u < c.n_units; ++u)
+            if (avae::plan::fft_amp_pack(c.ch[i + 1], c.unit_k, c.unit_dil[u]))
+                fbytes += round_up(
+                    avae::fft_conv_weight_floats(c.ch[i + 1], c.ch[i + 1]) * sizeof(float), 256);
+    if (fbytes) {
+        e = hipMalloc(&d->fblob, fbytes);
+        if (e != hipSuccess) {
+            (void)hipFree(d->blob);
+            delete d;
+            return fail(AVAE_ENOMEM, "avae_dav_create: hipMalloc(%zu): %s", fbytes,
+                        hipGetErrorString(e));
+        }
+        char* fp = (char*)d->fblob;
+        for (int i = 0; i < c.n_stages && e == hipSuccess; ++i)
+            for (int u = 0; u < c.n_units && e == hipSuccess; ++u) {
+                const int co = c.ch[i + 1];
+                if (!avae::plan::fft_amp_pack(co, c.unit_k, c.unit_dil[u])) continue;
+                e = avae::launch_fft_pack(d->w.w1[i][u], (float*)fp, co, co, c.unit_k,
+                                          c.unit_dil[u], nullptr);
+                d->fw1[i][u] = (const float*)fp;
+                fp += round_up(avae::fft_conv_weight_floats(co, co) * sizeof(float), 256);
+            }
+        if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
+        if (e != hipSuccess) {
+            (void)hipFree(d->fblob);
+            (void)hipFree(d->blob);
+            delete d;
+            return hip_fail(e, "avae_dav_create: frequency-domain weights");
+        }
+    }
     *out = d;
     return AVAE_OK;
 }
 
 extern "C" void avae_dav_destroy(avae_dav* dav) {
     if (!dav) return;
-    if (dav->blob) {
+    if (dav->blob || dav->fblob) {
         int cur = 0;
         (void)hipGetDevice(&cur);
         (void)hipSetDevice(dav->device);
-        (void)hipFree(dav->blob);
+        if (dav->blob) (void)hipFree(dav->blob);
+        if (dav->fblob) (void)hipFree(dav->fblob);
         (void)hipSetDevice(cur);
     }
     delete dav;

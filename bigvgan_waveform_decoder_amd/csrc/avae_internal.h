@@ -65,10 +65,11 @@ hipError_t launch_convtr1d(const float* x, float* y, const float* w, const float
 // Conv1d through 256-point overlap-save transforms (fftconv.hip), "same"
 // padding, shapes that plan::fft_supported takes.  wp holds
 // fft_conv_weight_floats(Cin, Cout) floats from launch_fft_pack; xspec and
-// yspec plan::fft_spectrum_bytes(B, Cin | Cout, T, K, d) bytes each.  The
-// epilogue's Snake fields must be null.  With act_log_alpha, act_log_beta
-// and act_taps all given, the convolution's input is Activation1d(x) (as
-// launch_act1d computes it), evaluated inside the forward transforms.
+// yspec plan::fft_spectrum_bytes(B, Cin | Cout, T, K, d) bytes each.  With
+// act_log_alpha, act_log_beta and act_taps all given, the convolution's
+// input is Activation1d(x) (as launch_act1d computes it), evaluated inside
+// the forward transforms; else with ep.in_alpha, the plain Snake of x there.
+// ep.snake_alpha applies the plain Snake after the bias, as launch_conv1d.
 size_t fft_conv_weight_floats(int Cin, int Cout);
 hipError_t launch_fft_pack(const float* w, float* wp, int Cin, int Cout, int K, int dilation,
                            hipStream_t s);

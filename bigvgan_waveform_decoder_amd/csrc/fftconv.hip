@@ -140,12 +140,16 @@ constexpr int kActX = kN + 12;   // x window per transform (a multiple of 4)
 constexpr int kActQ = kN + 8;    // phase pairs per transform (kN + 6, padded to 16 bytes)
 
 struct ActIn {
-    const float* log_alpha;  // [C]
-    const float* log_beta;   // [C]
-    ActTaps taps;
+    const float* log_alpha;    // [C] (mode 1)
+    const float* log_beta;     // [C] (mode 1)
+    ActTaps taps;              // (mode 1)
+    const float* snake_alpha;  // [C] (mode 2)
 };
 
-template <bool ACT>
+// Input transform of the forward kernel: 0 none, 1 Activation1d (SnakeBeta
+// between the resampling filters), 2 plain Snake ([H3] Snake, the DAV units:
+// pointwise, alpha as stored).
+template <int MODE>
 __global__ __launch_bounds__(kThreads) void fft_fwd_kernel(const float* __restrict__ x,
                                                            float2* __restrict__ xf, int C, int T,
                                                            int L, int P, int nb, int NP,
@@ -153,6 +157,7 @@ __global__ __launch_bounds__(kThreads) void fft_fwd_kernel(const float* __restri
     __shared__ float2 tw[kN];
     __shared__ float2 buf[kThreads / 64][kN];
     __shared__ float2 res[kSlots][kCols + 1];
+    constexpr bool ACT = MODE == 1;
     __shared__ __align__(16) float aw[ACT ? kThreads / 64 : 1][ACT ? kActX + 2 * kActQ : 1];
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int b = blockIdx.z, c = blockIdx.y, n0 = blockIdx.x * kCols;
@@ -200,6 +205,21 @@ __global__ __launch_bounds__(kThreads) void fft_fwd_kernel(const float* __restri
             for (int r = 0; r < 4; ++r) {
                 const int t = u0 + 64 * r;
                 xin[it][r] = (t >= 0 && t < T) ? xr[t] : 0.f;
+            }
+        }
+        if constexpr (MODE == 2) {
+            // plain Snake of the samples inside the row (the zero padding
+            // outside stays zero)
+            const float a = act.snake_alpha[c];
+            const float arev = a * 0.15915494309189535f, inv = 1.0f / (a + 1e-9f);
+#pragma unroll
+            for (int it = 0; it < kPerWave; ++it) {
+                const int u0 = (n0 + wid + (kThreads / 64) * it) * L - P + lane;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = u0 + 64 * r;
+                    if (t >= 0 && t < T) xin[it][r] = snake_beta(xin[it][r], arev, inv);
+                }
             }
         }
 #pragma unroll
@@ -370,7 +390,8 @@ __global__ __launch_bounds__(kThreads) void fft_inv_kernel(const float2* __restr
                                                            float* y, int Cout, int T, int L, int nb,
                                                            int NP, const float* __restrict__ bias,
                                                            const float* residual, float out_scale,
-                                                           int accumulate) {
+                                                           int accumulate,
+                                                           const float* __restrict__ snake_alpha) {
     __shared__ float2 tw[kN];
     __shared__ float2 buf[kThreads / 64][kN];
     __shared__ float2 res[kSlots][kCols + 1];
@@ -399,6 +420,9 @@ __global__ __launch_bounds__(kThreads) void fft_inv_kernel(const float2* __restr
     __syncthreads();
     const LaneTwiddles lt = lane_twiddles(lane, tw);
     const float bo = bias ? bias[o] : 0.f;
+    // plain Snake after the bias, as the direct kernels' epilogue
+    const float sa = snake_alpha ? snake_alpha[o] : 0.f;
+    const float sa_rev = sa * 0.15915494309189535f, sa_inv = 1.0f / (sa + 1e-9f);
     const size_t row = ((size_t)b * Cout + o) * (size_t)T;
     constexpr float inv_n = 1.0f / (float)kN;  // exact (power of two)
     // the residual and previous-output values of this wave's outputs are read
@@ -436,8 +460,11 @@ __global__ __launch_bounds__(kThreads) void fft_inv_kernel(const float2* __restr
     auto store = [&](int it, int n, int q, float val) {
         const int u = lane + 64 * q;
         const int t = n * L + u;
-        if (u < L && t < T)
-            y[row + t] = fmaf(fmaf(val, inv_n, bo) + rv[it][q], out_scale, ov[it][q]);
+        if (u < L && t < T) {
+            float v = fmaf(val, inv_n, bo);
+            if (snake_alpha) v = snake_beta(v, sa_rev, sa_inv);
+            y[row + t] = fmaf(v + rv[it][q], out_scale, ov[it][q]);
+        }
     };
     // two blocks per transform: both results are real, so the transform of
     // Z1 + i Z2 carries block 1 in its real part and block 2 in its imaginary
@@ -666,7 +693,8 @@ hipError_t launch_conv1d_fft(const float* x, float* y, const float* wp, int B, i
                              int T, int K, int dilation, const ConvEpilogue& ep, float* xspec,
                              float* yspec, hipStream_t s, const float* act_log_alpha,
                              const float* act_log_beta, const ActTaps* act_taps) {
-    if (!plan::fft_supported(Cin, Cout, K, dilation) || ep.snake_alpha || ep.in_alpha)
+    const bool act = act_log_alpha && act_log_beta && act_taps;
+    if (!plan::fft_supported(Cin, Cout, K, dilation) || (act && ep.in_alpha))
         return hipErrorInvalidValue;
     const plan::FftShape sh = plan::fft_shape(B, T, K, dilation);
     if (sh.ntiles < 1 || sh.NJ < 1 || sh.NJ > 8) return hipErrorInvalidValue;
@@ -676,20 +704,23 @@ hipError_t launch_conv1d_fft(const float* x, float* y, const float* wp, int B, i
     const dim3 tg((unsigned)((sh.nb + kCols - 1) / kCols), 1, (unsigned)B);
     const double blocks = (double)sh.NB;
 
-    const bool act = act_log_alpha && act_log_beta && act_taps;
-    ActIn ai{act_log_alpha, act_log_beta, {}};
+    ActIn ai{act_log_alpha, act_log_beta, {}, ep.in_alpha};
     if (act) ai.taps = *act_taps;
+    const dim3 fg(tg.x, (unsigned)Cin, tg.z);
     prof_pre(s);
     if (act)
-        hipLaunchKernelGGL(fft_fwd_kernel<true>, dim3(tg.x, (unsigned)Cin, tg.z), dim3(kThreads),
-                           0, s, x, xf, Cin, T, sh.L, P, sh.nb, sh.NP, ai);
+        hipLaunchKernelGGL(fft_fwd_kernel<1>, fg, dim3(kThreads), 0, s, x, xf, Cin, T, sh.L, P,
+                           sh.nb, sh.NP, ai);
+    else if (ep.in_alpha)
+        hipLaunchKernelGGL(fft_fwd_kernel<2>, fg, dim3(kThreads), 0, s, x, xf, Cin, T, sh.L, P,
+                           sh.nb, sh.NP, ai);
     else
-        hipLaunchKernelGGL(fft_fwd_kernel<false>, dim3(tg.x, (unsigned)Cin, tg.z), dim3(kThreads),
-                           0, s, x, xf, Cin, T, sh.L, P, sh.nb, sh.NP, ai);
+        hipLaunchKernelGGL(fft_fwd_kernel<0>, fg, dim3(kThreads), 0, s, x, xf, Cin, T, sh.L, P,
+                           sh.nb, sh.NP, ai);
     hipError_t e = hipGetLastError();
     // algorithmic: x read once (4 B per sample), the spectrum written once
-    prof_post(s, act ? "fft_fwd_kernel<act>" : "fft_fwd_kernel",
-              act ? 52.0 * B * Cin * (double)T : 0.0,
+    prof_post(s, act ? "fft_fwd_kernel<act>" : ep.in_alpha ? "fft_fwd_kernel<snake>" : "fft_fwd_kernel",
+              act ? 52.0 * B * Cin * (double)T : ep.in_alpha ? 4.0 * B * Cin * (double)T : 0.0,
               4.0 * B * Cin * (double)T + 8.0 * kSlots * Cin * blocks);
     if (e != hipSuccess) return e;
 
@@ -722,7 +753,7 @@ hipError_t launch_conv1d_fft(const float* x, float* y, const float* wp, int B, i
     prof_pre(s);
     hipLaunchKernelGGL(fft_inv_kernel, dim3(tg.x, (unsigned)Cout, tg.z), dim3(kThreads), 0, s, yf,
                        y, Cout, T, sh.L, sh.nb, sh.NP, ep.bias, ep.residual, ep.out_scale,
-                       ep.accumulate);
+                       ep.accumulate, ep.snake_alpha);
     e = hipGetLastError();
     const double n = (double)B * Cout * T;
     prof_post(s, "fft_inv_kernel", 0.0,

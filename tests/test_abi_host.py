@@ -145,7 +145,8 @@ def test_kernel_names_in_the_profiler_are_stable():
         "conv.hip": (r"(conv1d_(pipe|dma|mfma)_kernel<\d+(,\d+)*(,d\d+)?(,snake)?>"
                      r"|convtr1d_(dma|poly|mfma)_kernel<\d+(,\d+)*>|conv_out1_kernel"
                      r"|sum_into_kernel)$"),
-        "fftconv.hip": r"(fft_fwd_kernel(<act>)?|fft_inv_kernel|fft_pack_kernel|fft_gemm_kernel<\d>)$",
+        "fftconv.hip": (r"(fft_fwd_kernel(<act>|<snake>)?|fft_inv_kernel|fft_pack_kernel"
+                        r"|fft_gemm_kernel<\d>)$"),
         "act1d.hip": r"act1d_kernel$",
         "amp_unit.hip": r"(amp_unit_kernel<\d+,\d+>|pack_unit_weights_kernel)$",
     }
