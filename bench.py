@@ -434,19 +434,25 @@ def amp_configs(torch, avae, W, steps, parity):
     td = {k: torch.from_numpy(v).to(dev) for k, v in t.items()}
     xd = torch.from_numpy(x).to(dev)
     yd = torch.empty_like(xd)
-    ws = torch.empty(avae.amp_block_workspace_bytes(*x.shape), dtype=torch.uint8, device=dev)
+    # the direct kernels first (workspace of avae_amp_block_workspace_bytes),
+    # then the frequency-domain convolutions (the larger workspace selects them)
     lists = _amp_lists(td, "block", 3)
+    ws = torch.empty(avae.amp_block_workspace_bytes(*x.shape), dtype=torch.uint8, device=dev)
+    ms_direct = _timed(torch, lambda: avae.amp_block(xd, 3, dil, *lists, out=yd, workspace=ws), n)
+    del ws
+    ws = torch.empty(avae.amp_block_fft_workspace_bytes(*x.shape, 3, dil), dtype=torch.uint8,
+                     device=dev)
     call = lambda: avae.amp_block(xd, 3, dil, *lists, out=yd, workspace=ws)
     ms = _timed(torch, call, n)
     kernels = _profiled(avae, call, n, 16)
     B, C, T = x.shape
-    convs = {k: v for k, v in kernels.items() if k.startswith("conv1d")}
-    cf = sum(v["flops"] for v in convs.values())
+    convs = {k: v for k, v in kernels.items() if k.startswith(("conv1d", "fft_"))}
+    cf = 6 * 2.0 * C * C * 3 * T * B * n  # direct-form multiply-adds x 2
     ct = sum(v["total_ms"] for v in convs.values()) / 1e3
     extra = {"workload": "one AMP block, [2,512,65536], k=3, d=(1,3,5)",
              "samples_per_s": B * T / (ms / 1e3),
-             "conv_TFLOPs": cf / ct / 1e12,
-             "conv_frac_of_fp32_mfma_peak": cf / ct / 1e12 / FP32_MFMA_PEAK_TFLOPS,
+             "direct_kernels_ms": ms_direct,
+             "conv_direct_form_TFLOPs": cf / ct / 1e12,
              "conv_ms_per_call": ct * 1e3 / n}
     if parity:
         from oracle import avae_oracle as O
@@ -475,7 +481,8 @@ def amp_configs(torch, avae, W, steps, parity):
     xd = torch.from_numpy(x).to(dev)
     up = avae.convtr1d(xd, td["ups.0.weight"], td["ups.0.bias"], stride=5)
     yd = torch.empty_like(up)
-    ws = torch.empty(avae.amp_block_workspace_bytes(*up.shape), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(avae.amp_block_fft_workspace_bytes(*up.shape, k, dil) for k in (3, 7, 11)),
+                     dtype=torch.uint8, device=dev)
     blists = [_amp_lists(td, f"resblocks.{j}", 3) for j in range(3)]
 
     def stage():

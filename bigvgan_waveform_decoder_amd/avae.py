@@ -129,6 +129,8 @@ def lib() -> ctypes.CDLL:
     L.avae_convtr1d.argtypes = [P, P, c_int, c_int, c_int, c_int, P, P, c_int, c_int, c_int, P]
     L.avae_amp_block_workspace_bytes.restype = c_size_t
     L.avae_amp_block_workspace_bytes.argtypes = [c_int, c_int, c_int]
+    L.avae_amp_block_fft_workspace_bytes.restype = c_size_t
+    L.avae_amp_block_fft_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int, P]
     L.avae_amp_block.restype = c_int
     L.avae_amp_block.argtypes = [P, P, c_int, c_int, c_int, c_int, c_int, P, P, P, P, P, P, P,
                                  c_float, c_int, P, c_size_t, P]
@@ -404,10 +406,18 @@ def amp_block_workspace_bytes(B: int, C: int, T: int) -> int:
     return int(lib().avae_amp_block_workspace_bytes(B, C, T))
 
 
+def amp_block_fft_workspace_bytes(B: int, C: int, T: int, K: int, dil: Sequence[int]) -> int:
+    n = len(dil)
+    dil_a = (c_int * n)(*[int(d) for d in dil])
+    return int(lib().avae_amp_block_fft_workspace_bytes(B, C, T, K, n, ctypes.addressof(dil_a)))
+
+
 def amp_block(x, K: int, dil: Sequence[int], w1: List, b1: List, w2: List, b2: List,
               log_alpha: List, log_beta: List, out_scale: float = 1.0, accumulate: bool = False,
-              out=None, workspace=None, stream=None):
-    """avae_amp_block: out = [out +] out_scale * AMP(x)."""
+              out=None, workspace=None, stream=None, fft: bool = True):
+    """avae_amp_block: out = [out +] out_scale * AMP(x).  Without a workspace,
+    one is allocated: sized for the frequency-domain convolutions if fft,
+    else for the direct ones."""
     torch = _torch()
     B, C, T = x.shape
     n = len(dil)
@@ -416,8 +426,9 @@ def amp_block(x, K: int, dil: Sequence[int], w1: List, b1: List, w2: List, b2: L
             raise ValueError("accumulate needs an existing out tensor")
         out = torch.empty_like(x)
     if workspace is None:
-        workspace = torch.empty(amp_block_workspace_bytes(B, C, T), dtype=torch.uint8,
-                                device=x.device)
+        nb = (amp_block_fft_workspace_bytes(B, C, T, K, dil) if fft
+              else amp_block_workspace_bytes(B, C, T))
+        workspace = torch.empty(nb, dtype=torch.uint8, device=x.device)
     dil_a = (c_int * n)(*[int(d) for d in dil])
     arr = lambda ts, nm, shape: (P * len(ts))(*[_opt(t, nm, shape) for t in ts])
     w1a = arr(w1, "w1", (C, C, K))

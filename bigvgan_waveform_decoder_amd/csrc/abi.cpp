@@ -102,13 +102,15 @@ bool amp_fusable(int C, int K, int n_dil, const int* dil) {
 // plan::fft_amp_use takes the shape, that
 // activation + convolution then runs as launch_conv1d_fft with the
 // activation inside its forward transforms, the spectra in t1 and t2 (slots
-// of at least plan::fft_spectrum_bytes each).
+// of at least plan::fft_spectrum_bytes each).  fpack (or null): room for one
+// convolution's frequency-domain weights, packed from w1/w2 just before use
+// where fw1/fw2 give none.
 int run_amp(const float* x, float* y, int B, int C, int T, int K, int n_dil, const int* dil,
             const float* const* w1, const float* const* b1, const float* const* w2,
             const float* const* b2, const float* const* la, const float* const* lb,
             const float* const* pw1, const float* const* pw2, const float* const* fw1,
             const float* const* fw2, float out_scale, int accumulate, float* cur, float* t1,
-            float* t2, const ActTaps& taps, hipStream_t s) {
+            float* t2, const ActTaps& taps, hipStream_t s, float* fpack = nullptr) {
     if (pw1 && pw2) {
         float* bufs[2] = {t1, t2};
         for (int q = 0; q < n_dil; ++q) {
@@ -128,12 +130,15 @@ int run_amp(const float* x, float* y, int B, int C, int T, int K, int n_dil, con
         const int d = dil[q];
         ConvEpilogue e1{b1[q], nullptr, 1.0f, 0};
         // h = conv1(act(src)) lands in t2 either way
-        const bool f1 = fw1 && fw1[q] && avae::plan::fft_amp_use(B, C, T, K, d);
-        const bool f2 = fw2 && fw2[q] && avae::plan::fft_amp_use(B, C, T, K, 1);
+        const bool f1 = ((fw1 && fw1[q]) || fpack) && avae::plan::fft_amp_use(B, C, T, K, d);
+        const bool f2 = ((fw2 && fw2[q]) || fpack) && avae::plan::fft_amp_use(B, C, T, K, 1);
         if (f1) {
+            const float* wp = (fw1 && fw1[q]) ? fw1[q] : fpack;
+            if (wp == fpack)  // this call's weights, packed just before use
+                AVAE_TRY(avae::launch_fft_pack(w1[q], fpack, C, C, K, d, s), "fft weight packing");
             // act(src) inside the transforms: spectrum in t1, product in t2,
             // output in t1
-            AVAE_TRY(avae::launch_conv1d_fft(src, t1, fw1[q], B, C, C, T, K, d, e1, t1, t2, s,
+            AVAE_TRY(avae::launch_conv1d_fft(src, t1, wp, B, C, C, T, K, d, e1, t1, t2, s,
                                              la[2 * q], lb[2 * q], &taps),
                      "act + conv1d_fft (convs1)");
         } else {
@@ -149,9 +154,12 @@ int run_amp(const float* x, float* y, int B, int C, int T, int K, int n_dil, con
         ConvEpilogue e2{b2[q], src, last ? out_scale : 1.0f, last ? accumulate : 0};
         float* dst = last ? y : cur;
         if (f2) {
+            const float* wp = (fw2 && fw2[q]) ? fw2[q] : fpack;
+            if (wp == fpack)
+                AVAE_TRY(avae::launch_fft_pack(w2[q], fpack, C, C, K, 1, s), "fft weight packing");
             // act(h) inside the transforms: spectrum in fr, product in h,
             // then dst (+ residual src)
-            AVAE_TRY(avae::launch_conv1d_fft(h, dst, fw2[q], B, C, C, T, K, 1, e2, fr, h, s,
+            AVAE_TRY(avae::launch_conv1d_fft(h, dst, wp, B, C, C, T, K, 1, e2, fr, h, s,
                                              la[2 * q + 1], lb[2 * q + 1], &taps),
                      "act + conv1d_fft (convs2)");
         } else {
@@ -355,6 +363,37 @@ extern "C" size_t avae_amp_block_workspace_bytes(int B, int C, int T) {
 }
 
 namespace {
+// Slot size and packing room of the AMP block's frequency-domain path (0, 0
+// when none of its convolutions takes it).
+void amp_fft_plan(int B, int C, int T, int K, int n_dil, const int* dil, size_t* slot,
+                  size_t* pack) {
+    *slot = 0;
+    *pack = 0;
+    size_t m = avae::plan::tensor_bytes(B, C, T);
+    bool any = false;
+    for (int q = 0; q <= n_dil; ++q) {
+        const int d = q < n_dil ? dil[q] : 1;
+        if (d < 1 || !avae::plan::fft_amp_use(B, C, T, K, d)) continue;
+        const size_t f = avae::plan::fft_spectrum_bytes(B, C, T, K, d);
+        if (f == 0 || m == 0) return;
+        m = std::max(m, f);
+        any = true;
+    }
+    if (!any) return;
+    *slot = m;
+    *pack = round_up(avae::fft_conv_weight_floats(C, C) * sizeof(float), 256);
+}
+}  // namespace
+
+extern "C" size_t avae_amp_block_fft_workspace_bytes(int B, int C, int T, int K, int n_dil,
+                                                    const int* dil) {
+    if (B < 1 || C < 1 || T < 1 || !dil || n_dil < 1 || n_dil > AVAE_MAX_DIL) return 0;
+    size_t slot, pack;
+    amp_fft_plan(B, C, T, K, n_dil, dil, &slot, &pack);
+    return slot ? 3 * slot + pack : avae_amp_block_workspace_bytes(B, C, T);
+}
+
+namespace {
 // Argument checks shared by avae_amp_block and avae_amp_block_static
 // (`who` names the entry point in the messages).
 int amp_block_check(const char* who, const float* x, const float* y, int B, int C, int T, int K,
@@ -385,8 +424,19 @@ int amp_block_run(const float* x, float* y, int B, int C, int T, int K, int n_di
                   const int* dil, const float* const* w1, const float* const* b1,
                   const float* const* w2, const float* const* b2,
                   const float* const* log_alpha, const float* const* log_beta, float out_scale,
-                  int accumulate, void* workspace, hipStream_t s) {
+                  int accumulate, void* workspace, hipStream_t s, size_t fft_slot = 0) {
     static const float* const kNull[AVAE_MAX_DIL] = {nullptr, nullptr, nullptr, nullptr};
+    if (fft_slot) {
+        // the frequency-domain path: three slots of fft_slot bytes, then one
+        // convolution's packed weights
+        char* ws = (char*)workspace;
+        avae::prof_set_phase(avae::kPhaseNone);
+        return run_amp(x, y, B, C, T, K, n_dil, dil, w1, b1 ? b1 : kNull, w2, b2 ? b2 : kNull,
+                       log_alpha, log_beta, nullptr, nullptr, nullptr, nullptr, out_scale,
+                       accumulate, (float*)ws, (float*)(ws + fft_slot),
+                       (float*)(ws + 2 * fft_slot), make_taps(nullptr, nullptr), s,
+                       (float*)(ws + 3 * fft_slot));
+    }
     const size_t slot = avae::plan::tensor_bytes(B, C, T);
     char* ws = (char*)workspace;
     float* cur = (float*)ws;
@@ -434,8 +484,13 @@ extern "C" int avae_amp_block(const float* x, float* y, int B, int C, int T, int
     if (!workspace || ws_bytes < need)
         return fail(AVAE_EWORKSPACE, "avae_amp_block: workspace %zu bytes < %zu needed", ws_bytes,
                     need);
+    // a workspace that holds the frequency-domain path's spectra and packed
+    // weights selects that path for the convolutions that take it
+    size_t fslot, fpack;
+    amp_fft_plan(B, C, T, K, n_dil, dil, &fslot, &fpack);
+    const bool fft = fslot && workspace && ws_bytes >= 3 * fslot + fpack;
     return amp_block_run(x, y, B, C, T, K, n_dil, dil, w1, b1, w2, b2, log_alpha, log_beta,
-                         out_scale, accumulate, workspace, (hipStream_t)stream);
+                         out_scale, accumulate, workspace, (hipStream_t)stream, fft ? fslot : 0);
 }
 
 // -------------------------------------------------------------------------

@@ -638,12 +638,23 @@ __global__ __launch_bounds__(kThreads, 2) void fft_gemm_kernel(const float* __re
 __global__ __launch_bounds__(256) void fft_pack_kernel(const float* __restrict__ w,
                                                        float* __restrict__ wp, int Cin, int Cout,
                                                        int K, int d) {
+    // double twiddles e^{+2 pi i m / N}, one per thread of the workgroup
+    __shared__ double2 twd[kN];
+    {
+        double sn, cs;
+        sincospi(2.0 * (double)threadIdx.x / (double)kN, &sn, &cs);
+        twd[threadIdx.x] = make_double2(cs, sn);
+    }
+    __syncthreads();
+    // thread i writes float i of one plane pair: i = (((f OT + ot) S4 + s4) 64 + ln) 4 + e
     const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
     const long long total = (long long)kSlots * Cout * Cin;
     if (i >= total) return;
-    const int c = (int)(i % Cin);
-    const int o = (int)((i / Cin) % Cout);
-    const int f = (int)(i / ((long long)Cin * Cout));
+    const int e = (int)(i & 3), ln = (int)((i >> 2) & 63);
+    const long long g = i >> 8;  // ((f OT + ot) S4 + s4)
+    const int S4 = Cin / 16, OT = Cout / 16;
+    const int s4 = (int)(g % S4), ot = (int)((g / S4) % OT), f = (int)(g / ((long long)S4 * OT));
+    const int o = ot * 16 + (ln & 15), c = s4 * 16 + e * 4 + (ln >> 4);
     const float* wr = w + ((size_t)o * Cin + c) * K;
     double re = 0.0, im = 0.0;
     for (int j = 0; j < K; ++j) {
@@ -652,16 +663,12 @@ __global__ __launch_bounds__(256) void fft_pack_kernel(const float* __restrict__
             re += wj;
             im += ((j * d) & 1) ? -wj : wj;
         } else {
-            const int m = (int)(((long long)f * j * d) % kN);
-            double s, cs;
-            sincospi(2.0 * (double)m / (double)kN, &s, &cs);
-            re += wj * cs;
-            im += wj * s;
+            const double2 t = twd[(int)(((long long)f * j * d) & (kN - 1))];
+            re = fma(wj, t.x, re);
+            im = fma(wj, t.y, im);
         }
     }
-    const int ot = o >> 4, s4 = c >> 4;
-    const int ln = (o & 15) + 16 * (c & 3), e = (c & 15) >> 2;
-    const size_t base = ((((size_t)f * (Cout / 16) + ot) * (Cin / 16) + s4) * 2) * 256 + ln * 4 + e;
+    const size_t base = (size_t)g * 512 + ln * 4 + e;
     wp[base] = (float)re;
     wp[base + 256] = (float)im;
 }
@@ -684,8 +691,12 @@ hipError_t launch_fft_pack(const float* w, float* wp, int Cin, int Cout, int K, 
                            hipStream_t s) {
     if (!plan::fft_supported(Cin, Cout, K, dilation)) return hipErrorInvalidValue;
     const long long total = (long long)kSlots * Cout * Cin;
+    prof_pre(s);
     hipLaunchKernelGGL(fft_pack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, w,
                        wp, Cin, Cout, K, dilation);
+    // reads w once, writes the 2 x 128 x Cout x Cin packed floats
+    prof_post(s, "fft_pack_kernel", 4.0 * K * (double)total,
+              4.0 * ((double)Cout * Cin * K + 2.0 * (double)total));
     return hipGetLastError();
 }
 

@@ -178,10 +178,21 @@ int avae_convtr1d(const float* x, float* y, int B, int Cin, int Cout, int Tin,
  *   arrays [2*n_dil] of device pointers to [C] (activation q's parameters).
  *   Activations use the designed taps.
  *   workspace: device, at least avae_amp_block_workspace_bytes(B, C, T).
+ *   With at least avae_amp_block_fft_workspace_bytes(B, C, T, K, n_dil, dil)
+ *   bytes (larger for the shapes that take it), the block's convolutions
+ *   whose width and taps suit the 256-point overlap-save form (as in
+ *   avae_conv1d_fft, with the activation inside its forward transforms) run
+ *   that way, their weights packed into the workspace on each call; the
+ *   result is the same up to float32 rounding.
  * Errors: EINVAL, ESHAPE (n_dil > AVAE_MAX_DIL, K even or > AVAE_MAX_TAPS),
  *         EWORKSPACE.
  */
 size_t avae_amp_block_workspace_bytes(int B, int C, int T);
+/* Workspace bytes that select the frequency-domain path (equal to
+ * avae_amp_block_workspace_bytes(B, C, T) where no convolution takes it);
+ * 0 for invalid arguments (n_dil outside [1, AVAE_MAX_DIL], null dil). */
+size_t avae_amp_block_fft_workspace_bytes(int B, int C, int T, int K, int n_dil,
+                                          const int* dil);
 int avae_amp_block(const float* x, float* y, int B, int C, int T, int K,
                    int n_dil, const int* dil,
                    const float* const* w1, const float* const* b1,

@@ -1,6 +1,7 @@
 """avae_amp_block_static (the AMP block without a workspace argument, its
 scratch a static device array of the library) against avae_amp_block with a
-caller workspace: the same kernels, so the outputs must be bit-identical.
+caller workspace of avae_amp_block_workspace_bytes (the direct kernels, which
+the static entry point runs too): the outputs must be bit-identical.
 
 Two calls in a row through the static scratch, the second on a smaller
 input (and a narrower width, so it also takes the fused one-launch-per-step
@@ -40,7 +41,7 @@ def test_static_scratch_matches_workspace_two_calls():
         announce(f"amp_block_static B={B} C={C} T={T} K={K}")
         xd, td, prefix = _case(B, C, T, K, dil, tag)
         lists = _lists(td, prefix, len(dil))
-        ref = avae.amp_block(xd, K, dil, *lists)
+        ref = avae.amp_block(xd, K, dil, *lists, fft=False)
         got = avae.amp_block_static(xd, K, dil, *lists)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(host(got), host(ref))
@@ -56,7 +57,7 @@ def test_static_scratch_accumulate_matches_workspace():
     o0 = W.normal(0, "noalloc/c/o", [B, C, T])
     ref = cuda(o0)
     got = cuda(o0)
-    avae.amp_block(xd, K, dil, *lists, out_scale=0.25, accumulate=True, out=ref)
+    avae.amp_block(xd, K, dil, *lists, out_scale=0.25, accumulate=True, out=ref, fft=False)
     avae.amp_block_static(xd, K, dil, *lists, out_scale=0.25, accumulate=True, out=got)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(got), host(ref))
