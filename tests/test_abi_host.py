@@ -184,3 +184,37 @@ def test_amp_block_static_checks_before_any_launch():
                                  ctypes.addressof(ptrs), ctypes.addressof(ptrs),
                                  ctypes.c_float(1.0), 0, None)
     assert rc == -1
+
+
+def test_amp_block_fft_workspace_sizes():
+    """The workspace size that selects the AMP block's frequency-domain
+    convolutions: the direct size where no convolution takes that path, room
+    for three spectra slots and one packed weight otherwise, 0 for invalid
+    arguments (host logic only)."""
+    L = avae.lib()
+    L.avae_amp_block_fft_workspace_bytes.restype = ctypes.c_size_t
+    L.avae_amp_block_workspace_bytes.restype = ctypes.c_size_t
+    dil = (ctypes.c_int * 3)(1, 3, 5)
+    q = lambda B, C, T, K, n=3, d=ctypes.addressof(dil): int(
+        L.avae_amp_block_fft_workspace_bytes(B, C, T, K, n, d))
+    plain = lambda B, C, T: int(L.avae_amp_block_workspace_bytes(B, C, T))
+    # narrow widths, 3 taps below 192 channels: the direct kernels only
+    assert q(2, 12, 5000, 7) == plain(2, 12, 5000)
+    assert q(2, 64, 5000, 3) == plain(2, 64, 5000)
+    # 3 taps at 512 channels on long rows, 7 taps from 48 channels: spectra
+    # of 128 slots x 2 floats per (channel, 16-padded column) in each of the
+    # three slots, plus one convolution's 256 C^2 packed floats
+    for B, C, T, K in ((2, 512, 65536, 3), (2, 48, 5000, 7), (1, 96, 9000, 11)):
+        L_blk = 256 - (K - 1) * 5
+        cols = B * -(-T // L_blk)
+        spec_lb = 256 * C * (-(-cols // 16) * 16) * 4
+        got = q(B, C, T, K)
+        assert got >= 3 * spec_lb + 256 * C * C * 4, (B, C, T, K)
+        assert got > plain(B, C, T)
+    # 3 taps on short rows (fewer than 64 columns) stay direct
+    assert q(1, 256, 2000, 3) == plain(1, 256, 2000)
+    # invalid arguments
+    assert q(0, 512, 100, 3) == 0
+    assert q(1, 512, 100, 3, n=0) == 0
+    assert q(1, 512, 100, 3, n=5) == 0
+    assert q(1, 512, 100, 3, d=None) == 0
