@@ -444,7 +444,7 @@ def amp_configs(torch, avae, W, steps, parity):
                      device=dev)
     call = lambda: avae.amp_block(xd, 3, dil, *lists, out=yd, workspace=ws)
     ms = _timed(torch, call, n)
-    kernels = _profiled(avae, call, n, 16)
+    kernels = _profiled(avae, call, n, 32)  # 6 convolutions x (packing + 3)
     B, C, T = x.shape
     convs = {k: v for k, v in kernels.items() if k.startswith(("conv1d", "fft_"))}
     cf = 6 * 2.0 * C * C * 3 * T * B * n  # direct-form multiply-adds x 2
@@ -491,7 +491,7 @@ def amp_configs(torch, avae, W, steps, parity):
             avae.amp_block(up, k, dil, *blists[j], out_scale=1.0 / 3.0, accumulate=j > 0,
                            out=yd, workspace=ws)
     ms = _timed(torch, stage, n)
-    kernels = _profiled(avae, stage, n, 48)
+    kernels = _profiled(avae, stage, n, 96)  # 1 + 18 convolutions x (packing + 3)
     B, Cin, Tin = x.shape
     _, C, T = up.shape
     flops = 2.0 * Cin * C * 10 * Tin * B + sum(6 * 2.0 * C * C * k * T * B for k in (3, 7, 11))

@@ -635,6 +635,12 @@ __global__ __launch_bounds__(kThreads, 2) void fft_gemm_kernel(const float* __re
 //   W = sum_j w[o,c,j] e^{+2 pi i f j d / N},
 // slot 0 = (sum_j w_j, sum_j (-1)^{j d} w_j) (bins 0 and N/2), summed in
 // double and rounded once, stored in fft_gemm_kernel's fragment order.
+// Workgroup: one 16 x 16 (output row, input channel) tile, kPackSlots
+// consecutive slots; thread t owns the pair at float t of the tile's 256-float
+// planes, reads its K taps once and keeps a sum per slot, and every slot's
+// two planes are written as 1 KB runs.  The twiddles come from a double
+// table in LDS, one index for the whole workgroup at a time (a broadcast).
+constexpr int kPackSlots = 16;
 __global__ __launch_bounds__(256) void fft_pack_kernel(const float* __restrict__ w,
                                                        float* __restrict__ wp, int Cin, int Cout,
                                                        int K, int d) {
@@ -646,31 +652,39 @@ __global__ __launch_bounds__(256) void fft_pack_kernel(const float* __restrict__
         twd[threadIdx.x] = make_double2(cs, sn);
     }
     __syncthreads();
-    // thread i writes float i of one plane pair: i = (((f OT + ot) S4 + s4) 64 + ln) 4 + e
-    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-    const long long total = (long long)kSlots * Cout * Cin;
-    if (i >= total) return;
-    const int e = (int)(i & 3), ln = (int)((i >> 2) & 63);
-    const long long g = i >> 8;  // ((f OT + ot) S4 + s4)
     const int S4 = Cin / 16, OT = Cout / 16;
-    const int s4 = (int)(g % S4), ot = (int)((g / S4) % OT), f = (int)(g / ((long long)S4 * OT));
+    const int ot = blockIdx.x / S4, s4 = blockIdx.x - ot * S4;
+    const int f0 = blockIdx.y * kPackSlots;
+    // float t of a (slot, ot, s4) plane: lane ln = t / 4 of k-step e = t % 4,
+    // i.e. row ot 16 + ln % 16, channel s4 16 + 4 e + ln / 16
+    const int t = threadIdx.x, e = t & 3, ln = t >> 2;
     const int o = ot * 16 + (ln & 15), c = s4 * 16 + e * 4 + (ln >> 4);
     const float* wr = w + ((size_t)o * Cin + c) * K;
-    double re = 0.0, im = 0.0;
+    double re[kPackSlots], im[kPackSlots];
+#pragma unroll
+    for (int s = 0; s < kPackSlots; ++s) re[s] = im[s] = 0.0;
     for (int j = 0; j < K; ++j) {
         const double wj = (double)wr[j];
-        if (f == 0) {
-            re += wj;
-            im += ((j * d) & 1) ? -wj : wj;
-        } else {
-            const double2 t = twd[(int)(((long long)f * j * d) & (kN - 1))];
-            re = fma(wj, t.x, re);
-            im = fma(wj, t.y, im);
+        const int jd = (j * d) & (kN - 1);
+#pragma unroll
+        for (int s = 0; s < kPackSlots; ++s) {
+            const int f = f0 + s;
+            if (f == 0) {
+                re[s] += wj;
+                im[s] = fma(wj, twd[(jd * (kN / 2)) & (kN - 1)].x, im[s]);  // (-1)^{j d}
+            } else {
+                const double2 tw = twd[(f * jd) & (kN - 1)];
+                re[s] = fma(wj, tw.x, re[s]);
+                im[s] = fma(wj, tw.y, im[s]);
+            }
         }
     }
-    const size_t base = (size_t)g * 512 + ln * 4 + e;
-    wp[base] = (float)re;
-    wp[base + 256] = (float)im;
+#pragma unroll
+    for (int s = 0; s < kPackSlots; ++s) {
+        const size_t g = ((size_t)(f0 + s) * OT + ot) * S4 + s4;
+        wp[g * 512 + t] = (float)re[s];
+        wp[g * 512 + 256 + t] = (float)im[s];
+    }
 }
 
 template <int NJ>
@@ -691,9 +705,11 @@ hipError_t launch_fft_pack(const float* w, float* wp, int Cin, int Cout, int K, 
                            hipStream_t s) {
     if (!plan::fft_supported(Cin, Cout, K, dilation)) return hipErrorInvalidValue;
     const long long total = (long long)kSlots * Cout * Cin;
+    const long long tiles = (long long)(Cout / 16) * (Cin / 16);
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
     prof_pre(s);
-    hipLaunchKernelGGL(fft_pack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, w,
-                       wp, Cin, Cout, K, dilation);
+    hipLaunchKernelGGL(fft_pack_kernel, dim3((unsigned)tiles, kSlots / kPackSlots), dim3(256), 0, s,
+                       w, wp, Cin, Cout, K, dilation);
     // reads w once, writes the 2 x 128 x Cout x Cin packed floats
     prof_post(s, "fft_pack_kernel", 4.0 * K * (double)total,
               4.0 * ((double)Cout * Cin * K + 2.0 * (double)total));
