@@ -188,3 +188,44 @@ def test_upsample_stage_workload3_full_size_sampled_windows():
         xc, off = _crop(xo, a, a + 200, m)
         ref = O.mrf(xc, blocks)[..., off:off + 200]
         assert rel_err(y[..., a:a + 200], ref) <= TOL_BLOCK, a
+
+
+def test_amp_block_frequency_domain_mrf_and_reuse():
+    """avae_amp_block on a workspace of avae_amp_block_fft_workspace_bytes:
+    at 64 channels its 7- and 11-tap convolutions run in the frequency domain
+    (weights packed into the workspace per convolution) and the 3-tap ones on
+    the direct kernels; three blocks accumulated with 1/3 (the MRF), against
+    the oracle and against the same calls on the direct path's workspace.
+    Then a smaller call (48 channels) through the same workspace."""
+    import torch
+    announce("amp block frequency-domain MRF + workspace reuse")
+    C, T = 64, 3001
+    x = W.normal(0, "fdmrf/x", [2, C, T])
+    ts, blocks = [], []
+    for j, k in enumerate((3, 7, 11)):
+        t = W.amp_tensors(0, f"fdmrf{j}", C, k, (1, 3, 5), weight_var=2.0 / (C * k))
+        ts.append(cuda_dict(t))
+        blocks.append(amp_params(t, f"fdmrf{j}", k, (1, 3, 5)))
+    nb = max(avae.amp_block_fft_workspace_bytes(2, C, T, k, (1, 3, 5)) for k in (3, 7, 11))
+    assert nb > avae.amp_block_workspace_bytes(2, C, T)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    ws_direct = torch.empty(avae.amp_block_workspace_bytes(2, C, T), dtype=torch.uint8,
+                            device="cuda")
+    xd = cuda(x)
+    ref = O.mrf(x, blocks)
+    outs = []
+    for fft in (True, False):
+        out = cuda(np.zeros((2, C, T), np.float32))
+        for j, k in enumerate((3, 7, 11)):
+            _amp_call(xd, ts[j], f"fdmrf{j}", k, (1, 3, 5), out=out, scale=1.0 / 3.0,
+                      accumulate=j > 0, ws=ws if fft else ws_direct)
+        outs.append(host(out))
+        e = rel_err(outs[-1], ref)
+        print(f"fft={fft}: max|err|/RMS = {e:.3e}", flush=True)
+        assert e <= TOL_BLOCK
+    assert not np.array_equal(outs[0], outs[1])  # the two paths did run differently
+    C2, T2 = 48, 1000
+    x2 = W.normal(0, "fdmrf/x2", [1, C2, T2])
+    t2 = W.amp_tensors(0, "fdmrf2", C2, 11, (1, 3, 5), weight_var=2.0 / (C2 * 11))
+    y2 = host(_amp_call(cuda(x2), cuda_dict(t2), "fdmrf2", 11, (1, 3, 5), ws=ws))
+    assert rel_err(y2, O.amp_block(x2, amp_params(t2, "fdmrf2", 11, (1, 3, 5)))) <= TOL_BLOCK
