@@ -41,7 +41,11 @@ def test_amp_block_workload1_full():
     assert rel_err(y, ref) <= TOL_BLOCK
 
 
-@pytest.mark.parametrize("C,T,K", [(12, 2500, 11), (48, 1031, 7), (130, 700, 3)])
+# 48 and 64 channels at 7 and 11 taps take the frequency-domain path (the
+# default workspace of amp_block holds it), down to rows of 1 and 5 samples
+# where every activation and convolution index is clamped or padded.
+@pytest.mark.parametrize("C,T,K", [(12, 2500, 11), (48, 1031, 7), (130, 700, 3), (48, 1, 11),
+                                   (64, 5, 7), (64, 207, 11)])
 def test_amp_block_odd_shapes(C, T, K):
     announce(f"amp C={C} T={T} K={K}")
     x = W.normal(0, f"amp/{C}/{T}/x", [2, C, T])
