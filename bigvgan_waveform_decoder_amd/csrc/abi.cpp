@@ -110,10 +110,14 @@ int run_amp(const float* x, float* y, int B, int C, int T, int K, int n_dil, con
             const float* const* b2, const float* const* la, const float* const* lb,
             const float* const* pw1, const float* const* pw2, const float* const* fw1,
             const float* const* fw2, float out_scale, int accumulate, float* cur, float* t1,
-            float* t2, const ActTaps& taps, hipStream_t s, float* fpack = nullptr) {
+            float* t2, const ActTaps& taps, hipStream_t s, float* fpack = nullptr,
+            int q_begin = 0, int q_end = -1) {
+    // dilation steps [q_begin, q_end) (all by default): a caller interleaving
+    // several blocks on their own streams runs them one step at a time
+    const int qe = q_end < 0 ? n_dil : std::min(q_end, n_dil);
     if (pw1 && pw2) {
         float* bufs[2] = {t1, t2};
-        for (int q = 0; q < n_dil; ++q) {
+        for (int q = q_begin; q < qe; ++q) {
             const float* src = (q == 0) ? x : bufs[(q - 1) & 1];
             const bool last = (q == n_dil - 1);
             float* dst = last ? y : bufs[q & 1];
@@ -125,7 +129,7 @@ int run_amp(const float* x, float* y, int B, int C, int T, int K, int n_dil, con
         }
         return AVAE_OK;
     }
-    for (int q = 0; q < n_dil; ++q) {
+    for (int q = q_begin; q < qe; ++q) {
         const float* src = (q == 0) ? x : cur;
         const int d = dil[q];
         ConvEpilogue e1{b1[q], nullptr, 1.0f, 0};
@@ -964,19 +968,24 @@ int decode_impl(const avae_decoder* dec, const float* latent, int B, int frames,
             float* outs[AVAE_MAX_KERNELS] = {M};
             for (int k = 1; k < c.n_kernels; ++k)
                 outs[k] = (float*)(ws + (size_t)(1 + 3 * c.n_kernels + k) * slot);
-            for (int k = 0; k < c.n_kernels; ++k) {
-                hipStream_t sk = k == 0 ? s : dec->side[k - 1];
-                float* sc = (float*)(ws + (size_t)(2 + 3 * k) * slot);
-                float* s1 = (float*)(ws + (size_t)(3 + 3 * k) * slot);
-                float* s2 = (float*)(ws + (size_t)(4 + 3 * k) * slot);
-                const bool fused = dec->pw1[i][k][0] != nullptr;
-                int rc = run_amp(X, outs[k], B, co, To, c.rb_k[k], c.n_dil, c.rb_d[k], w.w1[i][k],
-                                 w.b1[i][k], w.w2[i][k], w.b2[i][k], w.act_la[i][k],
-                                 w.act_lb[i][k], fused ? dec->pw1[i][k] : nullptr,
-                                 fused ? dec->pw2[i][k] : nullptr, dec->fw1[i][k],
-                                 dec->fw2[i][k], inv_nk, 0, sc, s1, s2, dec->taps, sk);
-                if (rc) return rc;
-            }
+            // enqueued one dilation step of every block at a time, so that no
+            // stream waits for the host to finish enqueuing the blocks before it
+            for (int q = 0; q < c.n_dil; ++q)
+                for (int k = 0; k < c.n_kernels; ++k) {
+                    hipStream_t sk = k == 0 ? s : dec->side[k - 1];
+                    float* sc = (float*)(ws + (size_t)(2 + 3 * k) * slot);
+                    float* s1 = (float*)(ws + (size_t)(3 + 3 * k) * slot);
+                    float* s2 = (float*)(ws + (size_t)(4 + 3 * k) * slot);
+                    const bool fused = dec->pw1[i][k][0] != nullptr;
+                    int rc = run_amp(X, outs[k], B, co, To, c.rb_k[k], c.n_dil, c.rb_d[k],
+                                     w.w1[i][k], w.b1[i][k], w.w2[i][k], w.b2[i][k],
+                                     w.act_la[i][k], w.act_lb[i][k],
+                                     fused ? dec->pw1[i][k] : nullptr,
+                                     fused ? dec->pw2[i][k] : nullptr, dec->fw1[i][k],
+                                     dec->fw2[i][k], inv_nk, 0, sc, s1, s2, dec->taps, sk, nullptr,
+                                     q, q + 1);
+                    if (rc) return rc;
+                }
             // join, then M = block 0 + the others (each already scaled by 1/nk)
             for (int k = 1; k < c.n_kernels; ++k) {
                 AVAE_TRY(hipEventRecord(dec->join[k - 1], dec->side[k - 1]), "join event");
