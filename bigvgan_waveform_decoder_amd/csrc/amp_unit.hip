@@ -59,10 +59,17 @@ constexpr int kUT = 256;              // threads per block (4 waves)
 // longest run length act_stage picks: 20 with MT = 1, 28 with MT = 2
 constexpr int run_max(int MT) { return MT == 1 ? 20 : 28; }
 constexpr int kLdsBudget = 80 * 1024; // two blocks per CU
-// Three blocks per CU for C <= 16: smaller time tiles (more halo work) but a
-// third co-resident block to overlap the phases; measured -20% at C = 16
-// and -5% at C = 12, slower at C = 24 (whose tiles would shrink to 160).
+// More co-resident blocks for narrower rows: smaller time tiles (more halo
+// work) but more blocks to overlap the phases.  Measured on the decoders'
+// stages, each launch alone: three blocks per CU -20% at C = 16 and -5% at
+// C = 24 against two; four blocks per CU -7% at C = 12 against three, +6%
+// at C = 16.
 constexpr int kLdsBudget3 = 53 * 1024;
+constexpr int kLdsBudget4 = 40 * 1024;
+int unit_blocks_per_cu(int C) { return C <= 12 ? 4 : C <= 24 ? 3 : 2; }
+size_t unit_lds_budget(int C) {
+    return C <= 12 ? kLdsBudget4 : C <= 24 ? kLdsBudget3 : kLdsBudget;
+}
 
 struct UnitArgs {
     const float* x;
@@ -343,7 +350,12 @@ __device__ __forceinline__ void wait_vmem() {
 }
 
 template <int MT, int NTW>
-__global__ __launch_bounds__(kUT, (MT == 1 && NTW <= 8) ? 3 : 2) void amp_unit_kernel(UnitArgs a, ActTaps taps) {
+// The register budget of up to four (MT = 1, NTW <= 6) or three (NTW <= 8 with
+// MT = 1, NTW <= 4 with MT = 2) co-resident blocks, so that the register
+// file does not undo the LDS plan.
+__global__ __launch_bounds__(kUT, (MT == 1 && NTW <= 6) ? 4
+                                  : (NTW <= 8 && (MT == 1 || NTW <= 4)) ? 3
+                                                                        : 2) void amp_unit_kernel(UnitArgs a, ActTaps taps) {
     extern __shared__ __align__(16) float lds[];
     const int C = a.C, T = a.T, K = a.K, d = a.d, TT = a.TT, SP = a.SP, SQ = a.SQ;
     const int h1 = (K - 1) * d / 2, h2 = (K - 1) / 2, H = h1 + h2 + 10;
@@ -523,14 +535,13 @@ struct UnitPlan {
     size_t lds;
 };
 
-// Largest time tile whose LDS fits two blocks per CU (three for C <= 16),
-// with the per-wave tile count NTW chosen so that conv1's time tiles fill
-// the four waves exactly.
-// The largest time tile that fits, unless the grid of B rows of T samples
-// would then be less than one resident round of blocks (two, or three for
-// C <= 16, per CU): then the largest tile that still fills one round, or the
-// smallest one (short rows, such as a single [1, 32, 4096] block).  B = 0:
-// the largest tile (the support check).
+// The largest time tile whose LDS fits unit_blocks_per_cu(C) blocks per CU
+// (four for C <= 12, three for C <= 24, else two), with the per-wave tile
+// count NTW chosen so that conv1's time tiles fill the four waves exactly,
+// unless the grid of B rows of T samples would then be less than one
+// resident round of blocks: then the largest tile that still fills one
+// round, or the smallest one (short rows, such as a single [1, 32, 4096]
+// block).  B = 0: the largest tile (the support check).
 bool plan_unit(int C, int K, int d, int B, int T, UnitPlan* p) {
     if (C < 4 || C > 32 || C % 4 != 0 || K < 1 || K % 2 == 0 || d < 1) return false;
     if ((long long)(K - 1) * d > 4096) return false;
@@ -540,7 +551,7 @@ bool plan_unit(int C, int K, int d, int B, int T, UnitPlan* p) {
     static const int kNtw2[] = {6, 5, 4, 3, 2};
     const int* list = MT == 1 ? kNtw1 : kNtw2;
     const int n = MT == 1 ? 7 : 5;
-    const long long slots = 256LL * (C <= 16 ? 3 : 2);
+    const long long slots = 256LL * unit_blocks_per_cu(C);
     bool found = false;
     for (int i = 0; i < n; ++i) {
         const int NTW = list[i];
@@ -551,7 +562,7 @@ bool plan_unit(int C, int K, int d, int B, int T, UnitPlan* p) {
         const int SP = stride16(std::max(NX + run_max(MT) + 4, N1r));
         const int SQ = stride16(N1r + 2 * h1);
         const size_t lds = ((size_t)C * (SP + SQ) + 4 * (size_t)C) * sizeof(float);
-        if (lds > (size_t)(C <= 16 ? kLdsBudget3 : kLdsBudget)) continue;
+        if (lds > unit_lds_budget(C)) continue;
         *p = UnitPlan{MT, NTW, TT, SP, SQ, lds};
         found = true;
         if (B <= 0 || (long long)B * ((T + TT - 1) / TT) >= slots) return true;
