@@ -100,6 +100,12 @@ __device__ __forceinline__ void radix4(float2 (&v)[4], int p, const LaneTwiddles
     v[3] = make_float2(s1.x - s3.y, s1.y + s3.x);  // s1 + i s3
 }
 
+// Exchange-buffer index with its low four bits XORed by 5 x bits 4..5: a
+// bijection on each 16-element block that puts the 16 lanes of every
+// 8-byte LDS access of the exchanges of fft256 (the strided stage-0 and stage-1
+// writes, the contiguous reads) on distinct banks.
+__device__ __forceinline__ int swz(int i) { return i ^ (5 * ((i >> 4) & 3)); }
+
 // Forward 256-point DFT by one wave.  Entry: lane j holds a[j + 64 r] in
 // v[r]; exit: lane j holds A[j + 64 q] in v[q].  buf is this wave's own N
 // complex of LDS.  LDS operations of one wave complete in issue order and
@@ -113,10 +119,10 @@ __device__ __forceinline__ void fft256(float2 (&v)[4], int j, float2* buf, const
         const int k = j & (Ns - 1);
         const int dst = 4 * (j - k) + k;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) buf[dst + q * Ns] = v[q];
+        for (int q = 0; q < 4; ++q) buf[swz(dst + q * Ns)] = v[q];
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = buf[j + 64 * r];
+        for (int r = 0; r < 4; ++r) v[r] = buf[swz(j + 64 * r)];
         __builtin_amdgcn_wave_barrier();
     }
     radix4(v, 3, lt);  // Ns = 64, k = j: outputs j + 64 q stay in place
