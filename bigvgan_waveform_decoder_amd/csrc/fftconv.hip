@@ -54,18 +54,27 @@ __device__ __forceinline__ float2 cmul(float2 a, float2 b) {
 __device__ __forceinline__ float2 cadd(float2 a, float2 b) { return make_float2(a.x + b.x, a.y + b.y); }
 __device__ __forceinline__ float2 csub(float2 a, float2 b) { return make_float2(a.x - b.x, a.y - b.y); }
 
-// tw[m] = exp(-2 pi i m / N), from a double-precision sine and cosine.
+// The factors of the three stages that have them (Ns = 4, 16, 64), stage by
+// stage: tw[off + (r-1) Ns + k] = exp(-2 pi i r k step / N), step =
+// N / (4 Ns), off = 0, 12, 60 (252 entries), from a double-precision sine
+// and cosine.  Laid out by k, the lanes of a wave read consecutive entries
+// (or the same one), never two entries on one LDS bank (indexed by r k step,
+// up to four lanes' distinct entries shared a bank).
 __device__ void init_twiddles(float2* tw) {
-    for (int m = threadIdx.x; m < kN; m += blockDim.x) {
+    for (int t = threadIdx.x; t < 252; t += blockDim.x) {
+        const int Ns = t < 12 ? 4 : t < 60 ? 16 : 64;
+        const int u = t - (t < 12 ? 0 : t < 60 ? 12 : 60);
+        const int r = u / Ns + 1, k = u - (r - 1) * Ns;
+        const int m = r * k * (kN / (4 * Ns));
         double s, c;
         sincospi(-2.0 * (double)m / (double)kN, &s, &c);
-        tw[m] = make_float2((float)c, (float)s);
+        tw[t] = make_float2((float)c, (float)s);
     }
 }
 
-// Lane j's twiddles for the three stages that have them (Ns = 4, 16, 64):
-// w[s][r-1] = tw[r k step], k = j mod Ns, step = N / (4 Ns).  Read once per
-// wave from the LDS table and reused for every transform of the wave.
+// Lane j's twiddles for the three stages that have them: w[s][r-1] =
+// exp(-2 pi i r k step / N), k = j mod Ns.  Read once per wave from the LDS
+// table and reused for every transform of the wave.
 struct LaneTwiddles {
     float2 w[3][3];
 };
@@ -76,9 +85,9 @@ __device__ __forceinline__ LaneTwiddles lane_twiddles(int j, const float2* tw) {
     for (int s = 0; s < 3; ++s) {
         const int Ns = 4 << (2 * s);
         const int k = j & (Ns - 1);
-        const int step = kN / (4 * Ns);
+        const int off = s == 0 ? 0 : s == 1 ? 12 : 60;
 #pragma unroll
-        for (int r = 1; r < 4; ++r) t.w[s][r - 1] = tw[r * k * step];
+        for (int r = 1; r < 4; ++r) t.w[s][r - 1] = tw[off + (r - 1) * Ns + k];
     }
     return t;
 }
@@ -262,14 +271,22 @@ __global__ __launch_bounds__(kThreads) void fft_fwd_kernel(const float* __restri
             __builtin_amdgcn_wave_barrier();
             if (p0 >= 6 && p0 + kActX - 6 <= T) {
                 // interior window: no index is clamped.  Lane l evaluates the
-                // pairs j = 4l .. 4l + 3 from xw[4l .. 4l + 9] and the outputs
-                // u = 4l .. 4l + 3 from so[4l .. 4l + 8], se[4l + 1 .. 4l + 9]
-                // (16-byte LDS windows), then one LDS transposition gives the
-                // FFT its a[j + 64 r] order.
+                // odd samples of pairs j = 4l .. 4l + 3 and the even samples of
+                // pairs 4l + 1 .. 4l + 4 from xw[4l + 1 .. 4l + 9], kept one
+                // pair apart (se[j] = s(2(q+1)) here, q = p0 - 3 + j), so that
+                // the outputs u = 4l .. 4l + 3 read both from windows
+                // so[4l .. 4l + 8], se[4l .. 4l + 8] that start on a 16-byte
+                // boundary (16-byte LDS reads; a window starting one float
+                // later is read 4 bytes at a time, two lanes to a bank); then
+                // one LDS transposition gives the FFT its a[j + 64 r] order.
                 const int j0 = 4 * lane;
                 {
                     const float4* xp = reinterpret_cast<const float4*>(xw + j0);
                     const float4 w0 = xp[0], w1 = xp[1], w2 = xp[2];
+                    // xw[4l] and xw[4l + 10 ..] are not used; marking them used
+                    // keeps the three reads whole 16-byte LDS reads (trimmed,
+                    // they become 4- and 8-byte reads that share banks)
+                    asm volatile("" : : "v"(w0.x), "v"(w2.z), "v"(w2.w));
                     const float xwin[12] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y,
                                             w1.z, w1.w, w2.x, w2.y, w2.z, w2.w};
                     float ev[4], ov[4];
@@ -278,7 +295,7 @@ __global__ __launch_bounds__(kThreads) void fft_fwd_kernel(const float* __restri
                         float e = 0.f, o = 0.f;
 #pragma unroll
                         for (int m = 0; m < 6; ++m) {
-                            e = fmaf(act.taps.up2[2 * m + 1], xwin[k + 5 - m], e);
+                            e = fmaf(act.taps.up2[2 * m + 1], xwin[k + 6 - m], e);
                             o = fmaf(act.taps.up2[2 * m], xwin[k + 6 - m], o);
                         }
                         ev[k] = snake_beta(e, alpha_rev, inv_beta);
@@ -292,7 +309,7 @@ __global__ __launch_bounds__(kThreads) void fft_fwd_kernel(const float* __restri
                         float e = 0.f, o = 0.f;
 #pragma unroll
                         for (int m = 0; m < 6; ++m) {
-                            e = fmaf(act.taps.up2[2 * m + 1], xq[2 - m], e);
+                            e = fmaf(act.taps.up2[2 * m + 1], xq[3 - m], e);
                             o = fmaf(act.taps.up2[2 * m], xq[3 - m], o);
                         }
                         se[j] = snake_beta(e, alpha_rev, inv_beta);
@@ -305,6 +322,9 @@ __global__ __launch_bounds__(kThreads) void fft_fwd_kernel(const float* __restri
                     const float4* ep = reinterpret_cast<const float4*>(se + j0);
                     const float4 o0 = op[0], o1 = op[1], o2 = op[2];
                     const float4 e0 = ep[0], e1 = ep[1], e2 = ep[2];
+                    // whole 16-byte reads, as above (only o2.x and e2.x are used)
+                    asm volatile("" : : "v"(o2.y), "v"(o2.z), "v"(o2.w), "v"(e2.y), "v"(e2.z),
+                                 "v"(e2.w));
                     const float sw[12] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y,
                                           o1.z, o1.w, o2.x, o2.y, o2.z, o2.w};
                     const float ew[12] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y,
@@ -316,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void fft_fwd_kernel(const float* __restri
 #pragma unroll
                         for (int m = 0; m < 6; ++m) {
                             acc = fmaf(act.taps.down[2 * m], sw[k + m], acc);
-                            acc = fmaf(act.taps.down[2 * m + 1], ew[k + m + 1], acc);
+                            acc = fmaf(act.taps.down[2 * m + 1], ew[k + m], acc);
                         }
                         out[k] = acc;
                     }
