@@ -597,6 +597,20 @@ __global__ __launch_bounds__(WM * WN * 64, ((KT == 11 && KC == 4) || BN == 160) 
     }
     float xr[X_PT];
     float xa = 1.f;
+    // Up to 3 taps with KC KT a multiple of 16: the chunk's k-steps go in
+    // groups of four, and in group q lane g's four steps take the flattened
+    // (channel, tap) indices f = 16 q + 4 g + t, t = 0..3 (any assignment of
+    // the indices to (step, lane group) is the same sum), so that its four
+    // weights are one aligned 16-byte LDS read; its input row for step s is
+    // channel f / KT at tap offset (f % KT) dil.
+    constexpr bool kGrouped = KT <= 3 && (KC * KT) % 16 == 0;
+    constexpr int kSlotsG = kGrouped ? KC * KT / 4 : 1;
+    int boff[kSlotsG];
+#pragma unroll
+    for (int s4 = 0; s4 < kSlotsG; ++s4) {
+        const int f = 16 * (s4 >> 2) + 4 * g + (s4 & 3);
+        boff[s4] = (f / KT) * XS + (f % KT) * dil;
+    }
 
     auto dma_one = [&](const float* wc, float* wbuf, int i) {
         if (NG % NT == 0 || i + 1 < NI || i * NT + wid * 64 < NG)  // wave-uniform
@@ -659,6 +673,38 @@ __global__ __launch_bounds__(WM * WN * 64, ((KT == 11 && KC == 4) || BN == 160) 
                         for (int cc = 0; cc < NTL; ++cc)
                             part[a][cc] = __builtin_amdgcn_mfma_f32_16x16x4f32(
                                 av[cb][a], bv[cb][cc], part[a][cc], 0, 0, 0);
+#pragma unroll
+                    for (int it = 0; it < ITEMS; ++it)
+                        if ((it * SLOTS) / (kSpread * ITEMS) == slot) {
+                            if (it < NI) dma_one(wc, Wn, it);
+                            else gx_one(xrowp, it - NI);
+                            // pin the load here: only VALU, SALU (not MFMA) and LDS
+                            // reads may be scheduled across this point
+                            __builtin_amdgcn_sched_barrier(0x106);
+                        }
+                }
+            }
+        } else if constexpr (kGrouped) {
+#pragma unroll
+            for (int q = 0; q < SLOTS / 4; ++q) {
+                f32x4 a4[MT];
+#pragma unroll
+                for (int a = 0; a < MT; ++a)
+                    a4[a] = *reinterpret_cast<const f32x4*>(Wc + (wm0 + a * 16 + l16) * WS +
+                                                            16 * q + 4 * g);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int slot = 4 * q + t;
+                    float bv[NTL];
+#pragma unroll
+                    for (int cc = 0; cc < NTL; ++cc)
+                        bv[cc] = Xc[boff[slot] + wn0 + cc * 16 + l16];
+#pragma unroll
+                    for (int a = 0; a < MT; ++a)
+#pragma unroll
+                        for (int cc = 0; cc < NTL; ++cc)
+                            part[a][cc] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                a4[a][t], bv[cc], part[a][cc], 0, 0, 0);
 #pragma unroll
                     for (int it = 0; it < ITEMS; ++it)
                         if ((it * SLOTS) / (kSpread * ITEMS) == slot) {
