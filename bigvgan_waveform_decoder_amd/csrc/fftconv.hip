@@ -546,7 +546,8 @@ __global__ __launch_bounds__(kThreads, 2) void fft_gemm_kernel(const float* __re
     __shared__ __align__(16) float2 bsA[KC * NT];
     __shared__ __align__(16) float2 bsB[KC * NT];
 
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // XCD-contiguous tile order: workgroups are dealt to the 8 XCDs round robin
     const int mt = (Cout + 63) / 64;
     const int G = ntiles * mt * kSlots;
@@ -568,14 +569,24 @@ __global__ __launch_bounds__(kThreads, 2) void fft_gemm_kernel(const float* __re
                       ((size_t)(f * OT + min(ot, OT - 1)) * S4) * 128 + lane;
     const float2* xb = xf + (size_t)f * Cin * NP + n0;
 
-    // chunk ch -> buf: float4 q = 64 i + lane of the chunk image
+    // chunk ch -> buf: float4 q = 64 i + lane of the chunk image, i = wid + 4 t;
+    // the lane's offsets inside a chunk are the same for every chunk
+    constexpr int kDmaW = (kDma + kThreads / 64 - 1) / (kThreads / 64);
+    int doff[kDmaW];
+#pragma unroll
+    for (int t = 0; t < kDmaW; ++t) {
+        const int q = 64 * (wid + (kThreads / 64) * t) + lane;
+        const int kk = q / (NT / 2), c2 = q - kk * (NT / 2);
+        doff[t] = kk * NP + 2 * c2;
+    }
     auto issue_chunk = [&](int ch, float2* buf) {
-        for (int i = wid; i < kDma; i += kThreads / 64) {
-            const int q = 64 * i + lane;
-            const int kk = q / (NT / 2), c2 = q - kk * (NT / 2);
-            __builtin_amdgcn_global_load_lds(
-                (const void*)(xb + (size_t)(KC * ch + kk) * NP + 2 * c2), (void*)(buf + 128 * i),
-                16, 0, 0);
+        const float2* cb = xb + (size_t)KC * ch * NP;
+#pragma unroll
+        for (int t = 0; t < kDmaW; ++t) {
+            const int i = wid + (kThreads / 64) * t;
+            if (i < kDma)  // wave-uniform
+                __builtin_amdgcn_global_load_lds((const void*)(cb + doff[t]),
+                                                 (void*)(buf + 128 * i), 16, 0, 0);
         }
     };
 
@@ -592,11 +603,12 @@ __global__ __launch_bounds__(kThreads, 2) void fft_gemm_kernel(const float* __re
         p3a[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const int brow = lane >> 4, bcol = lane & 15;
-    f32x4 ar, ai;
-    // one chunk: matrix work on chunk ch from Bc while chunk ch + 1 lands in Bn
-    auto step = [&](int ch, const float2* Bc, float2* Bn) {
+    // one chunk: matrix work on chunk ch from Bc (weights ar, ai) while chunk
+    // ch + 1 lands in Bn (weights nar, nai: the other register set, so no
+    // copy between chunks)
+    auto step = [&](int ch, const float2* Bc, float2* Bn, const f32x4& ar, const f32x4& ai,
+                    f32x4& nar, f32x4& nai) {
         const bool more = ch + 1 < nchunk;
-        f32x4 nar = ar, nai = ai;
         if (more) {
             issue_chunk(ch + 1, Bn);
             nar = ap[(size_t)(ch + 1) * 128];
@@ -630,17 +642,14 @@ __global__ __launch_bounds__(kThreads, 2) void fft_gemm_kernel(const float* __re
         // with Bc before it is refilled
         wait_vmem_all();
         __syncthreads();
-        ar = nar;
-        ai = nai;
     };
     issue_chunk(0, bsA);
-    ar = ap[0];
-    ai = ap[64];
+    f32x4 arE = ap[0], aiE = ap[64], arO = arE, aiO = aiE;
     wait_vmem_all();
     __syncthreads();
     for (int ch = 0; ch < nchunk; ch += 2) {
-        step(ch, bsA, bsB);
-        if (ch + 1 < nchunk) step(ch + 1, bsB, bsA);
+        step(ch, bsA, bsB, arE, aiE, arO, aiO);
+        if (ch + 1 < nchunk) step(ch + 1, bsB, bsA, arO, aiO, arE, aiE);
     }
     // D layout: lane l holds rows 4 (l / 16) + i, column l % 16 of each tile
     if (!rows_ok) return;
