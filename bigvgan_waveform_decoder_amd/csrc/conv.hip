@@ -1237,6 +1237,19 @@ __global__ __launch_bounds__(WM * WN * 64) void convtr1d_dma_kernel(
     const int nch = Cin / kKCT;
     float xr[X_PT];
     float xa = 1.f;  // Snake alpha of this thread's staged input row
+    // this thread's input offsets, clamped into the row (the loads never
+    // leave it; samples outside [0, Tin) and past the window are zeroed when
+    // stored): the same for every chunk, so no index arithmetic per chunk
+    int xoff[X_PT];
+    bool xin[X_PT];
+#pragma unroll
+    for (int k = 0; k < X_PT; ++k) {
+        const int u = xcol + k * XR;
+        const int t = xbase + u;
+        xin[k] = u < XW && t >= 0 && t < Tin;
+        xoff[k] = min(max(t, 0), Tin - 1);
+    }
+    static_assert(X_PT * XR <= XS, "unconditional input stores stay inside the row");
 
     auto dma_w = [&](int ic0, float* wbuf) {
         const float* wc = w + (size_t)ic0 * Cout * KT;
@@ -1249,14 +1262,9 @@ __global__ __launch_bounds__(WM * WN * 64) void convtr1d_dma_kernel(
     };
     auto gx = [&](int ic0) {
         const int ic = ic0 + xrow;
+        const float* xrowp = xb + (size_t)ic * Tin;
 #pragma unroll
-        for (int k = 0; k < X_PT; ++k) {
-            const int u = xcol + k * XR;
-            const int t = xbase + u;
-            float v = 0.f;
-            if (u < XW && t >= 0 && t < Tin) v = xb[(size_t)ic * Tin + t];
-            xr[k] = v;
-        }
+        for (int k = 0; k < X_PT; ++k) xr[k] = xrowp[xoff[k]];
         if (in_alpha) xa = in_alpha[ic];
     };
     auto sx = [&](float* xbuf) {
@@ -1266,10 +1274,7 @@ __global__ __launch_bounds__(WM * WN * 64) void convtr1d_dma_kernel(
             for (int k = 0; k < X_PT; ++k) xr[k] = snake_beta(xr[k], arev, inv);
         }
 #pragma unroll
-        for (int k = 0; k < X_PT; ++k) {
-            const int u = xcol + k * XR;
-            if (u < XW) xbuf[xrow * XS + u] = xr[k];
-        }
+        for (int k = 0; k < X_PT; ++k) xbuf[xrow * XS + xcol + k * XR] = xin[k] ? xr[k] : 0.f;
     };
     auto step = [&](int c, const float* Wc, const float* Xc, float* Wn, float* Xn) {
         if (c + 1 < nch) {
