@@ -1174,7 +1174,7 @@ template <int WM, int WN, int NTL, int KT, int S>
 __global__ __launch_bounds__(WM * WN * 64) void convtr1d_dma_kernel(
     const float* __restrict__ x, float* __restrict__ y, const float* __restrict__ w,
     const float* __restrict__ bias, const float* __restrict__ in_alpha, int Cin, int Cout,
-    int Tin, int Tout, int pad, int qlo, int m_tiles, int q_tiles, int nblk, int flush) {
+    int Tin, int Tout, int pad, int qlo, int m_tiles, int q_tiles, int nblk) {
     constexpr int NT = WM * WN * 64;
     static_assert(NT == 256, "256 threads");
     constexpr int BMO = 16 * WM;              // output channels per block
@@ -1276,7 +1276,14 @@ __global__ __launch_bounds__(WM * WN * 64) void convtr1d_dma_kernel(
 #pragma unroll
         for (int k = 0; k < X_PT; ++k) xbuf[xrow * XS + xcol + k * XR] = xin[k] ? xr[k] : 0.f;
     };
-    auto step = [&](int c, const float* Wc, const float* Xc, float* Wn, float* Xn) {
+    // K chunks summed on the matrix cores before each add into acc, fixed by
+    // the tap count (the host computes the same value for the poly kernel).
+    // With one or two the add sits at a fixed place in the two-chunk loop
+    // body, so part stays in the accumulation registers across chunks
+    // instead of being copied out and back each chunk (k=11 s=5: 266 ->
+    // 257 us at 1536 -> 768 channels, same sums in the same order).
+    constexpr int FL = 24 / (NTAP * (kKCT / 4)) > 0 ? 24 / (NTAP * (kKCT / 4)) : 1;
+    auto step = [&](int c, const float* Wc, const float* Xc, float* Wn, float* Xn, bool fl) {
         if (c + 1 < nch) {
             dma_w((c + 1) * kKCT, Wn);
             gx((c + 1) * kKCT);
@@ -1344,7 +1351,7 @@ __global__ __launch_bounds__(WM * WN * 64) void convtr1d_dma_kernel(
                 }
             }
         }
-        if ((c + 1) % flush == 0 || c + 1 == nch) {
+        if (fl) {
 #pragma unroll
             for (int r = 0; r < S; ++r)
 #pragma unroll
@@ -1363,8 +1370,21 @@ __global__ __launch_bounds__(WM * WN * 64) void convtr1d_dma_kernel(
     sx(XsA);
     __syncthreads();
     for (int c = 0; c < nch; c += 2) {
-        step(c, WsA, XsA, WsB, XsB);
-        if (c + 1 < nch) step(c + 1, WsB, XsB, WsA, XsA);
+        if constexpr (FL <= 2) {
+            step(c, WsA, XsA, WsB, XsB, FL == 1);
+            if (c + 1 < nch) step(c + 1, WsB, XsB, WsA, XsA, true);
+        } else {
+            step(c, WsA, XsA, WsB, XsB, (c + 1) % FL == 0 || c + 1 == nch);
+            if (c + 1 < nch)
+                step(c + 1, WsB, XsB, WsA, XsA, (c + 2) % FL == 0 || c + 2 == nch);
+        }
+    }
+    if constexpr (FL == 2) {
+        // an odd chunk count leaves the last chunk in part (else part is 0)
+#pragma unroll
+        for (int r = 0; r < S; ++r)
+#pragma unroll
+            for (int cc = 0; cc < NTL; ++cc) acc[r][cc] += part[r][cc];
     }
 
     float* yb = y + (size_t)b * Cout * Tout;
@@ -1419,7 +1439,7 @@ hipError_t run_convtr1d_poly(const float* x, float* y, const float* w, const flo
     if (dma)
         hipLaunchKernelGGL((convtr1d_dma_kernel<WM, WN, NTL, KT, S>), dim3((unsigned)nblk),
                            dim3(WM * WN * 64), 0, stream, x, y, w, bias, in_alpha, Cin, Cout, Tin,
-                           Tout, pad, qlo, m_tiles, q_tiles, (int)nblk, flush);
+                           Tout, pad, qlo, m_tiles, q_tiles, (int)nblk);
     else
         hipLaunchKernelGGL((convtr1d_poly_kernel<WM, WN, NTL, KT, S>), dim3((unsigned)nblk),
                            dim3(WM * WN * 64), 0, stream, x, y, w, bias, in_alpha, Cin, Cout, Tin,
