@@ -481,6 +481,13 @@ hipError_t run_conv1d_pipe(const float* x, float* y, const float* w, int B, int 
     return e;
 }
 
+// Waits for every vector-memory operation of this wave, LDS DMA included
+// (s_waitcnt vmcnt(0), expcnt and lgkmcnt left at their maxima).  Put before
+// the barrier that publishes a DMA-staged buffer: the barrier alone does not
+// wait for the DMA, and whether the compiler adds the wait depends on the
+// schedule (a build with a different register budget dropped it).
+__device__ __forceinline__ void wait_dma_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Conv1d with the weight tiles staged by LDS DMA (global_load_lds_dwordx4:
 // each lane's 16 bytes go straight from global memory to LDS, no registers,
 // no LDS store instructions) into two LDS buffers, so the next K chunk's
@@ -757,6 +764,7 @@ __global__ __launch_bounds__(WM * WN * 64, ((KT == 11 && KC == 4) || BN == 160) 
                 }
         }
         sx(Xn);
+        wait_dma_all();
         __syncthreads();
     };
 
@@ -768,6 +776,7 @@ __global__ __launch_bounds__(WM * WN * 64, ((KT == 11 && KC == 4) || BN == 160) 
 #pragma unroll
         for (int r = 0; r < X_PT; ++r) gx_one(xrowp, r);
         sx(XsA);
+        wait_dma_all();
         __syncthreads();
     }
     for (int c = 0; c < nch; c += 2) {
@@ -1361,13 +1370,15 @@ __global__ __launch_bounds__(WM * WN * 64) void convtr1d_dma_kernel(
                 }
         }
         if (c + 1 < nch) sx(Xn);
-        // the barrier also waits for this wave's DMA of chunk c+1
+        // this wave's DMA of chunk c+1 has landed
+        wait_dma_all();
         __syncthreads();
     };
 
     dma_w(0, WsA);
     gx(0);
     sx(XsA);
+    wait_dma_all();
     __syncthreads();
     for (int c = 0; c < nch; c += 2) {
         if constexpr (FL <= 2) {
